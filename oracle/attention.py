@@ -1,0 +1,84 @@
+"""Decode attention oracle (fp64): materialise, then textbook softmax attention.
+
+Agentrix README (gitlink.org.cn page, section "前缀复用与 ForkAttention" and the CUDA
+ForkAttention item under "初赛基础与决赛演进"): branches that decode together split
+their context into a public and a private segment by the actual cache pages, reuse
+the loaded public K/V for several queries, then merge each branch's results.  What
+that computes is, per branch, ordinary attention over the branch's whole visible
+context; the oracle computes exactly that definition, by copying every visible K/V
+row out of its page pool into a contiguous array first (no sharing, no splitting).
+
+Readings:
+  * visible context = the sequence's own tokens in order, then each mount's token
+    range (Octopus page, "Attention-Only KV Mounting": a thread reads a sibling's
+    terminal KV block directly);
+  * grouped-query mapping: query head h reads KV head h // (Hq / Hkv);
+  * output O = softmax(scale * K q) V, LSE = natural log of the softmax normaliser
+    plus the max;
+  * a row with no keys has O = 0 and LSE = -inf.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
+    """One query row against n keys.  q [d], k [n, d], v [n, d] -> (o [d], lse)."""
+    q = np.asarray(q, np.float64)
+    if k.shape[0] == 0:
+        return np.zeros(q.shape[-1]), -np.inf
+    s = scale * (np.asarray(k, np.float64) @ q)
+    m = s.max()
+    p = np.exp(s - m)
+    l = p.sum()
+    return (p @ np.asarray(v, np.float64)) / l, m + np.log(l)
+
+
+def attend_heads(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
+    """q [Hq, d]; k, v [n, Hkv, d] -> (o [Hq, d], lse [Hq]) with head h reading KV head
+    h // (Hq / Hkv)."""
+    hq, d = q.shape
+    hkv = k.shape[1]
+    assert hq % hkv == 0
+    g = hq // hkv
+    o = np.zeros((hq, d))
+    lse = np.zeros(hq)
+    for h in range(hq):
+        o[h], lse[h] = attend(q[h], k[:, h // g, :], v[:, h // g, :], scale)
+    return o, lse
+
+
+def partial(q, k, v, scale):
+    """Partial softmax state of one query over a key subset: (m, l, o_unnormalised)."""
+    if k.shape[0] == 0:
+        return -np.inf, 0.0, np.zeros(np.asarray(q).shape[-1])
+    s = scale * (np.asarray(k, np.float64) @ np.asarray(q, np.float64))
+    m = s.max()
+    p = np.exp(s - m)
+    return m, p.sum(), p @ np.asarray(v, np.float64)
+
+
+def merge(parts):
+    """Log-sum-exp merge of partial states (m_i, l_i, o_i):
+    M = max m_i, L = sum l_i e^(m_i - M), O = sum o_i e^(m_i - M) / L, LSE = M + ln L.
+    Empty parts (m = -inf) contribute nothing."""
+    parts = [p for p in parts if np.isfinite(p[0])]
+    if not parts:
+        return None, -np.inf
+    M = max(p[0] for p in parts)
+    L = sum(p[1] * np.exp(p[0] - M) for p in parts)
+    O = sum(p[2] * np.exp(p[0] - M) for p in parts)
+    return O / L, M + np.log(L)
+
+
+def decode(table, seqs, q: np.ndarray, scale: float):
+    """Decode for every listed sequence of an oracle ``PageTable`` (with data).
+
+    q [n, Hq, d] (fp64) -> (o [n, Hq, d], lse [n, Hq])."""
+    n, hq, d = q.shape
+    o = np.zeros((n, hq, d))
+    lse = np.zeros((n, hq))
+    for i, sid in enumerate(seqs):
+        k, v = table.materialise(sid)
+        o[i], lse[i] = attend_heads(np.asarray(q[i], np.float64), k, v, scale)
+    return o, lse

@@ -1,0 +1,110 @@
+"""Packed DAG prefill oracle (fp64).
+
+Octopus (zicq.com page), "Packed DAG-GRPO": all branches of an episode are packed
+into one block-sparse attention whose mask encodes causality inside a thread, the
+allowed cross-thread read edges and the synchronisation dependencies; only block
+pairs the DAG allows are computed (the cost paragraph of that section).
+
+The oracle works at token level from the rule itself, never from a block list:
+  * a query in segment S at packed index i sees every token of S's ancestor
+    segments, the tokens of S at index <= i, and every edge range whose target
+    is S (the edge's source is earlier in sync order, hence complete);
+  * attention per row is dense softmax over the visible keys, in fp64.
+
+Block counts (what a block-sparse kernel must visit) are derived from the same
+token rule: a (query block, key block) pair is needed iff any of its token pairs
+is visible.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _segment_of(segments: np.ndarray, T: int) -> np.ndarray:
+    seg = np.full(T, -1, np.int64)
+    for sidx, (st, ln, _par) in enumerate(segments):
+        seg[st:st + ln] = sidx
+    return seg
+
+
+def visible_ranges(segments: np.ndarray, edges: np.ndarray, sidx: int):
+    """Key ranges (start, end) visible to every query of segment `sidx`, excluding the
+    segment's own causal part."""
+    out = []
+    par = int(segments[sidx][2])
+    while par >= 0:
+        st, ln, pp = (int(x) for x in segments[par])
+        out.append((st, st + ln))
+        par = pp
+    for src, off, ln, dst in edges:
+        if int(dst) == sidx:
+            st = int(segments[src][0]) + int(off)
+            out.append((st, st + int(ln)))
+    return out
+
+
+def visible_mask_row(segments, edges, T: int, i: int, seg_of=None) -> np.ndarray:
+    seg_of = _segment_of(segments, T) if seg_of is None else seg_of
+    s = int(seg_of[i])
+    row = np.zeros(T, bool)
+    for a, b in visible_ranges(segments, edges, s):
+        row[a:b] = True
+    row[int(segments[s][0]):i + 1] = True
+    return row
+
+
+def visible_mask(segments, edges, T: int) -> np.ndarray:
+    """Dense token mask [T, T] (small T only)."""
+    seg_of = _segment_of(segments, T)
+    return np.stack([visible_mask_row(segments, edges, T, i, seg_of) for i in range(T)])
+
+
+def visible_count(segments, edges, T: int) -> int:
+    """Number of visible (query, key) token pairs, counted row by row from the rule."""
+    seg_of = _segment_of(segments, T)
+    total = 0
+    for s, (st, ln, _p) in enumerate(segments):
+        row = np.zeros(T, bool)
+        for a, b in visible_ranges(segments, edges, s):
+            row[a:b] = True
+        fixed = int(row[:st].sum() + row[st + ln:].sum())  # ranges never overlap the own part
+        total += fixed * int(ln) + int(ln) * (int(ln) + 1) // 2
+    return total
+
+
+def block_pairs(segments, edges, T: int, block: int) -> np.ndarray:
+    """Boolean [nb, nb]: query block qb needs key block kb iff some token pair is visible."""
+    nb = -(-T // block)
+    seg_of = _segment_of(segments, T)
+    need = np.zeros((nb, nb), bool)
+    for qb in range(nb):
+        acc = np.zeros(T, bool)
+        for i in range(qb * block, min(T, (qb + 1) * block)):
+            acc |= visible_mask_row(segments, edges, T, i, seg_of)
+        pad = np.zeros(nb * block, bool)
+        pad[:T] = acc
+        need[qb] = pad.reshape(nb, block).any(axis=1)
+    return need
+
+
+def attend_rows(q, k, v, segments, edges, rows, scale: float):
+    """Dense masked attention for the listed query rows.
+
+    q [T, Hq, d], k/v [T, Hkv, d] (fp64) -> o [len(rows), Hq, d], lse [len(rows), Hq]."""
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    g = hq // hkv
+    seg_of = _segment_of(segments, T)
+    o = np.zeros((len(rows), hq, d))
+    lse = np.zeros((len(rows), hq))
+    for r, i in enumerate(rows):
+        idx = np.nonzero(visible_mask_row(segments, edges, T, int(i), seg_of))[0]
+        for h in range(hq):
+            kk = k[idx, h // g, :]
+            s = scale * (kk @ q[i, h])
+            m = s.max()
+            p = np.exp(s - m)
+            l = p.sum()
+            o[r, h] = (p @ v[idx, h // g, :]) / l
+            lse[r, h] = m + np.log(l)
+    return o, lse
