@@ -1,0 +1,147 @@
+"""Benchmark: one step = one fork_attn_decode over every branch of the shared-prefix fork
+workload (16 branches x 32 query heads, 8 KV heads, d=128, bf16, 32,768-token shared
+prefix + 2,048 private tokens per branch, page 16), inputs resident in HBM.
+
+Prints ONE JSON line.  `value` = branch-tokens/s (branches decoded per second); the
+roofline object prices the step against MI355X's 8 TB/s HBM with the algorithmic bytes
+(unique KV bytes + Q + O), timed with HIP events on the launch stream.  Steps rotate over
+several identical pool copies so that no step finds its KV in the 256 MB last-level
+cache left behind by the previous one.  The cpu_baseline leg times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fork-decode branch-tokens/s + achieved HBM GB/s (% of peak); DAG-prefill % MFMA peak"
+HBM_PEAK_GBPS = 8000.0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4, help="pool copies rotated between steps")
+    ap.add_argument("--workload", default="shared_prefix_fork_decode",
+                    choices=["shared_prefix_fork_decode", "octopus_dag_decode", "tiny_fork_decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on "
+              f"a single MI355X; see DESIGN.md for how the path would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import workloads as W
+    import fork_attention_decode_amd as fa
+    from tests.harness import build_device_pool, to_torch
+
+    torch.cuda.set_device(0)
+    sc = W.WORKLOADS[args.workload]()
+    print(f"[bench] workload {args.workload}: building {args.copies} pool copies", file=sys.stderr, flush=True)
+    pools = [build_device_pool(sc)[0] for _ in range(args.copies)]
+    q = to_torch(sc.q, sc.dtype)
+    n_br, hq, d = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty((n_br, hq), dtype=torch.float32, device=q.device)
+    wss = []
+    for p in pools:
+        need = fa.fork_attn_workspace_size(p.handle, sc.queries, hq)
+        wss.append(torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device))
+    stats = pools[0].plan_stats()
+    es = 2 if sc.dtype == "bf16" else 4
+    alg_bytes = stats["unique_kv_bytes"] + 2 * q.numel() * es  # + Q read + O written
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        p = pools[i % len(pools)]
+        ws = wss[i % len(pools)]
+        fa.fork_attn_decode(p.handle, sc.queries, hq, q.data_ptr(), out.data_ptr(), lse.data_ptr(), sc.sm_scale,
+                            ws.data_ptr(), ws.numel(), stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_step = wall * 1e3 / args.steps
+    t_kernel = float(np.mean(ev_ms)) * 1e-3
+    achieved = alg_bytes / t_kernel / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": n_br / (ms_step * 1e-3),
+        "unit": "branch-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sc.dtype,
+        "data": "synthetic (seeded N(0,1) Q/V, K/sqrt(d), RoPE theta 1e6 pre-applied; no weights)",
+        "config": {"workload": args.workload, "branches": n_br, "q_heads": hq, "kv_heads": sc.n_kv_heads,
+                   "head_dim": d, "page_size": sc.page_size, "pool_copies_rotated": args.copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "fork_attn_decode step (decode_kernel + merge_kernel)",
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "event_ms_mean": float(np.mean(ev_ms)), "event_ms_p10": float(np.percentile(ev_ms, 10)),
+                     "event_ms_p90": float(np.percentile(ev_ms, 90))},
+        "plan": stats,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(sc, args.cpu_budget)
+    print(json.dumps(result))
+
+
+def cpu_baseline(sc, budget_s):
+    """Time the fp64 oracle on a bounded sample of the same workload: branches are decoded
+    one at a time until `budget_s` of oracle work has been spent."""
+    import numpy as np
+    import workloads as W
+    from oracle import attention as att, pagetable as pt
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    print("[bench] cpu baseline: oracle replay", file=sys.stderr, flush=True)
+    table, _ = pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, sc.dtype))
+    q = W.storage_to_f64(sc.q, sc.dtype)
+    done = 0
+    t0 = time.perf_counter()
+    for i, sid in enumerate(sc.queries):
+        att.decode(table, [sid], q[i:i + 1], sc.sm_scale)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": done / t, "unit": "branch-tokens/s", "cores": blas_threads or cores, "kind": "oracle",
+            "host_cores_visible": cores,
+            "sample": f"{done} of {len(sc.queries)} branches decoded by the fp64 materialising oracle "
+                      f"({t:.1f} s; pool replay excluded)"}
+
+
+if __name__ == "__main__":
+    main()

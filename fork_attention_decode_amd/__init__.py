@@ -1,0 +1,419 @@
+"""Python binding of libforkattn.so -- attention over a shared, paged KV-state DAG on MI355X.
+
+Argument marshalling only: every step of the hot path runs in the library's HIP kernels
+(gfx950).  Functions carry the C ABI's names (see include/forkattn.h); PyTorch is used
+for device memory and streams.  Importing this package fails loudly when the library
+has not been built (``python -m fork_attention_decode_amd.build``); there is no CPU
+fallback.
+
+``Pool`` is a convenience holder of the torch buffers a pool needs.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libforkattn.so")
+
+KV_OK, KV_ERR_INVALID, KV_ERR_OOM, KV_ERR_NOT_FOUND, KV_ERR_HIP, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE = (
+    0, -1, -2, -3, -4, -5, -6)
+KV_BF16, KV_F32 = 0, 1
+KV_ROPE_NONE, KV_ROPE_NEOX = 0, 1
+KV_DROP_REPOS = 1
+
+
+class ForkAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {status} ({msg})")
+        self.status = status
+
+
+class kv_pool_config(C.Structure):
+    _fields_ = [("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("page_size", C.c_int32),
+                ("n_pages", C.c_int32), ("dtype", C.c_int32), ("rope_style", C.c_int32),
+                ("rope_theta", C.c_double)]
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m fork_attention_decode_amd.build`")
+    return C.CDLL(LIB_PATH)
+
+
+lib = _load()
+
+_P = C.c_void_p
+_i32, _i64, _sz = C.c_int32, C.c_int64, C.c_size_t
+_pi32, _pi64, _psz = C.POINTER(C.c_int32), C.POINTER(C.c_int64), C.POINTER(C.c_size_t)
+_SIGS = {
+    "kv_pool_bytes": [C.POINTER(kv_pool_config), _psz],
+    "kv_pool_workspace_size": [C.POINTER(kv_pool_config), _psz],
+    "kv_pool_create": [C.POINTER(kv_pool_config), _P, _P, _P, _sz, C.POINTER(_P)],
+    "kv_pool_destroy": [_P],
+    "kv_seq_create": [_P, _pi32],
+    "kv_append": [_P, _i32, _i64, _P, _P, _pi64, _P],
+    "kv_write": [_P, _i32, _i64, _i64, _P, _P, _P],
+    "kv_fork": [_P, _i32, _pi32],
+    "kv_mount": [_P, _i32, _i32, _i64, _i64],
+    "kv_drop": [_P, _i32, _pi64, _pi64, _i32, _i32, _pi64, _P],
+    "kv_repos": [_P, _i32, _P],
+    "kv_rewind": [_P, _i32, _i64],
+    "kv_commit": [_P, _i32],
+    "kv_release": [_P, _i32],
+    "kv_seq_info": [_P, _i32, _pi64, _pi64, _pi32, _pi32],
+    "kv_block_table": [_P, _i32, _pi32, _i32],
+    "kv_positions": [_P, _i32, _pi64, _i64],
+    "kv_page_refcount": [_P, _i32, _pi32],
+    "kv_free_pages": [_P, _pi32],
+    "kv_pool_read_page": [_P, _i32, _i32, _P, _P, _P],
+    "kv_pool_sync_status": [_P, _P, _pi32],
+    "fork_attn_workspace_size": [_P, _pi32, _i32, _i32, _psz],
+    "fork_attn_decode": [_P, _pi32, _i32, _i32, _P, _P, _P, C.c_float, _P, _sz, _P],
+    "fork_attn_plan_stats": [_P, _pi64, _i32],
+    "dag_mask_build": [_pi32, _i32, _pi32, _i32, _i32, _i32, _pi32, _pi32, C.POINTER(C.c_uint8), _pi64],
+    "dag_attn_workspace_size": [_i32, _i32, _i32, _i32, _psz],
+    "dag_attn_prefill": [_P, _P, _P, _P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, _i32, C.c_float, _P, _sz, _P],
+}
+EXPORTED = sorted(list(_SIGS) + ["kv_status_str", "kv_last_error"])
+for _name, _args in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.argtypes = _args
+    _f.restype = C.c_int
+lib.kv_status_str.argtypes = [C.c_int]
+lib.kv_status_str.restype = C.c_char_p
+lib.kv_last_error.argtypes = [_P]
+lib.kv_last_error.restype = C.c_char_p
+
+
+def kv_status_str(status: int) -> str:
+    return lib.kv_status_str(status).decode()
+
+
+def kv_last_error(pool: Optional[int] = None) -> str:
+    return lib.kv_last_error(pool).decode()
+
+
+def _check(fn: str, status: int, pool=None):
+    if status != KV_OK:
+        raise ForkAttnError(fn, status, f"{kv_status_str(status)}: {kv_last_error(pool)}")
+
+
+def _i64arr(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int64))
+
+
+def _ptr(a: np.ndarray, ct):
+    return a.ctypes.data_as(C.POINTER(ct))
+
+
+# ------------------------------------------------------------------ C ABI, same names
+def make_config(n_kv_heads, head_dim, n_pages, dtype=KV_BF16, page_size=16, rope_theta=0.0) -> kv_pool_config:
+    return kv_pool_config(n_kv_heads, head_dim, page_size, n_pages, dtype,
+                          KV_ROPE_NEOX if rope_theta else KV_ROPE_NONE, float(rope_theta))
+
+
+def kv_pool_bytes(cfg: kv_pool_config) -> int:
+    out = C.c_size_t()
+    _check("kv_pool_bytes", lib.kv_pool_bytes(C.byref(cfg), C.byref(out)))
+    return out.value
+
+
+def kv_pool_workspace_size(cfg: kv_pool_config) -> int:
+    out = C.c_size_t()
+    _check("kv_pool_workspace_size", lib.kv_pool_workspace_size(C.byref(cfg), C.byref(out)))
+    return out.value
+
+
+def kv_pool_create(cfg: kv_pool_config, k_pages: int = 0, v_pages: int = 0, workspace: int = 0,
+                   ws_bytes: int = 0) -> int:
+    h = C.c_void_p()
+    _check("kv_pool_create", lib.kv_pool_create(C.byref(cfg), k_pages or None, v_pages or None,
+                                                workspace or None, ws_bytes, C.byref(h)))
+    return h.value
+
+
+def kv_pool_destroy(pool: int):
+    _check("kv_pool_destroy", lib.kv_pool_destroy(pool), None)
+
+
+def kv_seq_create(pool: int) -> int:
+    s = C.c_int32()
+    _check("kv_seq_create", lib.kv_seq_create(pool, C.byref(s)), pool)
+    return s.value
+
+
+def kv_append(pool: int, seq: int, n: int, k: int = 0, v: int = 0, positions=None, stream: int = 0):
+    pos = None if positions is None else _i64arr(positions)
+    _check("kv_append", lib.kv_append(pool, seq, n, k or None, v or None,
+                                      None if pos is None else _ptr(pos, C.c_int64), stream or None), pool)
+
+
+def kv_write(pool: int, seq: int, start: int, n: int, k: int = 0, v: int = 0, stream: int = 0):
+    _check("kv_write", lib.kv_write(pool, seq, start, n, k or None, v or None, stream or None), pool)
+
+
+def kv_fork(pool: int, parent: int) -> int:
+    s = C.c_int32()
+    _check("kv_fork", lib.kv_fork(pool, parent, C.byref(s)), pool)
+    return s.value
+
+
+def kv_mount(pool: int, dst: int, src: int, begin: int, length: int):
+    _check("kv_mount", lib.kv_mount(pool, dst, src, begin, length), pool)
+
+
+def kv_drop(pool: int, seq: int, spans: Sequence[Tuple[int, int]], flags: int = 0, stream: int = 0) -> np.ndarray:
+    n_tok = kv_seq_info(pool, seq)[0]
+    b = _i64arr([s[0] for s in spans]) if len(spans) else np.zeros(1, np.int64)
+    L = _i64arr([s[1] for s in spans]) if len(spans) else np.zeros(1, np.int64)
+    kept = np.zeros(max(1, n_tok), np.int64)
+    _check("kv_drop", lib.kv_drop(pool, seq, _ptr(b, C.c_int64), _ptr(L, C.c_int64), len(spans), flags,
+                                  _ptr(kept, C.c_int64), stream or None), pool)
+    return kept[:kv_seq_info(pool, seq)[0]].copy()
+
+
+def kv_repos(pool: int, seq: int, stream: int = 0):
+    _check("kv_repos", lib.kv_repos(pool, seq, stream or None), pool)
+
+
+def kv_rewind(pool: int, seq: int, new_len: int):
+    _check("kv_rewind", lib.kv_rewind(pool, seq, new_len), pool)
+
+
+def kv_commit(pool: int, seq: int):
+    _check("kv_commit", lib.kv_commit(pool, seq), pool)
+
+
+def kv_release(pool: int, seq: int):
+    _check("kv_release", lib.kv_release(pool, seq), pool)
+
+
+def kv_seq_info(pool: int, seq: int) -> Tuple[int, int, int, int]:
+    n, p, np_, nm = C.c_int64(), C.c_int64(), C.c_int32(), C.c_int32()
+    _check("kv_seq_info", lib.kv_seq_info(pool, seq, C.byref(n), C.byref(p), C.byref(np_), C.byref(nm)), pool)
+    return n.value, p.value, np_.value, nm.value
+
+
+def kv_block_table(pool: int, seq: int) -> np.ndarray:
+    n_pages = kv_seq_info(pool, seq)[2]
+    out = np.zeros(max(1, n_pages), np.int32)
+    _check("kv_block_table", lib.kv_block_table(pool, seq, _ptr(out, C.c_int32), n_pages), pool)
+    return out[:n_pages].copy()
+
+
+def kv_positions(pool: int, seq: int) -> np.ndarray:
+    n = kv_seq_info(pool, seq)[0]
+    out = np.zeros(max(1, n), np.int64)
+    _check("kv_positions", lib.kv_positions(pool, seq, _ptr(out, C.c_int64), n), pool)
+    return out[:n].copy()
+
+
+def kv_page_refcount(pool: int, page: int) -> int:
+    rc = C.c_int32()
+    _check("kv_page_refcount", lib.kv_page_refcount(pool, page, C.byref(rc)), pool)
+    return rc.value
+
+
+def kv_free_pages(pool: int) -> int:
+    n = C.c_int32()
+    _check("kv_free_pages", lib.kv_free_pages(pool, C.byref(n)), pool)
+    return n.value
+
+
+def kv_pool_read_page(pool: int, page: int, head: int, k_out: np.ndarray, v_out: np.ndarray, stream: int = 0):
+    _check("kv_pool_read_page", lib.kv_pool_read_page(pool, page, head, k_out.ctypes.data, v_out.ctypes.data,
+                                                      stream or None), pool)
+
+
+def kv_pool_sync_status(pool: int, stream: int = 0) -> int:
+    n = C.c_int32()
+    _check("kv_pool_sync_status", lib.kv_pool_sync_status(pool, stream or None, C.byref(n)), pool)
+    return n.value
+
+
+def fork_attn_workspace_size(pool: int, seqs: Sequence[int], n_q_heads: int) -> int:
+    s = np.ascontiguousarray(np.asarray(seqs, np.int32))
+    out = C.c_size_t()
+    _check("fork_attn_workspace_size", lib.fork_attn_workspace_size(pool, _ptr(s, C.c_int32), len(s), n_q_heads,
+                                                                    C.byref(out)), pool)
+    return out.value
+
+
+def fork_attn_decode(pool: int, seqs: Sequence[int], n_q_heads: int, q: int, out: int, lse: int,
+                     sm_scale: float, workspace: int, ws_bytes: int, stream: int = 0):
+    s = np.ascontiguousarray(np.asarray(seqs, np.int32))
+    _check("fork_attn_decode", lib.fork_attn_decode(pool, _ptr(s, C.c_int32), len(s), n_q_heads, q, out,
+                                                    lse or None, sm_scale, workspace, ws_bytes, stream or None),
+           pool)
+
+
+def fork_attn_plan_stats(pool: int) -> dict:
+    out = np.zeros(6, np.int64)
+    _check("fork_attn_plan_stats", lib.fork_attn_plan_stats(pool, _ptr(out, C.c_int64), 6), pool)
+    keys = ["segments", "items", "chunks", "partials", "unique_kv_bytes", "rows"]
+    return dict(zip(keys, (int(x) for x in out)))
+
+
+def dag_mask_build(segments, edges, T: int, block: int = 64):
+    seg = np.ascontiguousarray(np.asarray(segments, np.int32).reshape(-1, 3))
+    ed = np.ascontiguousarray(np.asarray(edges, np.int32).reshape(-1, 4))
+    if ed.size == 0:
+        ed = np.zeros((1, 4), np.int32)
+    n_edges = 0 if np.asarray(edges).size == 0 else len(ed)
+    nb = -(-T // block)
+    row_ptr = np.zeros(nb + 1, np.int32)
+    nnz = C.c_int64()
+    _check("dag_mask_build", lib.dag_mask_build(_ptr(seg, C.c_int32), len(seg), _ptr(ed, C.c_int32), n_edges, T,
+                                                block, _ptr(row_ptr, C.c_int32), None, None, C.byref(nnz)))
+    col = np.zeros(max(1, nnz.value), np.int32)
+    kind = np.zeros(max(1, nnz.value), np.uint8)
+    _check("dag_mask_build", lib.dag_mask_build(_ptr(seg, C.c_int32), len(seg), _ptr(ed, C.c_int32), n_edges, T,
+                                                block, _ptr(row_ptr, C.c_int32), _ptr(col, C.c_int32),
+                                                _ptr(kind, C.c_uint8), C.byref(nnz)))
+    return row_ptr, col[:nnz.value].copy(), kind[:nnz.value].copy()
+
+
+def dag_attn_workspace_size(T: int, n_q_heads: int, n_kv_heads: int, block: int = 64) -> int:
+    out = C.c_size_t()
+    _check("dag_attn_workspace_size", lib.dag_attn_workspace_size(T, n_q_heads, n_kv_heads, block, C.byref(out)))
+    return out.value
+
+
+def dag_attn_prefill(q: int, k: int, v: int, out: int, lse: int, T: int, n_q_heads: int, n_kv_heads: int,
+                     head_dim: int, row_ptr: int, col: int, kind: int, block: int, sm_scale: float,
+                     workspace: int, ws_bytes: int, stream: int = 0):
+    _check("dag_attn_prefill", lib.dag_attn_prefill(q, k, v, out, lse or None, T, n_q_heads, n_kv_heads, head_dim,
+                                                    row_ptr, col, kind, block, sm_scale, workspace or None,
+                                                    ws_bytes, stream or None))
+
+
+# ------------------------------------------------------------------ torch-backed holder
+class Pool:
+    """Owns the torch device buffers of one pool (K pages, V pages, workspace) and its handle.
+
+    metadata_only=True creates a host-only pool (no device memory, no device work)."""
+
+    def __init__(self, n_kv_heads: int, head_dim: int, n_pages: int, dtype: str = "bf16", page_size: int = 16,
+                 rope_theta: float = 0.0, metadata_only: bool = False, device: str = "cuda"):
+        self.dtype = dtype
+        self.cfg = make_config(n_kv_heads, head_dim, n_pages, KV_BF16 if dtype == "bf16" else KV_F32, page_size,
+                               rope_theta)
+        self.k_pages = self.v_pages = self.workspace = None
+        self._dec_ws = None
+        if metadata_only:
+            self.handle = kv_pool_create(self.cfg)
+        else:
+            import torch
+            tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+            nbytes = kv_pool_bytes(self.cfg)
+            n_el = nbytes // (2 if dtype == "bf16" else 4)
+            self.k_pages = torch.zeros(n_el, dtype=tdt, device=device)
+            self.v_pages = torch.zeros(n_el, dtype=tdt, device=device)
+            wsb = kv_pool_workspace_size(self.cfg)
+            self.workspace = torch.zeros(wsb, dtype=torch.uint8, device=device)
+            self.handle = kv_pool_create(self.cfg, self.k_pages.data_ptr(), self.v_pages.data_ptr(),
+                                         self.workspace.data_ptr(), wsb)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            kv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _stream() -> int:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+
+    def seq_create(self) -> int:
+        return kv_seq_create(self.handle)
+
+    def append(self, seq: int, k=None, v=None, positions=None, n: Optional[int] = None):
+        if k is None:
+            kv_append(self.handle, seq, int(n), 0, 0, positions, 0)
+        else:
+            assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
+            kv_append(self.handle, seq, k.shape[0], k.data_ptr(), v.data_ptr(), positions, self._stream())
+
+    def write(self, seq: int, start: int, k=None, v=None, n: Optional[int] = None):
+        if k is None:
+            kv_write(self.handle, seq, start, int(n), 0, 0, 0)
+        else:
+            kv_write(self.handle, seq, start, k.shape[0], k.data_ptr(), v.data_ptr(), self._stream())
+
+    def fork(self, parent: int) -> int:
+        return kv_fork(self.handle, parent)
+
+    def mount(self, dst: int, src: int, begin: int, length: int):
+        kv_mount(self.handle, dst, src, begin, length)
+
+    def drop(self, seq: int, spans, repos: bool = False) -> np.ndarray:
+        st = 0 if self.k_pages is None else self._stream()
+        return kv_drop(self.handle, seq, spans, KV_DROP_REPOS if repos else 0, st)
+
+    def repos(self, seq: int):
+        kv_repos(self.handle, seq, 0 if self.k_pages is None else self._stream())
+
+    def rewind(self, seq: int, n: int):
+        kv_rewind(self.handle, seq, n)
+
+    def commit(self, seq: int):
+        kv_commit(self.handle, seq)
+
+    def release(self, seq: int):
+        kv_release(self.handle, seq)
+
+    def info(self, seq: int):
+        return kv_seq_info(self.handle, seq)
+
+    def block_table(self, seq: int) -> np.ndarray:
+        return kv_block_table(self.handle, seq)
+
+    def positions(self, seq: int) -> np.ndarray:
+        return kv_positions(self.handle, seq)
+
+    def refcount(self, page: int) -> int:
+        return kv_page_refcount(self.handle, page)
+
+    def free_pages(self) -> int:
+        return kv_free_pages(self.handle)
+
+    def read_page(self, page: int, head: int):
+        d = self.cfg.head_dim
+        dt = np.uint16 if self.dtype == "bf16" else np.float32
+        k = np.zeros((16, d), dt)
+        v = np.zeros((16, d), dt)
+        kv_pool_read_page(self.handle, page, head, k, v, self._stream())
+        return k, v
+
+    def sync_status(self) -> int:
+        return kv_pool_sync_status(self.handle, self._stream())
+
+    def decode(self, seqs: Sequence[int], q, sm_scale: float, out=None, lse=None, workspace=None):
+        """q: torch [n, Hq, d] on the device.  Returns (out, lse)."""
+        import torch
+        n, hq, d = q.shape
+        need = fork_attn_workspace_size(self.handle, seqs, hq)
+        if workspace is None:
+            if self._dec_ws is None or self._dec_ws.numel() < need:
+                self._dec_ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+            workspace = self._dec_ws
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+        fork_attn_decode(self.handle, seqs, hq, q.data_ptr(), out.data_ptr(), lse.data_ptr(), sm_scale,
+                         workspace.data_ptr(), workspace.numel(), self._stream())
+        return out, lse
+
+    def plan_stats(self) -> dict:
+        return fork_attn_plan_stats(self.handle)

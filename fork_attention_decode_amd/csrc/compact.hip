@@ -1,0 +1,153 @@
+// Fused Drop compaction + Repos re-rotation for gfx950.
+//
+// AKV (news.farwalk.ai), "AKV 如何工作": Drop removes entries from future attention;
+// Repos rewrites the kept keys to positions 0..r-1 by a rotary rotation and leaves the
+// values unchanged.  AgentKV (rit.work): kept entries are compacted physically and the
+// freed pages go back to the allocator.
+//
+// One workgroup per destination page (all KV heads).  Phase 1 gathers the page's kept
+// tokens from their old slots into an LDS image of the destination page, rotating each
+// key pair (i, i + d/2) by the token's offset with fp32 cos/sin rows computed on the
+// host in fp64 (an fp32 angle at 131K positions would be off by ~1e-2 rad); values are
+// copied bit-exactly.  Phase 2 writes the image back with contiguous 16-byte stores.
+//
+// In-place hazard: kept tokens only move to lower slots, so a page rewritten in place
+// may still be a source of lower destination pages.  Workgroups take list entries in
+// start order (an atomic ticket), publish "sources read" with a release store after
+// phase 1, and a page rewritten in place waits (acquire) for the lower entries that
+// read it.  A workgroup only ever waits for entries started before it, all of which
+// are resident and never wait for it, so every wait ends.
+#include <hip/hip_runtime.h>
+#include "plan.hpp"
+
+namespace fa {
+
+typedef __bf16 bf16_t;
+
+template <typename T> __device__ inline float to_f(T x) { return (float)x; }
+template <typename T> __device__ inline T from_f(float x) { return (T)x; }
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  constexpr int E = 16 / sizeof(T);                 // elements per 16-byte slot
+  constexpr int NF = D * (int)sizeof(T) / 64;       // K slots per token row and lane group
+  constexpr int HALF = NF / 2;                      // slot f pairs with f + HALF (d, d + D/2)
+  constexpr int BLK = 16 * D;                       // elements per (page, head) block
+  typedef T vec_t __attribute__((__vector_size__(16)));
+  const int hkv = p.n_kv_heads;
+  T* lk = reinterpret_cast<T*>(lds_raw);
+  T* lv = lk + (size_t)hkv * BLK;
+  __shared__ int s_k;
+  if (threadIdx.x == 0) s_k = (int)((unsigned)atomicAdd(p.ticket, 1) - (unsigned)p.ticket_base);
+  __syncthreads();
+  const int k = s_k;
+  const CompactPage cp = p.pages[k];
+  T* kp = reinterpret_cast<T*>(p.k_pages);
+  T* vp = reinterpret_cast<T*>(p.v_pages);
+  const size_t dst = (size_t)cp.dst_page * hkv * BLK;
+  const bool keep_rest = cp.first_slot > 0 || cp.n_slots < 16;
+
+  // ---- phase 1: gather K (with rotation) into the LDS image
+  const int n_ku = hkv * HALF * 64;
+  for (int u = threadIdx.x; u < n_ku; u += blockDim.x) {
+    const int t = u & 15, g = (u >> 4) & 3, fp = (u >> 6) % HALF, h = (u >> 6) / HALF;
+    const int s0 = ((fp * 4 + g) * 16 + t) * E, s1 = (((fp + HALF) * 4 + g) * 16 + t) * E;
+    vec_t a, b;
+    if (t >= cp.first_slot && t < cp.n_slots) {
+      const int loc = p.src_loc[cp.tok_base + t];
+      const size_t sb = ((size_t)(loc >> 4) * hkv + h) * BLK;
+      const int st = loc & 15;
+      a = *reinterpret_cast<const vec_t*>(kp + sb + ((fp * 4 + g) * 16 + st) * E);
+      b = *reinterpret_cast<const vec_t*>(kp + sb + (((fp + HALF) * 4 + g) * 16 + st) * E);
+      const int run = p.rot[cp.tok_base + t];
+      if (run >= 0) {
+        const float* cs = p.cos_sin + (size_t)run * D;  // [D/2][2]
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int d = sizeof(T) == 2 ? 32 * fp + 8 * g + e : 16 * fp + 4 * e + g;
+          const float c = cs[2 * d], s = cs[2 * d + 1];
+          const float x = to_f(a[e]), y = to_f(b[e]);
+          a[e] = from_f<T>(x * c - y * s);
+          b[e] = from_f<T>(y * c + x * s);
+        }
+      }
+    } else if (keep_rest) {
+      a = *reinterpret_cast<const vec_t*>(kp + dst + (size_t)h * BLK + s0);
+      b = *reinterpret_cast<const vec_t*>(kp + dst + (size_t)h * BLK + s1);
+    } else {
+      continue;
+    }
+    *reinterpret_cast<vec_t*>(lk + h * BLK + s0) = a;
+    *reinterpret_cast<vec_t*>(lk + h * BLK + s1) = b;
+  }
+  // ---- phase 1: gather V^T rows (bit-exact copies)
+  for (int r = threadIdx.x; r < hkv * D; r += blockDim.x) {
+    const int h = r / D, d = r % D;
+    vec_t row[16 / E];
+    if (keep_rest) {
+#pragma unroll
+      for (int i = 0; i < 16 / E; ++i)
+        row[i] = *reinterpret_cast<const vec_t*>(vp + dst + (size_t)h * BLK + d * 16 + i * E);
+    }
+    for (int t = cp.first_slot; t < cp.n_slots; ++t) {
+      const int loc = p.src_loc[cp.tok_base + t];
+      row[t / E][t % E] = vp[((size_t)(loc >> 4) * hkv + h) * BLK + d * 16 + (loc & 15)];
+    }
+#pragma unroll
+    for (int i = 0; i < 16 / E; ++i) *reinterpret_cast<vec_t*>(lv + h * BLK + d * 16 + i * E) = row[i];
+  }
+  __syncthreads();
+
+  // ---- publish "sources read", then wait for the lower entries that read this page
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(&p.done[k], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = cp.wait_lo; i < k; ++i) {
+      int spins = 0;
+      while (__hip_atomic_load(&p.done[i], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+        __builtin_amdgcn_s_sleep(4);
+        if (++spins > (1 << 26)) {  // ~seconds: never expected; counted, never hangs
+          atomicAdd(p.errors, 1);
+          break;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: write the image (all heads' K blocks, then V blocks: contiguous)
+  const int n_vec = hkv * BLK / E;
+  const vec_t* ik = reinterpret_cast<const vec_t*>(lk);
+  const vec_t* iv = reinterpret_cast<const vec_t*>(lv);
+  vec_t* ok = reinterpret_cast<vec_t*>(kp + dst);
+  vec_t* ov = reinterpret_cast<vec_t*>(vp + dst);
+  for (int i = threadIdx.x; i < n_vec; i += blockDim.x) {
+    ok[i] = ik[i];
+    ov[i] = iv[i];
+  }
+}
+
+size_t compact_lds_bytes(int dtype, int d, int hkv) {
+  return (size_t)2 * hkv * 16 * d * (dtype == 1 ? 4 : 2);
+}
+
+template <typename T, int D>
+static hipError_t compact_t(const CompactParams& p, hipStream_t s) {
+  if (p.n_pages == 0) return hipSuccess;
+  const size_t lds = compact_lds_bytes(sizeof(T) == 4 ? 1 : 0, D, p.n_kv_heads);
+  hipError_t e = hipFuncSetAttribute((const void*)compact_kernel<T, D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  compact_kernel<T, D><<<p.n_pages, 256, lds, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(int dtype, int d, const CompactParams& p, hipStream_t s) {
+  if (dtype == 0 && d == 128) return compact_t<bf16_t, 128>(p, s);
+  if (dtype == 0 && d == 64) return compact_t<bf16_t, 64>(p, s);
+  if (dtype == 1 && d == 128) return compact_t<float, 128>(p, s);
+  if (dtype == 1 && d == 64) return compact_t<float, 64>(p, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -1,0 +1,110 @@
+// Plan records shared by the host runtime (C++) and the gfx950 kernels (HIP).
+// Plain structs of fixed layout: the host fills them, copies them into a device
+// workspace, and the kernels read them.
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace fa {
+
+constexpr int kPage = 16;        // tokens per page on device pools
+constexpr int kMaxRows = 64;     // query rows per decode work item (4 MFMA row blocks of 16)
+constexpr int kWaves = 4;        // waves per decode workgroup
+constexpr int kMaxChunksPerWave = 64;
+
+// One page write of kv_append / kv_write: slots [lo, hi) of dst_page receive new tokens
+// tok_base, tok_base + 1, ...; when src_page >= 0 (copy-on-write) every other slot is
+// copied from src_page, otherwise the other slots are left untouched.
+struct PageWrite {
+  int32_t dst_page;
+  int32_t src_page;
+  int32_t lo, hi;
+  int64_t tok_base;
+};
+
+// A run of token slots inside one physical page, read by one segment's rows.
+struct Chunk {
+  int32_t page;
+  int32_t lohi;  // lo | hi << 8, 0 <= lo < hi <= 16
+};
+
+// One decode work item: chunks [chunk_begin, chunk_begin + n_chunks) of one segment,
+// for KV head kv_head and the segment's rows (n_readers * G rows, <= kMaxRows).
+// The kWaves waves of the workgroup take the item's chunks round robin and merge
+// their softmax states in LDS; the result is one partial (lse2, o) per row.
+struct DecodeItem {
+  int32_t chunk_begin;
+  int32_t n_chunks;
+  int32_t kv_head;
+  int32_t reader_begin;  // index into the readers array (query indices)
+  int32_t n_rows;
+  int32_t partial_base;
+  int32_t row_blocks;    // 1, 2 or 4 blocks of 16 rows
+  int32_t pad;
+};
+
+struct DecodeParams {
+  const void* q;          // [n_seqs][Hq][d]
+  const void* k_pages;
+  const void* v_pages;
+  const DecodeItem* items;
+  const Chunk* chunks;
+  const int32_t* readers;
+  float* part_lse2;       // [n_partials] log2-domain log-sum-exp of the partial
+  float* part_o;          // [n_partials][d] normalised partial output
+  int32_t n_items;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t group;          // Hq / Hkv
+  float scale_log2;       // sm_scale * log2(e)
+};
+
+struct MergeParams {
+  const int32_t* row_ptr;  // [n_rows + 1]
+  const int32_t* part_idx;
+  const float* part_lse2;
+  const float* part_o;
+  void* out;               // [n_rows][d]
+  float* lse;              // [n_rows] natural log, or null
+  int32_t n_rows;
+};
+
+// Drop / repos compaction: one record per destination page to (re)write.  Slots
+// [first_slot, n_slots) of dst_page receive the kept tokens tok_base + slot; when the
+// page is rewritten in place its old tokens may be sources of lower destination pages,
+// so the page is written only after list entries [wait_lo, self) have read their
+// sources (wait_lo == self: nothing to wait for).
+struct CompactPage {
+  int32_t dst_page;
+  int32_t first_slot;
+  int32_t n_slots;
+  int32_t tok_base;
+  int32_t wait_lo;
+  int32_t pad[3];
+};
+
+struct CompactParams {
+  void* k_pages;
+  void* v_pages;
+  const CompactPage* pages;
+  const int32_t* src_loc;    // [token] old page * 16 + old slot of the kept token
+  const int32_t* rot;        // [token] row of cos_sin, -1 = no rotation
+  const float* cos_sin;      // [n_rot][d/2][2] cos, sin of (offset * theta^(-2i/d))
+  int32_t* ticket;           // monotone counter: order in which workgroups start
+  int32_t* done;             // [list entry] = epoch once that entry has read its sources
+  int32_t* errors;           // incremented if a wait gives up (never expected)
+  int32_t ticket_base;
+  int32_t epoch;
+  int32_t n_pages;
+  int32_t n_kv_heads;
+};
+
+hipError_t launch_page_write(int dtype, int d, int hkv, void* k_pages, void* v_pages,
+                             const void* k_new, const void* v_new, const PageWrite* writes,
+                             int n_writes, hipStream_t s);
+hipError_t launch_decode(int dtype, int d, const DecodeParams& p, hipStream_t s);
+hipError_t launch_merge(int dtype, int d, const MergeParams& p, hipStream_t s);
+hipError_t launch_compact(int dtype, int d, const CompactParams& p, hipStream_t s);
+size_t compact_lds_bytes(int dtype, int d, int hkv);
+
+}  // namespace fa

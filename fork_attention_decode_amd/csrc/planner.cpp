@@ -1,0 +1,297 @@
+// Segment planner and fork_attn_decode.
+//
+// Agentrix README (gitlink.org.cn), "前缀复用与 ForkAttention" and the CUDA ForkAttention
+// item: the context of branches decoding together is split into public and private
+// segments by the actual cache pages; several queries reuse the loaded public K/V and
+// each branch's results are merged.  Octopus (zicq.com), "Attention-Only KV Mounting":
+// a thread also attends to mounted sibling blocks, so reader sets differ page by page.
+//
+// Plan:
+//   1. every query row's visible token runs (own pages, then mounts) as
+//      (page, lo, hi, reader) entries;
+//   2. per physical page, split the slot range at every run boundary and collect the
+//      reader multiset of each piece -> chunks; equal reader multisets form one segment
+//      (public = many readers, private = one);
+//   3. per segment, reader groups of at most 64 / G readers (64 MFMA rows), per KV head,
+//      the chunk list is cut into work items of about equal bytes sized so the whole
+//      decode is about one workgroup per compute unit;
+//   4. every (item, row) owns one partial slot; a CSR lists each output row's partials.
+#include "pool.hpp"
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+
+using namespace fa;
+
+int fa_set_err(kv_pool* P, int code, const std::string& m);
+Seq* fa_seq(kv_pool* P, kv_seq_t s);
+hipError_t fa_upload(kv_pool* P, void* dst, const void* src, size_t bytes, hipStream_t s);
+#define FAIL(P, code, msg) return fa_set_err((P), (code), (msg))
+
+namespace {
+
+struct Entry {
+  int32_t page;
+  int32_t lo, hi;
+  int32_t reader;
+};
+
+struct Segment {
+  std::vector<int32_t> readers;  // sorted multiset of query indices
+  std::vector<Chunk> chunks;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <typename T>
+void put(std::vector<char>& blob, size_t off, const std::vector<T>& v) {
+  if (!v.empty()) std::memcpy(blob.data() + off, v.data(), v.size() * sizeof(T));
+}
+
+}  // namespace
+
+static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq) {
+  const kv_pool_config& C = P->cfg;
+  if (n < 0 || (n > 0 && !seqs)) FAIL(P, KV_ERR_INVALID, "bad sequence list");
+  if (hq < C.n_kv_heads || hq % C.n_kv_heads) FAIL(P, KV_ERR_INVALID, "n_q_heads must be a multiple of n_kv_heads");
+  const int32_t G = hq / C.n_kv_heads;
+  if (G > kMaxRows) FAIL(P, KV_ERR_UNSUPPORTED, "more than 64 query heads per KV head");
+  const int32_t PS = C.page_size;
+  DecodePlanCache& pc = P->plan;
+  if (pc.valid && pc.version == P->version && pc.n_q_heads == hq && (int32_t)pc.seqs.size() == n &&
+      std::equal(pc.seqs.begin(), pc.seqs.end(), seqs))
+    return KV_OK;
+
+  // 1. visible runs
+  std::vector<Entry> ent;
+  for (int32_t i = 0; i < n; ++i) {
+    Seq* S = fa_seq(P, seqs[i]);
+    if (!S) FAIL(P, KV_ERR_NOT_FOUND, "no live sequence in the query list");
+    for (size_t L = 0; L < S->pages.size(); ++L)
+      ent.push_back({S->pages[L], 0, (int32_t)std::min<int64_t>(PS, S->n - (int64_t)L * PS), i});
+    for (const Mount& m : S->mounts) {
+      for (size_t j = 0; j < m.pages.size(); ++j) {
+        const int64_t a = std::max<int64_t>(0, m.off - (int64_t)j * PS);
+        const int64_t b = std::min<int64_t>(PS, m.off + m.n - (int64_t)j * PS);
+        if (a < b) ent.push_back({m.pages[j], (int32_t)a, (int32_t)b, i});
+      }
+    }
+  }
+  std::stable_sort(ent.begin(), ent.end(), [](const Entry& x, const Entry& y) { return x.page < y.page; });
+
+  // 2. chunks grouped into segments by reader multiset
+  std::vector<Segment> segs;
+  std::map<std::vector<int32_t>, int32_t> seg_of;
+  std::vector<int32_t> key, last_key;
+  int32_t last_seg = -1;
+  auto emit = [&](int32_t page, int32_t lo, int32_t hi, std::vector<int32_t>& readers) {
+    std::sort(readers.begin(), readers.end());
+    int32_t sid;
+    if (last_seg >= 0 && readers == last_key) {
+      sid = last_seg;
+    } else {
+      auto it = seg_of.find(readers);
+      if (it == seg_of.end()) {
+        sid = (int32_t)segs.size();
+        seg_of.emplace(readers, sid);
+        segs.push_back({readers, {}});
+      } else {
+        sid = it->second;
+      }
+      last_key = readers;
+      last_seg = sid;
+    }
+    segs[sid].chunks.push_back({page, lo | (hi << 8)});
+  };
+  for (size_t a = 0; a < ent.size();) {
+    size_t b = a;
+    bool uniform = true;
+    while (b < ent.size() && ent[b].page == ent[a].page) {
+      uniform = uniform && ent[b].lo == ent[a].lo && ent[b].hi == ent[a].hi;
+      ++b;
+    }
+    if (uniform) {
+      key.clear();
+      for (size_t e = a; e < b; ++e) key.push_back(ent[e].reader);
+      emit(ent[a].page, ent[a].lo, ent[a].hi, key);
+    } else {
+      std::vector<int32_t> cuts;
+      for (size_t e = a; e < b; ++e) {
+        cuts.push_back(ent[e].lo);
+        cuts.push_back(ent[e].hi);
+      }
+      std::sort(cuts.begin(), cuts.end());
+      cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+      for (size_t c = 0; c + 1 < cuts.size(); ++c) {
+        key.clear();
+        for (size_t e = a; e < b; ++e)
+          if (ent[e].lo <= cuts[c] && ent[e].hi >= cuts[c + 1]) key.push_back(ent[e].reader);
+        if (!key.empty()) emit(ent[a].page, cuts[c], cuts[c + 1], key);
+      }
+    }
+    a = b;
+  }
+
+  // 3. work items
+  const int32_t per_group = std::max(1, kMaxRows / G);
+  int64_t total = 0;
+  for (const Segment& s : segs) {
+    const int64_t groups = ((int64_t)s.readers.size() + per_group - 1) / per_group;
+    total += (int64_t)s.chunks.size() * C.n_kv_heads * groups;
+  }
+  const int64_t target_items = std::max<int64_t>(1, P->n_cu);
+  int64_t cpi = (total + target_items - 1) / target_items;
+  cpi = std::max<int64_t>(cpi, 2 * kWaves);
+  cpi = std::min<int64_t>(cpi, (int64_t)kWaves * kMaxChunksPerWave);
+
+  std::vector<Chunk> chunks;
+  std::vector<int32_t> readers;
+  std::vector<DecodeItem> items;
+  int64_t unique_tokens = 0;
+  const int32_t n_out = n * hq;
+  std::vector<std::vector<int32_t>> row_parts((size_t)n_out);
+  int32_t n_part = 0;
+  for (const Segment& s : segs) {
+    const int32_t cbase = (int32_t)chunks.size();
+    chunks.insert(chunks.end(), s.chunks.begin(), s.chunks.end());
+    for (const Chunk& c : s.chunks) unique_tokens += (c.lohi >> 8) - (c.lohi & 0xff);
+    const int32_t nc = (int32_t)s.chunks.size();
+    const int32_t n_it = (int32_t)((nc + cpi - 1) / cpi);
+    for (size_t g0 = 0; g0 < s.readers.size(); g0 += per_group) {
+      const int32_t ng = (int32_t)std::min<size_t>(per_group, s.readers.size() - g0);
+      const int32_t rbase = (int32_t)readers.size();
+      readers.insert(readers.end(), s.readers.begin() + g0, s.readers.begin() + g0 + ng);
+      const int32_t rows = ng * G;
+      for (int32_t h = 0; h < C.n_kv_heads; ++h) {
+        for (int32_t t = 0; t < n_it; ++t) {
+          const int32_t c0 = (int32_t)((int64_t)nc * t / n_it), c1 = (int32_t)((int64_t)nc * (t + 1) / n_it);
+          DecodeItem it;
+          it.chunk_begin = cbase + c0;
+          it.n_chunks = c1 - c0;
+          it.kv_head = h;
+          it.reader_begin = rbase;
+          it.n_rows = rows;
+          it.partial_base = n_part;
+          it.row_blocks = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
+          it.pad = 0;
+          for (int32_t r = 0; r < rows; ++r) {
+            const int32_t q = s.readers[g0 + r / G];
+            row_parts[(size_t)q * hq + h * G + r % G].push_back(n_part + r);
+          }
+          n_part += rows;
+          items.push_back(it);
+        }
+      }
+    }
+  }
+  // heaviest items first
+  std::stable_sort(items.begin(), items.end(), [](const DecodeItem& a, const DecodeItem& b) {
+    return (int64_t)a.n_chunks * (2 + a.row_blocks) > (int64_t)b.n_chunks * (2 + b.row_blocks);
+  });
+  std::vector<int32_t> mptr((size_t)n_out + 1, 0), midx;
+  midx.reserve((size_t)n_part);
+  for (int32_t r = 0; r < n_out; ++r) {
+    midx.insert(midx.end(), row_parts[r].begin(), row_parts[r].end());
+    mptr[r + 1] = (int32_t)midx.size();
+  }
+
+  // 4. workspace image
+  const int D = C.head_dim;
+  size_t off = 0;
+  pc.off_items = off; off = align256(off + items.size() * sizeof(DecodeItem));
+  pc.off_chunks = off; off = align256(off + chunks.size() * sizeof(Chunk));
+  pc.off_readers = off; off = align256(off + readers.size() * sizeof(int32_t));
+  pc.off_mptr = off; off = align256(off + mptr.size() * sizeof(int32_t));
+  pc.off_midx = off; off = align256(off + midx.size() * sizeof(int32_t));
+  const size_t plan_bytes = off;
+  pc.off_plse = off; off = align256(off + (size_t)n_part * sizeof(float));
+  pc.off_po = off; off = align256(off + (size_t)n_part * D * sizeof(float));
+  pc.ws_need = std::max<size_t>(off, 256);
+  pc.blob.assign(plan_bytes, 0);
+  put(pc.blob, pc.off_items, items);
+  put(pc.blob, pc.off_chunks, chunks);
+  put(pc.blob, pc.off_readers, readers);
+  put(pc.blob, pc.off_mptr, mptr);
+  put(pc.blob, pc.off_midx, midx);
+  pc.n_items = (int32_t)items.size();
+  pc.n_out_rows = n_out;
+  const size_t es = C.dtype == KV_F32 ? 4 : 2;
+  pc.stats[0] = (int64_t)segs.size();
+  pc.stats[1] = (int64_t)items.size();
+  pc.stats[2] = (int64_t)chunks.size();
+  pc.stats[3] = n_part;
+  pc.stats[4] = unique_tokens * C.n_kv_heads * 2 * D * (int64_t)es;
+  pc.stats[5] = n_out;
+  pc.valid = true;
+  pc.version = P->version;
+  pc.seqs.assign(seqs, seqs + n);
+  pc.n_q_heads = hq;
+  pc.ws = nullptr;  // not uploaded yet
+  return KV_OK;
+}
+
+extern "C" {
+
+int fork_attn_workspace_size(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, size_t* bytes) {
+  if (!P || !bytes) FAIL(P, KV_ERR_INVALID, "null argument");
+  int st = build_plan(P, seqs, n, hq);
+  if (st) return st;
+  *bytes = P->plan.ws_need;
+  return KV_OK;
+}
+
+int fork_attn_plan_stats(kv_pool_t* P, int64_t* out, int32_t n) {
+  if (!P || !out || n < 0) FAIL(P, KV_ERR_INVALID, "null argument");
+  if (!P->plan.valid) FAIL(P, KV_ERR_INVALID, "no plan yet");
+  for (int32_t i = 0; i < n && i < 6; ++i) out[i] = P->plan.stats[i];
+  return KV_OK;
+}
+
+int fork_attn_decode(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, const void* q, void* out,
+                     float* lse, float sm_scale, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!P) FAIL(P, KV_ERR_INVALID, "null pool");
+  if (!P->device) FAIL(P, KV_ERR_INVALID, "metadata-only pool has no KV data");
+  if (n == 0) return KV_OK;
+  if (!q || !out || !ws) FAIL(P, KV_ERR_INVALID, "null device pointer");
+  int st = build_plan(P, seqs, n, hq);
+  if (st) return st;
+  DecodePlanCache& pc = P->plan;
+  if (ws_bytes < pc.ws_need) FAIL(P, KV_ERR_WORKSPACE, "decode workspace too small");
+  char* w = (char*)ws;
+  hipError_t e = hipSuccess;
+  if (pc.ws != ws) {
+    e = fa_upload(P, w, pc.blob.data(), pc.blob.size(), s);
+    if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("plan upload: ") + hipGetErrorString(e));
+    pc.ws = ws;
+  }
+  DecodeParams dp;
+  dp.q = q;
+  dp.k_pages = P->k;
+  dp.v_pages = P->v;
+  dp.items = reinterpret_cast<const DecodeItem*>(w + pc.off_items);
+  dp.chunks = reinterpret_cast<const Chunk*>(w + pc.off_chunks);
+  dp.readers = reinterpret_cast<const int32_t*>(w + pc.off_readers);
+  dp.part_lse2 = reinterpret_cast<float*>(w + pc.off_plse);
+  dp.part_o = reinterpret_cast<float*>(w + pc.off_po);
+  dp.n_items = pc.n_items;
+  dp.n_q_heads = hq;
+  dp.n_kv_heads = P->cfg.n_kv_heads;
+  dp.group = hq / P->cfg.n_kv_heads;
+  dp.scale_log2 = sm_scale * 1.4426950408889634f;
+  e = launch_decode(P->cfg.dtype, P->cfg.head_dim, dp, s);
+  if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+  MergeParams mp;
+  mp.row_ptr = reinterpret_cast<const int32_t*>(w + pc.off_mptr);
+  mp.part_idx = reinterpret_cast<const int32_t*>(w + pc.off_midx);
+  mp.part_lse2 = dp.part_lse2;
+  mp.part_o = dp.part_o;
+  mp.out = out;
+  mp.lse = lse;
+  mp.n_rows = pc.n_out_rows;
+  e = launch_merge(P->cfg.dtype, P->cfg.head_dim, mp, s);
+  if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+  return KV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Host runtime of libforkattn: page pool, block tables, plans.  Single-threaded per pool.
+#pragma once
+#include <stdint.h>
+#include <string>
+#include <vector>
+#include <map>
+#include <hip/hip_runtime_api.h>
+#include "../../include/forkattn.h"
+#include "plan.hpp"
+
+namespace fa {
+
+struct Status {
+  int code;
+  std::string msg;
+};
+
+// Positions of consecutive tokens as runs p0, p0 + 1, ..., p0 + len - 1.
+struct PosRun {
+  int64_t p0;
+  int64_t len;
+};
+
+struct Mount {
+  std::vector<int32_t> pages;
+  int32_t off;  // token offset of the first mounted token in pages[0]
+  int64_t n;
+  std::vector<PosRun> pos;
+};
+
+struct Seq {
+  bool live = true;
+  std::vector<int32_t> pages;  // own context, logical page -> page id
+  int64_t n = 0;
+  std::vector<PosRun> pos;
+  int64_t next_pos = 0;
+  std::vector<Mount> mounts;
+};
+
+// Lowest-id-first free set over a bitmap.
+class FreeSet {
+ public:
+  void init(int32_t n);
+  int32_t count() const { return count_; }
+  // the k lowest free ids, without taking them
+  void peek_lowest(int32_t k, std::vector<int32_t>& out) const;
+  void take(int32_t id);
+  void give(int32_t id);
+  bool is_free(int32_t id) const { return (bits_[id >> 6] >> (id & 63)) & 1ull; }
+
+ private:
+  std::vector<uint64_t> bits_;  // 1 = free
+  int32_t n_ = 0, count_ = 0;
+  int32_t hint_ = 0;  // no free id below word hint_
+};
+
+struct DecodePlanCache {
+  bool valid = false;
+  uint64_t version = 0;
+  std::vector<int32_t> seqs;
+  int32_t n_q_heads = 0;
+  void* ws = nullptr;
+  size_t ws_need = 0;
+  // device offsets
+  size_t off_items = 0, off_chunks = 0, off_readers = 0, off_mptr = 0, off_midx = 0, off_plse = 0,
+         off_po = 0;
+  int32_t n_items = 0, n_out_rows = 0;
+  std::vector<char> blob;  // host image of the plan part of the workspace
+  int64_t stats[6] = {0, 0, 0, 0, 0, 0};
+};
+
+}  // namespace fa
+
+struct kv_pool {
+  kv_pool_config cfg;
+  bool device = false;
+  void* k = nullptr;
+  void* v = nullptr;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  std::vector<int32_t> rc;
+  fa::FreeSet free;
+  std::vector<fa::Seq> seqs;
+  uint64_t version = 1;
+  std::string err;
+  int32_t n_cu = 256;
+  // pinned staging buffer for plan uploads
+  void* stage = nullptr;
+  size_t stage_bytes = 0;
+  hipEvent_t stage_ev = nullptr;
+  bool stage_pending = false;
+  // drop-kernel ordering state (see CompactParams)
+  int32_t ticket = 0;
+  int32_t epoch = 0;
+  fa::DecodePlanCache plan;
+};

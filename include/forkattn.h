@@ -1,0 +1,239 @@
+/*
+ * forkattn.h -- C ABI of libforkattn.so: attention over a shared, paged KV-state DAG
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Many branches / threads read ONE physical copy of a common prefix:
+ *   - a host-side page table with reference counts and copy-on-write of shared pages
+ *     (zero-copy forks, read-only mounts, drop / repos compaction, rewind, release);
+ *   - fork_attn_decode: split-K decode that streams each shared KV page from HBM once
+ *     for every query row that reads it, followed by a log-sum-exp merge;
+ *   - dag_attn_prefill: block-sparse prefill over a packed DAG block mask.
+ *
+ * Sources (page title and section):
+ *   Octopus (zicq.com): "Zero-Copy Radix Forking", "Attention-Only KV Mounting",
+ *     "Packed DAG-GRPO", the core-idea section (fork / read_thread / wait_threads /
+ *     rewind / commit) and the developer-advice section (refcounts, snapshot
+ *     consistency, OOM fallback, thread-level cancellation).
+ *   Agentrix README (gitlink.org.cn): "前缀复用与 ForkAttention" and the CUDA
+ *     ForkAttention item (public / private segments by actual cache pages, merge),
+ *     the cache-lifecycle item (reclaim only at refcount zero), tool-data snapshots.
+ *   AKV (news.farwalk.ai): "AKV 如何工作" (Append / Drop / Repos; drop and reposition
+ *     nodes; free dropped KV only when no live request needs it).
+ *   AgentKV (rit.work): physical compaction returning freed pages to the allocator.
+ *
+ * Conventions
+ *   - Every call returns a kv_status (0 = OK, negative = error).  No exception crosses
+ *     the ABI.  A failing call leaves host metadata and device memory unchanged.
+ *   - Device memory (page pools, workspaces, Q / O / LSE, prefill tensors) is owned by
+ *     the caller and passed as raw device pointers; it must stay alive while the pool
+ *     or the launched work uses it.  The library owns host metadata and a pinned host
+ *     staging buffer only; it never allocates device memory.
+ *   - Device work is enqueued on the caller's hipStream_t (NULL = default stream) and
+ *     returns asynchronously; metadata changes are immediate.  Pages released by an
+ *     operation may be handed out again to later operations; their old contents are
+ *     read only by work already enqueued, so callers must keep all pool work on ONE
+ *     stream (or order streams themselves).
+ *   - A pool is not thread-safe: the caller serialises calls on one pool.
+ */
+#ifndef FORKATTN_H
+#define FORKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kv_pool kv_pool_t; /* opaque; host metadata only */
+typedef int32_t kv_seq_t;         /* sequence = branch / thread handle, assigned 0, 1, 2, ... */
+
+typedef enum {
+  KV_OK = 0,
+  KV_ERR_INVALID = -1,     /* bad argument, handle or range */
+  KV_ERR_OOM = -2,         /* not enough free pages; nothing was changed */
+  KV_ERR_NOT_FOUND = -3,   /* released or unknown sequence handle */
+  KV_ERR_HIP = -4,         /* a HIP runtime call failed */
+  KV_ERR_UNSUPPORTED = -5, /* shape / dtype / page size without a kernel */
+  KV_ERR_WORKSPACE = -6    /* workspace too small (query the *_workspace_size call) */
+} kv_status;
+
+typedef enum { KV_BF16 = 0, KV_F32 = 1 } kv_dtype;
+typedef enum { KV_ROPE_NONE = 0, KV_ROPE_NEOX = 1 } kv_rope_style;
+enum { KV_DROP_REPOS = 1 }; /* kv_drop flag: re-rotate kept keys to positions 0..r-1 */
+
+typedef struct {
+  int32_t n_kv_heads; /* Hkv */
+  int32_t head_dim;   /* d: 64 or 128 for device pools */
+  int32_t page_size;  /* tokens per page: 16 for device pools; any >= 1 for metadata-only pools */
+  int32_t n_pages;    /* pool capacity in pages */
+  int32_t dtype;      /* kv_dtype of K, V, Q and O */
+  int32_t rope_style; /* kv_rope_style used by Repos (keys are stored already rotated) */
+  double rope_theta;  /* rotary base, e.g. 1e6 */
+} kv_pool_config;
+
+/* ---------------------------------------------------------------------------------
+ * Device page layout (one page = page_size tokens of every KV head).
+ *
+ * k_pages and v_pages each hold n_pages * Hkv blocks; block (page p, head h) starts at
+ * element (p * Hkv + h) * 16 * d.  Inside a block:
+ *   K is stored in matrix-core operand order: the block is a sequence of 16-byte slots
+ *     indexed (f, g, t) with slot number (f * 4 + g) * 16 + t, and slot (f, g, t) holds
+ *       bf16: K[t][32 f + 8 g + e],      e = 0..7   (f < d/32)
+ *       fp32: K[t][16 f + 4 e + g],      e = 0..3   (f < d/16)
+ *     so that lane (t + 16 g) of a wave loads, with one contiguous 1 KiB access per f,
+ *     exactly the operand fragment it feeds to the matrix instruction.
+ *   V is stored transposed: element d * 16 + t holds V[t][d].
+ * Use kv_pool_read_page() to read a page back in plain [t][d] order.
+ * ------------------------------------------------------------------------------- */
+
+/* Bytes of ONE of the two pools (K or V) for cfg->n_pages pages. */
+int kv_pool_bytes(const kv_pool_config* cfg, size_t* bytes);
+
+/* Device workspace the pool needs for its own staging (append / write / drop plans). */
+int kv_pool_workspace_size(const kv_pool_config* cfg, size_t* bytes);
+
+/* Create a pool.  k_pages / v_pages: device buffers of kv_pool_bytes() each;
+ * workspace: device buffer of kv_pool_workspace_size() bytes.
+ * Passing k_pages = v_pages = workspace = NULL creates a METADATA-ONLY pool: every
+ * page-table operation works and is bit-identical, no device work is issued and the
+ * attention calls return KV_ERR_INVALID (capacity planning and host-side tests). */
+int kv_pool_create(const kv_pool_config* cfg, void* k_pages, void* v_pages, void* workspace,
+                   size_t ws_bytes, kv_pool_t** out);
+int kv_pool_destroy(kv_pool_t* pool);
+
+/* New empty root sequence (Octopus: a thread with no parent). */
+int kv_seq_create(kv_pool_t* pool, kv_seq_t* out);
+
+/* Append n tokens (AKV "Append").  k, v: DEVICE arrays [n][Hkv][d] in the pool dtype,
+ * keys already rotated for their positions.  positions: HOST int64[n] or NULL for
+ * next_pos, next_pos + 1, ...  A partially filled tail page shared with another
+ * sequence or mount (refcount > 1) is copied first (copy-on-write, lowest free page
+ * id); new pages are then taken lowest-id-first in logical order.  KV_ERR_OOM if the
+ * pool cannot hold the result (nothing changes). */
+int kv_append(kv_pool_t* pool, kv_seq_t seq, int64_t n, const void* k, const void* v,
+              const int64_t* positions, hipStream_t stream);
+
+/* Overwrite tokens [start, start + n) of the sequence's own context in place
+ * (positions unchanged).  Every touched page whose refcount > 1 is copied first, so a
+ * shared snapshot is never written (Agentrix: local edits create new versions while
+ * unchanged pages stay shared).  k, v as in kv_append. */
+int kv_write(kv_pool_t* pool, kv_seq_t seq, int64_t start, int64_t n, const void* k,
+             const void* v, hipStream_t stream);
+
+/* Fork (Octopus "Zero-Copy Radix Forking"): the child shares every page and mount of
+ * the parent (refcount + 1 each); no page is allocated and no KV byte moves. */
+int kv_fork(kv_pool_t* pool, kv_seq_t parent, kv_seq_t* child);
+
+/* Mount (Octopus "Attention-Only KV Mounting", read_thread): dst additionally attends
+ * to tokens [src_begin, src_begin + len) of src's own context as they are now; the
+ * touched pages gain one reference each, nothing is copied, and later writes by src
+ * copy away from the snapshot.  Mounted keys keep src's positions. */
+int kv_mount(kv_pool_t* pool, kv_seq_t dst, kv_seq_t src, int64_t src_begin, int64_t len);
+
+/* Drop (AKV "Drop", AgentKV physical compaction).  begin / len: HOST int64[n_spans],
+ * half-open token ranges of the own context (overlaps are unioned).  Kept tokens are
+ * packed in order into slots 0..r-1: logical pages before the first changed slot keep
+ * their ids, affected pages are rewritten in place when exclusive (refcount 1) or
+ * copied when shared, and pages from ceil(r / page_size) on are released.  Positions
+ * and next_pos are unchanged unless flags has KV_DROP_REPOS (AKV "Repos"): then kept
+ * token j gets position j, next_pos = r, and its key is re-rotated by
+ * (j - old position) in the same kernel; values are moved bit-exactly, never changed.
+ * kept_src_idx: optional HOST int64 buffer of at least the current token count;
+ * receives the old index of every kept token. */
+int kv_drop(kv_pool_t* pool, kv_seq_t seq, const int64_t* begin, const int64_t* len,
+            int32_t n_spans, int32_t flags, int64_t* kept_src_idx, hipStream_t stream);
+
+/* Repos alone: kv_drop with no spans and KV_DROP_REPOS. */
+int kv_repos(kv_pool_t* pool, kv_seq_t seq, hipStream_t stream);
+
+/* Rewind (Octopus primitive): truncate to new_len tokens, releasing pages past
+ * ceil(new_len / page_size); next_pos becomes position[new_len - 1] + 1 (0 if empty).
+ * Rewinding to the current length changes nothing. */
+int kv_rewind(kv_pool_t* pool, kv_seq_t seq, int64_t new_len);
+
+/* Commit (Octopus primitive): validates the handle; sequences are mountable at any
+ * time, so there is nothing else to do. */
+int kv_commit(kv_pool_t* pool, kv_seq_t seq);
+
+/* Release (thread-level cancellation / finish): drops every page and mount reference;
+ * pages still referenced by other sequences or mounts survive.  The handle dies. */
+int kv_release(kv_pool_t* pool, kv_seq_t seq);
+
+/* ---- introspection (exact integers, for tests and capacity planning) ---- */
+int kv_seq_info(kv_pool_t* pool, kv_seq_t seq, int64_t* n_tokens, int64_t* next_pos,
+                int32_t* n_pages, int32_t* n_mounts);
+/* Own-context block table (logical page -> page id).  cap: capacity of `pages`. */
+int kv_block_table(kv_pool_t* pool, kv_seq_t seq, int32_t* pages, int32_t cap);
+int kv_positions(kv_pool_t* pool, kv_seq_t seq, int64_t* pos, int64_t cap);
+int kv_page_refcount(kv_pool_t* pool, int32_t page, int32_t* rc);
+int kv_free_pages(kv_pool_t* pool, int32_t* n_free);
+/* Copy one page of one head back in plain [16][d] order for K and V (HOST buffers),
+ * synchronising the stream. */
+int kv_pool_read_page(kv_pool_t* pool, int32_t page, int32_t head, void* k_out, void* v_out,
+                      hipStream_t stream);
+
+/* Synchronise the stream and report how many in-place compaction waits gave up
+ * (a safety valve of the drop kernel's ordering; 0 unless the device misbehaved). */
+int kv_pool_sync_status(kv_pool_t* pool, hipStream_t stream, int32_t* n_wait_timeouts);
+
+/* ---- decode (Agentrix ForkAttention) ----
+ * For each i < n_seqs and query head h < n_q_heads (h reads KV head h / (Hq/Hkv)):
+ *   O[i][h] = softmax(sm_scale * K_i q[i][h]) V_i,  LSE[i][h] = ln sum exp(sm_scale K_i q)
+ * over sequence seqs[i]'s whole visible context (own tokens, then mounts).
+ * Pages are grouped by the exact set of query rows that read them (public / private
+ * segments by real cache pages); each group's pages are streamed from HBM once for all
+ * its rows; partial (max, sum, out) results are merged by log-sum-exp.
+ * q: DEVICE [n_seqs][Hq][d] (pool dtype); out: DEVICE [n_seqs][Hq][d] (pool dtype);
+ * lse: DEVICE fp32 [n_seqs][Hq] or NULL.
+ * workspace: DEVICE buffer of fork_attn_workspace_size() bytes for the same arguments.
+ * The plan is cached in the workspace: a later call with the same pool state, seqs,
+ * n_q_heads and workspace reuses it without host work or uploads, so the workspace
+ * must not be modified between such calls. */
+int fork_attn_workspace_size(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n_seqs,
+                             int32_t n_q_heads, size_t* bytes);
+int fork_attn_decode(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n_seqs, int32_t n_q_heads,
+                     const void* q, void* out, float* lse, float sm_scale, void* workspace,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* Plan statistics of the last fork_attn_decode / fork_attn_workspace_size call:
+ * out[0] segments, out[1] work items, out[2] chunks, out[3] partial rows,
+ * out[4] unique KV bytes streamed (algorithmic), out[5] query rows. */
+int fork_attn_plan_stats(kv_pool_t* pool, int64_t* out, int32_t n);
+
+/* ---- packed DAG prefill (Octopus Packed DAG-GRPO, forward) ----
+ * segments: HOST int32 [n_seg][3] = (start, length, parent); segment 0 has parent -1,
+ *   parents precede children, segments tile [0, T) in order.  A query of segment S at
+ *   packed index i sees every token of S's ancestors, the tokens of S at index <= i,
+ *   and every edge range targeting S.
+ * edges: HOST int32 [n_edges][4] = (src_segment, src_offset, length, dst_segment).
+ * Segment starts and edge ranges must be multiples of `block`, except that the last
+ * segment and an edge ending at its source segment's end may end anywhere.
+ * Output: CSR over block rows: row_ptr[nb + 1], col[nnz] (ascending), kind[nnz]
+ * (0 = every token pair visible, 1 = diagonal block, key <= query), nb = ceil(T/block).
+ * Call with col = kind = NULL to get nnz only. */
+int dag_mask_build(const int32_t* segments, int32_t n_seg, const int32_t* edges,
+                   int32_t n_edges, int32_t T, int32_t block, int32_t* row_ptr, int32_t* col,
+                   uint8_t* kind, int64_t* nnz);
+
+/* Block-sparse forward over the CSR (DEVICE arrays row_ptr / col / kind from
+ * dag_mask_build, block = 64).  q: DEVICE bf16 [T][Hq][d], k / v: DEVICE bf16
+ * [T][Hkv][d], out: DEVICE bf16 [T][Hq][d], lse: DEVICE fp32 [Hq][T] or NULL.
+ * d = 128.  workspace: DEVICE buffer of dag_attn_workspace_size() bytes. */
+int dag_attn_workspace_size(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t block,
+                            size_t* bytes);
+int dag_attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                     const int32_t* row_ptr, const int32_t* col, const uint8_t* kind,
+                     int32_t block, float sm_scale, void* workspace, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* ---- errors ---- */
+const char* kv_status_str(int status);
+const char* kv_last_error(kv_pool_t* pool); /* pool = NULL: last error of pool-less calls */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FORKATTN_H */
