@@ -41,6 +41,12 @@ class kv_pool_config(C.Structure):
 def _load() -> C.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python -m fork_attention_decode_amd.build`")
+    # torch ships its own HIP runtime (same soname): load it first so that the library
+    # binds to that one runtime instead of bringing a second copy into the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     return C.CDLL(LIB_PATH)
 
 

@@ -210,12 +210,23 @@ int kv_pool_create(const kv_pool_config* c, void* k, void* v, void* ws, size_t w
   P->free.init(c->n_pages);
   if (all) {
     int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipEventCreateWithFlags(&P->stage_ev, hipEventDisableTiming) != hipSuccess ||
-        hipMemset(ws, 0, fa_ws_plan_offset(c)) != hipSuccess) {
+    hipError_t e = hipGetDevice(&dev);
+    const char* what = "hipGetDevice";
+    if (e == hipSuccess) {
+      what = "hipDeviceGetAttribute";
+      e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    }
+    if (e == hipSuccess) {
+      what = "hipEventCreateWithFlags";
+      e = hipEventCreateWithFlags(&P->stage_ev, hipEventDisableTiming);
+    }
+    if (e == hipSuccess) {
+      what = "hipMemset";
+      e = hipMemset(ws, 0, fa_ws_plan_offset(c));
+    }
+    if (e != hipSuccess) {
       delete P;
-      FAIL(nullptr, KV_ERR_HIP, "HIP initialisation failed");
+      FAIL(nullptr, KV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
     }
     P->n_cu = ncu > 0 ? ncu : 256;
   }
