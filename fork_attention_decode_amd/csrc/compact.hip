@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
   const CompactPage cp = p.pages[k];
   T* kp = reinterpret_cast<T*>(p.k_pages);
   T* vp = reinterpret_cast<T*>(p.v_pages);
-  const size_t dst = (size_t)cp.dst_page * hkv * BLK;
+  const size_t np = (size_t)p.pool_pages;  // head-major pool: block (page, h) at h * np + page
+  const size_t dst = (size_t)cp.dst_page * BLK;
   const bool keep_rest = cp.first_slot > 0 || cp.n_slots < 16;
 
   // ---- phase 1: gather K (with rotation) into the LDS image
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
     vec_t a, b;
     if (t >= cp.first_slot && t < cp.n_slots) {
       const int loc = p.src_loc[cp.tok_base + t];
-      const size_t sb = ((size_t)(loc >> 4) * hkv + h) * BLK;
+      const size_t sb = ((size_t)h * np + (loc >> 4)) * BLK;
       const int st = loc & 15;
       a = *reinterpret_cast<const vec_t*>(kp + sb + ((fp * 4 + g) * 16 + st) * E);
       b = *reinterpret_cast<const vec_t*>(kp + sb + (((fp + HALF) * 4 + g) * 16 + st) * E);
@@ -73,8 +74,8 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
         }
       }
     } else if (keep_rest) {
-      a = *reinterpret_cast<const vec_t*>(kp + dst + (size_t)h * BLK + s0);
-      b = *reinterpret_cast<const vec_t*>(kp + dst + (size_t)h * BLK + s1);
+      a = *reinterpret_cast<const vec_t*>(kp + dst + (size_t)h * np * BLK + s0);
+      b = *reinterpret_cast<const vec_t*>(kp + dst + (size_t)h * np * BLK + s1);
     } else {
       continue;
     }
@@ -88,11 +89,11 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
     if (keep_rest) {
 #pragma unroll
       for (int i = 0; i < 16 / E; ++i)
-        row[i] = *reinterpret_cast<const vec_t*>(vp + dst + (size_t)h * BLK + d * 16 + i * E);
+        row[i] = *reinterpret_cast<const vec_t*>(vp + dst + (size_t)h * np * BLK + d * 16 + i * E);
     }
     for (int t = cp.first_slot; t < cp.n_slots; ++t) {
       const int loc = p.src_loc[cp.tok_base + t];
-      row[t / E][t % E] = vp[((size_t)(loc >> 4) * hkv + h) * BLK + d * 16 + (loc & 15)];
+      row[t / E][t % E] = vp[((size_t)h * np + (loc >> 4)) * BLK + d * 16 + (loc & 15)];
     }
 #pragma unroll
     for (int i = 0; i < 16 / E; ++i) *reinterpret_cast<vec_t*>(lv + h * BLK + d * 16 + i * E) = row[i];
@@ -115,15 +116,15 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
   }
   __syncthreads();
 
-  // ---- phase 2: write the image (all heads' K blocks, then V blocks: contiguous)
-  const int n_vec = hkv * BLK / E;
+  // ---- phase 2: write the image back, one contiguous block per head
+  constexpr int VPB = BLK / E;  // 16-byte vectors per block
+  const int n_vec = hkv * VPB;
   const vec_t* ik = reinterpret_cast<const vec_t*>(lk);
   const vec_t* iv = reinterpret_cast<const vec_t*>(lv);
-  vec_t* ok = reinterpret_cast<vec_t*>(kp + dst);
-  vec_t* ov = reinterpret_cast<vec_t*>(vp + dst);
   for (int i = threadIdx.x; i < n_vec; i += blockDim.x) {
-    ok[i] = ik[i];
-    ov[i] = iv[i];
+    const size_t at = ((size_t)(i / VPB) * np + cp.dst_page) * BLK + (size_t)(i % VPB) * E;
+    *reinterpret_cast<vec_t*>(kp + at) = ik[i];
+    *reinterpret_cast<vec_t*>(vp + at) = iv[i];
   }
 }
 

@@ -1,23 +1,26 @@
-// Split-K shared-prefix decode and log-sum-exp merge for gfx950 (CDNA4).
+// Split-K shared-prefix decode with a fused log-sum-exp merge, for gfx950 (CDNA4).
 //
 // Agentrix ForkAttention (gitlink.org.cn README, section "前缀复用与 ForkAttention"
 // and the CUDA ForkAttention item): the pages a group of branches share are read once
 // and reused by all of their queries; each branch's partial results are merged.
 //
 // Mapping onto CDNA4:
-//   * a work item = (segment of pages with one reader set, KV head, chunk range);
-//     its rows are every (reader, query head of this KV head) pair, up to 64;
-//   * one workgroup of 4 waves per item; the waves take the item's chunks round robin,
-//     each streaming whole 4 KiB K and V^T page blocks with contiguous 16 B / 8 B
-//     per-lane loads straight into matrix-core operand registers (the pool layout is
-//     operand-ordered, so no LDS staging is needed), PF chunks in flight per wave;
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (keys = M, query rows = N, d = K), whose
-//     accumulator layout is exactly the B-operand layout of O^T = V^T P^T on
-//     v_mfma_f32_16x16x16_bf16: no transposes; row statistics live with the lane's
-//     query row (lane % 16), the row max over a page needs two permlane swaps;
-//   * online softmax in fp32 (exp2 domain); the 4 waves merge their states through
-//     LDS and write one normalised partial (lse2, o) per row;
-//   * the merge kernel combines a row's partials by log-sum-exp.
+//   * a work item = (segment of pages with one reader set, KV head, chunk range); its
+//     rows are every (reader, query head of this KV head) pair, up to 64;
+//   * one workgroup of 4 waves per item streams every chunk (a 4 KiB K block and a
+//     4 KiB V^T block of one page and head) from HBM exactly once, with direct
+//     global->LDS loads into a ring (each wave loads a quarter, non-temporal), six
+//     chunks in flight; wave w computes rows [16 w, 16 w + 16) from LDS, so a shared
+//     page feeds all 64 rows with one HBM read;
+//   * chunks are consumed in pairs (32 keys): S^T = K Q^T on v_mfma_f32_16x16x32_bf16
+//     (keys = M, query rows = N, d = K) lands exactly in the B-operand layout of
+//     O^T = V^T P^T on v_mfma_f32_16x16x32_bf16 with the two chunks' keys interleaved
+//     along K: no transposes; row statistics live with the lane's query row;
+//   * online softmax in fp32 (exp2 domain) with a lazy, wave-uniform rescale;
+//   * each item writes one normalised partial (lse2, o) per row into slots ordered by
+//     output row, so a row's partials are contiguous; a second launch merges them (a
+//     kernel boundary is the cheapest device-wide synchronisation across the chip's
+//     separately cached dies).
 // fp32 pools use v_mfma_f32_16x16x4_f32 with the same structure.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -29,6 +32,14 @@ typedef __bf16 bf16_t;
 typedef bf16_t bf16x8 __attribute__((__vector_size__(8 * sizeof(bf16_t))));
 typedef bf16_t bf16x4 __attribute__((__vector_size__(4 * sizeof(bf16_t))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming (non-temporal) loads of KV data that is read once per decode.
+template <typename V, typename R>
+__device__ __forceinline__ V nt_load(const void* p) {
+  return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const R*>(p)));
+}
 
 template <typename T, int D> struct Tr;
 
@@ -39,10 +50,10 @@ template <int D> struct Tr<bf16_t, D> {
   using VF = bf16x4;
   using PF = bf16x4;
   __device__ static KF load_k(const bf16_t* blk, int f, int lane) {
-    return *reinterpret_cast<const KF*>(blk + (f * 64 + lane) * 8);
+    return nt_load<KF, i32x4>(blk + (f * 64 + lane) * 8);
   }
   __device__ static VF load_v(const bf16_t* blk, int db, int lane) {
-    return *reinterpret_cast<const VF*>(blk + (db * 16 + (lane & 15)) * 16 + 4 * (lane >> 4));
+    return nt_load<VF, i32x2>(blk + (db * 16 + (lane & 15)) * 16 + 4 * (lane >> 4));
   }
   __device__ static KF load_q(const bf16_t* row, int f, int lane) {
     return *reinterpret_cast<const KF*>(row + 32 * f + 8 * (lane >> 4));
@@ -66,6 +77,12 @@ template <int D> struct Tr<bf16_t, D> {
   __device__ static f32x4 pv(f32x4 c, VF v, PF p) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p, c, 0, 0, 0);
   }
+  // two chunks at once: K index 8 g + e is key 4 g + e of chunk e / 4
+  __device__ static f32x4 pv2(f32x4 c, VF v0, VF v1, PF p0, PF p1) {
+    const KF a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const KF b = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
 };
 
 template <int D> struct Tr<float, D> {
@@ -75,10 +92,10 @@ template <int D> struct Tr<float, D> {
   using VF = f32x4;
   using PF = f32x4;
   __device__ static KF load_k(const float* blk, int f, int lane) {
-    return *reinterpret_cast<const KF*>(blk + (f * 64 + lane) * 4);
+    return nt_load<KF, i32x4>(blk + (f * 64 + lane) * 4);
   }
   __device__ static VF load_v(const float* blk, int db, int lane) {
-    return *reinterpret_cast<const VF*>(blk + (db * 16 + (lane & 15)) * 16 + 4 * (lane >> 4));
+    return nt_load<VF, i32x4>(blk + (db * 16 + (lane & 15)) * 16 + 4 * (lane >> 4));
   }
   __device__ static KF load_q(const float* row, int f, int lane) {
     const int g = lane >> 4;
@@ -103,6 +120,7 @@ template <int D> struct Tr<float, D> {
     for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(v[i], p[i], c, 0, 0, 0);
     return c;
   }
+  __device__ static f32x4 pv2(f32x4 c, VF v0, VF v1, PF p0, PF p1) { return pv(pv(c, v0, p0), v1, p1); }
 };
 
 // max / sum over the four lanes {l, l^16, l^32, l^48} that hold one query row
@@ -121,226 +139,264 @@ __device__ inline float row_sum4(float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <typename T, int D, int RB, int PFD>
-__device__ __forceinline__ void decode_item(const DecodeParams& p, const DecodeItem& it, int wave,
-                                            int lane, float* lds) {
+constexpr int kCachePolicyNT = 2;  // non-temporal cache policy bit of global_load_lds
+constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units): p <= 256
+
+// Q fragments of one 16-row block (B operand of S^T = K Q^T); rows past n_rows are 0.
+// Returns the output row of this lane's query row (-1 past n_rows).
+template <typename T, int D>
+__device__ __forceinline__ int load_q_block(const DecodeParams& p, const DecodeItem& it, int rb, int lane,
+                                            typename Tr<T, D>::KF (&qf)[Tr<T, D>::NF]) {
+  using TR = Tr<T, D>;
+  const int r = rb * 16 + (lane & 15);
+  const int G = p.group;
+  if (r < it.n_rows) {
+    const int reader = p.readers[it.reader_begin + r / G];
+    const int orow = reader * p.n_q_heads + it.kv_head * G + r % G;
+    const T* row = reinterpret_cast<const T*>(p.q) + (size_t)orow * D;
+#pragma unroll
+    for (int f = 0; f < TR::NF; ++f) qf[f] = TR::load_q(row, f, lane);
+    return orow;
+  }
+#pragma unroll
+  for (int f = 0; f < TR::NF; ++f) qf[f] = TR::zero_q();
+  return -1;
+}
+
+// Scores of one chunk for one 16-row block, scaled to log2 units, slots outside
+// [lo, hi) masked to -inf (their values zeroed so 0 * garbage cannot appear).
+template <typename T, int D>
+__device__ __forceinline__ f32x4 chunk_scores(const typename Tr<T, D>::KF (&kf)[Tr<T, D>::NF],
+                                              typename Tr<T, D>::VF (&vf)[Tr<T, D>::NDB],
+                                              const typename Tr<T, D>::KF (&qf)[Tr<T, D>::NF], int lohi, int g,
+                                              float scale_log2) {
+  using TR = Tr<T, D>;
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int f = 0; f < TR::NF; ++f) sc = TR::qk(sc, kf[f], qf[f]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sc[i] *= scale_log2;
+  if (lohi != (16 << 8)) {  // wave-uniform
+    const int lo = lohi & 0xff, hi = lohi >> 8;
+#pragma unroll
+    for (int db = 0; db < TR::NDB; ++db) vf[db] = TR::mask_v(vf[db], g, lo, hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * g + i;
+      if (t < lo || t >= hi) sc[i] = -INFINITY;
+    }
+  }
+  return sc;
+}
+
+// Online-softmax update of one 16-row block with two chunks (32 keys).
+template <typename T, int D>
+__device__ __forceinline__ void softmax_pair(const typename Tr<T, D>::KF (&k0)[Tr<T, D>::NF],
+                                             typename Tr<T, D>::VF (&v0)[Tr<T, D>::NDB],
+                                             const typename Tr<T, D>::KF (&k1)[Tr<T, D>::NF],
+                                             typename Tr<T, D>::VF (&v1)[Tr<T, D>::NDB],
+                                             const typename Tr<T, D>::KF (&qf)[Tr<T, D>::NF],
+                                             f32x4 (&o)[Tr<T, D>::NDB], float& m, float& l, int lohi0, int lohi1,
+                                             int g, float scale_log2) {
+  using TR = Tr<T, D>;
+  const f32x4 s0 = chunk_scores<T, D>(k0, v0, qf, lohi0, g, scale_log2);
+  const f32x4 s1 = chunk_scores<T, D>(k1, v1, qf, lohi1, g, scale_log2);
+  // Lazy rescale: the running max m only moves when some row's max exceeds it by
+  // more than kTau (log2 units), so p = 2^(s - m) stays below 2^kTau and the O
+  // rescale (a multiply of every accumulator) is skipped for most pairs.  The branch
+  // is wave-uniform (ballot).
+  const float lmx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                          fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+  if (__builtin_amdgcn_ballot_w64(lmx > m + kTau)) {
+    const float mn = fmaxf(m, row_max4(lmx));
+    const float alpha = fast_exp2(m - mn);
+    l *= alpha;
+    m = mn;
+#pragma unroll
+    for (int db = 0; db < TR::NDB; ++db) o[db] *= alpha;
+  }
+  f32x4 p0, p1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    p0[i] = fast_exp2(s0[i] - m);
+    p1[i] = fast_exp2(s1[i] - m);
+  }
+  l += ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
+  const typename TR::PF q0 = TR::pack(p0), q1 = TR::pack(p1);
+#pragma unroll
+  for (int db = 0; db < TR::NDB; ++db) o[db] = TR::pv2(o[db], v0[db], v1[db], q0, q1);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---- one work item: every chunk streamed from HBM once per workgroup into an LDS ring
+// with direct global->LDS loads (each wave loads a quarter of every chunk); wave w
+// computes rows [16 w, 16 w + 16) from LDS, two chunks per step; NB - 2 chunks stay in
+// flight; one workgroup barrier per step.
+template <typename T, int D>
+__device__ __forceinline__ void decode_item(const DecodeParams& p, const DecodeItem& it, int wave, int lane,
+                                            char* ring) {
   using TR = Tr<T, D>;
   constexpr int NF = TR::NF;
   constexpr int NDB = TR::NDB;
-  const int c16 = lane & 15;
-  const int g = lane >> 4;
-  const int G = p.group;
+  constexpr int HALF = kPage * D * (int)sizeof(T);  // bytes of one K (or V^T) block
+  constexpr int CB = 2 * HALF;                        // bytes of one chunk in the ring
+  constexpr int NB = kRingBytes / CB;                 // ring slots (even)
+  constexpr int LPW = CB / 1024 / kWaves;             // 1 KiB loads per wave per chunk
+  static_assert(LPW >= 1 && NB >= 4 && NB % 2 == 0, "ring shape");
+  const int c16 = lane & 15, g = lane >> 4;
+  const int n = it.n_chunks;
+  const bool active = wave * 16 < it.n_rows;
 
-  // ---- query fragments (B operand of S^T = K Q^T), one per row block and d slot
-  typename TR::KF qf[RB][NF];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int r = rb * 16 + c16;
-    if (r < it.n_rows) {
-      const int reader = p.readers[it.reader_begin + r / G];
-      const int head = it.kv_head * G + r % G;
-      const T* row = reinterpret_cast<const T*>(p.q) + ((size_t)reader * p.n_q_heads + head) * D;
-#pragma unroll
-      for (int f = 0; f < NF; ++f) qf[rb][f] = TR::load_q(row, f, lane);
-    } else {
-#pragma unroll
-      for (int f = 0; f < NF; ++f) qf[rb][f] = TR::zero_q();
-    }
-  }
+  // chunk metadata: lane j holds chunks j and 64 + j
+  const Chunk c0 = p.chunks[it.chunk_begin + (lane < n ? lane : 0)];
+  const Chunk c1 = p.chunks[it.chunk_begin + (64 + lane < n ? 64 + lane : 0)];
+  const int mp0 = c0.page, ml0 = c0.lohi, mp1 = c1.page, ml1 = c1.lohi;
 
-  // ---- this wave's chunks: item chunks wave, wave + 4, ...; lane j holds chunk j's metadata
-  const int n_my = it.n_chunks > wave ? (it.n_chunks - wave + kWaves - 1) / kWaves : 0;
-  int meta_page = 0, meta_lohi = 16 << 8;
-  if (lane < n_my) {
-    const Chunk c = p.chunks[it.chunk_begin + wave + kWaves * lane];
-    meta_page = c.page;
-    meta_lohi = c.lohi;
-  }
+  // head-major pool: head h's blocks are contiguous, page q at h * n_pages + q
+  const char* kbase = reinterpret_cast<const char*>(p.k_pages) + (size_t)it.kv_head * p.n_pages * HALF;
+  const char* vbase = reinterpret_cast<const char*>(p.v_pages) + (size_t)it.kv_head * p.n_pages * HALF;
+  const int my_off = wave * (CB / kWaves);  // this wave's byte range of every chunk
+  const char* my_base = my_off < HALF ? kbase + my_off : vbase + (my_off - HALF);
 
-  f32x4 o[RB][NDB];
-  float m[RB], l[RB];
+  auto issue = [&](int j) {
+    const int jj = j < n ? j : n - 1;  // past the end: reload the last chunk into an unread slot
+    const int page = jj < 64 ? __builtin_amdgcn_readlane(mp0, jj) : __builtin_amdgcn_readlane(mp1, jj - 64);
+    const char* src = my_base + (size_t)page * HALF + lane * 16;
+    char* dst = ring + (j % NB) * CB + my_off;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = -INFINITY;
-    l[rb] = 0.f;
+    for (int i = 0; i < LPW; ++i)
+      __builtin_amdgcn_global_load_lds(src + i * 1024, (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                                       16, 0, kCachePolicyNT);
+  };
+  auto lohi_of = [&](int j) {
+    if (j >= n) return 0;  // empty slot range: every key masked
+    return j < 64 ? __builtin_amdgcn_readlane(ml0, j) : __builtin_amdgcn_readlane(ml1, j - 64);
+  };
+  auto frags = [&](int j, typename TR::KF (&kf)[NF], typename TR::VF (&vf)[NDB]) {
+    const char* slot = ring + (j % NB) * CB;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const size_t page_elems = (size_t)p.n_kv_heads * kPage * D;
-  const T* kbase = reinterpret_cast<const T*>(p.k_pages) + (size_t)it.kv_head * kPage * D;
-  const T* vbase = reinterpret_cast<const T*>(p.v_pages) + (size_t)it.kv_head * kPage * D;
-
-  typename TR::KF kb[PFD][NF];
-  typename TR::VF vb[PFD][NDB];
-
-  auto issue = [&](int s, int j) {
-    const int jj = j < n_my ? j : n_my - 1;  // past the end: reload the last chunk (cache hit)
-    const int page = __builtin_amdgcn_readlane(meta_page, jj);
-    const T* kblk = kbase + (size_t)page * page_elems;
-    const T* vblk = vbase + (size_t)page * page_elems;
+    for (int f = 0; f < NF; ++f) kf[f] = *reinterpret_cast<const typename TR::KF*>(slot + f * 1024 + lane * 16);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) kb[s][f] = TR::load_k(kblk, f, lane);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) vb[s][db] = TR::load_v(vblk, db, lane);
+    for (int db = 0; db < NDB; ++db)
+      vf[db] = *reinterpret_cast<const typename TR::VF*>(slot + HALF + ((db * 16 + c16) * 16 + 4 * g) * (int)sizeof(T));
   };
 
-  if (n_my > 0) {
+  f32x4 o[NDB];
+  float m = -INFINITY, l = 0.f;
 #pragma unroll
-    for (int s = 0; s < PFD; ++s) issue(s, s);
-  }
+  for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int base = 0; base < n_my; base += PFD) {
 #pragma unroll
-    for (int s = 0; s < PFD; ++s) {
-      const int j = base + s;
-      if (j < n_my) {
-        const int lohi = __builtin_amdgcn_readlane(meta_lohi, j);
-        const bool full = lohi == (16 << 8);
-        const int lo = lohi & 0xff, hi = lohi >> 8;
-        typename TR::VF vv[NDB];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) vv[db] = full ? vb[s][db] : TR::mask_v(vb[s][db], g, lo, hi);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int f = 0; f < NF; ++f) sc = TR::qk(sc, kb[s][f], qf[rb][f]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sc[i] *= p.scale_log2;
-            if (!full) {
-              const int t = 4 * g + i;
-              if (t < lo || t >= hi) sc[i] = -INFINITY;
-            }
-          }
-          const float mx = row_max4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-          const float mn = fmaxf(m[rb], mx);
-          const float alpha = fast_exp2(m[rb] - mn);
-          f32x4 pr;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - mn);
-          l[rb] = l[rb] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-          m[rb] = mn;
-          const typename TR::PF pp = TR::pack(pr);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            o[rb][db] *= alpha;
-            o[rb][db] = TR::pv(o[rb][db], vv[db], pp);
-          }
-        }
-        issue(s, j + PFD);
-      }
+  for (int j = 0; j < NB - 2; ++j) issue(j);
+  typename TR::KF qf[NF];  // queries load while the ring fills
+  const int orow = load_q_block<T, D>(p, it, wave, lane, qf);
+
+  const int n_pairs = (n + 1) / 2;
+  for (int i = 0; i < n_pairs; ++i) {
+    wait_vmcnt<(NB - 4) * LPW>();            // this wave's quarters of chunks 2i, 2i+1 landed
+    asm volatile("s_barrier" ::: "memory");  // ... and every other wave's; the previous pair's slots are free
+    issue(2 * i + NB - 2);
+    issue(2 * i + NB - 1);
+    if (active) {
+      typename TR::KF k0[NF], k1[NF];
+      typename TR::VF v0[NDB], v1[NDB];
+      frags(2 * i, k0, v0);
+      frags(2 * i + 1, k1, v1);
+      softmax_pair<T, D>(k0, v0, k1, v1, qf, o, m, l, lohi_of(2 * i), lohi_of(2 * i + 1), g, p.scale_log2);
     }
   }
-
+  wait_vmcnt<0>();  // no load may land in LDS after the workgroup ends
+  if (active) {
+    l = row_sum4(l);
+    if (orow >= 0) {
+      const int slot = p.slot_map[it.slot_base + wave * 16 + c16];
+      const float inv = 1.f / l;
+      float* dst = p.part_o + (size_t)slot * D + 4 * g;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) l[rb] = row_sum4(l[rb]);
-
-  // ---- merge the 4 waves' states in LDS (deterministic order 1, 2, 3 into wave 0)
-  float* lm = lds;                 // [RB * 16] row max (log2 domain)
-  float* ll = lds + RB * 16;       // [RB * 16] row sum
-  float* lo_ = lds + RB * 32;      // [RB * NDB * 4][64] accumulators in register order
-  for (int w = 1; w < kWaves; ++w) {
-    __syncthreads();
-    if (wave == w) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (g == 0) {
-          lm[rb * 16 + c16] = m[rb];
-          ll[rb * 16 + c16] = l[rb];
-        }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) lo_[((rb * NDB + db) * 4 + i) * 64 + lane] = o[rb][db][i];
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float mw = lm[rb * 16 + c16];
-        const float lw = ll[rb * 16 + c16];
-        const float mn = fmaxf(m[rb], mw);
-        const float a = mn == -INFINITY ? 0.f : fast_exp2(m[rb] - mn);
-        const float b = mn == -INFINITY ? 0.f : fast_exp2(mw - mn);
-        l[rb] = l[rb] * a + lw * b;
-        m[rb] = mn;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            o[rb][db][i] = o[rb][db][i] * a + lo_[((rb * NDB + db) * 4 + i) * 64 + lane] * b;
-      }
+      for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[db] * inv;
+      if (g == 0) p.part_lse2[slot] = m + __log2f(l);
     }
   }
-
-  if (wave == 0) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int r = rb * 16 + c16;
-      if (r < it.n_rows) {
-        const int slot = it.partial_base + r;
-        const float inv = 1.f / l[rb];
-        float* dst = p.part_o + (size_t)slot * D + 4 * g;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          f32x4 v = o[rb][db] * inv;
-          *reinterpret_cast<f32x4*>(dst + 16 * db) = v;
-        }
-        if (g == 0) p.part_lse2[slot] = m[rb] + __log2f(l[rb]);
-      }
-    }
-  }
-}
-
-template <typename T, int D>
-constexpr int lds_floats() { return 4 * 32 + 4 * Tr<T, D>::NDB * 4 * 64; }
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void decode_kernel(DecodeParams p) {
-  __shared__ float lds[lds_floats<T, D>()];
-  const DecodeItem it = p.items[blockIdx.x];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (it.row_blocks == 1) decode_item<T, D, 1, 4>(p, it, wave, lane, lds);
-  else if (it.row_blocks == 2) decode_item<T, D, 2, 4>(p, it, wave, lane, lds);
-  else decode_item<T, D, 4, 3>(p, it, wave, lane, lds);
 }
 
 template <typename T> __device__ inline T from_f32(float x);
 template <> __device__ inline bf16_t from_f32<bf16_t>(float x) { return (bf16_t)x; }
 template <> __device__ inline float from_f32<float>(float x) { return x; }
 
+__device__ inline float wave_max(float x) {
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ inline float wave_sum(float x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// ---- merge: one wave per output row.  Every lane fetches one partial's lse (64 per
+// round), then the partial rows are summed with 16-byte loads, 256 / d partials per
+// load instruction, issued back to back.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  constexpr int LPR = D / 4;     // lanes per partial row
+  constexpr int PPI = 64 / LPR;  // partials per load instruction
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;
+  const int row = blockIdx.x * kWaves + wave;
   if (row >= p.n_rows) return;
-  constexpr int V = D / 64;
   const int b = p.row_ptr[row], e = p.row_ptr[row + 1];
-  float M = -INFINITY;
-  for (int j = b; j < e; ++j) M = fmaxf(M, p.part_lse2[p.part_idx[j]]);
-  float acc[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  const int sub = lane / LPR, col = lane % LPR;
+  // single-round fast path (<= 64 partials): the lse values stay in registers
+  const float lse0 = b + lane < e ? p.part_lse2[b + lane] : -INFINITY;
+  float M = lse0;
+  for (int j0 = b + 64; j0 < e; j0 += 64) M = fmaxf(M, j0 + lane < e ? p.part_lse2[j0 + lane] : -INFINITY);
+  M = wave_max(M);
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
   float S = 0.f;
-  for (int j = b; j < e; ++j) {
-    const int idx = p.part_idx[j];
-    const float w = fast_exp2(p.part_lse2[idx] - M);
-    S += w;
-    const float* src = p.part_o + (size_t)idx * D + lane * V;
+  for (int j0 = b; j0 < e; j0 += 64) {
+    const float my_lse = j0 == b ? lse0 : (j0 + lane < e ? p.part_lse2[j0 + lane] : -INFINITY);
+    const float my_w = j0 + lane < e ? fast_exp2(my_lse - M) : 0.f;
+    S += wave_sum(my_w);
+    const int cnt = min(64, e - j0);
+#pragma unroll 16
+    for (int jj = 0; jj < cnt; jj += PPI) {
+      const int j = jj + sub;
+      const bool ok = j < cnt;
+      float w = 0.f;
 #pragma unroll
-    for (int v = 0; v < V; ++v) acc[v] += w * src[v];
+      for (int k = 0; k < PPI; ++k) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), min(jj + k, 63)));
+        w = sub == k ? wk : w;
+      }
+      const f4 v = *reinterpret_cast<const f4*>(p.part_o + (size_t)(j0 + (ok ? j : jj)) * D + 4 * col);
+      acc += (ok ? w : 0.f) * v;
+    }
   }
-  T* out = reinterpret_cast<T*>(p.out) + (size_t)row * D + lane * V;
-  const float inv = S > 0.f ? 1.f / S : 0.f;
 #pragma unroll
-  for (int v = 0; v < V; ++v) out[v] = from_f32<T>(acc[v] * inv);
+  for (int off = 32; off >= LPR; off >>= 1)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
+  const float inv = S > 0.f ? 1.f / S : 0.f;
+  if (sub == 0) {
+    T* out = reinterpret_cast<T*>(p.out) + (size_t)row * D + 4 * col;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[c] = from_f32<T>(acc[c] * inv);
+  }
   if (p.lse && lane == 0) p.lse[row] = S > 0.f ? (M + __log2f(S)) * 0.69314718055994531f : -INFINITY;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[kRingBytes];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  decode_item<T, D>(p, p.items[blockIdx.x], wave, lane, lds);
 }
 
 // ---------------------------------------------------------------- page writes (append)
@@ -350,13 +406,13 @@ __global__ __launch_bounds__(256) void page_write_kernel(T* __restrict__ kp, T* 
                                                          const T* __restrict__ kn,
                                                          const T* __restrict__ vn,
                                                          const PageWrite* __restrict__ writes,
-                                                         int hkv) {
+                                                         int hkv, int pool_pages) {
   constexpr int E = 16 / sizeof(T);           // elements per 16-byte slot
   constexpr int NSLOT = kPage * D / E;        // 16-byte slots per block
   const PageWrite w = writes[blockIdx.x];
   const int h = blockIdx.y;
-  const size_t blk = ((size_t)w.dst_page * hkv + h) * kPage * D;
-  const size_t sblk = w.src_page >= 0 ? ((size_t)w.src_page * hkv + h) * kPage * D : 0;
+  const size_t blk = ((size_t)h * pool_pages + w.dst_page) * kPage * D;
+  const size_t sblk = w.src_page >= 0 ? ((size_t)h * pool_pages + w.src_page) * kPage * D : 0;
   typedef T vec_t __attribute__((__vector_size__(16)));
   for (int sn = threadIdx.x; sn < NSLOT; sn += blockDim.x) {
     const int t = sn & 15, fg = sn >> 4, f = fg >> 2, g = fg & 3;
@@ -407,7 +463,7 @@ hipError_t launch_decode(int dtype, int d, const DecodeParams& p, hipStream_t s)
 template <typename T, int D>
 static hipError_t merge_t(const MergeParams& p, hipStream_t s) {
   if (p.n_rows == 0) return hipSuccess;
-  merge_kernel<T, D><<<(p.n_rows + 3) / 4, 256, 0, s>>>(p);
+  merge_kernel<T, D><<<(p.n_rows + kWaves - 1) / kWaves, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -420,20 +476,20 @@ hipError_t launch_merge(int dtype, int d, const MergeParams& p, hipStream_t s) {
 }
 
 template <typename T, int D>
-static hipError_t page_write_t(int hkv, void* kp, void* vp, const void* kn, const void* vn,
+static hipError_t page_write_t(int hkv, int pool_pages, void* kp, void* vp, const void* kn, const void* vn,
                                const PageWrite* w, int n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   dim3 grid(n, hkv);
-  page_write_kernel<T, D><<<grid, 256, 0, s>>>((T*)kp, (T*)vp, (const T*)kn, (const T*)vn, w, hkv);
+  page_write_kernel<T, D><<<grid, 256, 0, s>>>((T*)kp, (T*)vp, (const T*)kn, (const T*)vn, w, hkv, pool_pages);
   return hipGetLastError();
 }
 
-hipError_t launch_page_write(int dtype, int d, int hkv, void* kp, void* vp, const void* kn,
+hipError_t launch_page_write(int dtype, int d, int hkv, int pool_pages, void* kp, void* vp, const void* kn,
                              const void* vn, const PageWrite* w, int n, hipStream_t s) {
-  if (dtype == 0 && d == 128) return page_write_t<bf16_t, 128>(hkv, kp, vp, kn, vn, w, n, s);
-  if (dtype == 0 && d == 64) return page_write_t<bf16_t, 64>(hkv, kp, vp, kn, vn, w, n, s);
-  if (dtype == 1 && d == 128) return page_write_t<float, 128>(hkv, kp, vp, kn, vn, w, n, s);
-  if (dtype == 1 && d == 64) return page_write_t<float, 64>(hkv, kp, vp, kn, vn, w, n, s);
+  if (dtype == 0 && d == 128) return page_write_t<bf16_t, 128>(hkv, pool_pages, kp, vp, kn, vn, w, n, s);
+  if (dtype == 0 && d == 64) return page_write_t<bf16_t, 64>(hkv, pool_pages, kp, vp, kn, vn, w, n, s);
+  if (dtype == 1 && d == 128) return page_write_t<float, 128>(hkv, pool_pages, kp, vp, kn, vn, w, n, s);
+  if (dtype == 1 && d == 64) return page_write_t<float, 64>(hkv, pool_pages, kp, vp, kn, vn, w, n, s);
   return hipErrorInvalidValue;
 }
 

@@ -153,6 +153,7 @@ int kv_drop(kv_pool_t* P, kv_seq_t seq, const int64_t* begin, const int64_t* len
       cp.epoch = P->epoch + 1;
       cp.n_pages = (int32_t)n_list;
       cp.n_kv_heads = P->cfg.n_kv_heads;
+      cp.pool_pages = P->cfg.n_pages;
       e = launch_compact(P->cfg.dtype, D, cp, s);
       if (e == hipSuccess) {
         P->ticket = (int32_t)((uint32_t)P->ticket + (uint32_t)n_list);

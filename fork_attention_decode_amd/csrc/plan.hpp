@@ -10,7 +10,8 @@ namespace fa {
 constexpr int kPage = 16;        // tokens per page on device pools
 constexpr int kMaxRows = 64;     // query rows per decode work item (4 MFMA row blocks of 16)
 constexpr int kWaves = 4;        // waves per decode workgroup
-constexpr int kMaxChunksPerWave = 64;
+constexpr int kMaxItemChunks = 128;     // chunk metadata in two registers per lane
+constexpr int kRingBytes = 65536;       // LDS ring of a wide item
 
 // One page write of kv_append / kv_write: slots [lo, hi) of dst_page receive new tokens
 // tok_base, tok_base + 1, ...; when src_page >= 0 (copy-on-write) every other slot is
@@ -29,43 +30,46 @@ struct Chunk {
 };
 
 // One decode work item: chunks [chunk_begin, chunk_begin + n_chunks) of one segment,
-// for KV head kv_head and the segment's rows (n_readers * G rows, <= kMaxRows).
-// The kWaves waves of the workgroup take the item's chunks round robin and merge
-// their softmax states in LDS; the result is one partial (lse2, o) per row.
+// for KV head kv_head and up to 64 of the segment's rows (n_readers * G).  The
+// workgroup streams every chunk once into an LDS ring and wave w computes rows
+// [16 w, 16 w + 16).  Row r of the item writes its partial to slot_map[slot_base + r].
 struct DecodeItem {
   int32_t chunk_begin;
   int32_t n_chunks;
   int32_t kv_head;
   int32_t reader_begin;  // index into the readers array (query indices)
   int32_t n_rows;
-  int32_t partial_base;
-  int32_t row_blocks;    // 1, 2 or 4 blocks of 16 rows
-  int32_t pad;
+  int32_t slot_base;
+  int32_t pad[2];
 };
 
+// Decode launch: one workgroup per work item.
 struct DecodeParams {
-  const void* q;          // [n_seqs][Hq][d]
+  const void* q;            // [n_seqs][Hq][d]
   const void* k_pages;
   const void* v_pages;
   const DecodeItem* items;
   const Chunk* chunks;
   const int32_t* readers;
-  float* part_lse2;       // [n_partials] log2-domain log-sum-exp of the partial
-  float* part_o;          // [n_partials][d] normalised partial output
+  const int32_t* slot_map;  // item row -> partial slot (slots are ordered by output row)
+  float* part_lse2;         // [n_partials] log2-domain log-sum-exp of the partial
+  float* part_o;            // [n_partials][d] normalised partial output
   int32_t n_items;
   int32_t n_q_heads;
   int32_t n_kv_heads;
-  int32_t group;          // Hq / Hkv
-  float scale_log2;       // sm_scale * log2(e)
+  int32_t n_pages;          // pool capacity: head h's blocks start at h * n_pages
+  int32_t group;            // Hq / Hkv
+  float scale_log2;         // sm_scale * log2(e)
 };
 
+// Merge launch: output row r (= query * Hq + head) owns the partial slots
+// [row_ptr[r], row_ptr[r + 1]).
 struct MergeParams {
-  const int32_t* row_ptr;  // [n_rows + 1]
-  const int32_t* part_idx;
+  const int32_t* row_ptr;   // [n_rows + 1]
   const float* part_lse2;
   const float* part_o;
-  void* out;               // [n_rows][d]
-  float* lse;              // [n_rows] natural log, or null
+  void* out;                // [n_rows][d]
+  float* lse;               // [n_rows] natural log, or null
   int32_t n_rows;
 };
 
@@ -95,11 +99,12 @@ struct CompactParams {
   int32_t* errors;           // incremented if a wait gives up (never expected)
   int32_t ticket_base;
   int32_t epoch;
-  int32_t n_pages;
+  int32_t n_pages;           // destination pages in this launch
   int32_t n_kv_heads;
+  int32_t pool_pages;        // pool capacity: head h's blocks start at h * pool_pages
 };
 
-hipError_t launch_page_write(int dtype, int d, int hkv, void* k_pages, void* v_pages,
+hipError_t launch_page_write(int dtype, int d, int hkv, int pool_pages, void* k_pages, void* v_pages,
                              const void* k_new, const void* v_new, const PageWrite* writes,
                              int n_writes, hipStream_t s);
 hipError_t launch_decode(int dtype, int d, const DecodeParams& p, hipStream_t s);

@@ -14,8 +14,9 @@
 //      (public = many readers, private = one);
 //   3. per segment, reader groups of at most 64 / G readers (64 MFMA rows), per KV head,
 //      the chunk list is cut into work items of about equal bytes sized so the whole
-//      decode is about one workgroup per compute unit;
-//   4. every (item, row) owns one partial slot; a CSR lists each output row's partials.
+//      decode is about two workgroups per compute unit;
+//   4. every (item, row) owns one partial slot; slots are ordered by output row, so a
+//      row's partials are contiguous; the same launch merges them.
 #include "pool.hpp"
 
 #include <algorithm>
@@ -133,25 +134,25 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq) {
     a = b;
   }
 
-  // 3. work items
+  // 3. work items of <= 64 rows and <= kMaxItemChunks chunks, sized so the decode is
+  // about two workgroups per compute unit.
   const int32_t per_group = std::max(1, kMaxRows / G);
   int64_t total = 0;
   for (const Segment& s : segs) {
     const int64_t groups = ((int64_t)s.readers.size() + per_group - 1) / per_group;
     total += (int64_t)s.chunks.size() * C.n_kv_heads * groups;
   }
-  const int64_t target_items = std::max<int64_t>(1, P->n_cu);
-  int64_t cpi = (total + target_items - 1) / target_items;
-  cpi = std::max<int64_t>(cpi, 2 * kWaves);
-  cpi = std::min<int64_t>(cpi, (int64_t)kWaves * kMaxChunksPerWave);
+  const int64_t target_items = std::max<int64_t>(1, 2 * (int64_t)P->n_cu);
+  const int64_t cpi = std::min<int64_t>(kMaxItemChunks,
+                                        std::max<int64_t>(8, (total + target_items - 1) / target_items));
 
   std::vector<Chunk> chunks;
   std::vector<int32_t> readers;
   std::vector<DecodeItem> items;
+  std::vector<int32_t> item_rows;  // output row of every item row, in item order
   int64_t unique_tokens = 0;
   const int32_t n_out = n * hq;
-  std::vector<std::vector<int32_t>> row_parts((size_t)n_out);
-  int32_t n_part = 0;
+  std::vector<int32_t> row_count((size_t)n_out, 0);
   for (const Segment& s : segs) {
     const int32_t cbase = (int32_t)chunks.size();
     chunks.insert(chunks.end(), s.chunks.begin(), s.chunks.end());
@@ -172,38 +173,38 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq) {
           it.kv_head = h;
           it.reader_begin = rbase;
           it.n_rows = rows;
-          it.partial_base = n_part;
-          it.row_blocks = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
-          it.pad = 0;
+          it.slot_base = (int32_t)item_rows.size();
+          it.pad[0] = it.pad[1] = 0;
           for (int32_t r = 0; r < rows; ++r) {
             const int32_t q = s.readers[g0 + r / G];
-            row_parts[(size_t)q * hq + h * G + r % G].push_back(n_part + r);
+            const int32_t orow = q * hq + h * G + r % G;
+            item_rows.push_back(orow);
+            row_count[orow]++;
           }
-          n_part += rows;
           items.push_back(it);
         }
       }
     }
   }
+  // partial slots ordered by output row: row r owns [mptr[r], mptr[r + 1])
+  std::vector<int32_t> mptr((size_t)n_out + 1, 0);
+  for (int32_t r = 0; r < n_out; ++r) mptr[r + 1] = mptr[r] + row_count[r];
+  const int32_t n_part = mptr[n_out];
+  std::vector<int32_t> slot_map(item_rows.size()), fill(mptr.begin(), mptr.end() - 1);
+  for (size_t i = 0; i < item_rows.size(); ++i) slot_map[i] = fill[item_rows[i]]++;
   // heaviest items first
-  std::stable_sort(items.begin(), items.end(), [](const DecodeItem& a, const DecodeItem& b) {
-    return (int64_t)a.n_chunks * (2 + a.row_blocks) > (int64_t)b.n_chunks * (2 + b.row_blocks);
-  });
-  std::vector<int32_t> mptr((size_t)n_out + 1, 0), midx;
-  midx.reserve((size_t)n_part);
-  for (int32_t r = 0; r < n_out; ++r) {
-    midx.insert(midx.end(), row_parts[r].begin(), row_parts[r].end());
-    mptr[r + 1] = (int32_t)midx.size();
-  }
+  std::stable_sort(items.begin(), items.end(),
+                   [](const DecodeItem& a, const DecodeItem& b) { return a.n_chunks > b.n_chunks; });
 
-  // 4. workspace image
+  // 4. workspace image: [items | chunks | readers | row_ptr | slot map] is uploaded,
+  // then the partials
   const int D = C.head_dim;
   size_t off = 0;
   pc.off_items = off; off = align256(off + items.size() * sizeof(DecodeItem));
   pc.off_chunks = off; off = align256(off + chunks.size() * sizeof(Chunk));
   pc.off_readers = off; off = align256(off + readers.size() * sizeof(int32_t));
   pc.off_mptr = off; off = align256(off + mptr.size() * sizeof(int32_t));
-  pc.off_midx = off; off = align256(off + midx.size() * sizeof(int32_t));
+  pc.off_midx = off; off = align256(off + slot_map.size() * sizeof(int32_t));
   const size_t plan_bytes = off;
   pc.off_plse = off; off = align256(off + (size_t)n_part * sizeof(float));
   pc.off_po = off; off = align256(off + (size_t)n_part * D * sizeof(float));
@@ -213,7 +214,7 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq) {
   put(pc.blob, pc.off_chunks, chunks);
   put(pc.blob, pc.off_readers, readers);
   put(pc.blob, pc.off_mptr, mptr);
-  put(pc.blob, pc.off_midx, midx);
+  put(pc.blob, pc.off_midx, slot_map);
   pc.n_items = (int32_t)items.size();
   pc.n_out_rows = n_out;
   const size_t es = C.dtype == KV_F32 ? 4 : 2;
@@ -272,18 +273,19 @@ int fork_attn_decode(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, 
   dp.items = reinterpret_cast<const DecodeItem*>(w + pc.off_items);
   dp.chunks = reinterpret_cast<const Chunk*>(w + pc.off_chunks);
   dp.readers = reinterpret_cast<const int32_t*>(w + pc.off_readers);
+  dp.slot_map = reinterpret_cast<const int32_t*>(w + pc.off_midx);
   dp.part_lse2 = reinterpret_cast<float*>(w + pc.off_plse);
   dp.part_o = reinterpret_cast<float*>(w + pc.off_po);
   dp.n_items = pc.n_items;
   dp.n_q_heads = hq;
   dp.n_kv_heads = P->cfg.n_kv_heads;
+  dp.n_pages = P->cfg.n_pages;
   dp.group = hq / P->cfg.n_kv_heads;
   dp.scale_log2 = sm_scale * 1.4426950408889634f;
   e = launch_decode(P->cfg.dtype, P->cfg.head_dim, dp, s);
   if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   MergeParams mp;
   mp.row_ptr = reinterpret_cast<const int32_t*>(w + pc.off_mptr);
-  mp.part_idx = reinterpret_cast<const int32_t*>(w + pc.off_midx);
   mp.part_lse2 = dp.part_lse2;
   mp.part_o = dp.part_o;
   mp.out = out;

@@ -327,7 +327,7 @@ static int write_tokens(kv_pool* P, kv_seq_t seq, int64_t start, int64_t n, cons
     char* area = P->ws + fa_ws_plan_offset(&P->cfg);
     hipError_t e = fa_upload(P, area, writes.data(), writes.size() * sizeof(PageWrite), s);
     if (e == hipSuccess)
-      e = launch_page_write(P->cfg.dtype, P->cfg.head_dim, P->cfg.n_kv_heads, P->k, P->v, k, v,
+      e = launch_page_write(P->cfg.dtype, P->cfg.head_dim, P->cfg.n_kv_heads, P->cfg.n_pages, P->k, P->v, k, v,
                             reinterpret_cast<const PageWrite*>(area), (int)writes.size(), s);
     if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("page write: ") + hipGetErrorString(e));
   }
@@ -463,7 +463,7 @@ int kv_pool_read_page(kv_pool_t* P, int32_t page, int32_t head, void* k_out, voi
   const int D = P->cfg.head_dim;
   const size_t es = dtype_size(P->cfg.dtype);
   const size_t blk = (size_t)kPage * D * es;
-  const size_t off = ((size_t)page * P->cfg.n_kv_heads + head) * blk;
+  const size_t off = ((size_t)head * P->cfg.n_pages + page) * blk;
   std::vector<char> kr(blk), vr(blk);
   hipError_t e = hipMemcpyAsync(kr.data(), (char*)P->k + off, blk, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipMemcpyAsync(vr.data(), (char*)P->v + off, blk, hipMemcpyDeviceToHost, s);

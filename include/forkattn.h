@@ -76,8 +76,9 @@ typedef struct {
 /* ---------------------------------------------------------------------------------
  * Device page layout (one page = page_size tokens of every KV head).
  *
- * k_pages and v_pages each hold n_pages * Hkv blocks; block (page p, head h) starts at
- * element (p * Hkv + h) * 16 * d.  Inside a block:
+ * k_pages and v_pages each hold Hkv * n_pages blocks, head-major: block (page p, head h)
+ * starts at element (h * n_pages + p) * 16 * d, so the pages one decode work item
+ * streams for one head are contiguous whenever their ids are.  Inside a block:
  *   K is stored in matrix-core operand order: the block is a sequence of 16-byte slots
  *     indexed (f, g, t) with slot number (f * 4 + g) * 16 + t, and slot (f, g, t) holds
  *       bf16: K[t][32 f + 8 g + e],      e = 0..7   (f < d/32)
