@@ -142,25 +142,19 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kCachePolicyNT = 2;  // non-temporal cache policy bit of global_load_lds
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units): p <= 256
 
-// Q fragments of one 16-row block (B operand of S^T = K Q^T); rows past n_rows are 0.
-// Returns the output row of this lane's query row (-1 past n_rows).
+// Q fragments of this lane's query row (B operand of S^T = K Q^T); zero past n_rows.
 template <typename T, int D>
-__device__ __forceinline__ int load_q_block(const DecodeParams& p, const DecodeItem& it, int rb, int lane,
-                                            typename Tr<T, D>::KF (&qf)[Tr<T, D>::NF]) {
+__device__ __forceinline__ void load_q_row(const DecodeParams& p, int orow, int lane,
+                                           typename Tr<T, D>::KF (&qf)[Tr<T, D>::NF]) {
   using TR = Tr<T, D>;
-  const int r = rb * 16 + (lane & 15);
-  const int G = p.group;
-  if (r < it.n_rows) {
-    const int reader = p.readers[it.reader_begin + r / G];
-    const int orow = reader * p.n_q_heads + it.kv_head * G + r % G;
+  if (orow >= 0) {
     const T* row = reinterpret_cast<const T*>(p.q) + (size_t)orow * D;
 #pragma unroll
     for (int f = 0; f < TR::NF; ++f) qf[f] = TR::load_q(row, f, lane);
-    return orow;
-  }
+  } else {
 #pragma unroll
-  for (int f = 0; f < TR::NF; ++f) qf[f] = TR::zero_q();
-  return -1;
+    for (int f = 0; f < TR::NF; ++f) qf[f] = TR::zero_q();
+  }
 }
 
 // Scores of one chunk for one 16-row block, scaled to log2 units, slots outside
@@ -227,6 +221,14 @@ __device__ __forceinline__ void softmax_pair(const typename Tr<T, D>::KF (&k0)[T
   for (int db = 0; db < TR::NDB; ++db) o[db] = TR::pv2(o[db], v0[db], v1[db], q0, q1);
 }
 
+// LDS ring slots of one chunk each (K block + V^T block): about kRingBytes, even, >= 4.
+template <typename T, int D>
+constexpr int ring_slots() {
+  constexpr int cb = 2 * kPage * D * (int)sizeof(T);
+  constexpr int nb = (kRingBytes / cb) & ~1;
+  return nb < 4 ? 4 : nb;
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -239,28 +241,32 @@ __device__ __forceinline__ void wait_vmcnt() {
 // computes rows [16 w, 16 w + 16) from LDS, two chunks per step; NB - 2 chunks stay in
 // flight; one workgroup barrier per step.
 template <typename T, int D>
-__device__ __forceinline__ void decode_item(const DecodeParams& p, const DecodeItem& it, int wave, int lane,
-                                            char* ring) {
+__device__ __forceinline__ void decode_item(const DecodeParams& p, const int32_t* __restrict__ rec, int wave,
+                                            int lane, char* ring) {
   using TR = Tr<T, D>;
   constexpr int NF = TR::NF;
   constexpr int NDB = TR::NDB;
   constexpr int HALF = kPage * D * (int)sizeof(T);  // bytes of one K (or V^T) block
   constexpr int CB = 2 * HALF;                        // bytes of one chunk in the ring
-  constexpr int NB = kRingBytes / CB;                 // ring slots (even)
+  constexpr int NB = ring_slots<T, D>();              // ring slots (even)
   constexpr int LPW = CB / 1024 / kWaves;             // 1 KiB loads per wave per chunk
   static_assert(LPW >= 1 && NB >= 4 && NB % 2 == 0, "ring shape");
   const int c16 = lane & 15, g = lane >> 4;
-  const int n = it.n_chunks;
-  const bool active = wave * 16 < it.n_rows;
-
-  // chunk metadata: lane j holds chunks j and 64 + j
-  const Chunk c0 = p.chunks[it.chunk_begin + (lane < n ? lane : 0)];
-  const Chunk c1 = p.chunks[it.chunk_begin + (64 + lane < n ? 64 + lane : 0)];
-  const int mp0 = c0.page, ml0 = c0.lohi, mp1 = c1.page, ml1 = c1.lohi;
+  // one round of independent loads: header (scalar), chunk metadata (lane j holds
+  // chunks j and 64 + j) and this lane's row; the record is fixed size, so every
+  // address is in bounds and entries past the counts are simply never used
+  const int n = rec[0];
+  const int kv_head = rec[1];
+  const bool active = wave * 16 < rec[2];
+  const int2 c0 = reinterpret_cast<const int2*>(rec + kRecChunk)[lane];
+  const int2 c1 = reinterpret_cast<const int2*>(rec + kRecChunk)[64 + lane];
+  const int mp0 = c0.x, ml0 = c0.y, mp1 = c1.x, ml1 = c1.y;
+  const int orow = rec[kRecRow + wave * 16 + c16];
+  const int slot = rec[kRecSlot + wave * 16 + c16];
 
   // head-major pool: head h's blocks are contiguous, page q at h * n_pages + q
-  const char* kbase = reinterpret_cast<const char*>(p.k_pages) + (size_t)it.kv_head * p.n_pages * HALF;
-  const char* vbase = reinterpret_cast<const char*>(p.v_pages) + (size_t)it.kv_head * p.n_pages * HALF;
+  const char* kbase = reinterpret_cast<const char*>(p.k_pages) + (size_t)kv_head * p.n_pages * HALF;
+  const char* vbase = reinterpret_cast<const char*>(p.v_pages) + (size_t)kv_head * p.n_pages * HALF;
   const int my_off = wave * (CB / kWaves);  // this wave's byte range of every chunk
   const char* my_base = my_off < HALF ? kbase + my_off : vbase + (my_off - HALF);
 
@@ -295,7 +301,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, const DecodeI
 #pragma unroll
   for (int j = 0; j < NB - 2; ++j) issue(j);
   typename TR::KF qf[NF];  // queries load while the ring fills
-  const int orow = load_q_block<T, D>(p, it, wave, lane, qf);
+  load_q_row<T, D>(p, orow, lane, qf);
 
   const int n_pairs = (n + 1) / 2;
   for (int i = 0; i < n_pairs; ++i) {
@@ -315,7 +321,6 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, const DecodeI
   if (active) {
     l = row_sum4(l);
     if (orow >= 0) {
-      const int slot = p.slot_map[it.slot_base + wave * 16 + c16];
       const float inv = 1.f / l;
       float* dst = p.part_o + (size_t)slot * D + 4 * g;
 #pragma unroll
@@ -338,44 +343,64 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// ---- merge: one wave per output row.  Every lane fetches one partial's lse (64 per
-// round), then the partial rows are summed with 16-byte loads, 256 / d partials per
-// load instruction, issued back to back.
+// ---- merge: one wave per output row.  The row's partials sit at the fixed-stride block
+// [row * max_parts, ...), so the count, the lse values (one per lane) and the partial
+// rows (16-byte loads, 256 / d partials per load instruction) are all fetched in one
+// round trip; slots past the count are masked with selects, never multiplied in.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   typedef float f4 __attribute__((ext_vector_type(4)));
-  constexpr int LPR = D / 4;     // lanes per partial row
-  constexpr int PPI = 64 / LPR;  // partials per load instruction
+  constexpr int LPR = D / 4;      // lanes per partial row
+  constexpr int PPI = 64 / LPR;   // partials per load instruction
+  constexpr int NL = 64 / PPI;    // load instructions per 64 partials
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kWaves + wave;
   if (row >= p.n_rows) return;
-  const int b = p.row_ptr[row], e = p.row_ptr[row + 1];
   const int sub = lane / LPR, col = lane % LPR;
-  // single-round fast path (<= 64 partials): the lse values stay in registers
-  const float lse0 = b + lane < e ? p.part_lse2[b + lane] : -INFINITY;
-  float M = lse0;
-  for (int j0 = b + 64; j0 < e; j0 += 64) M = fmaxf(M, j0 + lane < e ? p.part_lse2[j0 + lane] : -INFINITY);
-  M = wave_max(M);
+  const int maxp = p.max_parts;
+  const size_t base = (size_t)row * maxp;
+  const int cnt = p.count[row];
   f4 acc = {0.f, 0.f, 0.f, 0.f};
-  float S = 0.f;
-  for (int j0 = b; j0 < e; j0 += 64) {
-    const float my_lse = j0 == b ? lse0 : (j0 + lane < e ? p.part_lse2[j0 + lane] : -INFINITY);
-    const float my_w = j0 + lane < e ? fast_exp2(my_lse - M) : 0.f;
-    S += wave_sum(my_w);
-    const int cnt = min(64, e - j0);
-#pragma unroll 16
-    for (int jj = 0; jj < cnt; jj += PPI) {
-      const int j = jj + sub;
-      const bool ok = j < cnt;
+  float M = -INFINITY, S = 0.f;
+  if (maxp <= 64) {
+    const float my_lse = lane < maxp ? p.part_lse2[base + lane] : -INFINITY;
+    f4 v[NL];
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
+      const int j = k * PPI + sub;
+      v[k] = j < maxp ? *reinterpret_cast<const f4*>(p.part_o + (base + j) * D + 4 * col) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+    M = wave_max(lane < cnt ? my_lse : -INFINITY);
+    const float my_w = lane < cnt ? fast_exp2(my_lse - M) : 0.f;
+    S = wave_sum(my_w);
+#pragma unroll
+    for (int k = 0; k < NL; ++k) {
       float w = 0.f;
 #pragma unroll
-      for (int k = 0; k < PPI; ++k) {
-        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), min(jj + k, 63)));
-        w = sub == k ? wk : w;
+      for (int q = 0; q < PPI; ++q) {
+        const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k * PPI + q));
+        w = sub == q ? wq : w;
       }
-      const f4 v = *reinterpret_cast<const f4*>(p.part_o + (size_t)(j0 + (ok ? j : jj)) * D + 4 * col);
-      acc += (ok ? w : 0.f) * v;
+      const int j = k * PPI + sub;
+      acc = j < cnt ? acc + w * v[k] : acc;
+    }
+  } else {
+    for (int j0 = 0; j0 < cnt; j0 += 64)
+      M = fmaxf(M, j0 + lane < cnt ? p.part_lse2[base + j0 + lane] : -INFINITY);
+    M = wave_max(M);
+    for (int j0 = 0; j0 < cnt; j0 += 64) {
+      const float my_w = j0 + lane < cnt ? fast_exp2(p.part_lse2[base + j0 + lane] - M) : 0.f;
+      S += wave_sum(my_w);
+      for (int k = 0; k < NL; ++k) {
+        float w = 0.f;
+        for (int q = 0; q < PPI; ++q) {
+          const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k * PPI + q));
+          w = sub == q ? wq : w;
+        }
+        const int j = j0 + k * PPI + sub;
+        if (j < cnt) acc += w * *reinterpret_cast<const f4*>(p.part_o + (base + j) * D + 4 * col);
+      }
     }
   }
 #pragma unroll
@@ -393,10 +418,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[kRingBytes];
+  __shared__ __attribute__((aligned(16))) char lds[ring_slots<T, D>() * 2 * kPage * D * sizeof(T)];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  decode_item<T, D>(p, p.items[blockIdx.x], wave, lane, lds);
+  decode_item<T, D>(p, p.items + (size_t)blockIdx.x * kRecInts, wave, lane, lds);
 }
 
 // ---------------------------------------------------------------- page writes (append)

@@ -29,48 +29,45 @@ struct Chunk {
   int32_t lohi;  // lo | hi << 8, 0 <= lo < hi <= 16
 };
 
-// One decode work item: chunks [chunk_begin, chunk_begin + n_chunks) of one segment,
-// for KV head kv_head and up to 64 of the segment's rows (n_readers * G).  The
-// workgroup streams every chunk once into an LDS ring and wave w computes rows
-// [16 w, 16 w + 16).  Row r of the item writes its partial to slot_map[slot_base + r].
-struct DecodeItem {
-  int32_t chunk_begin;
-  int32_t n_chunks;
-  int32_t kv_head;
-  int32_t reader_begin;  // index into the readers array (query indices)
-  int32_t n_rows;
-  int32_t slot_base;
-  int32_t pad[2];
-};
+// One decode work item: up to kMaxItemChunks chunks of one segment, for KV head kv_head
+// and up to 64 of the segment's rows (n_readers * G).  The workgroup streams every chunk
+// once into an LDS ring and wave w computes rows [16 w, 16 w + 16).
+// Items are self-contained fixed-stride records, so a workgroup finds everything it
+// needs with one round of independent loads (no pointer chasing before its first
+// K / V load):
+//   int32 [0, 4)          n_chunks, kv_head, n_rows, 0
+//   int32 [4, 68)         output row (query * Hq + head) of item row r, -1 past n_rows
+//   int32 [68, 132)       partial slot of item row r
+//   int32 [132, 388)      chunks: (page, lo | hi << 8) pairs
+constexpr int kRecRow = 4;
+constexpr int kRecSlot = 68;
+constexpr int kRecChunk = 132;
+constexpr int kRecInts = 416;  // 1664-byte stride
 
-// Decode launch: one workgroup per work item.
+// Decode launch: one workgroup per item record.
 struct DecodeParams {
   const void* q;            // [n_seqs][Hq][d]
   const void* k_pages;
   const void* v_pages;
-  const DecodeItem* items;
-  const Chunk* chunks;
-  const int32_t* readers;
-  const int32_t* slot_map;  // item row -> partial slot (slots are ordered by output row)
+  const int32_t* items;     // [n_items][kRecInts]
   float* part_lse2;         // [n_partials] log2-domain log-sum-exp of the partial
   float* part_o;            // [n_partials][d] normalised partial output
   int32_t n_items;
-  int32_t n_q_heads;
-  int32_t n_kv_heads;
   int32_t n_pages;          // pool capacity: head h's blocks start at h * n_pages
-  int32_t group;            // Hq / Hkv
   float scale_log2;         // sm_scale * log2(e)
 };
 
 // Merge launch: output row r (= query * Hq + head) owns the partial slots
-// [row_ptr[r], row_ptr[r + 1]).
+// [r * max_parts, r * max_parts + count[r]); the rest of its block is never read
+// into the result (masked by selects).
 struct MergeParams {
-  const int32_t* row_ptr;   // [n_rows + 1]
+  const int32_t* count;     // [n_rows] partials of each output row
   const float* part_lse2;
   const float* part_o;
   void* out;                // [n_rows][d]
   float* lse;               // [n_rows] natural log, or null
   int32_t n_rows;
+  int32_t max_parts;
 };
 
 // Drop / repos compaction: one record per destination page to (re)write.  Slots

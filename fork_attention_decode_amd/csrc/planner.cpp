@@ -146,81 +146,86 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq) {
   const int64_t cpi = std::min<int64_t>(kMaxItemChunks,
                                         std::max<int64_t>(8, (total + target_items - 1) / target_items));
 
-  std::vector<Chunk> chunks;
-  std::vector<int32_t> readers;
-  std::vector<DecodeItem> items;
-  std::vector<int32_t> item_rows;  // output row of every item row, in item order
-  int64_t unique_tokens = 0;
+  struct Item {
+    int32_t chunk_begin, n_chunks, kv_head, rows;
+    const Segment* seg;
+    size_t g0;
+    std::vector<int32_t> orow;
+  };
+  std::vector<Item> items;
+  int64_t unique_tokens = 0, n_chunks_total = 0;
   const int32_t n_out = n * hq;
   std::vector<int32_t> row_count((size_t)n_out, 0);
   for (const Segment& s : segs) {
-    const int32_t cbase = (int32_t)chunks.size();
-    chunks.insert(chunks.end(), s.chunks.begin(), s.chunks.end());
     for (const Chunk& c : s.chunks) unique_tokens += (c.lohi >> 8) - (c.lohi & 0xff);
+    n_chunks_total += (int64_t)s.chunks.size();
     const int32_t nc = (int32_t)s.chunks.size();
     const int32_t n_it = (int32_t)((nc + cpi - 1) / cpi);
     for (size_t g0 = 0; g0 < s.readers.size(); g0 += per_group) {
       const int32_t ng = (int32_t)std::min<size_t>(per_group, s.readers.size() - g0);
-      const int32_t rbase = (int32_t)readers.size();
-      readers.insert(readers.end(), s.readers.begin() + g0, s.readers.begin() + g0 + ng);
       const int32_t rows = ng * G;
       for (int32_t h = 0; h < C.n_kv_heads; ++h) {
         for (int32_t t = 0; t < n_it; ++t) {
           const int32_t c0 = (int32_t)((int64_t)nc * t / n_it), c1 = (int32_t)((int64_t)nc * (t + 1) / n_it);
-          DecodeItem it;
-          it.chunk_begin = cbase + c0;
-          it.n_chunks = c1 - c0;
-          it.kv_head = h;
-          it.reader_begin = rbase;
-          it.n_rows = rows;
-          it.slot_base = (int32_t)item_rows.size();
-          it.pad[0] = it.pad[1] = 0;
+          Item it{c0, c1 - c0, h, rows, &s, g0, {}};
           for (int32_t r = 0; r < rows; ++r) {
-            const int32_t q = s.readers[g0 + r / G];
-            const int32_t orow = q * hq + h * G + r % G;
-            item_rows.push_back(orow);
+            const int32_t orow = s.readers[g0 + r / G] * hq + h * G + r % G;
+            it.orow.push_back(orow);
             row_count[orow]++;
           }
-          items.push_back(it);
+          items.push_back(std::move(it));
         }
       }
     }
   }
-  // partial slots ordered by output row: row r owns [mptr[r], mptr[r + 1])
-  std::vector<int32_t> mptr((size_t)n_out + 1, 0);
-  for (int32_t r = 0; r < n_out; ++r) mptr[r + 1] = mptr[r] + row_count[r];
-  const int32_t n_part = mptr[n_out];
-  std::vector<int32_t> slot_map(item_rows.size()), fill(mptr.begin(), mptr.end() - 1);
-  for (size_t i = 0; i < item_rows.size(); ++i) slot_map[i] = fill[item_rows[i]]++;
   // heaviest items first
-  std::stable_sort(items.begin(), items.end(),
-                   [](const DecodeItem& a, const DecodeItem& b) { return a.n_chunks > b.n_chunks; });
+  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.n_chunks > b.n_chunks; });
+  // partial slots: output row r owns the block [r * max_parts, (r + 1) * max_parts)
+  int32_t max_parts = 1;
+  for (int32_t r = 0; r < n_out; ++r) max_parts = std::max(max_parts, row_count[r]);
+  const int64_t n_part_slots = (int64_t)n_out * max_parts;
+  int64_t n_part = 0;
+  std::vector<int32_t> fill((size_t)n_out, 0);
+  std::vector<int32_t> recs(items.size() * kRecInts, 0);
+  for (size_t i = 0; i < items.size(); ++i) {
+    const Item& it = items[i];
+    int32_t* rec = recs.data() + i * kRecInts;
+    rec[0] = it.n_chunks;
+    rec[1] = it.kv_head;
+    rec[2] = it.rows;
+    for (int32_t r = 0; r < kMaxRows; ++r) {
+      rec[kRecRow + r] = r < it.rows ? it.orow[r] : -1;
+      rec[kRecSlot + r] = r < it.rows ? it.orow[r] * max_parts + fill[it.orow[r]]++ : 0;
+    }
+    n_part += it.rows;
+    for (int32_t c = 0; c < it.n_chunks; ++c) {
+      const Chunk& ch = it.seg->chunks[it.chunk_begin + c];
+      rec[kRecChunk + 2 * c] = ch.page;
+      rec[kRecChunk + 2 * c + 1] = ch.lohi;
+    }
+  }
+  std::vector<int32_t>& mptr = row_count;  // uploaded as the per-row partial count
 
-  // 4. workspace image: [items | chunks | readers | row_ptr | slot map] is uploaded,
-  // then the partials
+  // 4. workspace image: [item records | per-row partial counts] is uploaded, then the
+  // partials
   const int D = C.head_dim;
   size_t off = 0;
-  pc.off_items = off; off = align256(off + items.size() * sizeof(DecodeItem));
-  pc.off_chunks = off; off = align256(off + chunks.size() * sizeof(Chunk));
-  pc.off_readers = off; off = align256(off + readers.size() * sizeof(int32_t));
+  pc.off_items = off; off = align256(off + recs.size() * sizeof(int32_t));
   pc.off_mptr = off; off = align256(off + mptr.size() * sizeof(int32_t));
-  pc.off_midx = off; off = align256(off + slot_map.size() * sizeof(int32_t));
   const size_t plan_bytes = off;
-  pc.off_plse = off; off = align256(off + (size_t)n_part * sizeof(float));
-  pc.off_po = off; off = align256(off + (size_t)n_part * D * sizeof(float));
+  pc.off_plse = off; off = align256(off + (size_t)n_part_slots * sizeof(float));
+  pc.off_po = off; off = align256(off + (size_t)n_part_slots * D * sizeof(float));
+  pc.max_parts = max_parts;
   pc.ws_need = std::max<size_t>(off, 256);
   pc.blob.assign(plan_bytes, 0);
-  put(pc.blob, pc.off_items, items);
-  put(pc.blob, pc.off_chunks, chunks);
-  put(pc.blob, pc.off_readers, readers);
+  put(pc.blob, pc.off_items, recs);
   put(pc.blob, pc.off_mptr, mptr);
-  put(pc.blob, pc.off_midx, slot_map);
   pc.n_items = (int32_t)items.size();
   pc.n_out_rows = n_out;
   const size_t es = C.dtype == KV_F32 ? 4 : 2;
   pc.stats[0] = (int64_t)segs.size();
   pc.stats[1] = (int64_t)items.size();
-  pc.stats[2] = (int64_t)chunks.size();
+  pc.stats[2] = n_chunks_total;
   pc.stats[3] = n_part;
   pc.stats[4] = unique_tokens * C.n_kv_heads * 2 * D * (int64_t)es;
   pc.stats[5] = n_out;
@@ -270,22 +275,17 @@ int fork_attn_decode(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, 
   dp.q = q;
   dp.k_pages = P->k;
   dp.v_pages = P->v;
-  dp.items = reinterpret_cast<const DecodeItem*>(w + pc.off_items);
-  dp.chunks = reinterpret_cast<const Chunk*>(w + pc.off_chunks);
-  dp.readers = reinterpret_cast<const int32_t*>(w + pc.off_readers);
-  dp.slot_map = reinterpret_cast<const int32_t*>(w + pc.off_midx);
+  dp.items = reinterpret_cast<const int32_t*>(w + pc.off_items);
   dp.part_lse2 = reinterpret_cast<float*>(w + pc.off_plse);
   dp.part_o = reinterpret_cast<float*>(w + pc.off_po);
   dp.n_items = pc.n_items;
-  dp.n_q_heads = hq;
-  dp.n_kv_heads = P->cfg.n_kv_heads;
   dp.n_pages = P->cfg.n_pages;
-  dp.group = hq / P->cfg.n_kv_heads;
   dp.scale_log2 = sm_scale * 1.4426950408889634f;
   e = launch_decode(P->cfg.dtype, P->cfg.head_dim, dp, s);
   if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   MergeParams mp;
-  mp.row_ptr = reinterpret_cast<const int32_t*>(w + pc.off_mptr);
+  mp.count = reinterpret_cast<const int32_t*>(w + pc.off_mptr);
+  mp.max_parts = pc.max_parts;
   mp.part_lse2 = dp.part_lse2;
   mp.part_o = dp.part_o;
   mp.out = out;

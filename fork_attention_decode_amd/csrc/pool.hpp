@@ -62,8 +62,8 @@ struct DecodePlanCache {
   void* ws = nullptr;
   size_t ws_need = 0;
   // device offsets
-  size_t off_items = 0, off_chunks = 0, off_readers = 0, off_mptr = 0, off_midx = 0, off_plse = 0, off_po = 0;
-  int32_t n_items = 0, n_out_rows = 0;
+  size_t off_items = 0, off_mptr = 0, off_plse = 0, off_po = 0;
+  int32_t n_items = 0, n_out_rows = 0, max_parts = 1;
   std::vector<char> blob;  // host image of the plan part of the workspace
   int64_t stats[6] = {0, 0, 0, 0, 0, 0};
 };
