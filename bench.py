@@ -58,32 +58,40 @@ def main():
         wss.append(torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device))
     stats = pools[0].plan_stats()
     es = 2 if sc.dtype == "bf16" else 4
-    alg_bytes = stats["unique_kv_bytes"] + 2 * q.numel() * es  # + Q read + O written
+    kernel_bytes = stats["unique_kv_bytes"] + q.numel() * es   # decode kernel: unique KV + Q read
+    step_bytes = kernel_bytes + q.numel() * es                 # whole step: + O written by the merge
     stream = torch.cuda.current_stream().cuda_stream
 
-    def step(i):
+    def step(i, ev=None):
+        # one step = the decode kernel (partials) + the merge kernel; events on the
+        # launch stream bracket the decode kernel alone and the whole step
         p = pools[i % len(pools)]
         ws = wss[i % len(pools)]
-        fa.fork_attn_decode(p.handle, sc.queries, hq, q.data_ptr(), out.data_ptr(), lse.data_ptr(), sc.sm_scale,
-                            ws.data_ptr(), ws.numel(), stream)
+        if ev:
+            ev[0].record()
+        fa.fork_attn_partials(p.handle, sc.queries, hq, q.data_ptr(), sc.sm_scale, ws.data_ptr(), ws.numel(), stream)
+        if ev:
+            ev[1].record()
+        fa.fork_attn_merge(p.handle, sc.queries, hq, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        if ev:
+            ev[2].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record()
-        step(i)
-        ev[i][1].record()
+        step(i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    k_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])      # decode kernel
+    s_ms = np.array([a.elapsed_time(c) for a, _, c in ev])      # whole step (decode + merge)
     ms_step = wall * 1e3 / args.steps
-    t_kernel = float(np.mean(ev_ms)) * 1e-3
-    achieved = alg_bytes / t_kernel / 1e9
+    t_kernel = float(np.mean(k_ms)) * 1e-3
+    achieved = kernel_bytes / t_kernel / 1e9
 
     result = {
         "metric": METRIC,
@@ -102,10 +110,15 @@ def main():
                    "head_dim": d, "page_size": sc.page_size, "pool_copies_rotated": args.copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "fork_attn_decode step (decode_kernel + merge_kernel)",
-                     "algorithmic_bytes_per_launch": alg_bytes,
-                     "event_ms_mean": float(np.mean(ev_ms)), "event_ms_p10": float(np.percentile(ev_ms, 10)),
-                     "event_ms_p90": float(np.percentile(ev_ms, 90))},
+                     "kernel": "decode_kernel (fork_attn_partials)",
+                     "algorithmic_bytes_per_launch": kernel_bytes,
+                     "kernel_us_mean": float(np.mean(k_ms)) * 1e3,
+                     "kernel_us_p10": float(np.percentile(k_ms, 10)) * 1e3,
+                     "kernel_us_p90": float(np.percentile(k_ms, 90)) * 1e3},
+        "step": {"us_mean_events": float(np.mean(s_ms)) * 1e3, "algorithmic_bytes": step_bytes,
+                 "achieved_GBps": step_bytes / (float(np.mean(s_ms)) * 1e-3) / 1e9,
+                 "frac_of_peak": step_bytes / (float(np.mean(s_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                 "merge_us_mean": float(np.mean(s_ms - k_ms)) * 1e3},
         "plan": stats,
     }
 

@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the hot path runs in the library's HIP kernels
 (gfx950).  Functions carry the C ABI's names (see include/forkattn.h); PyTorch is used
 for device memory and streams.  Importing this package fails loudly when the library
-has not been built (``python -m fork_attention_decode_amd.build``); there is no CPU
+has not been built (``python fork_attention_decode_amd/build.py``); there is no CPU
 fallback.
 
 ``Pool`` is a convenience holder of the torch buffers a pool needs.
@@ -40,7 +40,7 @@ class kv_pool_config(C.Structure):
 
 def _load() -> C.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run `python -m fork_attention_decode_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built: run `python fork_attention_decode_amd/build.py`")
     # torch ships its own HIP runtime (same soname): load it first so that the library
     # binds to that one runtime instead of bringing a second copy into the process.
     try:
@@ -80,6 +80,8 @@ _SIGS = {
     "fork_attn_workspace_size": [_P, _pi32, _i32, _i32, _psz],
     "fork_attn_decode": [_P, _pi32, _i32, _i32, _P, _P, _P, C.c_float, _P, _sz, _P],
     "fork_attn_plan_stats": [_P, _pi64, _i32],
+    "fork_attn_partials": [_P, _pi32, _i32, _i32, _P, C.c_float, _P, _sz, _P],
+    "fork_attn_merge": [_P, _pi32, _i32, _i32, _P, _P, _P, _sz, _P],
     "dag_mask_build": [_pi32, _i32, _pi32, _i32, _i32, _i32, _pi32, _pi32, C.POINTER(C.c_uint8), _pi64],
     "dag_attn_workspace_size": [_i32, _i32, _i32, _i32, _psz],
     "dag_attn_prefill": [_P, _P, _P, _P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, _i32, C.c_float, _P, _sz, _P],
@@ -255,6 +257,20 @@ def fork_attn_decode(pool: int, seqs: Sequence[int], n_q_heads: int, q: int, out
     _check("fork_attn_decode", lib.fork_attn_decode(pool, _ptr(s, C.c_int32), len(s), n_q_heads, q, out,
                                                     lse or None, sm_scale, workspace, ws_bytes, stream or None),
            pool)
+
+
+def fork_attn_partials(pool: int, seqs: Sequence[int], n_q_heads: int, q: int, sm_scale: float, workspace: int,
+                       ws_bytes: int, stream: int = 0):
+    s = np.ascontiguousarray(np.asarray(seqs, np.int32))
+    _check("fork_attn_partials", lib.fork_attn_partials(pool, _ptr(s, C.c_int32), len(s), n_q_heads, q, sm_scale,
+                                                        workspace, ws_bytes, stream or None), pool)
+
+
+def fork_attn_merge(pool: int, seqs: Sequence[int], n_q_heads: int, out: int, lse: int, workspace: int,
+                    ws_bytes: int, stream: int = 0):
+    s = np.ascontiguousarray(np.asarray(seqs, np.int32))
+    _check("fork_attn_merge", lib.fork_attn_merge(pool, _ptr(s, C.c_int32), len(s), n_q_heads, out, lse or None,
+                                                  workspace, ws_bytes, stream or None), pool)
 
 
 def fork_attn_plan_stats(pool: int) -> dict:

@@ -1,6 +1,7 @@
 """Build libforkattn.so (HIP kernels for gfx950 + C++ host runtime) in-tree with hipcc.
 
-Usage: python -m fork_attention_decode_amd.build  (or build() from Python).
+Usage: python fork_attention_decode_amd/build.py  (run by path: importing the package
+would load the library being rebuilt).
 """
 import os
 import subprocess

@@ -254,23 +254,32 @@ int fork_attn_plan_stats(kv_pool_t* P, int64_t* out, int32_t n) {
   return KV_OK;
 }
 
-int fork_attn_decode(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, const void* q, void* out,
-                     float* lse, float sm_scale, void* ws, size_t ws_bytes, hipStream_t s) {
+// Plan (cached) and upload it into the workspace if needed.
+static int prepare(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, void* ws, size_t ws_bytes,
+                   hipStream_t s) {
   if (!P) FAIL(P, KV_ERR_INVALID, "null pool");
   if (!P->device) FAIL(P, KV_ERR_INVALID, "metadata-only pool has no KV data");
-  if (n == 0) return KV_OK;
-  if (!q || !out || !ws) FAIL(P, KV_ERR_INVALID, "null device pointer");
+  if (!ws) FAIL(P, KV_ERR_INVALID, "null workspace");
   int st = build_plan(P, seqs, n, hq);
   if (st) return st;
   DecodePlanCache& pc = P->plan;
   if (ws_bytes < pc.ws_need) FAIL(P, KV_ERR_WORKSPACE, "decode workspace too small");
-  char* w = (char*)ws;
-  hipError_t e = hipSuccess;
   if (pc.ws != ws) {
-    e = fa_upload(P, w, pc.blob.data(), pc.blob.size(), s);
+    hipError_t e = fa_upload(P, ws, pc.blob.data(), pc.blob.size(), s);
     if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("plan upload: ") + hipGetErrorString(e));
     pc.ws = ws;
   }
+  return KV_OK;
+}
+
+int fork_attn_partials(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, const void* q, float sm_scale,
+                       void* ws, size_t ws_bytes, hipStream_t s) {
+  if (P && n == 0) return KV_OK;
+  if (!q) FAIL(P, KV_ERR_INVALID, "null q");
+  int st = prepare(P, seqs, n, hq, ws, ws_bytes, s);
+  if (st) return st;
+  DecodePlanCache& pc = P->plan;
+  char* w = (char*)ws;
   DecodeParams dp;
   dp.q = q;
   dp.k_pages = P->k;
@@ -281,19 +290,39 @@ int fork_attn_decode(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, 
   dp.n_items = pc.n_items;
   dp.n_pages = P->cfg.n_pages;
   dp.scale_log2 = sm_scale * 1.4426950408889634f;
-  e = launch_decode(P->cfg.dtype, P->cfg.head_dim, dp, s);
+  hipError_t e = launch_decode(P->cfg.dtype, P->cfg.head_dim, dp, s);
   if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
+  return KV_OK;
+}
+
+int fork_attn_merge(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, void* out, float* lse, void* ws,
+                    size_t ws_bytes, hipStream_t s) {
+  if (P && n == 0) return KV_OK;
+  if (!out) FAIL(P, KV_ERR_INVALID, "null out");
+  int st = prepare(P, seqs, n, hq, ws, ws_bytes, s);
+  if (st) return st;
+  DecodePlanCache& pc = P->plan;
+  char* w = (char*)ws;
   MergeParams mp;
   mp.count = reinterpret_cast<const int32_t*>(w + pc.off_mptr);
   mp.max_parts = pc.max_parts;
-  mp.part_lse2 = dp.part_lse2;
-  mp.part_o = dp.part_o;
+  mp.part_lse2 = reinterpret_cast<const float*>(w + pc.off_plse);
+  mp.part_o = reinterpret_cast<const float*>(w + pc.off_po);
   mp.out = out;
   mp.lse = lse;
   mp.n_rows = pc.n_out_rows;
-  e = launch_merge(P->cfg.dtype, P->cfg.head_dim, mp, s);
+  hipError_t e = launch_merge(P->cfg.dtype, P->cfg.head_dim, mp, s);
   if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
   return KV_OK;
+}
+
+int fork_attn_decode(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, const void* q, void* out,
+                     float* lse, float sm_scale, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (P && n == 0) return KV_OK;
+  if (!q || !out) FAIL(P, KV_ERR_INVALID, "null device pointer");
+  int st = fork_attn_partials(P, seqs, n, hq, q, sm_scale, ws, ws_bytes, s);
+  if (st) return st;
+  return fork_attn_merge(P, seqs, n, hq, out, lse, ws, ws_bytes, s);
 }
 
 }  // extern "C"

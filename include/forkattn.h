@@ -198,6 +198,17 @@ int fork_attn_decode(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n_seqs, int3
                      const void* q, void* out, float* lse, float sm_scale, void* workspace,
                      size_t ws_bytes, hipStream_t stream);
 
+/* fork_attn_decode in two launches, for callers that overlap the merge with other work
+ * (or time the kernels apart): fork_attn_partials streams the KV pages and writes one
+ * partial (max, sum, output) per (work item, row) into the workspace;
+ * fork_attn_merge combines each row's partials into out / lse.  Same arguments and
+ * workspace as fork_attn_decode; the merge must follow the partials on the stream. */
+int fork_attn_partials(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n_seqs, int32_t n_q_heads,
+                       const void* q, float sm_scale, void* workspace, size_t ws_bytes,
+                       hipStream_t stream);
+int fork_attn_merge(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n_seqs, int32_t n_q_heads,
+                    void* out, float* lse, void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Plan statistics of the last fork_attn_decode / fork_attn_workspace_size call:
  * out[0] segments, out[1] work items, out[2] chunks, out[3] partial rows,
  * out[4] unique KV bytes streamed (algorithmic), out[5] query rows. */

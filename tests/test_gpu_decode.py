@@ -103,6 +103,25 @@ def test_plan_cache_reuse_and_second_call():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_split_partials_merge_equals_decode():
+    import torch
+    import fork_attention_decode_amd as fa
+    sc = W.dag_scenario(root=300, threads=3, private=90, mounts_per_thread=2, mount_len=33, hq=8, hkv=2, d=128,
+                        seed=6)
+    print("[case] fork_attn_partials + fork_attn_merge == fork_attn_decode", flush=True)
+    pool, _ = build_device_pool(sc)
+    q = to_torch(sc.q, "bf16")
+    o1, l1 = pool.decode(sc.queries, q, sc.sm_scale)
+    ws = pool._dec_ws
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    st = torch.cuda.current_stream().cuda_stream
+    fa.fork_attn_partials(pool.handle, sc.queries, 8, q.data_ptr(), sc.sm_scale, ws.data_ptr(), ws.numel(), st)
+    fa.fork_attn_merge(pool.handle, sc.queries, 8, o2.data_ptr(), l2.data_ptr(), ws.data_ptr(), ws.numel(), st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_shared_prefix_full_size():
     sc = W.shared_prefix_fork()
     pool, o, lse = _run(sc, "shared-prefix fork decode, full size")
