@@ -2,9 +2,10 @@
 workload (16 branches x 32 query heads, 8 KV heads, d=128, bf16, 32,768-token shared
 prefix + 2,048 private tokens per branch, page 16), inputs resident in HBM.
 
-Prints ONE JSON line.  `value` = branch-tokens/s (branches decoded per second); the
-roofline object prices the step against MI355X's 8 TB/s HBM with the algorithmic bytes
-(unique KV bytes + Q + O), timed with HIP events on the launch stream.  Steps rotate over
+Prints ONE JSON line.  `value` = branch-tokens/s (branches decoded per second, wall clock
+over the timed steps); the roofline object prices the dominant kernel (decode_kernel)
+against MI355X's 8 TB/s HBM with its algorithmic bytes (unique KV + Q), timed with HIP
+events on the launch stream; `step` reports the whole step (decode + merge) the same way.  Steps rotate over
 several identical pool copies so that no step finds its KV in the 256 MB last-level
 cache left behind by the previous one.  The cpu_baseline leg times the fp64 oracle on a
 bounded sample of the same workload on the host cores.
@@ -20,6 +21,21 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fork-decode branch-tokens/s + achieved HBM GB/s (% of peak); DAG-prefill % MFMA peak"
 HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per decode_kernel launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs, or None once the kernel sources differ from the profiled ones."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        h = hashlib.sha256()
+        for f in rec["source_files"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -31,7 +47,10 @@ def main():
     ap.add_argument("--workload", default="shared_prefix_fork_decode",
                     choices=["shared_prefix_fork_decode", "octopus_dag_decode", "tiny_fork_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to sample")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work to sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, copy 256 MiB device to device once (a kernel of known "
+                         "traffic to scale hardware byte counters against)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on "
@@ -87,6 +106,11 @@ def main():
         step(i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=q.device)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
     k_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])      # decode kernel
     s_ms = np.array([a.elapsed_time(c) for a, _, c in ev])      # whole step (decode + merge)
     ms_step = wall * 1e3 / args.steps
@@ -109,7 +133,8 @@ def main():
         "config": {"workload": args.workload, "branches": n_br, "q_heads": hq, "kv_heads": sc.n_kv_heads,
                    "head_dim": d, "page_size": sc.page_size, "pool_copies_rotated": args.copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic() if args.workload == "shared_prefix_fork_decode" else None,
                      "kernel": "decode_kernel (fork_attn_partials)",
                      "algorithmic_bytes_per_launch": kernel_bytes,
                      "kernel_us_mean": float(np.mean(k_ms)) * 1e3,
@@ -129,7 +154,8 @@ def main():
 
 def cpu_baseline(sc, budget_s):
     """Time the fp64 oracle on a bounded sample of the same workload: branches are decoded
-    one at a time until `budget_s` of oracle work has been spent."""
+    one at a time (cycling over the workload's branches) until `budget_s` of oracle work
+    has been spent."""
     import numpy as np
     import workloads as W
     from oracle import attention as att, pagetable as pt
@@ -143,17 +169,16 @@ def cpu_baseline(sc, budget_s):
     q = W.storage_to_f64(sc.q, sc.dtype)
     done = 0
     t0 = time.perf_counter()
-    for i, sid in enumerate(sc.queries):
-        att.decode(table, [sid], q[i:i + 1], sc.sm_scale)
+    while time.perf_counter() - t0 < budget_s:
+        i = done % len(sc.queries)
+        att.decode(table, [sc.queries[i]], q[i:i + 1], sc.sm_scale)
         done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
     t = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
     return {"value": done / t, "unit": "branch-tokens/s", "cores": blas_threads or cores, "kind": "oracle",
             "host_cores_visible": cores,
-            "sample": f"{done} of {len(sc.queries)} branches decoded by the fp64 materialising oracle "
-                      f"({t:.1f} s; pool replay excluded)"}
+            "sample": f"{done} branch decodes (cycling over the {len(sc.queries)} branches of the same "
+                      f"workload) by the fp64 materialising oracle in {t:.1f} s; pool replay excluded"}
 
 
 if __name__ == "__main__":
