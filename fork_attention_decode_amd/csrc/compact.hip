@@ -42,6 +42,10 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
   if (threadIdx.x == 0) s_k = (int)((unsigned)atomicAdd(p.ticket, 1) - (unsigned)p.ticket_base);
   __syncthreads();
   const int k = s_k;
+  if (k < 0 || k >= p.n_pages) {  // ticket out of step with the host: count it, touch nothing
+    if (threadIdx.x == 0) atomicAdd(p.errors, 1);
+    return;
+  }
   const CompactPage cp = p.pages[k];
   T* kp = reinterpret_cast<T*>(p.k_pages);
   T* vp = reinterpret_cast<T*>(p.v_pages);

@@ -28,6 +28,8 @@ bf16 tensors are stored as ``uint16`` bit patterns.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import List, Optional, Tuple
 
@@ -40,16 +42,16 @@ import numpy as np
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp64 values to bf16 (round-to-nearest-even) and return the uint16 bits.
 
-    Rounds directly from fp64 (no fp32 double rounding): x = m * 2^e with
-    0.5 <= |m| < 1, so the bf16 grid at that binade is 2^(e-8) and rint() on
-    m * 256 is an exact round-half-even.  Inputs are N(0,1) draws, far from the
-    bf16 overflow and subnormal ranges.
+    Rounds directly from fp64 (no fp32 double rounding) on the integer image of the
+    fp64 value: bf16 keeps the top 7 of fp64's 52 fraction bits, so adding
+    2^44 - 1 plus the lowest kept bit and clearing the 45 low bits is an exact
+    round-half-even (a carry moves into the exponent as it should).  The result is
+    a bf16 value, so its fp32 conversion is exact.  Inputs are N(0,1) draws, far
+    from the bf16 overflow and subnormal ranges.
     """
-    x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)
-    y = np.ldexp(np.rint(m * 256.0), e - 8)
-    bits = y.astype(np.float32).view(np.uint32)
-    return (bits >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float64).view(np.uint64)
+    u = (u + (np.uint64((1 << 44) - 1) + ((u >> np.uint64(45)) & np.uint64(1)))) & ~np.uint64((1 << 45) - 1)
+    return (u.view(np.float64).astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
@@ -131,17 +133,38 @@ class Scenario:
         return len(self.queries)
 
 
+_CHUNK = 16384  # tokens per generation chunk (bounds the fp64 transients)
+
+
 def _tokens(cid: int, purpose_k: int, purpose_v: int, seed: int, sub: int, n: int, hkv: int, d: int,
             pos: np.ndarray, dtype: str, rope_theta: Optional[float], k_scale: float,
             keep_raw: bool = False) -> TokenBlock:
-    xk = _rng(cid, purpose_k, seed, sub).standard_normal((n, hkv, d))
-    xv = _rng(cid, purpose_v, seed, sub).standard_normal((n, hkv, d))
-    k = xk
-    if rope_theta:
-        k = _rotate_neox(k, pos, rope_theta)
-    k = k * k_scale
-    return TokenBlock(k=_store(k, dtype), v=_store(xv, dtype), pos=pos.astype(np.int64),
-                      raw_k=xk if keep_raw else None)
+    """n tokens of one append.  Drawn in chunks: consecutive draws from one generator
+    continue its stream, so the values equal one draw of shape (n, hkv, d)."""
+    gk = _rng(cid, purpose_k, seed, sub)
+    gv = _rng(cid, purpose_v, seed, sub)
+    sdt = np.uint16 if dtype == "bf16" else np.float32
+    k = np.empty((n, hkv, d), sdt)
+    v = np.empty((n, hkv, d), sdt)
+    raw = np.empty((n, hkv, d)) if keep_raw else None
+    for a in range(0, n, _CHUNK):
+        b = min(n, a + _CHUNK)
+        xk = gk.standard_normal((b - a, hkv, d))
+        if keep_raw:
+            raw[a:b] = xk
+        kk = _rotate_neox(xk, pos[a:b], rope_theta) if rope_theta else xk
+        k[a:b] = _store(kk * k_scale, dtype)
+        v[a:b] = _store(gv.standard_normal((b - a, hkv, d)), dtype)
+    return TokenBlock(k=k, v=v, pos=pos.astype(np.int64), raw_k=raw)
+
+
+def _parallel(fn, args_list):
+    """Map fn over independent generation jobs on threads (numpy's draws and ufuncs
+    release the GIL); results in job order, so values do not depend on scheduling."""
+    if len(args_list) <= 1:
+        return [fn(*a) for a in args_list]
+    with ThreadPoolExecutor(max_workers=min(8, len(args_list), os.cpu_count() or 1)) as ex:
+        return list(ex.map(lambda a: fn(*a), args_list))
 
 
 def _queries(cid: int, seed: int, nq: int, hq: int, d: int, qpos: np.ndarray, dtype: str,
@@ -165,8 +188,11 @@ def fork_scenario(prefix: int = 32768, branches: int = 16, private=2048, hq: int
     scaled = dtype == "bf16"
     k_scale = 1.0 / np.sqrt(d) if scaled else 1.0
     sm_scale = 1.0 if scaled else 1.0 / np.sqrt(d)
-    blocks = [_tokens(config_id, P_K, P_V, seed, 0, prefix, hkv, d, np.arange(prefix), dtype,
-                      rope_theta, k_scale)]
+    jobs = [(config_id, P_K, P_V, seed, 0, prefix, hkv, d, np.arange(prefix), dtype, rope_theta, k_scale)]
+    jobs += [(config_id, P_K, P_V, seed, 1 + b, priv[b], hkv, d, prefix + np.arange(priv[b]), dtype, rope_theta,
+              k_scale) for b in range(branches) if priv[b] > 0]
+    gen = _parallel(_tokens, jobs)
+    blocks = [gen[0]]
     ops: List[tuple] = [("create",), ("append", 0, 0)]
     qpos = []
     for b in range(branches):
@@ -174,9 +200,7 @@ def fork_scenario(prefix: int = 32768, branches: int = 16, private=2048, hq: int
         sid = 1 + b
         n = priv[b]
         if n > 0:
-            pos = prefix + np.arange(n)
-            blocks.append(_tokens(config_id, P_K, P_V, seed, 1 + b, n, hkv, d, pos, dtype, rope_theta,
-                                  k_scale))
+            blocks.append(gen[len(blocks)])
             ops.append(("append", sid, len(blocks) - 1))
         qpos.append(prefix + max(n, 1) - 1)
     queries = list(range(1, branches + 1))
@@ -195,16 +219,15 @@ def dag_scenario(root: int = 65536, threads: int = 8, private: int = 8192, mount
     seed-chosen siblings (read-only, no copy); one query per thread at its last position."""
     assert mount_len <= private and mounts_per_thread <= threads - 1
     k_scale = 1.0 / np.sqrt(d)
-    blocks = [_tokens(config_id, P_K, P_V, seed, 0, root, hkv, d, np.arange(root), dtype, rope_theta,
-                      k_scale)]
+    jobs = [(config_id, P_K, P_V, seed, 0, root, hkv, d, np.arange(root), dtype, rope_theta, k_scale)]
+    jobs += [(config_id, P_K, P_V, seed, 1 + t, private, hkv, d, root + np.arange(private), dtype, rope_theta,
+              k_scale) for t in range(threads)]
+    blocks = _parallel(_tokens, jobs)
     ops: List[tuple] = [("create",), ("append", 0, 0)]
     for t in range(threads):
         ops.append(("fork", 0))
     for t in range(threads):
-        pos = root + np.arange(private)
-        blocks.append(_tokens(config_id, P_K, P_V, seed, 1 + t, private, hkv, d, pos, dtype, rope_theta,
-                              k_scale))
-        ops.append(("append", 1 + t, len(blocks) - 1))
+        ops.append(("append", 1 + t, 1 + t))
     rng = _rng(config_id, P_MOUNT, seed)
     for t in range(threads):
         others = [s for s in range(threads) if s != t]
@@ -257,15 +280,17 @@ def drop_scenario(requests: int = 16, ctx: int = 131072, frac: float = 0.4, span
     ops: List[tuple] = []
     blocks: List[TokenBlock] = []
     qpos = []
+    span_lists = [drop_spans(_rng(config_id, P_SPANS, seed, i), ctx, frac, span_min, span_max)
+                  for i in range(requests)]
+    dpos = [(ctx - sum(L for _, L in sp)) if repos else ctx for sp in span_lists]
+    ctx_blocks = _parallel(_tokens, [(config_id, P_K, P_V, seed, 1 + i, ctx, hkv, d, np.arange(ctx), dtype,
+                                      rope_theta, k_scale, keep_raw) for i in range(requests)])
     for i in range(requests):
         ops.append(("create",))
-        blocks.append(_tokens(config_id, P_K, P_V, seed, 1 + i, ctx, hkv, d, np.arange(ctx), dtype,
-                              rope_theta, k_scale, keep_raw=keep_raw))
+        blocks.append(ctx_blocks[i])
         ops.append(("append", i, len(blocks) - 1))
-        spans = drop_spans(_rng(config_id, P_SPANS, seed, i), ctx, frac, span_min, span_max)
-        ops.append(("drop", i, spans, repos))
-        r = ctx - sum(L for _, L in spans)
-        p = r if repos else ctx
+        ops.append(("drop", i, span_lists[i], repos))
+        p = dpos[i]
         blocks.append(_tokens(config_id, P_DECODE_K, P_DECODE_V, seed, 1 + i, 1, hkv, d,
                               np.array([p]), dtype, rope_theta, k_scale, keep_raw=keep_raw))
         ops.append(("append", i, len(blocks) - 1))
