@@ -313,6 +313,41 @@ def dag_attn_prefill(q: int, k: int, v: int, out: int, lse: int, T: int, n_q_hea
                                                     ws_bytes, stream or None))
 
 
+# ------------------------------------------------------------------ packed DAG prefill
+class DagMask:
+    """Device copy of the CSR block mask of a packed DAG (dag_mask_build on the host)."""
+
+    def __init__(self, segments, edges, T: int, block: int = 64, device: str = "cuda"):
+        import torch
+        row_ptr, col, kind = dag_mask_build(segments, edges, T, block)
+        self.T, self.block, self.nnz = T, block, len(col)
+        self.host = (row_ptr, col, kind)
+        self.row_ptr = torch.from_numpy(row_ptr).to(device)
+        self.col = torch.from_numpy(col if len(col) else np.zeros(1, np.int32)).to(device)
+        self.kind = torch.from_numpy(kind if len(kind) else np.zeros(1, np.uint8)).to(device)
+
+
+def prefill(q, k, v, mask: DagMask, sm_scale: float, out=None, lse=None, workspace=None, with_lse: bool = True):
+    """Block-sparse prefill over `mask`.  q [T, Hq, 128], k / v [T, Hkv, 128] bf16 torch
+    tensors on the device.  Returns (out [T, Hq, 128] bf16, lse [Hq, T] fp32 or None)."""
+    import torch
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    assert q.is_contiguous() and k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
+    assert T == mask.T and q.dtype == torch.bfloat16
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
+    need = dag_attn_workspace_size(T, hq, hkv, mask.block)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dag_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else 0,
+                     T, hq, hkv, d, mask.row_ptr.data_ptr(), mask.col.data_ptr(), mask.kind.data_ptr(), mask.block,
+                     sm_scale, workspace.data_ptr(), workspace.numel(), torch.cuda.current_stream().cuda_stream)
+    return out, lse
+
+
 # ------------------------------------------------------------------ torch-backed holder
 class Pool:
     """Owns the torch device buffers of one pool (K pages, V pages, workspace) and its handle.

@@ -1,16 +1,381 @@
-// Packed DAG prefill (placeholder until the block-sparse kernel lands).
+// Packed DAG prefill: block-sparse attention forward over a DAG block mask, for gfx950.
+//
+// Octopus (zicq.com), "Packed DAG-GRPO": the branches of a rollout are packed into one
+// sequence and one block-sparse matrix encodes causality inside a thread, cross-thread
+// read edges and synchronisation dependencies, so only the block pairs the DAG allows
+// are computed.  The CSR over 64 x 64 blocks comes from dag_mask_build; kind 1 marks a
+// diagonal block (key <= query inside it), kind 0 a fully visible block.
+//
+// Mapping onto CDNA4:
+//   * relayout pass: K and V of every (KV head, 64-key block) are copied once into a
+//     16 KiB image in matrix-core operand order (zero past T), so each operand read in
+//     the main kernel is one contiguous 1 KiB wave read from LDS (no bank conflicts)
+//     and each block moves into LDS as two contiguous 16 KiB copies;
+//   * one workgroup per (64-token query block, KV head, group of 4 query heads): the
+//     4 waves take the 4 query heads (GQA packing), so every K / V block staged in LDS
+//     feeds 256 query rows;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = M, queries = N, d = K): each lane
+//     holds one query column, so row max / sum stay in the lane plus one permlane32
+//     swap; its accumulator layout is the B operand of O^T = V^T P^T once the key
+//     order of the V image matches it (done in the relayout), so P needs no shuffles;
+//   * online softmax in fp32 in the exp2 domain with a lazy, wave-uniform rescale;
+//   * K / V blocks stream through a 3-stage LDS ring with direct global->LDS loads
+//     (each wave copies a quarter), one workgroup barrier per block;
+//   * workgroups are ordered by descending row cost (a rank pass over row_ptr) so the
+//     longest rows start first, and consecutive workgroups take consecutive KV heads,
+//     so with 8 KV heads each die (and its L2) serves one head.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <string>
 #include "../../include/forkattn.h"
 
 int fa_set_err(struct kv_pool* P, int code, const std::string& m);
 
-extern "C" int dag_attn_workspace_size(int32_t, int32_t, int32_t, int32_t, size_t* bytes) {
-  if (bytes) *bytes = 0;
-  return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill kernel not built");
+namespace fa {
+namespace {
+
+typedef __bf16 bf16_t;
+typedef bf16_t bf16x8 __attribute__((__vector_size__(8 * sizeof(bf16_t))));
+typedef bf16_t bf16x4 __attribute__((__vector_size__(4 * sizeof(bf16_t))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kB = 64;               // block edge (tokens)
+constexpr int kD = 128;              // head dim
+constexpr int kImg = kB * kD * 2;    // bytes of one K (or V) block image
+constexpr int kStage = 2 * kImg;     // K image + V image
+constexpr int kStages = 3;           // LDS ring depth
+constexpr int kLoadsPerWave = kStage / 4 / 1024;  // 1 KiB wave loads per stage per wave
+constexpr float kTau = 8.f;          // lazy rescale threshold (log2 units)
+
+struct Params {
+  const bf16_t* q;
+  const char* kimg;
+  const char* vimg;
+  bf16_t* out;
+  float* lse;
+  const int32_t* row_ptr;
+  const int32_t* col;
+  const uint8_t* kind;
+  const int32_t* order;
+  int32_t T, hq, hkv, G, n_hg, nb;
+  float scale_log2, sm_scale;
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-extern "C" int dag_attn_prefill(const void*, const void*, const void*, void*, float*, int32_t, int32_t,
-                                int32_t, int32_t, const int32_t*, const int32_t*, const uint8_t*, int32_t,
-                                float, void*, size_t, hipStream_t) {
-  return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill kernel not built");
+
+// ---- relayout: one workgroup per (64-key block, KV head)
+//   K image slot (kt, ks, lane) = K[32 kt + lane % 32][16 ks + 8 (lane / 32) + 0..7]
+//   V image slot (dt, kt, hf, lane) = V[key(e)][32 dt + lane % 32] for e = 0..7 with
+//     key(e) = 32 kt + 16 hf + 8 (e / 4) + 4 (lane / 32) + e % 4
+// (16-byte slots, slot index = ((..) * 64 + lane)), keys >= T read as zero.
+__global__ __launch_bounds__(256) void relayout_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                                       char* __restrict__ kimg, char* __restrict__ vimg, int T,
+                                                       int hkv, int nb) {
+  const int c = blockIdx.x, h = blockIdx.y;
+  const size_t img = ((size_t)h * nb + c) * kImg;
+  const size_t row = (size_t)hkv * kD;  // elements between consecutive tokens
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = i * 256 + threadIdx.x;
+    const int lane = s & 63;
+    {  // K slot
+      const int ks = (s >> 6) & 7, kt = s >> 9;
+      const int key = c * kB + 32 * kt + (lane & 31);
+      i32x4 val = {0, 0, 0, 0};
+      if (key < T)
+        val = *reinterpret_cast<const i32x4*>(k + key * row + (size_t)h * kD + 16 * ks + 8 * (lane >> 5));
+      *reinterpret_cast<i32x4*>(kimg + img + (size_t)s * 16) = val;
+    }
+    {  // V slot
+      const int hf = (s >> 6) & 1, kt = (s >> 7) & 1, dt = s >> 8;
+      const int d = 32 * dt + (lane & 31);
+      bf16x8 val;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = c * kB + 32 * kt + 16 * hf + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        val[e] = key < T ? v[key * row + (size_t)h * kD + d] : (bf16_t)0.f;
+      }
+      *reinterpret_cast<bf16x8*>(vimg + img + (size_t)s * 16) = val;
+    }
+  }
+}
+
+// ---- rows by descending cost (ties by index): order[rank] = row
+__global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ row_ptr, int32_t* __restrict__ order,
+                                                   int nb) {
+  __shared__ int tile[256];
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int cr = r < nb ? row_ptr[r + 1] - row_ptr[r] : 0;
+  int rank = 0;
+  for (int base = 0; base < nb; base += 256) {
+    const int t = base + threadIdx.x;
+    __syncthreads();
+    tile[threadIdx.x] = t < nb ? row_ptr[t + 1] - row_ptr[t] : -1;
+    __syncthreads();
+    const int m = nb - base < 256 ? nb - base : 256;
+    for (int i = 0; i < m; ++i) {
+      const int ci = tile[i];
+      rank += (ci > cr) || (ci == cr && base + i < r);
+    }
+  }
+  if (r < nb) order[rank] = r;
+}
+
+// max / sum with lane ^ 32: the swap returns {x[l], x[l ^ 32]} in some order per lane
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(256, 1) void prefill_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) char ring[kStages * kStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  const int h = b % p.hkv;
+  const int rest = b / p.hkv;
+  const int hg = rest % p.n_hg;
+  const int row = p.order[rest / p.n_hg];
+  const int hslot = hg * 4 + wave;
+  const bool active = hslot < p.G;
+  const int qhead = h * p.G + (active ? hslot : 0);
+  const int q0 = row * kB;
+  const int j0 = p.row_ptr[row];
+  const int n = p.row_ptr[row + 1] - j0;
+  const int hi = lane >> 5, lo = lane & 31;
+
+  // this wave's quarter of every stage: waves 0, 1 copy the K image, waves 2, 3 the V image
+  const int my_off = wave * (kStage / 4);
+  const char* my_src = (my_off < kImg ? p.kimg + my_off : p.vimg + (my_off - kImg)) + (size_t)h * p.nb * kImg;
+  auto col_of = [&](int j) {
+    int c = p.col[j0 + (j < n ? j : n - 1)];
+    return c < 0 ? 0 : (c >= p.nb ? p.nb - 1 : c);  // never leave the images
+  };
+  auto issue = [&](int j) {  // past the end: reload the last block into a slot nobody reads
+    const char* src = my_src + (size_t)col_of(j) * kImg + lane * 16;
+    char* dst = ring + (j % kStages) * kStage + my_off;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i)
+      __builtin_amdgcn_global_load_lds(src + i * 1024, (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                                       16, 0, 0);
+  };
+
+  if (n > 0) issue(0);
+  if (n > 0) issue(1);
+
+  // queries: B operand of S^T = K Q^T, lane holds Q[q0 + 32 qt + lo][16 ks + 8 hi + 0..7]
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int tq = q0 + 32 * qt + lo;
+    const bf16_t* src = p.q + ((size_t)(tq < p.T ? tq : 0) * p.hq + qhead) * kD + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[qt][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+      if (tq >= p.T) qf[qt][ks] = bf16x8{};
+    }
+  }
+
+  f32x16 o[4][2];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = f32x16{};
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  const float c2 = p.scale_log2;
+  const bool ragged = (p.T & (kB - 1)) != 0;
+
+  for (int j = 0; j < n; ++j) {
+    wait_vmcnt<(kStages - 2) * kLoadsPerWave>();  // this wave's part of block j landed
+    asm volatile("s_barrier" ::: "memory");       // ... every wave's; slot (j - 1) % 3 is free
+    issue(j + kStages - 1);
+    if (!active) continue;
+    const int c = col_of(j);
+    const char* kslot = ring + (j % kStages) * kStage;
+    const char* vslot = kslot + kImg;
+
+    f32x16 s[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kslot + ((kt * 8 + ks) * 64 + lane) * 16);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma32(a, qf[qt][ks], s[kt][qt]);
+      }
+    }
+
+    // mask: diagonal block (key > query) and keys past T
+    const bool diag = p.kind[j0 + j] == 1;
+    if (diag || (ragged && c == p.nb - 1)) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = c * kB + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
+            const int qry = q0 + 32 * qt + lo;
+            if ((diag && key > qry) || key >= p.T) s[kt][qt][r] = -INFINITY;
+          }
+    }
+
+    // online softmax per query column (this lane's query, plus its partner lane ^ 32)
+    bf16x8 pk[2][2][2];  // [kt][qt][half of the 32 keys]
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][qt][r]);
+      mx = xhalf_max(mx);
+      const float mn = fmaxf(m[qt], mx);
+      const bool grow = (mn - m[qt]) * c2 > kTau;  // false while both are -inf
+      if (__builtin_amdgcn_ballot_w64(grow)) {     // wave-uniform: rescale to each lane's new max
+        const float alpha = m[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[qt] - mn) * c2);
+        m[qt] = mn;
+        l[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt][qt] *= alpha;
+      }
+      const float mc = m[qt] == -INFINITY ? 0.f : m[qt] * c2;
+      float ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][8 * hf + e], c2, -mc));
+            ls += pe;
+            pk[kt][qt][hf][e] = (bf16_t)pe;
+          }
+      l[qt] += ls;
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vslot + (((dt * 2 + kt) * 2 + hf) * 64 + lane) * 16);
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma32(a, pk[kt][qt][hf], o[dt][qt]);
+        }
+  }
+  wait_vmcnt<0>();  // no load may land in LDS after the workgroup ends
+  if (!active) return;
+
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float lt = xhalf_sum(l[qt]);
+    const int tq = q0 + 32 * qt + lo;
+    if (tq >= p.T) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a row with no visible key: zeros, lse -inf
+    bf16_t* dst = p.out + ((size_t)tq * p.hq + qhead) * kD + 4 * hi;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16_t)(o[dt][qt][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * g) = w;
+      }
+    if (p.lse && hi == 0)
+      p.lse[(size_t)qhead * p.T + tq] = lt > 0.f ? (m[qt] * c2 + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t order, kimg, vimg, total;
+};
+WsLayout ws_layout(int32_t T, int32_t hkv) {
+  const size_t nb = (size_t)(T + kB - 1) / kB;
+  WsLayout w;
+  w.order = 0;
+  w.kimg = align256(nb * 4);
+  w.vimg = w.kimg + (size_t)hkv * nb * kImg;
+  w.total = w.vimg + (size_t)hkv * nb * kImg;
+  return w;
+}
+
+}  // namespace
+}  // namespace fa
+
+using namespace fa;
+
+extern "C" int dag_attn_workspace_size(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t block,
+                                       size_t* bytes) {
+  if (!bytes || T < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads)
+    return fa_set_err(nullptr, KV_ERR_INVALID, "bad prefill shape");
+  if (block != kB) return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill block must be 64");
+  *bytes = ws_layout(T, n_kv_heads).total;
+  return KV_OK;
+}
+
+extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int32_t T,
+                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, const int32_t* row_ptr,
+                                const int32_t* col, const uint8_t* kind, int32_t block, float sm_scale,
+                                void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || !(sm_scale > 0.f))
+    return fa_set_err(nullptr, KV_ERR_INVALID, "bad prefill shape or scale");
+  if (head_dim != kD || block != kB)
+    return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill needs head_dim 128 and block 64");
+  if (T == 0) return KV_OK;
+  if (!q || !k || !v || !out || !row_ptr || !col || !kind || !workspace)
+    return fa_set_err(nullptr, KV_ERR_INVALID, "null pointer");
+  const WsLayout w = ws_layout(T, n_kv_heads);
+  if (ws_bytes < w.total) return fa_set_err(nullptr, KV_ERR_WORKSPACE, "prefill workspace too small");
+  const int nb = (T + kB - 1) / kB;
+  char* ws = static_cast<char*>(workspace);
+  Params p;
+  p.q = static_cast<const bf16_t*>(q);
+  p.kimg = ws + w.kimg;
+  p.vimg = ws + w.vimg;
+  p.out = static_cast<bf16_t*>(out);
+  p.lse = lse;
+  p.row_ptr = row_ptr;
+  p.col = col;
+  p.kind = kind;
+  p.order = reinterpret_cast<const int32_t*>(ws + w.order);
+  p.T = T;
+  p.hq = n_q_heads;
+  p.hkv = n_kv_heads;
+  p.G = n_q_heads / n_kv_heads;
+  p.n_hg = (p.G + 3) / 4;
+  p.nb = nb;
+  p.sm_scale = sm_scale;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  relayout_kernel<<<dim3(nb, n_kv_heads), 256, 0, stream>>>(static_cast<const bf16_t*>(k),
+                                                           static_cast<const bf16_t*>(v), ws + w.kimg, ws + w.vimg,
+                                                           T, n_kv_heads, nb);
+  rank_kernel<<<(nb + 255) / 256, 256, 0, stream>>>(row_ptr, reinterpret_cast<int32_t*>(ws + w.order), nb);
+  prefill_kernel<<<(size_t)nb * n_kv_heads * p.n_hg, 256, 0, stream>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill: ") + hipGetErrorString(e));
+  return KV_OK;
 }
