@@ -83,8 +83,9 @@ _SIGS = {
     "fork_attn_partials": [_P, _pi32, _i32, _i32, _P, C.c_float, _P, _sz, _P],
     "fork_attn_merge": [_P, _pi32, _i32, _i32, _P, _P, _P, _sz, _P],
     "dag_mask_build": [_pi32, _i32, _pi32, _i32, _i32, _i32, _pi32, _pi32, C.POINTER(C.c_uint8), _pi64],
-    "dag_attn_workspace_size": [_i32, _i32, _i32, _i32, _psz],
-    "dag_attn_prefill": [_P, _P, _P, _P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, _i32, C.c_float, _P, _sz, _P],
+    "dag_attn_workspace_size": [_i32, _i32, _i32, _i32, C.c_int64, _psz],
+    "dag_attn_prefill": [_P, _P, _P, _P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, C.c_int64, _i32, C.c_float, _P,
+                         _sz, _P],
 }
 EXPORTED = sorted(list(_SIGS) + ["kv_status_str", "kv_last_error"])
 for _name, _args in _SIGS.items():
@@ -299,17 +300,18 @@ def dag_mask_build(segments, edges, T: int, block: int = 64):
     return row_ptr, col[:nnz.value].copy(), kind[:nnz.value].copy()
 
 
-def dag_attn_workspace_size(T: int, n_q_heads: int, n_kv_heads: int, block: int = 64) -> int:
+def dag_attn_workspace_size(T: int, n_q_heads: int, n_kv_heads: int, block: int = 64, nnz: int = 0) -> int:
     out = C.c_size_t()
-    _check("dag_attn_workspace_size", lib.dag_attn_workspace_size(T, n_q_heads, n_kv_heads, block, C.byref(out)))
+    _check("dag_attn_workspace_size", lib.dag_attn_workspace_size(T, n_q_heads, n_kv_heads, block, nnz,
+                                                                  C.byref(out)))
     return out.value
 
 
 def dag_attn_prefill(q: int, k: int, v: int, out: int, lse: int, T: int, n_q_heads: int, n_kv_heads: int,
-                     head_dim: int, row_ptr: int, col: int, kind: int, block: int, sm_scale: float,
+                     head_dim: int, row_ptr: int, col: int, kind: int, nnz: int, block: int, sm_scale: float,
                      workspace: int, ws_bytes: int, stream: int = 0):
     _check("dag_attn_prefill", lib.dag_attn_prefill(q, k, v, out, lse or None, T, n_q_heads, n_kv_heads, head_dim,
-                                                    row_ptr, col, kind, block, sm_scale, workspace or None,
+                                                    row_ptr, col, kind, nnz, block, sm_scale, workspace or None,
                                                     ws_bytes, stream or None))
 
 
@@ -339,12 +341,13 @@ def prefill(q, k, v, mask: DagMask, sm_scale: float, out=None, lse=None, workspa
         out = torch.empty_like(q)
     if lse is None and with_lse:
         lse = torch.empty((hq, T), dtype=torch.float32, device=q.device)
-    need = dag_attn_workspace_size(T, hq, hkv, mask.block)
+    need = dag_attn_workspace_size(T, hq, hkv, mask.block, mask.nnz)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     dag_attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr() if lse is not None else 0,
-                     T, hq, hkv, d, mask.row_ptr.data_ptr(), mask.col.data_ptr(), mask.kind.data_ptr(), mask.block,
-                     sm_scale, workspace.data_ptr(), workspace.numel(), torch.cuda.current_stream().cuda_stream)
+                     T, hq, hkv, d, mask.row_ptr.data_ptr(), mask.col.data_ptr(), mask.kind.data_ptr(), mask.nnz,
+                     mask.block, sm_scale, workspace.data_ptr(), workspace.numel(),
+                     torch.cuda.current_stream().cuda_stream)
     return out, lse
 
 

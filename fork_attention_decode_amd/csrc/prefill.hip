@@ -54,10 +54,6 @@ struct Params {
   const char* vimg;
   bf16_t* out;
   float* lse;
-  const int32_t* row_ptr;
-  const int32_t* col;
-  const uint8_t* kind;
-  const int32_t* order;
   int32_t T, hq, hkv, G, n_hg, nb;
   float scale_log2, sm_scale;
 };
@@ -106,6 +102,17 @@ __global__ __launch_bounds__(256) void relayout_kernel(const bf16_t* __restrict_
   }
 }
 
+// ---- column list for the main kernel: col clamped to [0, nb), kind in the sign bit
+constexpr int32_t kDiagBit = (int32_t)0x80000000u;
+__global__ __launch_bounds__(256) void pack_kernel(const int32_t* __restrict__ col, const uint8_t* __restrict__ kind,
+                                                   int32_t* __restrict__ ent, int64_t nnz, int nb) {
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < nnz; j += (int64_t)gridDim.x * 256) {
+    int c = col[j];
+    c = c < 0 ? 0 : (c >= nb ? nb - 1 : c);
+    ent[j] = c | (kind[j] ? kDiagBit : 0);
+  }
+}
+
 // ---- rows by descending cost (ties by index): order[rank] = row
 __global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ row_ptr, int32_t* __restrict__ order,
                                                    int nb) {
@@ -141,7 +148,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256, 1) void prefill_kernel(Params p) {
+// row_ptr / ent / order are read-only here and never alias the outputs, so their
+// wave-uniform reads become scalar loads (a vector load would have to wait for every
+// global->LDS copy in flight before it).
+__global__ __launch_bounds__(256, 1) void prefill_kernel(Params p, const int32_t* __restrict__ row_ptr,
+                                                         const int32_t* __restrict__ ent,
+                                                         const int32_t* __restrict__ order) {
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kStage];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -149,22 +161,20 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(Params p) {
   const int h = b % p.hkv;
   const int rest = b / p.hkv;
   const int hg = rest % p.n_hg;
-  const int row = p.order[rest / p.n_hg];
+  const int row = order[rest / p.n_hg];
   const int hslot = hg * 4 + wave;
   const bool active = hslot < p.G;
   const int qhead = h * p.G + (active ? hslot : 0);
   const int q0 = row * kB;
-  const int j0 = p.row_ptr[row];
-  const int n = p.row_ptr[row + 1] - j0;
+  const int j0 = row_ptr[row];
+  const int n = row_ptr[row + 1] - j0;
   const int hi = lane >> 5, lo = lane & 31;
 
   // this wave's quarter of every stage: waves 0, 1 copy the K image, waves 2, 3 the V image
   const int my_off = wave * (kStage / 4);
   const char* my_src = (my_off < kImg ? p.kimg + my_off : p.vimg + (my_off - kImg)) + (size_t)h * p.nb * kImg;
-  auto col_of = [&](int j) {
-    int c = p.col[j0 + (j < n ? j : n - 1)];
-    return c < 0 ? 0 : (c >= p.nb ? p.nb - 1 : c);  // never leave the images
-  };
+  auto ent_of = [&](int j) { return ent[j0 + (j < n ? j : n - 1)]; };
+  auto col_of = [&](int j) { return ent_of(j) & ~kDiagBit; };
   auto issue = [&](int j) {  // past the end: reload the last block into a slot nobody reads
     const char* src = my_src + (size_t)col_of(j) * kImg + lane * 16;
     char* dst = ring + (j % kStages) * kStage + my_off;
@@ -173,9 +183,6 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(Params p) {
       __builtin_amdgcn_global_load_lds(src + i * 1024, (__attribute__((address_space(3))) void*)(dst + i * 1024),
                                        16, 0, 0);
   };
-
-  if (n > 0) issue(0);
-  if (n > 0) issue(1);
 
   // queries: B operand of S^T = K Q^T, lane holds Q[q0 + 32 qt + lo][16 ks + 8 hi + 0..7]
   bf16x8 qf[2][8];
@@ -189,6 +196,9 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(Params p) {
       if (tq >= p.T) qf[qt][ks] = bf16x8{};
     }
   }
+
+  if (n > 0) issue(0);
+  if (n > 0) issue(1);
 
   f32x16 o[4][2];
 #pragma unroll
@@ -204,7 +214,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(Params p) {
     asm volatile("s_barrier" ::: "memory");       // ... every wave's; slot (j - 1) % 3 is free
     issue(j + kStages - 1);
     if (!active) continue;
-    const int c = col_of(j);
+    const int e = ent_of(j);
+    const int c = e & ~kDiagBit;
     const char* kslot = ring + (j % kStages) * kStage;
     const char* vslot = kslot + kImg;
 
@@ -224,17 +235,19 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(Params p) {
     }
 
     // mask: diagonal block (key > query) and keys past T
-    const bool diag = p.kind[j0 + j] == 1;
+    const bool diag = e < 0;
     if (diag || (ragged && c == p.nb - 1)) {
+      const int kb = c * kB + 4 * hi;  // key of register r in tile kt: kb + 32 kt + 8 (r / 4) + r % 4
+      const int lim = diag ? q0 + lo : 0x7fffffff;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = c * kB + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-            const int qry = q0 + 32 * qt + lo;
-            if ((diag && key > qry) || key >= p.T) s[kt][qt][r] = -INFINITY;
+            const int key = kb + 32 * kt + 8 * (r >> 2) + (r & 3);
+            const bool off = key > lim + 32 * qt || key >= p.T;
+            s[kt][qt][r] = off ? -INFINITY : s[kt][qt][r];
           }
     }
 
@@ -311,13 +324,14 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(Params p) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t order, kimg, vimg, total;
+  size_t order, ent, kimg, vimg, total;
 };
-WsLayout ws_layout(int32_t T, int32_t hkv) {
+WsLayout ws_layout(int32_t T, int32_t hkv, int64_t nnz) {
   const size_t nb = (size_t)(T + kB - 1) / kB;
   WsLayout w;
   w.order = 0;
-  w.kimg = align256(nb * 4);
+  w.ent = align256(nb * 4);
+  w.kimg = align256(w.ent + (size_t)nnz * 4);
   w.vimg = w.kimg + (size_t)hkv * nb * kImg;
   w.total = w.vimg + (size_t)hkv * nb * kImg;
   return w;
@@ -329,26 +343,26 @@ WsLayout ws_layout(int32_t T, int32_t hkv) {
 using namespace fa;
 
 extern "C" int dag_attn_workspace_size(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t block,
-                                       size_t* bytes) {
-  if (!bytes || T < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads)
+                                       int64_t nnz, size_t* bytes) {
+  if (!bytes || T < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || nnz < 0)
     return fa_set_err(nullptr, KV_ERR_INVALID, "bad prefill shape");
   if (block != kB) return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill block must be 64");
-  *bytes = ws_layout(T, n_kv_heads).total;
+  *bytes = ws_layout(T, n_kv_heads, nnz).total;
   return KV_OK;
 }
 
 extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int32_t T,
                                 int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, const int32_t* row_ptr,
-                                const int32_t* col, const uint8_t* kind, int32_t block, float sm_scale,
-                                void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (T < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || !(sm_scale > 0.f))
-    return fa_set_err(nullptr, KV_ERR_INVALID, "bad prefill shape or scale");
+                                const int32_t* col, const uint8_t* kind, int64_t nnz, int32_t block,
+                                float sm_scale, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || !(sm_scale > 0.f) || nnz < 0)
+    return fa_set_err(nullptr, KV_ERR_INVALID, "bad prefill shape, scale or nnz");
   if (head_dim != kD || block != kB)
     return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill needs head_dim 128 and block 64");
   if (T == 0) return KV_OK;
-  if (!q || !k || !v || !out || !row_ptr || !col || !kind || !workspace)
+  if (!q || !k || !v || !out || !row_ptr || !workspace || (nnz > 0 && (!col || !kind)))
     return fa_set_err(nullptr, KV_ERR_INVALID, "null pointer");
-  const WsLayout w = ws_layout(T, n_kv_heads);
+  const WsLayout w = ws_layout(T, n_kv_heads, nnz);
   if (ws_bytes < w.total) return fa_set_err(nullptr, KV_ERR_WORKSPACE, "prefill workspace too small");
   const int nb = (T + kB - 1) / kB;
   char* ws = static_cast<char*>(workspace);
@@ -358,10 +372,6 @@ extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, voi
   p.vimg = ws + w.vimg;
   p.out = static_cast<bf16_t*>(out);
   p.lse = lse;
-  p.row_ptr = row_ptr;
-  p.col = col;
-  p.kind = kind;
-  p.order = reinterpret_cast<const int32_t*>(ws + w.order);
   p.T = T;
   p.hq = n_q_heads;
   p.hkv = n_kv_heads;
@@ -370,11 +380,17 @@ extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, voi
   p.nb = nb;
   p.sm_scale = sm_scale;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
+  int32_t* ent = reinterpret_cast<int32_t*>(ws + w.ent);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + w.order);
   relayout_kernel<<<dim3(nb, n_kv_heads), 256, 0, stream>>>(static_cast<const bf16_t*>(k),
                                                            static_cast<const bf16_t*>(v), ws + w.kimg, ws + w.vimg,
                                                            T, n_kv_heads, nb);
-  rank_kernel<<<(nb + 255) / 256, 256, 0, stream>>>(row_ptr, reinterpret_cast<int32_t*>(ws + w.order), nb);
-  prefill_kernel<<<(size_t)nb * n_kv_heads * p.n_hg, 256, 0, stream>>>(p);
+  if (nnz > 0) {
+    const int64_t blocks = (nnz + 255) / 256;
+    pack_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(col, kind, ent, nnz, nb);
+  }
+  rank_kernel<<<(nb + 255) / 256, 256, 0, stream>>>(row_ptr, order, nb);
+  prefill_kernel<<<(size_t)nb * n_kv_heads * p.n_hg, 256, 0, stream>>>(p, row_ptr, ent, order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill: ") + hipGetErrorString(e));
   return KV_OK;

@@ -230,16 +230,26 @@ int dag_mask_build(const int32_t* segments, int32_t n_seg, const int32_t* edges,
                    uint8_t* kind, int64_t* nnz);
 
 /* Block-sparse forward over the CSR (DEVICE arrays row_ptr / col / kind from
- * dag_mask_build, block = 64).  q: DEVICE bf16 [T][Hq][d], k / v: DEVICE bf16
- * [T][Hkv][d], out: DEVICE bf16 [T][Hq][d], lse: DEVICE fp32 [Hq][T] or NULL.
- * d = 128.  workspace: DEVICE buffer of dag_attn_workspace_size() bytes. */
+ * dag_mask_build, block = 64, nnz = row_ptr[nb]).  Octopus "Packed DAG-GRPO": only
+ * the block pairs listed are computed; kind 1 blocks mask key > query (global token
+ * indices), keys >= T are always masked.
+ *   q: DEVICE bf16 [T][Hq][d], k / v: DEVICE bf16 [T][Hkv][d], out: DEVICE bf16
+ *   [T][Hq][d], lse: DEVICE fp32 [Hq][T] (natural log of the softmax denominator of
+ *   sm_scale * q.k) or NULL.  d = 128; Hq a multiple of Hkv (query head h reads KV
+ *   head h / (Hq / Hkv)).  A row with no visible key yields zeros and lse = -inf.
+ *   workspace: DEVICE buffer of at least dag_attn_workspace_size() bytes for the same
+ *   T, heads, block and nnz; it receives operand-order images of K and V and the
+ *   packed column list.  Column indices outside [0, nb) are clamped, never followed.
+ * Errors: KV_ERR_INVALID (shapes, null pointers, scale <= 0), KV_ERR_UNSUPPORTED
+ * (d != 128 or block != 64), KV_ERR_WORKSPACE (workspace too small), KV_ERR_HIP
+ * (launch failure).  T = 0 returns KV_OK and does nothing. */
 int dag_attn_workspace_size(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t block,
-                            size_t* bytes);
+                            int64_t nnz, size_t* bytes);
 int dag_attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse,
                      int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                      const int32_t* row_ptr, const int32_t* col, const uint8_t* kind,
-                     int32_t block, float sm_scale, void* workspace, size_t ws_bytes,
-                     hipStream_t stream);
+                     int64_t nnz, int32_t block, float sm_scale, void* workspace,
+                     size_t ws_bytes, hipStream_t stream);
 
 /* ---- errors ---- */
 const char* kv_status_str(int status);
