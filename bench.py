@@ -54,7 +54,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on "
-              f"a single MI355X; see DESIGN.md for how the path would shard).", file=sys.stderr)
+              f"a single MI355X; decode shards by KV head with no exchange across GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

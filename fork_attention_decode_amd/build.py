@@ -14,15 +14,20 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libforkattn.so")
 SOURCES = ["pool.cpp", "planner.cpp", "drop.cpp", "dagmask.cpp", "decode.hip", "compact.hip", "prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed fp32 VALU forms are disabled for every device pass (numerics).
+# Packed fp32 VALU forms (v_pk_*_f32) are disabled for every device pass: the kernels
+# use plain fp32 VALU arithmetic only.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source device flags.  The prefill kernel keeps its matrix-core results in
+# architectural VGPRs (the softmax reads them with VALU instructions); without this the
+# allocator parks them in AGPRs and copies them back every block.
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
 
 def _compile(src: str, out_dir: str) -> str:
     obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
-    cmd = [HIPCC] + COMMON + DEVICE_FLAGS + ["-c", path, "-o", obj]
+    cmd = [HIPCC] + COMMON + DEVICE_FLAGS + EXTRA.get(src, []) + ["-c", path, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC] + COMMON + ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include", "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -45,7 +45,9 @@ constexpr int kD = 128;              // head dim
 constexpr int kImg = kB * kD * 2;    // bytes of one K (or V) block image
 constexpr int kStage = 2 * kImg;     // K image + V image
 constexpr int kStages = 3;           // LDS ring depth
-constexpr int kLoadsPerWave = kStage / 4 / 1024;  // 1 KiB wave loads per stage per wave
+constexpr int kWaves = 8;            // waves per workgroup (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLoadsPerWave = kStage / kWaves / 1024;  // 1 KiB wave loads per stage per wave
 constexpr float kTau = 8.f;          // lazy rescale threshold (log2 units)
 
 struct Params {
@@ -151,9 +153,13 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // row_ptr / ent / order are read-only here and never alias the outputs, so their
 // wave-uniform reads become scalar loads (a vector load would have to wait for every
 // global->LDS copy in flight before it).
-__global__ __launch_bounds__(256, 1) void prefill_kernel(Params p, const int32_t* __restrict__ row_ptr,
-                                                         const int32_t* __restrict__ ent,
-                                                         const int32_t* __restrict__ order) {
+//
+// 8 waves, two per SIMD: wave w takes query head slot w / 2 and tokens
+// [q0 + 32 (w % 2), +32) of the block, so each SIMD interleaves two waves and one wave's
+// LDS latency and softmax overlap the other's matrix instructions.
+__global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32_t* __restrict__ row_ptr,
+                                                          const int32_t* __restrict__ ent,
+                                                          const int32_t* __restrict__ order) {
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kStage];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -162,16 +168,16 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(Params p, const int32_t
   const int rest = b / p.hkv;
   const int hg = rest % p.n_hg;
   const int row = order[rest / p.n_hg];
-  const int hslot = hg * 4 + wave;
+  const int hslot = hg * 4 + (wave >> 1);
   const bool active = hslot < p.G;
-  const int qhead = h * p.G + (active ? hslot : 0);
-  const int q0 = row * kB;
+  const int qhead = h * p.G + (active ? hslot : 0);  // an idle wave computes head 0 and stores nothing
+  const int q0 = row * kB + 32 * (wave & 1);         // this wave's 32 queries
   const int j0 = row_ptr[row];
   const int n = row_ptr[row + 1] - j0;
   const int hi = lane >> 5, lo = lane & 31;
 
-  // this wave's quarter of every stage: waves 0, 1 copy the K image, waves 2, 3 the V image
-  const int my_off = wave * (kStage / 4);
+  // this wave's eighth of every stage: waves 0-3 copy the K image, waves 4-7 the V image
+  const int my_off = wave * (kStage / kWaves);
   const char* my_src = (my_off < kImg ? p.kimg + my_off : p.vimg + (my_off - kImg)) + (size_t)h * p.nb * kImg;
   auto ent_of = [&](int j) { return ent[j0 + (j < n ? j : n - 1)]; };
   auto col_of = [&](int j) { return ent_of(j) & ~kDiagBit; };
@@ -184,28 +190,24 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(Params p, const int32_t
                                        16, 0, 0);
   };
 
-  // queries: B operand of S^T = K Q^T, lane holds Q[q0 + 32 qt + lo][16 ks + 8 hi + 0..7]
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int tq = q0 + 32 * qt + lo;
+  // queries: B operand of S^T = K Q^T, lane holds Q[q0 + lo][16 ks + 8 hi + 0..7]
+  bf16x8 qf[8];
+  {
+    const int tq = q0 + lo;
     const bf16_t* src = p.q + ((size_t)(tq < p.T ? tq : 0) * p.hq + qhead) * kD + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      qf[qt][ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
-      if (tq >= p.T) qf[qt][ks] = bf16x8{};
+      qf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
+      if (tq >= p.T) qf[ks] = bf16x8{};
     }
   }
-
   if (n > 0) issue(0);
   if (n > 0) issue(1);
 
-  f32x16 o[4][2];
+  f32x16 o[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) o[dt][qt] = f32x16{};
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+  float m = -INFINITY, l = 0.f;
   const float c2 = p.scale_log2;
   const bool ragged = (p.T & (kB - 1)) != 0;
 
@@ -213,112 +215,91 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(Params p, const int32_t
     wait_vmcnt<(kStages - 2) * kLoadsPerWave>();  // this wave's part of block j landed
     asm volatile("s_barrier" ::: "memory");       // ... every wave's; slot (j - 1) % 3 is free
     issue(j + kStages - 1);
-    if (!active) continue;
     const int e = ent_of(j);
     const int c = e & ~kDiagBit;
     const char* kslot = ring + (j % kStages) * kStage;
     const char* vslot = kslot + kImg;
 
-    f32x16 s[2][2];
+    // S^T for the 64 keys of the block: two independent accumulation chains (kt)
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) s[kt][qt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kslot + ((kt * 8 + ks) * 64 + lane) * 16);
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[kt][qt] = mfma32(a, qf[qt][ks], s[kt][qt]);
+        s[kt] = mfma32(a, qf[ks], s[kt]);
       }
-    }
-
-    // mask: diagonal block (key > query) and keys past T
     const bool diag = e < 0;
-    if (diag || (ragged && c == p.nb - 1)) {
-      const int kb = c * kB + 4 * hi;  // key of register r in tile kt: kb + 32 kt + 8 (r / 4) + r % 4
+    if (diag || (ragged && c == p.nb - 1)) {  // diagonal block (key > query) and keys past T
+      const int kb = c * kB + 4 * hi;          // key of register r in tile kt: kb + 32 kt + 8 (r / 4) + r % 4
       const int lim = diag ? q0 + lo : 0x7fffffff;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb + 32 * kt + 8 * (r >> 2) + (r & 3);
-            const bool off = key > lim + 32 * qt || key >= p.T;
-            s[kt][qt][r] = off ? -INFINITY : s[kt][qt][r];
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb + 32 * kt + 8 * (r >> 2) + (r & 3);
+          s[kt][r] = (key > lim || key >= p.T) ? -INFINITY : s[kt][r];
+        }
     }
 
-    // online softmax per query column (this lane's query, plus its partner lane ^ 32)
-    bf16x8 pk[2][2][2];  // [kt][qt][half of the 32 keys]
+    // online softmax for this lane's query (its 64 keys are split with lane ^ 32)
+    float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float mx = -INFINITY;
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    mx = xhalf_max(mx);
+    const float mn = fmaxf(m, mx);
+    if (__builtin_amdgcn_ballot_w64((mn - m) * c2 > kTau)) {  // wave-uniform; false while both are -inf
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
+      m = mn;
+      l *= alpha;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][qt][r]);
-      mx = xhalf_max(mx);
-      const float mn = fmaxf(m[qt], mx);
-      const bool grow = (mn - m[qt]) * c2 > kTau;  // false while both are -inf
-      if (__builtin_amdgcn_ballot_w64(grow)) {     // wave-uniform: rescale to each lane's new max
-        const float alpha = m[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m[qt] - mn) * c2);
-        m[qt] = mn;
-        l[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt][qt] *= alpha;
-      }
-      const float mc = m[qt] == -INFINITY ? 0.f : m[qt] * c2;
-      float ls = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][8 * hf + e], c2, -mc));
-            ls += pe;
-            pk[kt][qt][hf][e] = (bf16_t)pe;
-          }
-      l[qt] += ls;
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
+    const float mc = m == -INFINITY ? 0.f : m * c2;
+    bf16x8 pk[2][2];  // [kt][half of the 32 keys]
+    float ls = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][8 * hf + q], c2, -mc));
+          ls += pe;
+          pk[kt][hf][q] = (bf16_t)pe;
+        }
+    l += ls;
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        for (int dt = 0; dt < 4; ++dt) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(vslot + (((dt * 2 + kt) * 2 + hf) * 64 + lane) * 16);
-#pragma unroll
-          for (int qt = 0; qt < 2; ++qt) o[dt][qt] = mfma32(a, pk[kt][qt][hf], o[dt][qt]);
+          o[dt] = mfma32(a, pk[kt][hf], o[dt]);
         }
   }
   wait_vmcnt<0>();  // no load may land in LDS after the workgroup ends
   if (!active) return;
 
+  const float lt = xhalf_sum(l);
+  const int tq = q0 + lo;
+  if (tq >= p.T) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a row with no visible key: zeros, lse -inf
+  bf16_t* dst = p.out + ((size_t)tq * p.hq + qhead) * kD + 4 * hi;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float lt = xhalf_sum(l[qt]);
-    const int tq = q0 + 32 * qt + lo;
-    if (tq >= p.T) continue;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a row with no visible key: zeros, lse -inf
-    bf16_t* dst = p.out + ((size_t)tq * p.hq + qhead) * kD + 4 * hi;
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 w;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16_t)(o[dt][qt][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * g) = w;
-      }
-    if (p.lse && hi == 0)
-      p.lse[(size_t)qhead * p.T + tq] = lt > 0.f ? (m[qt] * c2 + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
-  }
+      for (int q = 0; q < 4; ++q) w[q] = (bf16_t)(o[dt][4 * g + q] * inv);
+      *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * g) = w;
+    }
+  if (p.lse && hi == 0)
+    p.lse[(size_t)qhead * p.T + tq] = lt > 0.f ? (m * c2 + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -390,7 +371,7 @@ extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, voi
     pack_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(col, kind, ent, nnz, nb);
   }
   rank_kernel<<<(nb + 255) / 256, 256, 0, stream>>>(row_ptr, order, nb);
-  prefill_kernel<<<(size_t)nb * n_kv_heads * p.n_hg, 256, 0, stream>>>(p, row_ptr, ent, order);
+  prefill_kernel<<<(size_t)nb * n_kv_heads * p.n_hg, kThreads, 0, stream>>>(p, row_ptr, ent, order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill: ") + hipGetErrorString(e));
   return KV_OK;

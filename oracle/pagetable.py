@@ -20,7 +20,7 @@ Sources (page / section):
   * AgentKV (rit.work page): kept entries are physically compacted and the freed
     pages are returned to the allocator.
 
-Readings taken where the pages are silent (each is also listed in the design doc):
+Readings taken where the pages are silent:
   1. allocation takes the lowest free page id; within one operation copy-on-write
      destinations come first, then new pages in logical order; every allocation of an
      operation happens before any of its frees;
