@@ -1,14 +1,23 @@
-"""Benchmark: one step = one fork_attn_decode over every branch of the shared-prefix fork
-workload (16 branches x 32 query heads, 8 KV heads, d=128, bf16, 32,768-token shared
-prefix + 2,048 private tokens per branch, page 16), inputs resident in HBM.
+"""Benchmark of the fork / DAG attention hot path on one MI355X.  Prints ONE JSON line.
 
-Prints ONE JSON line.  `value` = branch-tokens/s (branches decoded per second, wall clock
-over the timed steps); the roofline object prices the dominant kernel (decode_kernel)
-against MI355X's 8 TB/s HBM with its algorithmic bytes (unique KV + Q), timed with HIP
-events on the launch stream; `step` reports the whole step (decode + merge) the same way.  Steps rotate over
-several identical pool copies so that no step finds its KV in the 256 MB last-level
-cache left behind by the previous one.  The cpu_baseline leg times the fp64 oracle on a
-bounded sample of the same workload on the host cores.
+Step (the headline `value`): one fork_attn_decode over every branch of the shared-prefix
+fork workload -- 16 branches x 32 query heads, 8 KV heads, d = 128, bf16, a 32,768-token
+shared prefix + 2,048 private tokens per branch, page 16 -- with every input resident
+in HBM.  `value` = branch-tokens/s (branches decoded per second of wall clock over the
+timed steps).  `roofline` prices the dominant kernel (decode_kernel, launched by
+fork_attn_partials) against MI355X's 8 TB/s HBM with its algorithmic bytes (each unique
+KV byte once + Q), timed with HIP events on the launch stream.  Steps rotate over
+several identical pool copies so no step finds its KV in the last-level cache left by
+the previous one.
+
+Further objects in the same line (each timed the same way, on its own workload):
+  prefill       the packed DAG prefill attention kernel (dag_attn_run) on the
+                81,920-token packed workload, priced against 2.5 PFLOP/s dense bf16 with
+                its algorithmic FLOPs (4 d per visible query-key pair per query head);
+  octopus_dag   decode over the Octopus-style DAG (mounted sibling blocks);
+  akv           drop + repos compaction of 16 x 131,072-token requests (40 % dropped),
+                then decode over the compacted requests.
+cpu_baseline times the fp64 oracle on a bounded sample of the headline workload.
 """
 import argparse
 import json
@@ -21,7 +30,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fork-decode branch-tokens/s + achieved HBM GB/s (% of peak); DAG-prefill % MFMA peak"
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
+PREFILL_FLOPS = 27488461783040  # 4 * 128 * 1,677,762,560 visible pairs * 32 query heads
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def measured_traffic():
@@ -38,16 +53,245 @@ def measured_traffic():
         return None
 
 
+class DecodeBench:
+    """fork_attn_partials + fork_attn_merge over prepared pools (plans cached)."""
+
+    def __init__(self, pools, sc, q):
+        import torch
+        import fork_attention_decode_amd as fa
+        self.fa, self.torch = fa, torch
+        self.pools, self.sc, self.q = pools, sc, q
+        self.n, self.hq, self.d = q.shape
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((self.n, self.hq), dtype=torch.float32, device=q.device)
+        self.wss = []
+        for p in pools:
+            need = fa.fork_attn_workspace_size(p.handle, sc.queries, self.hq)
+            self.wss.append(torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device))
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.stats = pools[0].plan_stats()
+        es = 2 if sc.dtype == "bf16" else 4
+        self.kernel_bytes = self.stats["unique_kv_bytes"] + q.numel() * es  # decode kernel: unique KV + Q
+        self.step_bytes = self.kernel_bytes + q.numel() * es                # whole step: + O written
+
+    def step(self, i, ev=None):
+        p, ws = self.pools[i % len(self.pools)], self.wss[i % len(self.pools)]
+        if ev:
+            ev[0].record()
+        self.fa.fork_attn_partials(p.handle, self.sc.queries, self.hq, self.q.data_ptr(), self.sc.sm_scale,
+                                   ws.data_ptr(), ws.numel(), self.stream)
+        if ev:
+            ev[1].record()
+        self.fa.fork_attn_merge(p.handle, self.sc.queries, self.hq, self.out.data_ptr(), self.lse.data_ptr(),
+                                ws.data_ptr(), ws.numel(), self.stream)
+        if ev:
+            ev[2].record()
+
+    def settle(self, seconds):
+        """Untimed steps for `seconds` of wall clock before the warmup: the first few
+        hundred launches of a fresh process run several times slower than the steady state
+        (measured: ~200 us per step for the first ~200 steps, then ~52 us), whatever the
+        warmup count asked for."""
+        torch = self.torch
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            self.step(i)
+            i += 1
+            if i % 64 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return i
+
+    def run(self, steps, warmup, settle_s=0.0):  # -> wall seconds, decode-kernel ms, step ms
+        import numpy as np
+        torch = self.torch
+        self.settled_steps = self.settle(settle_s) if settle_s > 0 else 0
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(i, ev[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        k_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+        s_ms = np.array([a.elapsed_time(c) for a, _, c in ev])
+        return wall, k_ms, s_ms
+
+    def summary(self, steps, warmup, settle_s=0.5):
+        import numpy as np
+        wall, k_ms, s_ms = self.run(steps, warmup, settle_s)
+        t_k = float(np.mean(k_ms)) * 1e-3
+        t_s = float(np.mean(s_ms)) * 1e-3
+        return {
+            "branch_tokens_per_s": self.n / (wall / steps),
+            "ms_per_step_wall": wall * 1e3 / steps,
+            "decode_kernel_us_mean": t_k * 1e6,
+            "decode_kernel_GBps": self.kernel_bytes / t_k / 1e9,
+            "decode_kernel_frac_of_8TBps": self.kernel_bytes / t_k / 1e9 / HBM_PEAK_GBPS,
+            "step_us_mean_events": t_s * 1e6,
+            "step_GBps": self.step_bytes / t_s / 1e9,
+            "step_frac_of_8TBps": self.step_bytes / t_s / 1e9 / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": self.kernel_bytes,
+            "steps": steps,
+            "settle_steps": self.settled_steps,
+            "plan": self.stats,
+        }
+
+
+def bench_prefill(reps, warmup):
+    """dag_attn_run (attention kernel alone, HIP events on its stream) on the packed DAG
+    workload; the preparation (K / V relayout, column packing, row order) is timed apart."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import fork_attention_decode_amd as fa
+    from tests.harness import to_torch
+    log("prefill: generating the packed DAG workload")
+    pi = W.dag_prefill()
+    mask = fa.DagMask(pi.segments, pi.edges, pi.T, pi.block)
+    q, k, v = (to_torch(x, "bf16") for x in (pi.q, pi.k, pi.v))
+    pi.q = pi.k = pi.v = None
+    hq, hkv = q.shape[1], k.shape[1]
+    out = torch.empty_like(q)
+    lse = torch.empty((hq, pi.T), dtype=torch.float32, device=q.device)
+    ws = torch.empty(fa.dag_attn_workspace_size(pi.T, hq, hkv, 64, mask.nnz), dtype=torch.uint8, device=q.device)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def prepare():
+        fa.dag_attn_prepare(k.data_ptr(), v.data_ptr(), pi.T, hq, hkv, 128, mask.row_ptr.data_ptr(),
+                            mask.col.data_ptr(), mask.kind.data_ptr(), mask.nnz, 64, ws.data_ptr(), ws.numel(), st)
+
+    def run():
+        fa.dag_attn_run(q.data_ptr(), out.data_ptr(), lse.data_ptr(), pi.T, hq, hkv, 128, mask.row_ptr.data_ptr(),
+                        mask.nnz, 64, pi.sm_scale, ws.data_ptr(), ws.numel(), st)
+
+    prepare()
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    log(f"prefill: timing {reps} calls")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        prepare()
+        e[1].record()
+        run()
+        e[2].record()
+    torch.cuda.synchronize()
+    prep_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    run_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    t = float(np.mean(run_ms)) * 1e-3
+    tflops = PREFILL_FLOPS / t / 1e12
+    return {
+        "workload": "packed_dag_prefill (16,384-token prefix + 8 x 8,192 branches, 12 edges of 2,048 tokens; "
+                    "T = 81,920; 32 / 8 heads, d = 128, bf16)",
+        "block_pairs": mask.nnz,
+        "visible_token_pairs": 1677762560,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "prefill_kernel (dag_attn_run)", "algorithmic_flops_per_launch": PREFILL_FLOPS,
+                     "kernel_ms_mean": t * 1e3, "kernel_ms_p10": float(np.percentile(run_ms, 10)),
+                     "kernel_ms_p90": float(np.percentile(run_ms, 90))},
+        "prepare_ms_mean": float(np.mean(prep_ms)),
+        "call_ms_mean": float(np.mean(prep_ms + run_ms)),
+        "reps": reps,
+    }
+
+
+def bench_octopus(steps, warmup):
+    import workloads as W
+    from tests.harness import build_device_pool, to_torch
+    log("octopus_dag: building 2 pool copies")
+    sc = W.octopus_dag()
+    pools = [build_device_pool(sc)[0] for _ in range(2)]
+    d = DecodeBench(pools, sc, to_torch(sc.q, sc.dtype)).summary(steps, warmup)
+    d["workload"] = ("octopus_dag_decode (65,536-token root, 8 threads x 8,192 private tokens, each mounting "
+                     "the last 4,096 tokens of 2 siblings)")
+    return d
+
+
+def bench_akv(steps, warmup):
+    """Drop + repos of every request (the compaction kernels timed back to back behind a
+    device sleep that covers the host planning), then decode over the compacted pool."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import fork_attention_decode_amd as fa
+    from tests.harness import to_torch
+    log("akv: generating 16 x 131,072-token requests")
+    sc = W.akv_drop_repos()
+    pool = fa.Pool(sc.n_kv_heads, sc.head_dim, sc.n_pages, dtype=sc.dtype, rope_theta=sc.rope_theta)
+    drops, tail, dropped = [], [], set()
+    for op in sc.ops:
+        if op[0] == "create":
+            pool.seq_create()
+        elif op[0] == "drop":
+            drops.append(op)
+            dropped.add(op[1])
+        elif op[0] == "append" and op[1] not in dropped:
+            blk = sc.blocks[op[2]]
+            pool.append(op[1], to_torch(blk.k, sc.dtype), to_torch(blk.v, sc.dtype), positions=blk.pos)
+            torch.cuda.synchronize()
+        else:
+            tail.append(op)
+    moved = 0  # tokens the compaction rewrites: every slot from the first changed page on
+    for _, sid, spans, _ in drops:
+        gone = np.zeros(int(pool.info(sid)[0]), bool)
+        for b, L in spans:
+            gone[b:b + L] = True
+        kept = np.nonzero(~gone)[0]
+        diff = kept != np.arange(len(kept))
+        first = int(np.argmax(diff)) if diff.any() else len(kept)
+        moved += len(kept) - 16 * (first // 16)
+    log("akv: compaction")
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    torch.cuda._sleep(400_000_000)  # device busy while the host plans every drop
+    e1.record()
+    t0 = time.perf_counter()
+    for _, sid, spans, repos in drops:
+        pool.drop(sid, spans, repos=repos)
+    host_s = time.perf_counter() - t0
+    e2.record()
+    torch.cuda.synchronize()
+    covered = e0.elapsed_time(e1) * 1e-3 > host_s
+    comp_ms = e1.elapsed_time(e2)
+    assert pool.sync_status() == 0
+    for op in tail:
+        blk = sc.blocks[op[2]]
+        pool.append(op[1], to_torch(blk.k, sc.dtype), to_torch(blk.v, sc.dtype), positions=blk.pos)
+    torch.cuda.synchronize()
+    comp_bytes = moved * 4 * sc.n_kv_heads * sc.head_dim * 2  # read + write of K and V
+    d = DecodeBench([pool], sc, to_torch(sc.q, sc.dtype)).summary(steps, warmup)
+    d.update({"workload": "akv_drop_repos (16 x 131,072 tokens, 40 % dropped as 2,048-8,192-token spans, repos, "
+                          "then 1 decode token each)",
+              "compaction": {"kernels_ms_total": comp_ms, "moved_tokens": moved,
+                             "algorithmic_bytes": comp_bytes, "GBps": comp_bytes / (comp_ms * 1e-3) / 1e9,
+                             "frac_of_8TBps": comp_bytes / (comp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                             "host_planning_ms_total": host_s * 1e3, "host_hidden_behind_device": covered},
+              "note": "one pool, no rotation: its 5.15 GB of KV exceed the last-level cache"})
+    return d
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup steps (launch path settling)")
     ap.add_argument("--copies", type=int, default=4, help="pool copies rotated between steps")
     ap.add_argument("--workload", default="shared_prefix_fork_decode",
                     choices=["shared_prefix_fork_decode", "octopus_dag_decode", "tiny_fork_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work to sample")
+    ap.add_argument("--only-decode", action="store_true", help="skip the prefill / DAG / AKV objects")
+    ap.add_argument("--only-prefill", action="store_true", help="time the prefill object alone (profiling)")
+    ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy 256 MiB device to device once (a kernel of known "
                          "traffic to scale hardware byte counters against)")
@@ -60,63 +304,32 @@ def main():
     import numpy as np
     import torch
     import workloads as W
-    import fork_attention_decode_amd as fa
     from tests.harness import build_device_pool, to_torch
 
     torch.cuda.set_device(0)
+    if args.only_prefill:
+        pf = bench_prefill(args.prefill_reps, 3)
+        if args.copy_calibration:
+            src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+            torch.empty_like(src).copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"prefill": pf}))
+        return
     sc = W.WORKLOADS[args.workload]()
-    print(f"[bench] workload {args.workload}: building {args.copies} pool copies", file=sys.stderr, flush=True)
+    log(f"workload {args.workload}: building {args.copies} pool copies")
     pools = [build_device_pool(sc)[0] for _ in range(args.copies)]
     q = to_torch(sc.q, sc.dtype)
-    n_br, hq, d = q.shape
-    out = torch.empty_like(q)
-    lse = torch.empty((n_br, hq), dtype=torch.float32, device=q.device)
-    wss = []
-    for p in pools:
-        need = fa.fork_attn_workspace_size(p.handle, sc.queries, hq)
-        wss.append(torch.zeros(max(need, 256), dtype=torch.uint8, device=q.device))
-    stats = pools[0].plan_stats()
-    es = 2 if sc.dtype == "bf16" else 4
-    kernel_bytes = stats["unique_kv_bytes"] + q.numel() * es   # decode kernel: unique KV + Q read
-    step_bytes = kernel_bytes + q.numel() * es                 # whole step: + O written by the merge
-    stream = torch.cuda.current_stream().cuda_stream
-
-    def step(i, ev=None):
-        # one step = the decode kernel (partials) + the merge kernel; events on the
-        # launch stream bracket the decode kernel alone and the whole step
-        p = pools[i % len(pools)]
-        ws = wss[i % len(pools)]
-        if ev:
-            ev[0].record()
-        fa.fork_attn_partials(p.handle, sc.queries, hq, q.data_ptr(), sc.sm_scale, ws.data_ptr(), ws.numel(), stream)
-        if ev:
-            ev[1].record()
-        fa.fork_attn_merge(p.handle, sc.queries, hq, out.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(), stream)
-        if ev:
-            ev[2].record()
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    db = DecodeBench(pools, sc, q)
+    log(f"timing {args.steps} steps after {args.warmup} warmup steps")
+    wall, k_ms, s_ms = db.run(args.steps, args.warmup, args.settle)
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=q.device)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.empty_like(src).copy_(src)
         torch.cuda.synchronize()
-    k_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])      # decode kernel
-    s_ms = np.array([a.elapsed_time(c) for a, _, c in ev])      # whole step (decode + merge)
     ms_step = wall * 1e3 / args.steps
     t_kernel = float(np.mean(k_ms)) * 1e-3
-    achieved = kernel_bytes / t_kernel / 1e9
-
+    achieved = db.kernel_bytes / t_kernel / 1e9
+    n_br, hq, d = q.shape
     result = {
         "metric": METRIC,
         "value": n_br / (ms_step * 1e-3),
@@ -131,21 +344,32 @@ def main():
         "dtype": sc.dtype,
         "data": "synthetic (seeded N(0,1) Q/V, K/sqrt(d), RoPE theta 1e6 pre-applied; no weights)",
         "config": {"workload": args.workload, "branches": n_br, "q_heads": hq, "kv_heads": sc.n_kv_heads,
-                   "head_dim": d, "page_size": sc.page_size, "pool_copies_rotated": args.copies},
+                   "head_dim": d, "page_size": sc.page_size, "pool_copies_rotated": args.copies,
+                   "settle_s": args.settle, "settle_steps": db.settled_steps},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic() if args.workload == "shared_prefix_fork_decode" else None,
                      "kernel": "decode_kernel (fork_attn_partials)",
-                     "algorithmic_bytes_per_launch": kernel_bytes,
-                     "kernel_us_mean": float(np.mean(k_ms)) * 1e3,
+                     "algorithmic_bytes_per_launch": db.kernel_bytes,
+                     "kernel_us_mean": t_kernel * 1e6,
                      "kernel_us_p10": float(np.percentile(k_ms, 10)) * 1e3,
                      "kernel_us_p90": float(np.percentile(k_ms, 90)) * 1e3},
-        "step": {"us_mean_events": float(np.mean(s_ms)) * 1e3, "algorithmic_bytes": step_bytes,
-                 "achieved_GBps": step_bytes / (float(np.mean(s_ms)) * 1e-3) / 1e9,
-                 "frac_of_peak": step_bytes / (float(np.mean(s_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "step": {"us_mean_events": float(np.mean(s_ms)) * 1e3, "algorithmic_bytes": db.step_bytes,
+                 "achieved_GBps": db.step_bytes / (float(np.mean(s_ms)) * 1e-3) / 1e9,
+                 "frac_of_peak": db.step_bytes / (float(np.mean(s_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                  "merge_us_mean": float(np.mean(s_ms - k_ms)) * 1e3},
-        "plan": stats,
+        "plan": db.stats,
     }
+    del db, pools
+    torch.cuda.empty_cache()
+
+    if not args.only_decode:
+        result["prefill"] = bench_prefill(args.prefill_reps, 3)
+        torch.cuda.empty_cache()
+        result["octopus_dag"] = bench_octopus(max(20, args.steps // 4), 5)
+        torch.cuda.empty_cache()
+        result["akv"] = bench_akv(max(20, args.steps // 4), 5)
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sc, args.cpu_budget)
@@ -156,7 +380,6 @@ def cpu_baseline(sc, budget_s):
     """Time the fp64 oracle on a bounded sample of the same workload: branches are decoded
     one at a time (cycling over the workload's branches) until `budget_s` of oracle work
     has been spent."""
-    import numpy as np
     import workloads as W
     from oracle import attention as att, pagetable as pt
     try:
@@ -164,7 +387,7 @@ def cpu_baseline(sc, budget_s):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = None
-    print("[bench] cpu baseline: oracle replay", file=sys.stderr, flush=True)
+    log("cpu baseline: oracle replay")
     table, _ = pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, sc.dtype))
     q = W.storage_to_f64(sc.q, sc.dtype)
     done = 0

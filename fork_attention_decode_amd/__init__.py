@@ -86,6 +86,8 @@ _SIGS = {
     "dag_attn_workspace_size": [_i32, _i32, _i32, _i32, C.c_int64, _psz],
     "dag_attn_prefill": [_P, _P, _P, _P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, C.c_int64, _i32, C.c_float, _P,
                          _sz, _P],
+    "dag_attn_prepare": [_P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, C.c_int64, _i32, _P, _sz, _P],
+    "dag_attn_run": [_P, _P, _P, _i32, _i32, _i32, _i32, _P, C.c_int64, _i32, C.c_float, _P, _sz, _P],
 }
 EXPORTED = sorted(list(_SIGS) + ["kv_status_str", "kv_last_error"])
 for _name, _args in _SIGS.items():
@@ -313,6 +315,18 @@ def dag_attn_prefill(q: int, k: int, v: int, out: int, lse: int, T: int, n_q_hea
     _check("dag_attn_prefill", lib.dag_attn_prefill(q, k, v, out, lse or None, T, n_q_heads, n_kv_heads, head_dim,
                                                     row_ptr, col, kind, nnz, block, sm_scale, workspace or None,
                                                     ws_bytes, stream or None))
+
+
+def dag_attn_prepare(k: int, v: int, T: int, n_q_heads: int, n_kv_heads: int, head_dim: int, row_ptr: int, col: int,
+                     kind: int, nnz: int, block: int, workspace: int, ws_bytes: int, stream: int = 0):
+    _check("dag_attn_prepare", lib.dag_attn_prepare(k, v, T, n_q_heads, n_kv_heads, head_dim, row_ptr, col, kind, nnz,
+                                                    block, workspace or None, ws_bytes, stream or None))
+
+
+def dag_attn_run(q: int, out: int, lse: int, T: int, n_q_heads: int, n_kv_heads: int, head_dim: int, row_ptr: int,
+                 nnz: int, block: int, sm_scale: float, workspace: int, ws_bytes: int, stream: int = 0):
+    _check("dag_attn_run", lib.dag_attn_run(q, out, lse or None, T, n_q_heads, n_kv_heads, head_dim, row_ptr, nnz, block,
+                                            sm_scale, workspace or None, ws_bytes, stream or None))
 
 
 # ------------------------------------------------------------------ packed DAG prefill

@@ -220,15 +220,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
     const char* kslot = ring + (j % kStages) * kStage;
     const char* vslot = kslot + kImg;
 
-    // S^T for the 64 keys of the block: two independent accumulation chains (kt)
+    // S^T for the 64 keys of the block: two independent accumulation chains (kt).  All
+    // 16 K fragments are requested before the first matrix instruction and the V
+    // fragments under it (the scheduling barriers keep the compiler from sinking each
+    // read next to its use, which would expose every LDS latency in turn).
+    bf16x8 kf[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        kf[kt][ks] = *reinterpret_cast<const bf16x8*>(kslot + ((kt * 8 + ks) * 64 + lane) * 16);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kslot + ((kt * 8 + ks) * 64 + lane) * 16);
-        s[kt] = mfma32(a, qf[ks], s[kt]);
-      }
+      for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32(kf[kt][ks], qf[ks], s[kt]);
+    bf16x8 vf[2][2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          vf[kt][hf][dt] = *reinterpret_cast<const bf16x8*>(vslot + (((dt * 2 + kt) * 2 + hf) * 64 + lane) * 16);
+    __builtin_amdgcn_sched_barrier(0);
+
     const bool diag = e < 0;
     if (diag || (ragged && c == p.nb - 1)) {  // diagonal block (key > query) and keys past T
       const int kb = c * kB + 4 * hi;          // key of register r in tile kt: kb + 32 kt + 8 (r / 4) + r % 4
@@ -276,10 +293,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vslot + (((dt * 2 + kt) * 2 + hf) * 64 + lane) * 16);
-          o[dt] = mfma32(a, pk[kt][hf], o[dt]);
-        }
+        for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vf[kt][hf][dt], pk[kt][hf], o[dt]);
   }
   wait_vmcnt<0>();  // no load may land in LDS after the workgroup ends
   if (!active) return;
@@ -332,21 +346,51 @@ extern "C" int dag_attn_workspace_size(int32_t T, int32_t n_q_heads, int32_t n_k
   return KV_OK;
 }
 
-extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int32_t T,
-                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, const int32_t* row_ptr,
-                                const int32_t* col, const uint8_t* kind, int64_t nnz, int32_t block,
-                                float sm_scale, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  if (T < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || !(sm_scale > 0.f) || nnz < 0)
-    return fa_set_err(nullptr, KV_ERR_INVALID, "bad prefill shape, scale or nnz");
+namespace {
+int check_shape(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int64_t nnz, int32_t block) {
+  if (T < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || nnz < 0)
+    return fa_set_err(nullptr, KV_ERR_INVALID, "bad prefill shape or nnz");
   if (head_dim != kD || block != kB)
     return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill needs head_dim 128 and block 64");
+  return KV_OK;
+}
+}  // namespace
+
+extern "C" int dag_attn_prepare(const void* k, const void* v, int32_t T, int32_t n_q_heads, int32_t n_kv_heads,
+                                int32_t head_dim, const int32_t* row_ptr, const int32_t* col, const uint8_t* kind,
+                                int64_t nnz, int32_t block, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (int st = check_shape(T, n_q_heads, n_kv_heads, head_dim, nnz, block)) return st;
   if (T == 0) return KV_OK;
-  if (!q || !k || !v || !out || !row_ptr || !workspace || (nnz > 0 && (!col || !kind)))
+  if (!k || !v || !row_ptr || !workspace || (nnz > 0 && (!col || !kind)))
     return fa_set_err(nullptr, KV_ERR_INVALID, "null pointer");
   const WsLayout w = ws_layout(T, n_kv_heads, nnz);
   if (ws_bytes < w.total) return fa_set_err(nullptr, KV_ERR_WORKSPACE, "prefill workspace too small");
   const int nb = (T + kB - 1) / kB;
   char* ws = static_cast<char*>(workspace);
+  relayout_kernel<<<dim3(nb, n_kv_heads), 256, 0, stream>>>(static_cast<const bf16_t*>(k),
+                                                           static_cast<const bf16_t*>(v), ws + w.kimg, ws + w.vimg,
+                                                           T, n_kv_heads, nb);
+  if (nnz > 0) {
+    const int64_t blocks = (nnz + 255) / 256;
+    pack_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(
+        col, kind, reinterpret_cast<int32_t*>(ws + w.ent), nnz, nb);
+  }
+  rank_kernel<<<(nb + 255) / 256, 256, 0, stream>>>(row_ptr, reinterpret_cast<int32_t*>(ws + w.order), nb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill prepare: ") + hipGetErrorString(e));
+  return KV_OK;
+}
+
+extern "C" int dag_attn_run(const void* q, void* out, float* lse, int32_t T, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, const int32_t* row_ptr, int64_t nnz, int32_t block, float sm_scale,
+                            const void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (int st = check_shape(T, n_q_heads, n_kv_heads, head_dim, nnz, block)) return st;
+  if (!(sm_scale > 0.f)) return fa_set_err(nullptr, KV_ERR_INVALID, "softmax scale must be positive");
+  if (T == 0) return KV_OK;
+  if (!q || !out || !row_ptr || !workspace) return fa_set_err(nullptr, KV_ERR_INVALID, "null pointer");
+  const WsLayout w = ws_layout(T, n_kv_heads, nnz);
+  if (ws_bytes < w.total) return fa_set_err(nullptr, KV_ERR_WORKSPACE, "prefill workspace too small");
+  const char* ws = static_cast<const char*>(workspace);
   Params p;
   p.q = static_cast<const bf16_t*>(q);
   p.kimg = ws + w.kimg;
@@ -358,21 +402,27 @@ extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, voi
   p.hkv = n_kv_heads;
   p.G = n_q_heads / n_kv_heads;
   p.n_hg = (p.G + 3) / 4;
-  p.nb = nb;
+  p.nb = (T + kB - 1) / kB;
   p.sm_scale = sm_scale;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  int32_t* ent = reinterpret_cast<int32_t*>(ws + w.ent);
-  int32_t* order = reinterpret_cast<int32_t*>(ws + w.order);
-  relayout_kernel<<<dim3(nb, n_kv_heads), 256, 0, stream>>>(static_cast<const bf16_t*>(k),
-                                                           static_cast<const bf16_t*>(v), ws + w.kimg, ws + w.vimg,
-                                                           T, n_kv_heads, nb);
-  if (nnz > 0) {
-    const int64_t blocks = (nnz + 255) / 256;
-    pack_kernel<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>(col, kind, ent, nnz, nb);
-  }
-  rank_kernel<<<(nb + 255) / 256, 256, 0, stream>>>(row_ptr, order, nb);
-  prefill_kernel<<<(size_t)nb * n_kv_heads * p.n_hg, kThreads, 0, stream>>>(p, row_ptr, ent, order);
+  prefill_kernel<<<(size_t)p.nb * n_kv_heads * p.n_hg, kThreads, 0, stream>>>(
+      p, row_ptr, reinterpret_cast<const int32_t*>(ws + w.ent), reinterpret_cast<const int32_t*>(ws + w.order));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill: ") + hipGetErrorString(e));
   return KV_OK;
+}
+
+extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, void* out, float* lse, int32_t T,
+                                int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, const int32_t* row_ptr,
+                                const int32_t* col, const uint8_t* kind, int64_t nnz, int32_t block,
+                                float sm_scale, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (int st = check_shape(T, n_q_heads, n_kv_heads, head_dim, nnz, block)) return st;
+  if (!(sm_scale > 0.f)) return fa_set_err(nullptr, KV_ERR_INVALID, "softmax scale must be positive");
+  if (T == 0) return KV_OK;
+  if (!q || !out) return fa_set_err(nullptr, KV_ERR_INVALID, "null pointer");
+  if (int st = dag_attn_prepare(k, v, T, n_q_heads, n_kv_heads, head_dim, row_ptr, col, kind, nnz, block, workspace,
+                                ws_bytes, stream))
+    return st;
+  return dag_attn_run(q, out, lse, T, n_q_heads, n_kv_heads, head_dim, row_ptr, nnz, block, sm_scale, workspace,
+                      ws_bytes, stream);
 }

@@ -251,6 +251,22 @@ int dag_attn_prefill(const void* q, const void* k, const void* v, void* out, flo
                      int64_t nnz, int32_t block, float sm_scale, void* workspace,
                      size_t ws_bytes, hipStream_t stream);
 
+/* dag_attn_prefill in two steps, for callers that reuse K / V and the mask across
+ * several query sets, or time the attention kernel alone:
+ *   dag_attn_prepare: copies K / V into the workspace's operand-order images and packs
+ *     the column list and the row order (reads k, v, row_ptr, col, kind);
+ *   dag_attn_run: the attention itself from a workspace prepared for the same T,
+ *     heads, row_ptr, nnz and block (reads q, row_ptr and the workspace).
+ * Same arguments, errors and workspace size as dag_attn_prefill. */
+int dag_attn_prepare(const void* k, const void* v, int32_t T, int32_t n_q_heads,
+                     int32_t n_kv_heads, int32_t head_dim, const int32_t* row_ptr,
+                     const int32_t* col, const uint8_t* kind, int64_t nnz, int32_t block,
+                     void* workspace, size_t ws_bytes, hipStream_t stream);
+int dag_attn_run(const void* q, void* out, float* lse, int32_t T, int32_t n_q_heads,
+                 int32_t n_kv_heads, int32_t head_dim, const int32_t* row_ptr, int64_t nnz,
+                 int32_t block, float sm_scale, const void* workspace, size_t ws_bytes,
+                 hipStream_t stream);
+
 /* ---- errors ---- */
 const char* kv_status_str(int status);
 const char* kv_last_error(kv_pool_t* pool); /* pool = NULL: last error of pool-less calls */

@@ -100,3 +100,30 @@ def test_packed_dag_full_size():
     rows = sorted(rows)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     _check(pi, o, lse, rows, "packed DAG prefill, full size")
+
+
+def test_prepare_run_equals_prefill():
+    # the two-step form gives the same bits as the one-call form, and a prepared
+    # workspace serves a second query set
+    import torch
+    import fork_attention_decode_amd as fa
+    pi = W.prefill_inputs(prefix=192, branches=3, branch_len=[128, 256, 100], n_edges=3, edge_len=64, hq=8, hkv=2,
+                          seed=34)
+    print("[case] dag_attn_prepare + dag_attn_run == dag_attn_prefill", flush=True)
+    mask = fa.DagMask(pi.segments, pi.edges, pi.T, pi.block)
+    q, k, v = (to_torch(x, "bf16") for x in (pi.q, pi.k, pi.v))
+    o1, l1 = fa.prefill(q, k, v, mask, pi.sm_scale)
+    ws = torch.empty(fa.dag_attn_workspace_size(pi.T, 8, 2, 64, mask.nnz), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    fa.dag_attn_prepare(k.data_ptr(), v.data_ptr(), pi.T, 8, 2, 128, mask.row_ptr.data_ptr(), mask.col.data_ptr(),
+                        mask.kind.data_ptr(), mask.nnz, 64, ws.data_ptr(), ws.numel(), st)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    q2 = torch.flip(q, dims=[1]).contiguous()
+    o3, l3 = torch.empty_like(o1), torch.empty_like(l1)
+    for qq, oo, ll in ((q, o2, l2), (q2, o3, l3)):
+        fa.dag_attn_run(qq.data_ptr(), oo.data_ptr(), ll.data_ptr(), pi.T, 8, 2, 128, mask.row_ptr.data_ptr(), mask.nnz,
+                        64, pi.sm_scale, ws.data_ptr(), ws.numel(), st)
+    o4, l4 = fa.prefill(q2, k, v, mask, pi.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o3, o4) and torch.equal(l3, l4)
