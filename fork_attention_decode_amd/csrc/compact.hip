@@ -5,18 +5,20 @@
 // values unchanged.  AgentKV (rit.work): kept entries are compacted physically and the
 // freed pages go back to the allocator.
 //
-// One workgroup per destination page (all KV heads).  Phase 1 gathers the page's kept
+// One workgroup per batch of kCompactBatch consecutive destination pages (all KV heads),
+// taken in order.  Phase 1 gathers the page's kept
 // tokens from their old slots into an LDS image of the destination page, rotating each
 // key pair (i, i + d/2) by the token's offset with fp32 cos/sin rows computed on the
 // host in fp64 (an fp32 angle at 131K positions would be off by ~1e-2 rad); values are
 // copied bit-exactly.  Phase 2 writes the image back with contiguous 16-byte stores.
 //
 // In-place hazard: kept tokens only move to lower slots, so a page rewritten in place
-// may still be a source of lower destination pages.  Workgroups take list entries in
-// start order (an atomic ticket), publish "sources read" with a release store after
-// phase 1, and a page rewritten in place waits (acquire) for the lower entries that
-// read it.  A workgroup only ever waits for entries started before it, all of which
-// are resident and never wait for it, so every wait ends.
+// may still be a source of lower destination pages (at most two: a source page's kept
+// tokens are consecutive).  Workgroups take list entries in start order (an atomic
+// ticket), publish "sources read" with a release store after phase 1, and a page
+// rewritten in place waits (acquire) for exactly the lower entries that read it.  A
+// workgroup only ever waits for entries started before it, all of which are resident
+// and never wait for it, so every wait ends.
 #include <hip/hip_runtime.h>
 #include "plan.hpp"
 
@@ -38,97 +40,117 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
   const int hkv = p.n_kv_heads;
   T* lk = reinterpret_cast<T*>(lds_raw);
   T* lv = lk + (size_t)hkv * BLK;
-  __shared__ int s_k;
-  if (threadIdx.x == 0) s_k = (int)((unsigned)atomicAdd(p.ticket, 1) - (unsigned)p.ticket_base);
+  __shared__ int s_b;
+  __shared__ int s_loc[16], s_rot[16];
+  if (threadIdx.x == 0) s_b = (int)((unsigned)atomicAdd(p.ticket, 1) - (unsigned)p.ticket_base);
   __syncthreads();
-  const int k = s_k;
-  if (k < 0 || k >= p.n_pages) {  // ticket out of step with the host: count it, touch nothing
+  const int b = s_b;
+  if (b < 0 || b * kCompactBatch >= p.n_pages) {  // ticket out of step with the host: count it, touch nothing
     if (threadIdx.x == 0) atomicAdd(p.errors, 1);
     return;
   }
-  const CompactPage cp = p.pages[k];
   T* kp = reinterpret_cast<T*>(p.k_pages);
   T* vp = reinterpret_cast<T*>(p.v_pages);
   const size_t np = (size_t)p.pool_pages;  // head-major pool: block (page, h) at h * np + page
-  const size_t dst = (size_t)cp.dst_page * BLK;
-  const bool keep_rest = cp.first_slot > 0 || cp.n_slots < 16;
+  const int k_end = min((b + 1) * kCompactBatch, p.n_pages);
+  for (int k = b * kCompactBatch; k < k_end; ++k) {  // this batch's list entries, in order
+    const CompactPage cp = p.pages[k];
+    const size_t dst = (size_t)cp.dst_page * BLK;
+    const bool keep_rest = cp.first_slot > 0 || cp.n_slots < 16;
+    // the page's 16 source locations and rotation rows, once, so that every gather below
+    // issues its loads independently instead of behind a dependent index load
+    if (threadIdx.x < 16) {
+      const int t = threadIdx.x;
+      const bool mine = t >= cp.first_slot && t < cp.n_slots;
+      s_loc[t] = mine ? p.src_loc[cp.tok_base + t] : -1;
+      s_rot[t] = mine ? p.rot[cp.tok_base + t] : -1;
+    }
+    __syncthreads();
 
-  // ---- phase 1: gather K (with rotation) into the LDS image
-  const int n_ku = hkv * HALF * 64;
-  for (int u = threadIdx.x; u < n_ku; u += blockDim.x) {
-    const int t = u & 15, g = (u >> 4) & 3, fp = (u >> 6) % HALF, h = (u >> 6) / HALF;
-    const int s0 = ((fp * 4 + g) * 16 + t) * E, s1 = (((fp + HALF) * 4 + g) * 16 + t) * E;
-    vec_t a, b;
-    if (t >= cp.first_slot && t < cp.n_slots) {
-      const int loc = p.src_loc[cp.tok_base + t];
-      const size_t sb = ((size_t)h * np + (loc >> 4)) * BLK;
-      const int st = loc & 15;
-      a = *reinterpret_cast<const vec_t*>(kp + sb + ((fp * 4 + g) * 16 + st) * E);
-      b = *reinterpret_cast<const vec_t*>(kp + sb + (((fp + HALF) * 4 + g) * 16 + st) * E);
-      const int run = p.rot[cp.tok_base + t];
-      if (run >= 0) {
-        const float* cs = p.cos_sin + (size_t)run * D;  // [D/2][2]
+    // ---- phase 1: gather K (with rotation) into the LDS image
+    const int n_ku = hkv * HALF * 64;
+    for (int u = threadIdx.x; u < n_ku; u += blockDim.x) {
+      const int t = u & 15, g = (u >> 4) & 3, fp = (u >> 6) % HALF, h = (u >> 6) / HALF;
+      const int s0 = ((fp * 4 + g) * 16 + t) * E, s1 = (((fp + HALF) * 4 + g) * 16 + t) * E;
+      vec_t a, bb;
+      const int loc = s_loc[t];
+      if (loc >= 0) {
+        const size_t sb = ((size_t)h * np + (loc >> 4)) * BLK;
+        const int st = loc & 15;
+        a = *reinterpret_cast<const vec_t*>(kp + sb + ((fp * 4 + g) * 16 + st) * E);
+        bb = *reinterpret_cast<const vec_t*>(kp + sb + (((fp + HALF) * 4 + g) * 16 + st) * E);
+        const int run = s_rot[t];
+        if (run >= 0) {
+          const float* cs = p.cos_sin + (size_t)run * D;  // [D/2][2]
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int d = sizeof(T) == 2 ? 32 * fp + 8 * g + e : 16 * fp + 4 * e + g;
-          const float c = cs[2 * d], s = cs[2 * d + 1];
-          const float x = to_f(a[e]), y = to_f(b[e]);
-          a[e] = from_f<T>(x * c - y * s);
-          b[e] = from_f<T>(y * c + x * s);
+          for (int e = 0; e < E; ++e) {
+            const int d = sizeof(T) == 2 ? 32 * fp + 8 * g + e : 16 * fp + 4 * e + g;
+            const float c = cs[2 * d], sn = cs[2 * d + 1];
+            const float x = to_f(a[e]), y = to_f(bb[e]);
+            a[e] = from_f<T>(x * c - y * sn);
+            bb[e] = from_f<T>(y * c + x * sn);
+          }
+        }
+      } else if (keep_rest) {
+        a = *reinterpret_cast<const vec_t*>(kp + dst + (size_t)h * np * BLK + s0);
+        bb = *reinterpret_cast<const vec_t*>(kp + dst + (size_t)h * np * BLK + s1);
+      } else {
+        continue;
+      }
+      *reinterpret_cast<vec_t*>(lk + h * BLK + s0) = a;
+      *reinterpret_cast<vec_t*>(lk + h * BLK + s1) = bb;
+    }
+    // ---- phase 1: gather V^T rows (bit-exact copies)
+    for (int r = threadIdx.x; r < hkv * D; r += blockDim.x) {
+      const int h = r / D, d = r % D;
+      vec_t row[16 / E];
+      if (keep_rest) {
+#pragma unroll
+        for (int i = 0; i < 16 / E; ++i)
+          row[i] = *reinterpret_cast<const vec_t*>(vp + dst + (size_t)h * np * BLK + d * 16 + i * E);
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int loc = s_loc[t];
+        if (loc >= 0) row[t / E][t % E] = vp[((size_t)h * np + (loc >> 4)) * BLK + d * 16 + (loc & 15)];
+      }
+#pragma unroll
+      for (int i = 0; i < 16 / E; ++i) *reinterpret_cast<vec_t*>(lv + h * BLK + d * 16 + i * E) = row[i];
+    }
+    __syncthreads();
+
+    // ---- publish "sources read", then wait for the lower entries that read this page
+    // (earlier entries of this batch published theirs already).  The hazard is
+    // write-after-read only: a reader publishes after its loads have returned (their
+    // values are in LDS behind the barrier above) and a writer's stores issue only after
+    // its poll has seen the flag, so relaxed device-scope atomics order it; acquire /
+    // release would write back or invalidate this die's L2 on every poll.
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(&p.done[k], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = cp.wait_lo; i < cp.wait_hi && i < k; ++i) {
+        int spins = 0;
+        while (__hip_atomic_load(&p.done[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
+          __builtin_amdgcn_s_sleep(4);
+          if (++spins > (1 << 26)) {  // ~seconds: never expected; counted, never hangs
+            atomicAdd(p.errors, 1);
+            break;
+          }
         }
       }
-    } else if (keep_rest) {
-      a = *reinterpret_cast<const vec_t*>(kp + dst + (size_t)h * np * BLK + s0);
-      b = *reinterpret_cast<const vec_t*>(kp + dst + (size_t)h * np * BLK + s1);
-    } else {
-      continue;
     }
-    *reinterpret_cast<vec_t*>(lk + h * BLK + s0) = a;
-    *reinterpret_cast<vec_t*>(lk + h * BLK + s1) = b;
-  }
-  // ---- phase 1: gather V^T rows (bit-exact copies)
-  for (int r = threadIdx.x; r < hkv * D; r += blockDim.x) {
-    const int h = r / D, d = r % D;
-    vec_t row[16 / E];
-    if (keep_rest) {
-#pragma unroll
-      for (int i = 0; i < 16 / E; ++i)
-        row[i] = *reinterpret_cast<const vec_t*>(vp + dst + (size_t)h * np * BLK + d * 16 + i * E);
-    }
-    for (int t = cp.first_slot; t < cp.n_slots; ++t) {
-      const int loc = p.src_loc[cp.tok_base + t];
-      row[t / E][t % E] = vp[((size_t)h * np + (loc >> 4)) * BLK + d * 16 + (loc & 15)];
-    }
-#pragma unroll
-    for (int i = 0; i < 16 / E; ++i) *reinterpret_cast<vec_t*>(lv + h * BLK + d * 16 + i * E) = row[i];
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- publish "sources read", then wait for the lower entries that read this page
-  if (threadIdx.x == 0) {
-    __hip_atomic_store(&p.done[k], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    for (int i = cp.wait_lo; i < k; ++i) {
-      int spins = 0;
-      while (__hip_atomic_load(&p.done[i], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
-        __builtin_amdgcn_s_sleep(4);
-        if (++spins > (1 << 26)) {  // ~seconds: never expected; counted, never hangs
-          atomicAdd(p.errors, 1);
-          break;
-        }
-      }
+    // ---- phase 2: write the image back, one contiguous block per head
+    constexpr int VPB = BLK / E;  // 16-byte vectors per block
+    const int n_vec = hkv * VPB;
+    const vec_t* ik = reinterpret_cast<const vec_t*>(lk);
+    const vec_t* iv = reinterpret_cast<const vec_t*>(lv);
+    for (int i = threadIdx.x; i < n_vec; i += blockDim.x) {
+      const size_t at = ((size_t)(i / VPB) * np + cp.dst_page) * BLK + (size_t)(i % VPB) * E;
+      *reinterpret_cast<vec_t*>(kp + at) = ik[i];
+      *reinterpret_cast<vec_t*>(vp + at) = iv[i];
     }
-  }
-  __syncthreads();
-
-  // ---- phase 2: write the image back, one contiguous block per head
-  constexpr int VPB = BLK / E;  // 16-byte vectors per block
-  const int n_vec = hkv * VPB;
-  const vec_t* ik = reinterpret_cast<const vec_t*>(lk);
-  const vec_t* iv = reinterpret_cast<const vec_t*>(lv);
-  for (int i = threadIdx.x; i < n_vec; i += blockDim.x) {
-    const size_t at = ((size_t)(i / VPB) * np + cp.dst_page) * BLK + (size_t)(i % VPB) * E;
-    *reinterpret_cast<vec_t*>(kp + at) = ik[i];
-    *reinterpret_cast<vec_t*>(vp + at) = iv[i];
+    __syncthreads();  // the image is rebuilt for the next entry
   }
 }
 
@@ -143,7 +165,7 @@ static hipError_t compact_t(const CompactParams& p, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)compact_kernel<T, D>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  compact_kernel<T, D><<<p.n_pages, 256, lds, s>>>(p);
+  compact_kernel<T, D><<<(p.n_pages + kCompactBatch - 1) / kCompactBatch, 256, lds, s>>>(p);
   return hipGetLastError();
 }
 

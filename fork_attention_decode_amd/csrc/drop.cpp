@@ -81,7 +81,7 @@ int kv_drop(kv_pool_t* P, kv_seq_t seq, const int64_t* begin, const int64_t* len
     std::vector<CompactPage> pages((size_t)n_list);
     std::vector<int32_t> src_loc((size_t)(r - tok0)), rot((size_t)(r - tok0), -1);
     std::map<int64_t, int32_t> rot_of;
-    std::vector<int64_t> min_reader((size_t)S->pages.size(), -1);
+    std::vector<int64_t> min_reader((size_t)S->pages.size(), -1), max_reader((size_t)S->pages.size(), -1);
     size_t ci = 0;
     for (int64_t L = first; L < n_new; ++L) {
       const bool is_cow = ci < cow.size() && cow[ci] == L;
@@ -90,15 +90,16 @@ int kv_drop(kv_pool_t* P, kv_seq_t seq, const int64_t* begin, const int64_t* len
       cp.first_slot = (!is_cow && L == first) ? (int32_t)(c % PS) : 0;
       cp.n_slots = (int32_t)std::min<int64_t>(PS, r - L * PS);
       cp.tok_base = (int32_t)(L * PS - tok0);
-      cp.wait_lo = (int32_t)(L - first);
-      cp.pad[0] = is_cow ? 1 : 0;  // host bookkeeping only
-      cp.pad[1] = cp.pad[2] = 0;
+      cp.wait_lo = cp.wait_hi = (int32_t)(L - first);  // set below for pages rewritten in place
+      cp.pad[0] = is_cow ? 1 : 0;                        // host bookkeeping only
+      cp.pad[1] = 0;
       if (is_cow) ++ci;
       for (int64_t j = L * PS + cp.first_slot; j < L * PS + cp.n_slots; ++j) {
         const int64_t src = kept[j];
         const int64_t Lo = src / PS;
         src_loc[(size_t)(j - tok0)] = S->pages[Lo] * 16 + (int32_t)(src % PS);
         if (min_reader[Lo] < 0) min_reader[Lo] = L;
+        max_reader[Lo] = L;
         const int64_t delta = newpos[j] - oldpos[src];
         if (repos && delta != 0) {
           auto it = rot_of.find(delta);
@@ -112,7 +113,10 @@ int kv_drop(kv_pool_t* P, kv_seq_t seq, const int64_t* begin, const int64_t* len
     }
     for (int64_t L = first; L < n_new; ++L) {
       CompactPage& cp = pages[(size_t)(L - first)];
-      if (!cp.pad[0] && min_reader[L] >= 0) cp.wait_lo = (int32_t)(min_reader[L] - first);
+      if (!cp.pad[0] && min_reader[L] >= 0) {  // in place: wait for the lower entries that read it
+        cp.wait_lo = (int32_t)(min_reader[L] - first);
+        cp.wait_hi = (int32_t)(std::min<int64_t>(max_reader[L], L - 1) - first + 1);
+      }
       cp.pad[0] = 0;
     }
     std::vector<float> cs((size_t)rot_of.size() * D, 0.f);
@@ -156,7 +160,7 @@ int kv_drop(kv_pool_t* P, kv_seq_t seq, const int64_t* begin, const int64_t* len
       cp.pool_pages = P->cfg.n_pages;
       e = launch_compact(P->cfg.dtype, D, cp, s);
       if (e == hipSuccess) {
-        P->ticket = (int32_t)((uint32_t)P->ticket + (uint32_t)n_list);
+        P->ticket = (int32_t)((uint32_t)P->ticket + (uint32_t)((n_list + kCompactBatch - 1) / kCompactBatch));
         P->epoch += 1;
       }
     }

@@ -72,17 +72,24 @@ struct MergeParams {
 
 // Drop / repos compaction: one record per destination page to (re)write.  Slots
 // [first_slot, n_slots) of dst_page receive the kept tokens tok_base + slot; when the
-// page is rewritten in place its old tokens may be sources of lower destination pages,
-// so the page is written only after list entries [wait_lo, self) have read their
-// sources (wait_lo == self: nothing to wait for).
+// page is rewritten in place its old tokens may be sources of lower destination pages
+// (kept tokens only move down), so the page is written only after the list entries
+// [wait_lo, wait_hi) that read it have read their sources (an empty range: nothing to
+// wait for).  A source page's kept tokens are consecutive in the kept order, so at most
+// two destination pages read it.
 struct CompactPage {
   int32_t dst_page;
   int32_t first_slot;
   int32_t n_slots;
   int32_t tok_base;
   int32_t wait_lo;
-  int32_t pad[3];
+  int32_t wait_hi;
+  int32_t pad[2];
 };
+
+// Destination pages per compaction workgroup (one start-order ticket per batch: the
+// tickets are device-wide atomics on one address, which serialise across the dies).
+constexpr int kCompactBatch = 1;
 
 struct CompactParams {
   void* k_pages;

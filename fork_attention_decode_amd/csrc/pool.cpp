@@ -105,26 +105,30 @@ static std::vector<PosRun> pos_slice(const std::vector<PosRun>& v, int64_t b, in
 static void pos_truncate(std::vector<PosRun>& v, int64_t n) { v = pos_slice(v, 0, n); }
 static int64_t pos_last(const std::vector<PosRun>& v) { return v.back().p0 + v.back().len - 1; }
 
-// Upload a host blob to device memory on `s` through the pinned staging buffer.
+// Upload a host blob to device memory on `s` through the next slot of the pinned staging
+// ring (waiting only if that slot's previous copy has not run yet).
 hipError_t fa_upload(kv_pool* P, void* dst, const void* src, size_t bytes, hipStream_t s) {
   if (bytes == 0) return hipSuccess;
+  kv_pool::StageSlot& slot = P->stage[P->stage_next];
   hipError_t e;
-  if (P->stage_pending) {
-    if ((e = hipEventSynchronize(P->stage_ev)) != hipSuccess) return e;
-    P->stage_pending = false;
+  if (!slot.ev && (e = hipEventCreateWithFlags(&slot.ev, hipEventDisableTiming)) != hipSuccess) return e;
+  if (slot.pending) {
+    if ((e = hipEventSynchronize(slot.ev)) != hipSuccess) return e;
+    slot.pending = false;
   }
-  if (bytes > P->stage_bytes) {
-    if (P->stage) (void)hipHostFree(P->stage);
-    P->stage = nullptr;
-    P->stage_bytes = 0;
-    size_t sz = std::max(bytes, (size_t)1 << 20);
-    if ((e = hipHostMalloc(&P->stage, sz, hipHostMallocDefault)) != hipSuccess) return e;
-    P->stage_bytes = sz;
+  if (bytes > slot.bytes) {
+    if (slot.ptr) (void)hipHostFree(slot.ptr);
+    slot.ptr = nullptr;
+    slot.bytes = 0;
+    const size_t sz = std::max(bytes, (size_t)1 << 20);
+    if ((e = hipHostMalloc(&slot.ptr, sz, hipHostMallocDefault)) != hipSuccess) return e;
+    slot.bytes = sz;
   }
-  std::memcpy(P->stage, src, bytes);
-  if ((e = hipMemcpyAsync(dst, P->stage, bytes, hipMemcpyHostToDevice, s)) != hipSuccess) return e;
-  if ((e = hipEventRecord(P->stage_ev, s)) != hipSuccess) return e;
-  P->stage_pending = true;
+  std::memcpy(slot.ptr, src, bytes);
+  if ((e = hipMemcpyAsync(dst, slot.ptr, bytes, hipMemcpyHostToDevice, s)) != hipSuccess) return e;
+  if ((e = hipEventRecord(slot.ev, s)) != hipSuccess) return e;
+  slot.pending = true;
+  P->stage_next = (P->stage_next + 1) % kv_pool::kStageSlots;
   return hipSuccess;
 }
 
@@ -217,10 +221,6 @@ int kv_pool_create(const kv_pool_config* c, void* k, void* v, void* ws, size_t w
       e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     }
     if (e == hipSuccess) {
-      what = "hipEventCreateWithFlags";
-      e = hipEventCreateWithFlags(&P->stage_ev, hipEventDisableTiming);
-    }
-    if (e == hipSuccess) {
       what = "hipMemset";
       e = hipMemset(ws, 0, fa_ws_plan_offset(c));
     }
@@ -236,9 +236,11 @@ int kv_pool_create(const kv_pool_config* c, void* k, void* v, void* ws, size_t w
 
 int kv_pool_destroy(kv_pool_t* P) {
   if (!P) FAIL(nullptr, KV_ERR_INVALID, "null pool");
-  if (P->stage_pending) (void)hipEventSynchronize(P->stage_ev);
-  if (P->stage) (void)hipHostFree(P->stage);
-  if (P->stage_ev) (void)hipEventDestroy(P->stage_ev);
+  for (auto& slot : P->stage) {
+    if (slot.pending) (void)hipEventSynchronize(slot.ev);
+    if (slot.ptr) (void)hipHostFree(slot.ptr);
+    if (slot.ev) (void)hipEventDestroy(slot.ev);
+  }
   delete P;
   return KV_OK;
 }

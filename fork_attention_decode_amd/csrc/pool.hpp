@@ -83,11 +83,17 @@ struct kv_pool {
   uint64_t version = 1;
   std::string err;
   int32_t n_cu = 256;
-  // pinned staging buffer for plan uploads
-  void* stage = nullptr;
-  size_t stage_bytes = 0;
-  hipEvent_t stage_ev = nullptr;
-  bool stage_pending = false;
+  // pinned staging ring for plan uploads: a slot is reused once the copy that read it
+  // has run, so the host can plan several operations ahead of the device
+  struct StageSlot {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+  };
+  static constexpr int kStageSlots = 8;
+  StageSlot stage[kStageSlots];
+  int stage_next = 0;
   // drop-kernel ordering state (see CompactParams)
   int32_t ticket = 0;
   int32_t epoch = 0;
