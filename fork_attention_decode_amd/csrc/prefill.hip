@@ -37,6 +37,7 @@ namespace {
 typedef __bf16 bf16_t;
 typedef bf16_t bf16x8 __attribute__((__vector_size__(8 * sizeof(bf16_t))));
 typedef bf16_t bf16x4 __attribute__((__vector_size__(4 * sizeof(bf16_t))));
+typedef bf16_t bf16x2 __attribute__((__vector_size__(2 * sizeof(bf16_t))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -44,7 +45,7 @@ constexpr int kB = 64;               // block edge (tokens)
 constexpr int kD = 128;              // head dim
 constexpr int kImg = kB * kD * 2;    // bytes of one K (or V) block image
 constexpr int kStage = 2 * kImg;     // K image + V image
-constexpr int kStages = 3;           // LDS ring depth
+constexpr int kStages = 4;           // LDS ring depth: block j - 1 (lagging waves), j, j + 1, j + 2
 constexpr int kWaves = 8;            // waves per workgroup (two per SIMD)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLoadsPerWave = kStage / kWaves / 1024;  // 1 KiB wave loads per stage per wave
@@ -211,19 +212,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
   const float c2 = p.scale_log2;
   const bool ragged = (p.T & (kB - 1)) != 0;
 
-  for (int j = 0; j < n; ++j) {
-    wait_vmcnt<(kStages - 2) * kLoadsPerWave>();  // this wave's part of block j landed
-    asm volatile("s_barrier" ::: "memory");       // ... every wave's; slot (j - 1) % 3 is free
-    issue(j + kStages - 1);
+  bf16x8 pk[2][2];  // P of the block being multiplied: [kt][half of the 32 keys]
+
+  // S^T for one block and its online softmax (leaves P in pk).  All 16 K fragments are
+  // requested before the first matrix instruction (the scheduling barriers keep the
+  // compiler from sinking each read next to its use, which would expose every LDS
+  // latency in turn).
+  auto scores = [&](int j) {
     const int e = ent_of(j);
     const int c = e & ~kDiagBit;
     const char* kslot = ring + (j % kStages) * kStage;
-    const char* vslot = kslot + kImg;
-
-    // S^T for the 64 keys of the block: two independent accumulation chains (kt).  All
-    // 16 K fragments are requested before the first matrix instruction and the V
-    // fragments under it (the scheduling barriers keep the compiler from sinking each
-    // read next to its use, which would expose every LDS latency in turn).
     bf16x8 kf[2][8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
@@ -231,19 +229,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
       for (int kt = 0; kt < 2; ++kt)
         kf[kt][ks] = *reinterpret_cast<const bf16x8*>(kslot + ((kt * 8 + ks) * 64 + lane) * 16);
     __builtin_amdgcn_sched_barrier(0);
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    f32x16 s[2] = {f32x16{}, f32x16{}};  // two independent accumulation chains (kt)
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32(kf[kt][ks], qf[ks], s[kt]);
-    bf16x8 vf[2][2][4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          vf[kt][hf][dt] = *reinterpret_cast<const bf16x8*>(vslot + (((dt * 2 + kt) * 2 + hf) * 64 + lane) * 16);
     __builtin_amdgcn_sched_barrier(0);
 
     const bool diag = e < 0;
@@ -259,10 +249,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
         }
     }
 
-    // online softmax for this lane's query (its 64 keys are split with lane ^ 32)
-    float mx = fmaxf(s[0][0], s[1][0]);
+    // online softmax for this lane's query (its 64 keys are split with lane ^ 32); the
+    // maximum as 3-input steps (v_max3)
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+    for (int r = 1; r < 16; ++r) {
+      const float a = r == 1 ? s[1][1] : s[0][r];
+      mx = r == 1 ? fmaxf(mx, a) : fmaxf(fmaxf(mx, a), s[1][r]);
+    }
     mx = xhalf_max(mx);
     const float mn = fmaxf(m, mx);
     if (__builtin_amdgcn_ballot_w64((mn - m) * c2 > kTau)) {  // wave-uniform; false while both are -inf
@@ -273,28 +267,63 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
     const float mc = m == -INFINITY ? 0.f : m * c2;
-    bf16x8 pk[2][2];  // [kt][half of the 32 keys]
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) pk[kt][hf][q] = (bf16_t)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][8 * hf + q], c2, -mc));
+    // row sum of the bf16 probabilities (what P V multiplies), two per dot2 instruction
+    const bf16x2 one = {(bf16_t)1.f, (bf16_t)1.f};
     float ls = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][8 * hf + q], c2, -mc));
-          ls += pe;
-          pk[kt][hf][q] = (bf16_t)pe;
+        for (int q = 0; q < 8; q += 2) {
+          const bf16x2 pair = {pk[kt][hf][q], pk[kt][hf][q + 1]};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls, false);
         }
     l += ls;
-
-    // O^T += V^T P^T
+  };
+  // O^T += V^T P^T with block j's V (fragments requested together)
+  auto values = [&](int j) {
+    const char* vslot = ring + (j % kStages) * kStage + kImg;
+    bf16x8 vf[2][2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          vf[kt][hf][dt] = *reinterpret_cast<const bf16x8*>(vslot + (((dt * 2 + kt) * 2 + hf) * 64 + lane) * 16);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vf[kt][hf][dt], pk[kt][hf], o[dt]);
+  };
+
+  // The two waves that share a SIMD (w and w + 4) run half a block apart: wave w does
+  // S, softmax, PV of block j; wave w + 4 does PV of block j - 1, then S, softmax of
+  // block j.  So one wave's softmax runs while the other issues matrix instructions.
+  const bool lag = wave >= kWaves / 2;
+  for (int j = 0; j < n; ++j) {
+    wait_vmcnt<kLoadsPerWave>();             // this wave's part of block j landed (j + 1 in flight)
+    asm volatile("s_barrier" ::: "memory");  // ... every wave's; block j - 2 is consumed by all
+    issue(j + 2);
+    if (lag) {
+      if (j > 0) values(j - 1);
+      scores(j);
+    } else {
+      scores(j);
+      values(j);
+    }
   }
+  if (lag && n > 0) values(n - 1);
   wait_vmcnt<0>();  // no load may land in LDS after the workgroup ends
   if (!active) return;
 
