@@ -45,6 +45,8 @@ int kv_drop(kv_pool_t* P, kv_seq_t seq, const int64_t* begin, const int64_t* len
   const bool repos = flags & KV_DROP_REPOS;
   if (repos && P->device && P->cfg.rope_style != KV_ROPE_NEOX)
     FAIL(P, KV_ERR_UNSUPPORTED, "repos needs a rotary pool");
+  if (P->device && !compact_supported(P->cfg.dtype, P->cfg.head_dim, P->cfg.n_kv_heads))
+    FAIL(P, KV_ERR_UNSUPPORTED, "drop supports up to 16 KV heads (bf16, d = 128) on device pools");
   const int64_t N = S->n;
   const int32_t PS = P->cfg.page_size;
   std::vector<char> gone((size_t)N, 0);
