@@ -11,16 +11,21 @@
 //     16 KiB image in matrix-core operand order (zero past T), so each operand read in
 //     the main kernel is one contiguous 1 KiB wave read from LDS (no bank conflicts)
 //     and each block moves into LDS as two contiguous 16 KiB copies;
-//   * one workgroup per (64-token query block, KV head, group of 4 query heads): the
-//     4 waves take the 4 query heads (GQA packing), so every K / V block staged in LDS
-//     feeds 256 query rows;
+//   * one workgroup per (64-token query block, KV head, group of 4 query heads): 8
+//     waves, two per query head with 32 queries each (GQA packing), so every K / V
+//     block staged in LDS feeds 256 query rows;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys = M, queries = N, d = K): each lane
 //     holds one query column, so row max / sum stay in the lane plus one permlane32
 //     swap; its accumulator layout is the B operand of O^T = V^T P^T once the key
 //     order of the V image matches it (done in the relayout), so P needs no shuffles;
 //   * online softmax in fp32 in the exp2 domain with a lazy, wave-uniform rescale;
-//   * K / V blocks stream through a 3-stage LDS ring with direct global->LDS loads
-//     (each wave copies a quarter), one workgroup barrier per block;
+//   * K / V blocks stream through a 4-stage LDS ring with buffer loads straight into
+//     LDS (each wave copies an eighth), one workgroup barrier per block;
+//   * on MI355X the kernel runs at the chip's power limit (the shader clock settles
+//     near 1.9 GHz), so its time follows energy: LDS bytes and vector instructions per
+//     FLOP count for more than the issue schedule.  32 query rows per wave with two
+//     waves per SIMD is the register budget's best point; 64 rows per wave halves LDS
+//     reads but leaves one wave per SIMD, which cannot hide its own softmax latency;
 //   * workgroups are ordered by descending row cost (a rank pass over row_ptr) so the
 //     longest rows start first, and consecutive workgroups take consecutive KV heads,
 //     so with 8 KV heads each die (and its L2) serves one head.
@@ -45,7 +50,7 @@ constexpr int kB = 64;               // block edge (tokens)
 constexpr int kD = 128;              // head dim
 constexpr int kImg = kB * kD * 2;    // bytes of one K (or V) block image
 constexpr int kStage = 2 * kImg;     // K image + V image
-constexpr int kStages = 4;           // LDS ring depth: block j - 1 (lagging waves), j, j + 1, j + 2
+constexpr int kStages = 4;           // LDS ring depth: blocks j (V), j + 1 (K), j + 2 and j + 3 in flight
 constexpr int kWaves = 8;            // waves per workgroup (two per SIMD)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLoadsPerWave = kStage / kWaves / 1024;  // 1 KiB wave loads per stage per wave
@@ -155,15 +160,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // wave-uniform reads become scalar loads (a vector load would have to wait for every
 // global->LDS copy in flight before it).
 //
-// 8 waves, two per SIMD: wave w takes query head slot w / 2 and tokens
-// [q0 + 32 (w % 2), +32) of the block, so each SIMD interleaves two waves and one wave's
-// LDS latency and softmax overlap the other's matrix instructions.
+// 8 waves, two per SIMD (waves w and w + 4 share one): wave w takes query head slot
+// w / 2 and tokens [q0 + 32 (w % 2), +32) of the block.
 __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32_t* __restrict__ row_ptr,
                                                           const int32_t* __restrict__ ent,
                                                           const int32_t* __restrict__ order) {
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kStage];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in a scalar register
   const int b = blockIdx.x;
   const int h = b % p.hkv;
   const int rest = b / p.hkv;
@@ -177,18 +181,24 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
   const int n = row_ptr[row + 1] - j0;
   const int hi = lane >> 5, lo = lane & 31;
 
-  // this wave's eighth of every stage: waves 0-3 copy the K image, waves 4-7 the V image
+  // this wave's eighth of every stage: waves 0-3 copy the K image, waves 4-7 the V image.
+  // The copies are buffer loads into LDS over one descriptor per (image, head): the
+  // hardware drops any load past the head's image, and unlike the flat-encoded global
+  // form they leave the compiler's LDS wait counts exact (it has to assume a flat load
+  // may touch LDS out of order and would wait for every outstanding LDS read).
   const int my_off = wave * (kStage / kWaves);
-  const char* my_src = (my_off < kImg ? p.kimg + my_off : p.vimg + (my_off - kImg)) + (size_t)h * p.nb * kImg;
+  const int my_part = my_off < kImg ? my_off : my_off - kImg;
+  const __amdgpu_buffer_rsrc_t my_img = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((my_off < kImg ? p.kimg : p.vimg) + (size_t)h * p.nb * kImg), 0, p.nb * kImg, 0x00020000);
   auto ent_of = [&](int j) { return ent[j0 + (j < n ? j : n - 1)]; };
   auto col_of = [&](int j) { return ent_of(j) & ~kDiagBit; };
   auto issue = [&](int j) {  // past the end: reload the last block into a slot nobody reads
-    const char* src = my_src + (size_t)col_of(j) * kImg + lane * 16;
+    const int src = col_of(j) * kImg + my_part + lane * 16;
     char* dst = ring + (j % kStages) * kStage + my_off;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i)
-      __builtin_amdgcn_global_load_lds(src + i * 1024, (__attribute__((address_space(3))) void*)(dst + i * 1024),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(my_img, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                               src + i * 1024, 0, 0, 0);
   };
 
   // queries: B operand of S^T = K Q^T, lane holds Q[q0 + lo][16 ks + 8 hi + 0..7]
@@ -202,9 +212,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
       if (tq >= p.T) qf[ks] = bf16x8{};
     }
   }
-  if (n > 0) issue(0);
-  if (n > 0) issue(1);
-
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
@@ -212,34 +219,35 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
   const float c2 = p.scale_log2;
   const bool ragged = (p.T & (kB - 1)) != 0;
 
-  bf16x8 pk[2][2];  // P of the block being multiplied: [kt][half of the 32 keys]
-
-  // S^T for one block and its online softmax (leaves P in pk).  All 16 K fragments are
-  // requested before the first matrix instruction (the scheduling barriers keep the
-  // compiler from sinking each read next to its use, which would expose every LDS
-  // latency in turn).
-  auto scores = [&](int j) {
-    const int e = ent_of(j);
-    const int c = e & ~kDiagBit;
-    const char* kslot = ring + (j % kStages) * kStage;
+  // K fragment (kt, ks) of ring slot j: A operand, keys 32 kt + lane % 32, dims 16 ks + 8 (lane / 32) + 0..7
+  auto kfrag = [&](int j, int kt, int ks) {
+    return *reinterpret_cast<const bf16x8*>(ring + (j % kStages) * kStage + ((kt * 8 + ks) * 64 + lane) * 16);
+  };
+  // V fragment (kt, hf, dt) of ring slot j: A operand of O^T += V^T P^T
+  auto vfrag = [&](int j, int kt, int hf, int dt) {
+    return *reinterpret_cast<const bf16x8*>(ring + (j % kStages) * kStage + kImg +
+                                            (((dt * 2 + kt) * 2 + hf) * 64 + lane) * 16);
+  };
+  // S^T of block j into s, all at once (the prologue only)
+  auto scores = [&](int j, f32x16 (&s)[2]) {
     bf16x8 kf[2][8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        kf[kt][ks] = *reinterpret_cast<const bf16x8*>(kslot + ((kt * 8 + ks) * 64 + lane) * 16);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 s[2] = {f32x16{}, f32x16{}};  // two independent accumulation chains (kt)
+      for (int kt = 0; kt < 2; ++kt) kf[kt][ks] = kfrag(j, kt, ks);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32(kf[kt][ks], qf[ks], s[kt]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    const bool diag = e < 0;
-    if (diag || (ragged && c == p.nb - 1)) {  // diagonal block (key > query) and keys past T
-      const int kb = c * kB + 4 * hi;          // key of register r in tile kt: kb + 32 kt + 8 (r / 4) + r % 4
-      const int lim = diag ? q0 + lo : 0x7fffffff;
+  };
+  // diagonal block (key > query) and keys past T -> -inf; rare, so behind a branch
+  auto mask = [&](int e, f32x16 (&s)[2]) {
+    const int c = e & ~kDiagBit;
+    if (e < 0 || (ragged && c == p.nb - 1)) {
+      const int kb = c * kB + 4 * hi;  // key of register r in tile kt: kb + 32 kt + 8 (r / 4) + r % 4
+      const int lim = e < 0 ? q0 + lo : 0x7fffffff;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -248,18 +256,37 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
           s[kt][r] = (key > lim || key >= p.T) ? -INFINITY : s[kt][r];
         }
     }
-
-    // online softmax for this lane's query (its 64 keys are split with lane ^ 32); the
-    // maximum as 3-input steps (v_max3)
+  };
+  // new running maximum for a block: this lane's 32 keys in 3-input steps, then the
+  // other half-wave's 32
+  auto block_max = [&](const f32x16 (&s)[2]) {
     float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) {
       const float a = r == 1 ? s[1][1] : s[0][r];
       mx = r == 1 ? fmaxf(mx, a) : fmaxf(fmaxf(mx, a), s[1][r]);
     }
-    mx = xhalf_max(mx);
-    const float mn = fmaxf(m, mx);
-    if (__builtin_amdgcn_ballot_w64((mn - m) * c2 > kTau)) {  // wave-uniform; false while both are -inf
+    return fmaxf(m, xhalf_max(mx));
+  };
+
+  // Software pipeline inside each wave.  Step j: (1) S of block j + 1 on the matrix core
+  // while the vector unit turns S of block j into P = exp2(S c2 - m c2) (bf16) and its
+  // row sum; (2) O += P V of block j while it takes the maximum of block j + 1.  The code
+  // is cut into chunks fenced by scheduling barriers, each one or two matrix
+  // instructions plus the vector work that fits under them, with LDS reads issued
+  // three chunks ahead.  Ring: step j reads slots j (V) and j + 1 (K) and fills slot
+  // j + 3 (block j - 1's, read by every wave before the barrier).  Past the last block
+  // issue() reloads the last block, so the S computed for block n is harmless.
+  f32x16 sa[2], sb[2];
+  bf16x8 pk[2][2];
+  float mn = -INFINITY;
+  bool resc = false;
+  auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    const int e1 = ent_of(j + 1);
+    wait_vmcnt<kLoadsPerWave>();             // this wave's part of block j + 1 landed (j + 2 in flight)
+    asm volatile("s_barrier" ::: "memory");  // ... every wave's; slot j - 1 is consumed by all
+    issue(j + 3);
+    if (resc) {  // wave-uniform, rare: the new maximum outgrew the stale one by more than tau
       const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
       m = mn;
       l *= alpha;
@@ -267,63 +294,94 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
     const float mc = m == -INFINITY ? 0.f : m * c2;
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (1) chunk ks: S instructions (0, ks) and (1, ks); P for 4 of this lane's 32 keys
+    bf16x8 kf[2][8];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int ks = 0; ks < 3; ++ks)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) pk[kt][hf][q] = (bf16_t)__builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][8 * hf + q], c2, -mc));
-    // row sum of the bf16 probabilities (what P V multiplies), two per dot2 instruction
-    const bf16x2 one = {(bf16_t)1.f, (bf16_t)1.f};
+      for (int kt = 0; kt < 2; ++kt) kf[kt][ks] = kfrag(j + 1, kt, ks);
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
     float ls = 0.f;
+    const bf16x2 one = {(bf16_t)1.f, (bf16_t)1.f};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks + 3 < 8) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int q = 0; q < 8; q += 2) {
-          const bf16x2 pair = {pk[kt][hf][q], pk[kt][hf][q + 1]};
-          ls = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls, false);
-        }
+        for (int kt = 0; kt < 2; ++kt) kf[kt][ks + 3] = kfrag(j + 1, kt, ks + 3);
+      }
+      // P of chunk ks: registers 8 hf + q .. + 3 of S tile t (t = ks / 4, hf = ks / 2 % 2, q = 4 (ks % 2))
+      sn[0] = mfma32(kf[0][ks], qf[ks], sn[0]);
+      {
+        const int t = ks >> 2, hf = (ks >> 1) & 1, q = 4 * (ks & 1);
+        pk[t][hf][q + 0] = (bf16_t)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * hf + q + 0], c2, -mc));
+        pk[t][hf][q + 1] = (bf16_t)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * hf + q + 1], c2, -mc));
+      }
+      sn[1] = mfma32(kf[1][ks], qf[ks], sn[1]);
+      {
+        const int t = ks >> 2, hf = (ks >> 1) & 1, q = 4 * (ks & 1);
+        pk[t][hf][q + 2] = (bf16_t)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * hf + q + 2], c2, -mc));
+        pk[t][hf][q + 3] = (bf16_t)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * hf + q + 3], c2, -mc));
+        const bf16x2 p01 = {pk[t][hf][q + 0], pk[t][hf][q + 1]};
+        const bf16x2 p23 = {pk[t][hf][q + 2], pk[t][hf][q + 3]};
+        ls = __builtin_amdgcn_fdot2_f32_bf16(p01, one, ls, false);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(p23, one, ls, false);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     l += ls;
-  };
-  // O^T += V^T P^T with block j's V (fragments requested together)
-  auto values = [&](int j) {
-    const char* vslot = ring + (j % kStages) * kStage + kImg;
-    bf16x8 vf[2][2][4];
+    // P and the row sum stay here, ahead of the mask branch (the compiler would sink them
+    // next to their use otherwise, away from the S instructions they overlap)
+    asm volatile("" ::"v"(pk[0][0]), "v"(pk[0][1]), "v"(pk[1][0]), "v"(pk[1][1]), "v"(l));
+    mask(e1, sn);
+
+    // (2) chunk c = (kt, hf): four P V instructions (one per 32-dim tile) + part of the max
+    bf16x8 vf[4][4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          vf[kt][hf][dt] = *reinterpret_cast<const bf16x8*>(vslot + (((dt * 2 + kt) * 2 + hf) * 64 + lane) * 16);
+      for (int dt = 0; dt < 4; ++dt) vf[c][dt] = vfrag(j, c >> 1, c & 1, dt);
+    float mx = fmaxf(fmaxf(sn[0][0], sn[0][1]), sn[1][0]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int c = 0; c < 4; ++c) {
+      if (c + 2 < 4) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+        for (int dt = 0; dt < 4; ++dt) vf[c + 2][dt] = vfrag(j, (c + 2) >> 1, (c + 2) & 1, dt);
+      }
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt] = mfma32(vf[kt][hf][dt], pk[kt][hf], o[dt]);
+      for (int dt = 0; dt < 4; ++dt) {
+        o[dt] = mfma32(vf[c][dt], pk[c >> 1][c & 1], o[dt]);
+        // registers 4 c + dt of both tiles (register 0, 1 of tile 0 and 0 of tile 1 are in mx)
+        const int r = 4 * c + dt;
+        if (r == 1) mx = fmaxf(mx, sn[1][1]);
+        else if (r > 1) mx = fmaxf(fmaxf(mx, sn[0][r]), sn[1][r]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    mn = fmaxf(m, xhalf_max(mx));
+    resc = __builtin_amdgcn_ballot_w64((mn - m) * c2 > kTau) != 0;  // false while both are -inf
   };
 
-  // The two waves that share a SIMD (w and w + 4) run half a block apart: wave w does
-  // S, softmax, PV of block j; wave w + 4 does PV of block j - 1, then S, softmax of
-  // block j.  So one wave's softmax runs while the other issues matrix instructions.
-  const bool lag = wave >= kWaves / 2;
-  for (int j = 0; j < n; ++j) {
-    wait_vmcnt<kLoadsPerWave>();             // this wave's part of block j landed (j + 1 in flight)
-    asm volatile("s_barrier" ::: "memory");  // ... every wave's; block j - 2 is consumed by all
-    issue(j + 2);
-    if (lag) {
-      if (j > 0) values(j - 1);
-      scores(j);
-    } else {
-      scores(j);
-      values(j);
+  if (n > 0) {
+    issue(0);
+    issue(1);
+    issue(2);
+    wait_vmcnt<2 * kLoadsPerWave>();         // block 0 landed for this wave ...
+    asm volatile("s_barrier" ::: "memory");  // ... and for every wave
+    scores(0, sa);
+    mask(ent_of(0), sa);
+    mn = block_max(sa);
+    resc = __builtin_amdgcn_ballot_w64((mn - m) * c2 > kTau) != 0;
+    int j = 0;
+    for (; j + 1 < n; j += 2) {
+      step(j, sa, sb);
+      step(j + 1, sb, sa);
     }
+    if (j < n) step(j, sa, sb);
   }
-  if (lag && n > 0) values(n - 1);
   wait_vmcnt<0>();  // no load may land in LDS after the workgroup ends
   if (!active) return;
 
@@ -381,6 +439,8 @@ int check_shape(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_d
     return fa_set_err(nullptr, KV_ERR_INVALID, "bad prefill shape or nnz");
   if (head_dim != kD || block != kB)
     return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill needs head_dim 128 and block 64");
+  if ((int64_t)(T + kB - 1) / kB * kImg > INT32_MAX)  // one head's operand image is addressed with 32-bit offsets
+    return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill supports at most 8,388,608 tokens");
   return KV_OK;
 }
 }  // namespace
