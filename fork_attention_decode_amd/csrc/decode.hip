@@ -139,7 +139,7 @@ __device__ inline float row_sum4(float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-constexpr int kCachePolicyNT = 2;  // non-temporal cache policy bit of global_load_lds
+constexpr int kCachePolicyNT = 2;  // non-temporal cache policy bit of the ring loads
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units): p <= 256
 
 // Q fragments of this lane's query row (B operand of S^T = K Q^T); zero past n_rows.
@@ -273,12 +273,17 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, const int32_t
   auto issue = [&](int j) {
     const int jj = j < n ? j : n - 1;  // past the end: reload the last chunk into an unread slot
     const int page = jj < 64 ? __builtin_amdgcn_readlane(mp0, jj) : __builtin_amdgcn_readlane(mp1, jj - 64);
-    const char* src = my_base + (size_t)page * HALF + lane * 16;
+    // a buffer descriptor over this wave's share of the page: the hardware drops any
+    // load outside it, and unlike the flat-encoded global form, buffer loads leave the
+    // compiler's LDS wait counts exact (it has to assume a flat load may touch LDS out
+    // of order and would wait for every outstanding LDS read)
+    const __amdgpu_buffer_rsrc_t src =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(my_base + (size_t)page * HALF), 0, LPW * 1024, 0x00020000);
     char* dst = ring + (j % NB) * CB + my_off;
 #pragma unroll
     for (int i = 0; i < LPW; ++i)
-      __builtin_amdgcn_global_load_lds(src + i * 1024, (__attribute__((address_space(3))) void*)(dst + i * 1024),
-                                       16, 0, kCachePolicyNT);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                               lane * 16 + i * 1024, 0, 0, kCachePolicyNT);
   };
   auto lohi_of = [&](int j) {
     if (j >= n) return 0;  // empty slot range: every key masked

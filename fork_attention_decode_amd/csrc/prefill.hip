@@ -182,23 +182,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
   const int hi = lane >> 5, lo = lane & 31;
 
   // this wave's eighth of every stage: waves 0-3 copy the K image, waves 4-7 the V image.
-  // The copies are buffer loads into LDS over one descriptor per (image, head): the
-  // hardware drops any load past the head's image, and unlike the flat-encoded global
+  // The copies are buffer loads into LDS over a descriptor for this wave's part of the
+  // block: the hardware drops any load outside it, and unlike the flat-encoded global
   // form they leave the compiler's LDS wait counts exact (it has to assume a flat load
   // may touch LDS out of order and would wait for every outstanding LDS read).
   const int my_off = wave * (kStage / kWaves);
-  const int my_part = my_off < kImg ? my_off : my_off - kImg;
-  const __amdgpu_buffer_rsrc_t my_img = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((my_off < kImg ? p.kimg : p.vimg) + (size_t)h * p.nb * kImg), 0, p.nb * kImg, 0x00020000);
+  const char* my_img = (my_off < kImg ? p.kimg + my_off : p.vimg + (my_off - kImg)) + (size_t)h * p.nb * kImg;
   auto ent_of = [&](int j) { return ent[j0 + (j < n ? j : n - 1)]; };
   auto col_of = [&](int j) { return ent_of(j) & ~kDiagBit; };
   auto issue = [&](int j) {  // past the end: reload the last block into a slot nobody reads
-    const int src = col_of(j) * kImg + my_part + lane * 16;
+    const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(my_img + (size_t)col_of(j) * kImg), 0, kLoadsPerWave * 1024, 0x00020000);
     char* dst = ring + (j % kStages) * kStage + my_off;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(my_img, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
-                                               src + i * 1024, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                               lane * 16 + i * 1024, 0, 0, 0);
   };
 
   // queries: B operand of S^T = K Q^T, lane holds Q[q0 + lo][16 ks + 8 hi + 0..7]
@@ -439,8 +438,6 @@ int check_shape(int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_d
     return fa_set_err(nullptr, KV_ERR_INVALID, "bad prefill shape or nnz");
   if (head_dim != kD || block != kB)
     return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill needs head_dim 128 and block 64");
-  if ((int64_t)(T + kB - 1) / kB * kImg > INT32_MAX)  // one head's operand image is addressed with 32-bit offsets
-    return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "prefill supports at most 8,388,608 tokens");
   return KV_OK;
 }
 }  // namespace
