@@ -74,18 +74,59 @@ class DecodeBench:
         self.kernel_bytes = self.stats["unique_kv_bytes"] + q.numel() * es  # decode kernel: unique KV + Q
         self.step_bytes = self.kernel_bytes + q.numel() * es                # whole step: + O written
 
-    def step(self, i, ev=None):
+    def step(self, i, ev=None, stream=None, merge=True):
         p, ws = self.pools[i % len(self.pools)], self.wss[i % len(self.pools)]
+        s = stream or self.stream
         if ev:
             ev[0].record()
         self.fa.fork_attn_partials(p.handle, self.sc.queries, self.hq, self.q.data_ptr(), self.sc.sm_scale,
-                                   ws.data_ptr(), ws.numel(), self.stream)
+                                   ws.data_ptr(), ws.numel(), s)
         if ev:
             ev[1].record()
-        self.fa.fork_attn_merge(p.handle, self.sc.queries, self.hq, self.out.data_ptr(), self.lse.data_ptr(),
-                                ws.data_ptr(), ws.numel(), self.stream)
+        if merge:
+            self.fa.fork_attn_merge(p.handle, self.sc.queries, self.hq, self.out.data_ptr(), self.lse.data_ptr(),
+                                    ws.data_ptr(), ws.numel(), s)
         if ev:
             ev[2].record()
+
+    def capture(self, steps, merge=True):
+        """A HIP graph of `steps` decode steps (pools rotated as in the eager loop), or with
+        merge=False of `steps` back-to-back decode kernels.  The plans are cached by then, so
+        each call is a bare kernel launch and the graph replays exactly the eager work."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            s = torch.cuda.current_stream().cuda_stream
+            for i in range(steps):
+                self.step(i, stream=s, merge=merge)
+        torch.cuda.synchronize()
+        return g
+
+    def run_graph(self, steps):  # -> wall seconds of `steps` graph-replayed steps, decode-kernel us
+        """The step loop as one graph replay (no per-launch host work), then the decode
+        kernel's launch duration: HIP events on the launching stream around a replay of
+        `steps` back-to-back decode kernels, divided by `steps` (ROCm cannot record timing
+        events inside a graph)."""
+        torch = self.torch
+        g = self.capture(steps)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gd = self.capture(steps, merge=False)
+        gd.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        gd.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del g, gd
+        return wall, a.elapsed_time(b) * 1e3 / steps
 
     def settle(self, seconds):
         """Untimed steps for `seconds` of wall clock before the warmup: the first few
@@ -336,14 +377,21 @@ def main():
     pools = [build_device_pool(sc)[0] for _ in range(args.copies)]
     q = to_torch(sc.q, sc.dtype)
     db = DecodeBench(pools, sc, q)
-    log(f"timing {args.steps} steps after {args.warmup} warmup steps")
-    wall, k_ms, s_ms = db.run(args.steps, args.warmup, args.settle)
+    log(f"eager pass: {args.steps} steps after {args.warmup} warmup steps (per-launch events)")
+    wall_eager, k_ms, s_ms = db.run(args.steps, args.warmup, args.settle)
+    launch = "hip_graph"
+    try:
+        log(f"timed region: {args.steps} steps as one HIP graph replay")
+        wall, k_us = db.run_graph(args.steps)
+    except RuntimeError as e:  # no graph capture here: the eager loop is the timed region
+        log(f"graph capture unavailable ({e}); timing the eager loop")
+        launch, wall, k_us = "eager", wall_eager, float(np.mean(k_ms)) * 1e3
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=q.device)
         torch.empty_like(src).copy_(src)
         torch.cuda.synchronize()
     ms_step = wall * 1e3 / args.steps
-    t_kernel = float(np.mean(k_ms)) * 1e-3
+    t_kernel = k_us * 1e-6
     achieved = db.kernel_bytes / t_kernel / 1e9
     n_br, hq, d = q.shape
     result = {
@@ -361,16 +409,20 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/V, K/sqrt(d), RoPE theta 1e6 pre-applied; no weights)",
         "config": {"workload": args.workload, "branches": n_br, "q_heads": hq, "kv_heads": sc.n_kv_heads,
                    "head_dim": d, "page_size": sc.page_size, "pool_copies_rotated": args.copies,
-                   "settle_s": args.settle, "settle_steps": db.settled_steps},
+                   "settle_s": args.settle, "settle_steps": db.settled_steps, "launch": launch},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic() if args.workload == "shared_prefix_fork_decode" else None,
                      "kernel": "decode_kernel (fork_attn_partials)",
                      "algorithmic_bytes_per_launch": db.kernel_bytes,
                      "kernel_us_mean": t_kernel * 1e6,
-                     "kernel_us_p10": float(np.percentile(k_ms, 10)) * 1e3,
-                     "kernel_us_p90": float(np.percentile(k_ms, 90)) * 1e3},
-        "step": {"us_mean_events": float(np.mean(s_ms)) * 1e3, "algorithmic_bytes": db.step_bytes,
+                     "kernel_timing": ("HIP events around a graph replay of back-to-back launches" if launch ==
+                                       "hip_graph" else "HIP events around each launch"),
+                     "kernel_us_eager_events_mean": float(np.mean(k_ms)) * 1e3,
+                     "kernel_us_eager_events_p10": float(np.percentile(k_ms, 10)) * 1e3,
+                     "kernel_us_eager_events_p90": float(np.percentile(k_ms, 90)) * 1e3},
+        "step": {"us_per_step_timed": ms_step * 1e3, "us_per_step_eager_wall": wall_eager * 1e6 / args.steps,
+                 "us_mean_events": float(np.mean(s_ms)) * 1e3, "algorithmic_bytes": db.step_bytes,
                  "achieved_GBps": db.step_bytes / (float(np.mean(s_ms)) * 1e-3) / 1e9,
                  "frac_of_peak": db.step_bytes / (float(np.mean(s_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                  "merge_us_mean": float(np.mean(s_ms - k_ms)) * 1e3},
