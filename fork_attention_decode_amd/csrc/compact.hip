@@ -11,9 +11,11 @@
 // Phase 1 gathers the page's kept tokens from their old slots into registers: each
 // thread holds a few 16-byte K slot pairs (i, i + d/2) -- rotated by the token's offset
 // with fp32 cos/sin rows computed on the host in fp64 (an fp32 angle at 131K positions
-// would be off by ~1e-2 rad) -- and a few 16-slot V^T rows copied bit-exactly.  Phase 2
-// stores them into the destination page with 16-byte stores.  No LDS image, so many
-// workgroups share a CU and hide each other's latency.
+// would be off by ~1e-2 rad) -- and a few 16-slot V^T rows, copied bit-exactly: the
+// page's kept tokens form a few runs of consecutive source slots, and each run's part of
+// a row is its whole source row shifted by the run's slot offset.  Phase 2 stores them
+// into the destination page with 16-byte stores.  No LDS image, so many workgroups share
+// a CU and hide each other's latency.
 //
 // In-place hazard: kept tokens only move to lower slots, so a page rewritten in place
 // may still be a source of lower destination pages (at most two: a source page's kept
@@ -40,11 +42,11 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
   constexpr int NF = D * (int)sizeof(T) / 64;  // K slots per token row and lane group
   constexpr int HALF = NF / 2;                 // slot f pairs with f + HALF (d, d + D/2)
   constexpr int BLK = 16 * D;                  // elements per (page, head) block
-  constexpr int VR = 16 / E;                   // 16-byte vectors per V^T row (16 slots)
   typedef T vec_t __attribute__((__vector_size__(16)));
   const int hkv = p.n_kv_heads;
   __shared__ int s_b;
   __shared__ int s_loc[16], s_rot[16];
+  __shared__ int s_run[16][3], s_nrun;  // runs of the page: first slot, length, source location of the first
   if (threadIdx.x == 0) s_b = (int)((unsigned)atomicAdd(p.ticket, 1) - (unsigned)p.ticket_base);
   __syncthreads();
   const int b = s_b;
@@ -67,6 +69,26 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
     const bool mine = t >= cp.first_slot && t < cp.n_slots;
     s_loc[t] = mine ? p.src_loc[cp.tok_base + t] : -1;
     s_rot[t] = mine ? p.rot[cp.tok_base + t] : -1;
+  }
+  __syncthreads();
+  // runs: maximal slot ranges whose sources are consecutive slots of one source page
+  // (kept tokens are consecutive between dropped spans, so a page has one to three)
+  if (threadIdx.x == 0) {
+    int nr = 0;
+    for (int t = 0; t < 16; ++t) {
+      const int loc = s_loc[t];
+      if (loc < 0) continue;
+      if (nr > 0 && s_run[nr - 1][0] + s_run[nr - 1][1] == t && s_run[nr - 1][2] + s_run[nr - 1][1] == loc &&
+          (loc >> 4) == (s_run[nr - 1][2] >> 4)) {
+        ++s_run[nr - 1][1];
+        continue;
+      }
+      s_run[nr][0] = t;
+      s_run[nr][1] = 1;
+      s_run[nr][2] = loc;
+      ++nr;
+    }
+    s_nrun = nr;
   }
   __syncthreads();
 
@@ -97,23 +119,58 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
       }
     }
   }
-  // ---- phase 1b: V^T rows (bit-exact); row r = h * D + d holds slots 0..15
+  // ---- phase 1b: V^T rows (bit-exact); row r = h * D + d holds slots 0..15 as WPR 32-bit
+  // words.  Per run, the whole source row is loaded (two 16-byte loads) and shifted by the
+  // run's slot offset: word moves with a wave-uniform index, alignbyte for half-word
+  // shifts of bf16; the run's slots are then merged into the row.
+  constexpr int WPR = 16 * (int)sizeof(T) / 4;  // 32-bit words per V^T row
+  constexpr int SPW = 4 / (int)sizeof(T);       // slots per word
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const int n_vr = hkv * D;
-  vec_t vr[UV][VR];
+  const int nrun = s_nrun;
+  unsigned vr[UV][WPR];
 #pragma unroll
   for (int i = 0; i < UV; ++i) {
     const int r = threadIdx.x + i * 256;
     if (r < n_vr) {
       const int h = r / D, d = r % D;
-      if (keep_rest) {
+      const u32x4* old = reinterpret_cast<const u32x4*>(vp + dst + (size_t)h * np * BLK + d * 16);
 #pragma unroll
-        for (int w = 0; w < VR; ++w)
-          vr[i][w] = *reinterpret_cast<const vec_t*>(vp + dst + (size_t)h * np * BLK + d * 16 + w * E);
+      for (int w4 = 0; w4 < WPR / 4; ++w4) {
+        const u32x4 x = keep_rest ? old[w4] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vr[i][4 * w4 + e] = x[e];
       }
+      for (int k = 0; k < nrun; ++k) {  // wave-uniform
+        const int t0 = s_run[k][0], len = s_run[k][1], loc = s_run[k][2];
+        const int delta = (loc & 15) - t0;  // source slot of destination slot t: t + delta
+        const u32x4* srow = reinterpret_cast<const u32x4*>(vp + ((size_t)h * np + (loc >> 4)) * BLK + d * 16);
+        unsigned src[WPR + 2];  // the source row with a zero word on either side
+        src[0] = 0u;
+        src[WPR + 1] = 0u;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int loc = s_loc[t];
-        if (loc >= 0) vr[i][t / E][t % E] = vp[((size_t)h * np + (loc >> 4)) * BLK + d * 16 + (loc & 15)];
+        for (int w4 = 0; w4 < WPR / 4; ++w4) {
+          const u32x4 x = srow[w4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) src[1 + 4 * w4 + e] = x[e];
+        }
+#pragma unroll
+        for (int w = 0; w < WPR; ++w) {
+          const int a = SPW * w + delta;            // source slot of this word's first slot
+          int kw = SPW == 2 ? (a >> 1) : a;         // source word holding it (floor)
+          kw = kw < -1 ? -1 : (kw > WPR - 1 ? WPR - 1 : kw);
+          unsigned val = src[kw + 1];
+          if (SPW == 2 && (a & 1)) val = __builtin_amdgcn_alignbyte(src[kw + 2], src[kw + 1], 2);
+          const int lo_slot = SPW * w, hi_slot = SPW * w + SPW - 1;
+          const bool lo_in = lo_slot >= t0 && lo_slot < t0 + len;
+          const bool hi_in = hi_slot >= t0 && hi_slot < t0 + len;
+          if (SPW == 1) {
+            vr[i][w] = lo_in ? val : vr[i][w];
+          } else {
+            const unsigned keep = (lo_in ? 0u : 0x0000ffffu) | (hi_in ? 0u : 0xffff0000u);
+            vr[i][w] = (vr[i][w] & keep) | (val & ~keep);
+          }
+        }
       }
     }
   }
@@ -153,12 +210,13 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
     const int r = threadIdx.x + i * 256;
     if (r < n_vr) {
       const int h = r / D, d = r % D;
+      u32x4* row = reinterpret_cast<u32x4*>(vp + dst + (size_t)h * np * BLK + d * 16);
 #pragma unroll
-      for (int w = 0; w < VR; ++w)
-        *reinterpret_cast<vec_t*>(vp + dst + (size_t)h * np * BLK + d * 16 + w * E) = vr[i][w];
+      for (int w4 = 0; w4 < WPR / 4; ++w4)
+        row[w4] = u32x4{vr[i][4 * w4], vr[i][4 * w4 + 1], vr[i][4 * w4 + 2], vr[i][4 * w4 + 3]};
     }
   }
-  __syncthreads();  // s_loc / s_rot are refilled for the next entry
+  __syncthreads();  // s_loc / s_rot / s_run are refilled for the next entry
   }
 }
 
