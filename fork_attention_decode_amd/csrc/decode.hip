@@ -348,21 +348,27 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// ---- merge: one wave per output row.  The row's partials sit at the fixed-stride block
-// [row * max_parts, ...), so the count, the lse values (one per lane) and the partial
-// rows (16-byte loads, 256 / d partials per load instruction) are all fetched in one
-// round trip; slots past the count are masked with selects, never multiplied in.
+// ---- merge: two waves per output row, one per half of the head dimension (so a
+// decode's few hundred rows still cover every compute unit).  The row's partials sit at
+// the fixed-stride block [row * max_parts, ...), so the count, the lse values (one per
+// lane) and the partial half-rows (16-byte loads, 512 / d partials per load instruction)
+// are all fetched in one round trip; slots past the count are masked with selects,
+// never multiplied in.  Both waves of a row compute the same weights.
+constexpr int kMergeSplit = 2;
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   typedef float f4 __attribute__((ext_vector_type(4)));
-  constexpr int LPR = D / 4;      // lanes per partial row
-  constexpr int PPI = 64 / LPR;   // partials per load instruction
-  constexpr int NL = 64 / PPI;    // load instructions per 64 partials
+  constexpr int DW = D / kMergeSplit;  // dims per wave
+  constexpr int LPR = DW / 4;          // lanes per partial half-row
+  constexpr int PPI = 64 / LPR;        // partials per load instruction
+  constexpr int NL = 64 / PPI;         // load instructions per 64 partials
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kWaves + wave;
+  const int gw = blockIdx.x * kWaves + wave;
+  const int row = gw / kMergeSplit, half = gw % kMergeSplit;
   if (row >= p.n_rows) return;
   const int sub = lane / LPR, col = lane % LPR;
+  const int d0 = half * DW;  // this wave's dims [d0, d0 + DW)
   const int maxp = p.max_parts;
   const size_t base = (size_t)row * maxp;
   const int cnt = p.count[row];
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 #pragma unroll
     for (int k = 0; k < NL; ++k) {
       const int j = k * PPI + sub;
-      v[k] = j < maxp ? *reinterpret_cast<const f4*>(p.part_o + (base + j) * D + 4 * col) : f4{0.f, 0.f, 0.f, 0.f};
+      v[k] = j < maxp ? *reinterpret_cast<const f4*>(p.part_o + (base + j) * D + d0 + 4 * col) : f4{0.f, 0.f, 0.f, 0.f};
     }
     M = wave_max(lane < cnt ? my_lse : -INFINITY);
     const float my_w = lane < cnt ? fast_exp2(my_lse - M) : 0.f;
@@ -404,7 +410,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
           w = sub == q ? wq : w;
         }
         const int j = j0 + k * PPI + sub;
-        if (j < cnt) acc += w * *reinterpret_cast<const f4*>(p.part_o + (base + j) * D + 4 * col);
+        if (j < cnt) acc += w * *reinterpret_cast<const f4*>(p.part_o + (base + j) * D + d0 + 4 * col);
       }
     }
   }
@@ -414,11 +420,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
   const float inv = S > 0.f ? 1.f / S : 0.f;
   if (sub == 0) {
-    T* out = reinterpret_cast<T*>(p.out) + (size_t)row * D + 4 * col;
+    T* out = reinterpret_cast<T*>(p.out) + (size_t)row * D + d0 + 4 * col;
 #pragma unroll
     for (int c = 0; c < 4; ++c) out[c] = from_f32<T>(acc[c] * inv);
   }
-  if (p.lse && lane == 0) p.lse[row] = S > 0.f ? (M + __log2f(S)) * 0.69314718055994531f : -INFINITY;
+  if (p.lse && half == 0 && lane == 0) p.lse[row] = S > 0.f ? (M + __log2f(S)) * 0.69314718055994531f : -INFINITY;
 }
 
 template <typename T, int D>
@@ -493,7 +499,7 @@ hipError_t launch_decode(int dtype, int d, const DecodeParams& p, hipStream_t s)
 template <typename T, int D>
 static hipError_t merge_t(const MergeParams& p, hipStream_t s) {
   if (p.n_rows == 0) return hipSuccess;
-  merge_kernel<T, D><<<(p.n_rows + kWaves - 1) / kWaves, 256, 0, s>>>(p);
+  merge_kernel<T, D><<<(p.n_rows * kMergeSplit + kWaves - 1) / kWaves, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
