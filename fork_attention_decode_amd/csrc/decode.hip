@@ -8,8 +8,8 @@
 //   * a work item = (segment of pages with one reader set, KV head, chunk range); its
 //     rows are every (reader, query head of this KV head) pair, up to 64;
 //   * one workgroup of 4 waves per item streams every chunk (a 4 KiB K block and a
-//     4 KiB V^T block of one page and head) from HBM exactly once, with direct
-//     global->LDS loads into a ring (each wave loads a quarter, non-temporal), six
+//     4 KiB V^T block of one page and head) from HBM exactly once, with buffer loads
+//     straight into an LDS ring (each wave loads a quarter, non-temporal), six
 //     chunks in flight; wave w computes rows [16 w, 16 w + 16) from LDS, so a shared
 //     page feeds all 64 rows with one HBM read;
 //   * chunks are consumed in pairs (32 keys): S^T = K Q^T on v_mfma_f32_16x16x32_bf16
@@ -237,7 +237,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // ---- one work item: every chunk streamed from HBM once per workgroup into an LDS ring
-// with direct global->LDS loads (each wave loads a quarter of every chunk); wave w
+// with buffer loads straight into LDS (each wave loads a quarter of every chunk); wave w
 // computes rows [16 w, 16 w + 16) from LDS, two chunks per step; NB - 2 chunks stay in
 // flight; one workgroup barrier per step.
 template <typename T, int D>

@@ -158,7 +158,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // row_ptr / ent / order are read-only here and never alias the outputs, so their
 // wave-uniform reads become scalar loads (a vector load would have to wait for every
-// global->LDS copy in flight before it).
+// copy into LDS in flight before it).
 //
 // 8 waves, two per SIMD (waves w and w + 4 share one): wave w takes query head slot
 // w / 2 and tokens [q0 + 32 (w % 2), +32) of the block.
