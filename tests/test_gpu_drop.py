@@ -22,12 +22,13 @@ def _oracle(sc):
     return pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, sc.dtype))
 
 
-def _k_close(got_bits, ref, what):
-    """got_bits: bf16 bits [n, d]; ref: fp64 [n, d].  One ulp of the reference value, plus the
-    fp32 product error of a rotation of the pair (x_i, x_{i+d/2})."""
-    got = W.bf16_bits_to_f64(got_bits)
+def _k_close(got_st, ref, what, dtype="bf16"):
+    """got_st: keys in storage form [n, d] (bf16 bits or fp32); ref: fp64 [n, d].  One ulp
+    of the reference value in the storage type, plus the fp32 product error of a rotation of
+    the pair (x_i, x_{i+d/2})."""
+    got = W.storage_to_f64(got_st, dtype)
     _, e = np.frexp(ref)
-    ulp = np.ldexp(1.0, e - 8)
+    ulp = np.ldexp(1.0, e - (8 if dtype == "bf16" else 24))
     h = ref.shape[-1] // 2
     pair = np.abs(ref) + np.abs(np.concatenate([ref[..., h:], ref[..., :h]], axis=-1))
     bad = np.abs(got - ref) > ulp + 4e-7 * pair
@@ -48,11 +49,11 @@ def _check_state(sc, pool, ora, seqs, pages=None, exact_k=None):
             for h in range(sc.n_kv_heads):
                 k, v = pool.read_page(page, h)
                 rk, rv = ora.kdata[page][:nv, h], ora.vdata[page][:nv, h]
-                assert np.array_equal(W.bf16_bits_to_f64(v[:nv]), rv), f"V of seq {s} page {L} head {h}"
+                assert np.array_equal(W.storage_to_f64(v[:nv], sc.dtype), rv), f"V of seq {s} page {L} head {h}"
                 if exact_k is not None and exact_k(s):
-                    assert np.array_equal(W.bf16_bits_to_f64(k[:nv]), rk), f"K of seq {s} page {L} head {h}"
+                    assert np.array_equal(W.storage_to_f64(k[:nv], sc.dtype), rk), f"K of seq {s} page {L} head {h}"
                 else:
-                    _k_close(k[:nv], rk, f"K of seq {s} page {L} head {h}")
+                    _k_close(k[:nv], rk, f"K of seq {s} page {L} head {h}", sc.dtype)
     assert pool.free_pages() == ora.n_free
     for p in range(sc.n_pages):
         assert pool.refcount(p) == ora.rc[p], f"refcount of page {p}"
@@ -69,6 +70,28 @@ def test_drop_compaction_contents(repos):
     for a, b in zip(kept, okept):
         assert np.array_equal(a, b)
     _check_state(sc, pool, ora, [0, 1], exact_k=lambda s: not repos)
+
+
+@pytest.mark.parametrize("dtype,d", [("fp32", 128), ("bf16", 64), ("fp32", 64)])
+def test_drop_repos_other_storage(dtype, d):
+    # the compaction kernel's other instantiations: fp32 pools (one slot per 32-bit word of a
+    # V^T row, no half-word shifts) and head dim 64; page contents, then a decode
+    import torch
+    sc = W.drop_scenario(requests=2, ctx=900, frac=0.4, span_min=17, span_max=150, hq=4, hkv=2, d=d, dtype=dtype,
+                         seed=27, repos=True)
+    print(f"[case] drop + repos, {dtype} d={d}", flush=True)
+    pool, kept = build_device_pool(sc)
+    ora, okept = _oracle(sc)
+    for a, b in zip(kept, okept):
+        assert np.array_equal(a, b)
+    _check_state(sc, pool, ora, [0, 1])
+    out, lse = pool.decode(sc.queries, to_torch(sc.q, dtype), sc.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(sc)
+    tol = (BF16_MAX, BF16_MEAN) if dtype == "bf16" else (1e-4, 1e-4)
+    mx, mn = check_close(out_to_f64(out, dtype), ro, *tol, f"decode after drop {dtype} d={d}")
+    check_close(lse.double().cpu().numpy(), rl, LSE_MAX, LSE_MAX, "lse")
+    print(f"[ok] max-abs {mx:.3g} mean-abs {mn:.3g}", flush=True)
 
 
 def test_drop_many_offsets_and_edge_spans():
