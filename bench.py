@@ -89,6 +89,35 @@ class DecodeBench:
         if ev:
             ev[2].record()
 
+    def host_call_us(self, reps=20):
+        """Host time of one fork_attn_partials call (ctypes call, plan lookup, launch) with
+        the plan cached, and when the plan must be rebuilt and uploaded (the query list
+        changes between calls).  Runs before the timed work; leaves the usual plan cached."""
+        import numpy as np
+        torch = self.torch
+        p, ws = self.pools[0], self.wss[0]
+        seqs, alt = list(self.sc.queries), list(reversed(self.sc.queries))
+
+        def call(qs):
+            t0 = time.perf_counter()
+            self.fa.fork_attn_partials(p.handle, qs, self.hq, self.q.data_ptr(), self.sc.sm_scale, ws.data_ptr(),
+                                       ws.numel(), self.stream)
+            return (time.perf_counter() - t0) * 1e6
+
+        call(seqs)
+        torch.cuda.synchronize()
+        cached = [call(seqs) for _ in range(reps)]
+        torch.cuda.synchronize()
+        rebuilt = []
+        for i in range(reps):
+            rebuilt.append(call(alt if i % 2 == 0 else seqs))
+            torch.cuda.synchronize()
+        call(seqs)
+        torch.cuda.synchronize()
+        return {"plan_cached_us_median": float(np.median(cached)), "plan_rebuilt_us_median": float(np.median(rebuilt)),
+                "note": "host wall time of one fork_attn_partials call from Python (ctypes included); rebuilt = the "
+                        "query list changed, so the segment plan is recomputed and uploaded"}
+
     def capture(self, steps, merge=True):
         """A HIP graph of `steps` decode steps (pools rotated as in the eager loop), or with
         merge=False of `steps` back-to-back decode kernels.  The plans are cached by then, so
@@ -183,9 +212,12 @@ class DecodeBench:
         }
 
 
-def bench_prefill(reps, warmup):
+def bench_prefill(reps, warmup, cpu_budget=0.0):
     """dag_attn_run (attention kernel alone, HIP events on its stream) on the packed DAG
-    workload; the preparation (K / V relayout, column packing, row order) is timed apart."""
+    workload; the preparation (K / V relayout, column packing, row order) is timed apart.
+    With cpu_budget > 0 the fp64 oracle is also timed on query rows drawn uniformly at
+    random for about that many seconds, and its full-workload time extrapolated (mean time
+    per row x T)."""
     import numpy as np
     import torch
     import workloads as W
@@ -195,6 +227,7 @@ def bench_prefill(reps, warmup):
     pi = W.dag_prefill()
     mask = fa.DagMask(pi.segments, pi.edges, pi.T, pi.block)
     q, k, v = (to_torch(x, "bf16") for x in (pi.q, pi.k, pi.v))
+    host = (pi.q, pi.k, pi.v) if cpu_budget > 0 else None
     pi.q = pi.k = pi.v = None
     hq, hkv = q.shape[1], k.shape[1]
     out = torch.empty_like(q)
@@ -227,7 +260,10 @@ def bench_prefill(reps, warmup):
     run_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
     t = float(np.mean(run_ms)) * 1e-3
     tflops = PREFILL_FLOPS / t / 1e12
-    return {
+    cpu = None
+    if host is not None:
+        cpu = prefill_cpu_baseline(pi, host, cpu_budget)
+    out_obj = {
         "workload": "packed_dag_prefill (16,384-token prefix + 8 x 8,192 branches, 12 edges of 2,048 tokens; "
                     "T = 81,920; 32 / 8 heads, d = 128, bf16)",
         "block_pairs": mask.nnz,
@@ -241,6 +277,9 @@ def bench_prefill(reps, warmup):
         "call_ms_mean": float(np.mean(prep_ms + run_ms)),
         "reps": reps,
     }
+    if cpu is not None:
+        out_obj["cpu_baseline"] = cpu
+    return out_obj
 
 
 def bench_octopus(steps, warmup):
@@ -377,6 +416,7 @@ def main():
     pools = [build_device_pool(sc)[0] for _ in range(args.copies)]
     q = to_torch(sc.q, sc.dtype)
     db = DecodeBench(pools, sc, q)
+    host_call = db.host_call_us()
     log(f"eager pass: {args.steps} steps after {args.warmup} warmup steps (per-launch events)")
     wall_eager, k_ms, s_ms = db.run(args.steps, args.warmup, args.settle)
     launch = "hip_graph"
@@ -422,6 +462,9 @@ def main():
                      "kernel_us_eager_events_p10": float(np.percentile(k_ms, 10)) * 1e3,
                      "kernel_us_eager_events_p90": float(np.percentile(k_ms, 90)) * 1e3},
         "step": {"us_per_step_timed": ms_step * 1e3, "us_per_step_eager_wall": wall_eager * 1e6 / args.steps,
+                 "achieved_GBps_timed": db.step_bytes / (ms_step * 1e-3) / 1e9,
+                 "frac_of_peak_timed": db.step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                 "host_call": host_call,
                  "us_mean_events": float(np.mean(s_ms)) * 1e3, "algorithmic_bytes": db.step_bytes,
                  "achieved_GBps": db.step_bytes / (float(np.mean(s_ms)) * 1e-3) / 1e9,
                  "frac_of_peak": db.step_bytes / (float(np.mean(s_ms)) * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -432,7 +475,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.only_decode:
-        result["prefill"] = bench_prefill(args.prefill_reps, 3)
+        result["prefill"] = bench_prefill(args.prefill_reps, 3, 0.0 if args.no_cpu_baseline else 8.0)
         torch.cuda.empty_cache()
         result["octopus_dag"] = bench_octopus(max(20, args.steps // 4), 5)
         torch.cuda.empty_cache()
@@ -442,6 +485,36 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sc, args.cpu_budget)
     print(json.dumps(result))
+
+
+def prefill_cpu_baseline(pi, host, budget_s):
+    """fp64 oracle on the packed DAG prefill: query rows drawn uniformly at random
+    (seeded) until budget_s of oracle work is spent; the full run's time is estimated as
+    the mean time per row x T (an unbiased estimate under uniform sampling)."""
+    import numpy as np
+    import workloads as W
+    from oracle import prefill as pf
+    q_bits, k_bits, v_bits = host
+    k64, v64 = W.bf16_bits_to_f64(k_bits), W.bf16_bits_to_f64(v_bits)
+
+    class Rows:  # q rows converted to fp64 on access
+        shape = q_bits.shape
+
+        def __getitem__(self, i):
+            return W.bf16_bits_to_f64(q_bits[i])
+
+    order = np.random.default_rng(11).permutation(pi.T)
+    done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < pi.T:
+        pf.attend_rows(Rows(), k64, v64, pi.segments, pi.edges, [int(order[done])], pi.sm_scale)
+        done += 1
+    t = time.perf_counter() - t0
+    t_full = t / done * pi.T
+    return {"value": PREFILL_FLOPS / t_full / 1e12, "unit": "TFLOP/s", "cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle", "extrapolated": True, "oracle_full_run_s_estimate": t_full,
+            "sample": f"{done} query rows (all {pi.n_q_heads} heads) drawn uniformly at random from the {pi.T:,} by the fp64 "
+                      f"dense-masked oracle in {t:.1f} s; full run estimated as mean time per row x T"}
 
 
 def cpu_baseline(sc, budget_s):
