@@ -88,6 +88,10 @@ _SIGS = {
                          _sz, _P],
     "dag_attn_prepare": [_P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, C.c_int64, _i32, _P, _sz, _P],
     "dag_attn_run": [_P, _P, _P, _i32, _i32, _i32, _i32, _P, C.c_int64, _i32, C.c_float, _P, _sz, _P],
+    "kv_score_workspace_size": [_P, _i32, _i32, _i32, _psz],
+    "kv_score": [_P, _i32, _P, _i32, _i32, C.c_float, _P, _P, _sz, _P],
+    "kv_select_keep": [_P, C.c_int64, C.c_int64, _P, _P],
+    "kv_drop_keep": [_P, _i32, C.POINTER(C.c_uint8), C.c_int64, _i32, _P],
 }
 EXPORTED = sorted(list(_SIGS) + ["kv_status_str", "kv_last_error"])
 for _name, _args in _SIGS.items():
@@ -276,6 +280,27 @@ def fork_attn_merge(pool: int, seqs: Sequence[int], n_q_heads: int, out: int, ls
                                                   workspace, ws_bytes, stream or None), pool)
 
 
+def kv_score_workspace_size(pool: int, seq: int, n_rep: int, n_q_heads: int) -> int:
+    out = C.c_size_t(0)
+    _check("kv_score_workspace_size", lib.kv_score_workspace_size(pool, seq, n_rep, n_q_heads, C.byref(out)), pool)
+    return out.value
+
+
+def kv_score(pool: int, seq: int, q_rep: int, n_rep: int, n_q_heads: int, sm_scale: float, scores: int,
+             workspace: int, ws_bytes: int, stream: int = 0):
+    _check("kv_score", lib.kv_score(pool, seq, q_rep, n_rep, n_q_heads, sm_scale, scores, workspace, ws_bytes,
+                                    stream or None), pool)
+
+
+def kv_select_keep(scores: int, n: int, budget: int, keep: int, stream: int = 0):
+    _check("kv_select_keep", lib.kv_select_keep(scores, n, budget, keep, stream or None))
+
+
+def kv_drop_keep(pool: int, seq: int, keep: np.ndarray, flags: int = 0, stream: int = 0):
+    k = np.ascontiguousarray(np.asarray(keep, np.uint8))
+    _check("kv_drop_keep", lib.kv_drop_keep(pool, seq, _ptr(k, C.c_uint8), len(k), flags, stream or None), pool)
+
+
 def fork_attn_plan_stats(pool: int) -> dict:
     out = np.zeros(6, np.int64)
     _check("fork_attn_plan_stats", lib.fork_attn_plan_stats(pool, _ptr(out, C.c_int64), 6), pool)
@@ -330,6 +355,16 @@ def dag_attn_run(q: int, out: int, lse: int, T: int, n_q_heads: int, n_kv_heads:
 
 
 # ------------------------------------------------------------------ packed DAG prefill
+def select_keep(scores, budget: int, keep=None):
+    """keep (uint8 tensor): 1 for the `budget` highest scores, ties to the lower index."""
+    import torch
+    n = scores.numel()
+    if keep is None:
+        keep = torch.empty(max(n, 1), dtype=torch.uint8, device=scores.device)[:n]
+    kv_select_keep(scores.data_ptr(), n, budget, keep.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    return keep
+
+
 class DagMask:
     """Device copy of the CSR block mask of a packed DAG (dag_mask_build on the host)."""
 
@@ -433,6 +468,35 @@ class Pool:
     def drop(self, seq: int, spans, repos: bool = False) -> np.ndarray:
         st = 0 if self.k_pages is None else self._stream()
         return kv_drop(self.handle, seq, spans, KV_DROP_REPOS if repos else 0, st)
+
+    def score(self, seq: int, q_rep, sm_scale: float, workspace=None):
+        """Mean attention of the representative queries q_rep (torch [n_rep, Hq, d] on the
+        device) on each own token of `seq`.  Returns a float32 tensor [n_tokens]."""
+        import torch
+        n_rep, hq, _ = q_rep.shape
+        n_tok = self.info(seq)[0]
+        need = kv_score_workspace_size(self.handle, seq, n_rep, hq)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q_rep.device)
+        scores = torch.empty(max(n_tok, 1), dtype=torch.float32, device=q_rep.device)[:n_tok]
+        kv_score(self.handle, seq, q_rep.data_ptr(), n_rep, hq, sm_scale, scores.data_ptr(), workspace.data_ptr(),
+                 workspace.numel(), self._stream())
+        return scores
+
+    def drop_keep(self, seq: int, keep, repos: bool = False):
+        """Drop the tokens whose keep entry (host array, one per own token) is 0."""
+        kv_drop_keep(self.handle, seq, keep, KV_DROP_REPOS if repos else 0,
+                     0 if self.k_pages is None else self._stream())
+
+    def select_and_drop(self, seq: int, q_rep, sm_scale: float, budget: int, repos: bool = False):
+        """Score, keep the `budget` best own tokens, drop the rest.  Returns the keep mask."""
+        import torch
+        scores = self.score(seq, q_rep, sm_scale)
+        keep = select_keep(scores, budget)
+        torch.cuda.current_stream().synchronize()
+        mask = keep.cpu().numpy()
+        self.drop_keep(seq, mask, repos)
+        return mask
 
     def repos(self, seq: int):
         kv_repos(self.handle, seq, 0 if self.k_pages is None else self._stream())

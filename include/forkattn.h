@@ -268,6 +268,37 @@ int dag_attn_run(const void* q, void* out, float* lse, int32_t T, int32_t n_q_he
                  hipStream_t stream);
 
 /* ---- errors ---- */
+/* ---- key scoring and keep selection in front of Drop ----
+ * AgentKV (rit.work), section "Как AgentKV выбирает и освобождает записи кэша": before a
+ * compression the per-phase queues of recent queries are merged, every key is scored
+ * against the merged set and the entries with the highest mean attention are kept; the
+ * rest is dropped and the freed pages returned.
+ *
+ * kv_score: scores[t] for each own token t of `seq` (t < n_tokens of kv_seq_info) = the
+ * mean over the n_rep x n_q_heads (representative query, head) pairs of t's softmax
+ * probability in that query's attention over the sequence's whole visible context (own
+ * tokens, then mounts; query head h reads KV head h / (n_q_heads / Hkv); logits =
+ * sm_scale * q.k).  q_rep: device, pool dtype, [n_rep][n_q_heads][head_dim], rotated by
+ * the caller.  scores: device float [n_tokens].  Needs a device bf16 pool (head_dim 64 or
+ * 128; KV_ERR_UNSUPPORTED otherwise) and n_rep * n_q_heads / Hkv <= 256.  The workspace
+ * (kv_score_workspace_size bytes, caller-owned device memory) holds a decode over the
+ * representative queries (their normalisers) and per-KV-head partial sums; it replaces
+ * the pool's cached decode plan.  Stream-ordered; scores are valid once the stream has
+ * run the call. */
+int kv_score_workspace_size(kv_pool_t* pool, kv_seq_t seq, int32_t n_rep, int32_t n_q_heads, size_t* bytes);
+int kv_score(kv_pool_t* pool, kv_seq_t seq, const void* q_rep, int32_t n_rep, int32_t n_q_heads, float sm_scale,
+             float* scores, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* keep[t] = 1 for the `budget` highest scores (ties to the lower index), 0 for the rest;
+ * budget <= 0 keeps nothing, budget >= n keeps everything.  scores: device float [n];
+ * keep: device uint8 [n].  No workspace; stream-ordered. */
+int kv_select_keep(const float* scores, int64_t n, int64_t budget, uint8_t* keep, hipStream_t stream);
+
+/* Drop the tokens whose keep entry is 0: kv_drop with the maximal spans of zeros.  keep:
+ * HOST uint8 [n], n = the sequence's n_tokens (copy the device mask back first: the page
+ * table lives on the host).  flags as for kv_drop. */
+int kv_drop_keep(kv_pool_t* pool, kv_seq_t seq, const uint8_t* keep, int64_t n, int32_t flags, hipStream_t stream);
+
 const char* kv_status_str(int status);
 const char* kv_last_error(kv_pool_t* pool); /* pool = NULL: last error of pool-less calls */
 

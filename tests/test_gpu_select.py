@@ -1,0 +1,118 @@
+"""GPU parity of key scoring (kv_score), keep selection (kv_select_keep) and the drop that
+follows (kv_drop_keep), against the fp64 oracle (oracle/select.py).
+
+Bars: scores within 1e-2 relative (+1e-9 absolute) of the fp64 scores: each probability
+is exp2(s c2 - lse2) with the normaliser from the decode path, whose LSE is held to 2e-3
+absolute, i.e. ~2e-3 relative on every probability; the fp32 dot products add ~1e-6.
+Keep masks are bit-exact against the oracle's selection applied to the GPU's own fp32
+scores (the decision is taken in the same precision on both sides).  After the drop, the
+page table is bit-exact and the decode is within the decode bars.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from tests.harness import build_device_pool, check_close, oracle_decode, out_to_f64, to_torch
+
+pytestmark = pytest.mark.gpu
+
+REL, ABS = 1e-2, 1e-9
+
+
+def _q_rep(n_rep, hq, d, seed):
+    # representative queries: seeded N(0,1) draws, one rounding to bf16 (fed to both sides)
+    return W.to_bf16_bits(np.random.default_rng(seed).standard_normal((n_rep, hq, d)))
+
+
+def _oracle_table(sc):
+    from oracle import pagetable as pt
+    return pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, sc.dtype))
+
+
+def _scores(sc, seq, n_rep, seed, label):
+    import torch
+    from oracle import select as sel
+    print(f"[case] {label}: seq {seq}, {n_rep} representative queries", flush=True)
+    pool, _ = build_device_pool(sc)
+    qb = _q_rep(n_rep, sc.n_q_heads, sc.head_dim, seed)
+    got = pool.score(seq, to_torch(qb, "bf16"), sc.sm_scale)
+    torch.cuda.synchronize()
+    got = got.double().cpu().numpy()
+    table, _ = _oracle_table(sc)
+    ref = sel.key_scores(table, seq, W.bf16_bits_to_f64(qb), sc.sm_scale)
+    assert got.shape == ref.shape
+    err = np.abs(got - ref)
+    bad = err > REL * ref + ABS
+    assert not bad.any(), f"{label}: {int(bad.sum())} scores off, worst rel {float((err / (ref + 1e-30)).max()):.3g}"
+    print(f"[ok] {label}: n={len(ref)} max rel {float((err / (ref + 1e-30)).max()):.3g} sum {got.sum():.6f}",
+          flush=True)
+    return pool, got, ref
+
+
+@pytest.mark.parametrize("n_rep,private", [(1, 37), (8, 300), (32, 1000)])
+def test_scores_fork(n_rep, private):
+    # a fork over a shared prefix: the fork's own context is prefix + private tokens
+    sc = W.fork_scenario(prefix=517, branches=2, private=[private, 5], hq=8, hkv=2, d=128, seed=41)
+    _, got, ref = _scores(sc, 1, n_rep, 42, f"scores n_rep={n_rep} private={private}")
+    assert abs(got.sum() - 1.0) < 1e-2  # no mounts: every softmax sums to 1
+
+
+def test_scores_d64_and_many_rows():
+    # head dim 64, G = 8 and 32 queries: 256 rows per KV head, the most one launch takes
+    sc = W.fork_scenario(prefix=200, branches=1, private=[90], hq=16, hkv=2, d=64, seed=43)
+    _scores(sc, 1, 32, 44, "scores d=64, 256 rows per KV head")
+
+
+def test_scores_with_mounts():
+    sc = W.dag_scenario(root=300, threads=3, private=90, mounts_per_thread=2, mount_len=33, hq=8, hkv=2, d=128,
+                        seed=45)
+    _, got, _ = _scores(sc, 2, 8, 46, "scores of a thread with mounts")
+    assert 0.0 < got.sum() < 1.0  # mounted keys take part of the mass and are not scored
+
+
+@pytest.mark.parametrize("n", [1, 1000, 131072])
+def test_select_keep_exact(n):
+    import torch
+    import fork_attention_decode_amd as fa
+    from oracle import select as sel
+    rng = np.random.default_rng(47 + n)
+    # quantised values: many exact ties around every threshold
+    sc = (rng.integers(0, max(2, n // 50), size=n) / 7.0).astype(np.float32)
+    sc[rng.random(n) < 0.01] = 0.0
+    t = torch.from_numpy(sc).cuda()
+    for budget in sorted({0, 1, n // 3, n // 2, n - 1, n, n + 5}):
+        print(f"[case] select n={n} budget={budget}", flush=True)
+        keep = fa.select_keep(t, budget)
+        torch.cuda.synchronize()
+        got = keep.cpu().numpy().astype(bool)
+        want = sel.select_keep(sc.astype(np.float64), budget)
+        assert np.array_equal(got, want), f"n={n} budget={budget}: {int((got != want).sum())} entries differ"
+
+
+@pytest.mark.parametrize("repos", [True, False])
+def test_select_drop_then_decode(repos):
+    import torch
+    from oracle import select as sel
+    sc = W.fork_scenario(prefix=700, branches=2, private=[900, 40], hq=8, hkv=2, d=128, seed=48)
+    sc.n_pages += 60
+    pool, _ = build_device_pool(sc)
+    qb = _q_rep(16, sc.n_q_heads, sc.head_dim, 49)
+    n_own = pool.info(1)[0]
+    budget = int(0.6 * n_own)
+    print(f"[case] score + keep {budget} of {n_own} + drop (repos={repos}) + decode", flush=True)
+    keep = pool.select_and_drop(1, to_torch(qb, "bf16"), sc.sm_scale, budget, repos=repos)
+    torch.cuda.synchronize()
+    assert int(keep.sum()) == budget
+    # the oracle replays the same scenario, then drops the spans of the GPU's keep mask
+    sc.ops = sc.ops + [("drop", 1, sel.drop_spans(keep.astype(bool)), repos)]
+    table, _ = _oracle_table(sc)
+    assert list(pool.block_table(1)) == table.block_table(1)
+    assert np.array_equal(pool.positions(1), table.positions(1))
+    for p in range(sc.n_pages):
+        assert pool.refcount(p) == table.rc[p], f"refcount of page {p}"
+    out, lse = pool.decode(sc.queries, to_torch(sc.q, "bf16"), sc.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(sc)
+    check_close(out_to_f64(out, "bf16"), ro, 2e-2, 2e-3, "decode after select + drop")
+    check_close(lse.double().cpu().numpy(), rl, 2e-3, 2e-3, "lse")
+    print("[ok] select + drop + decode", flush=True)
