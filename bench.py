@@ -282,6 +282,72 @@ def bench_prefill(reps, warmup, cpu_budget=0.0):
     return out_obj
 
 
+def bench_select(reps, warmup):
+    """Key scoring + keep selection (AgentKV's choice of entries before a compression) on
+    one 131,072-token sequence (32 / 8 heads, d = 128, bf16) with 32 representative
+    queries: kv_score and kv_select_keep timed with HIP events on their stream, then one
+    score -> select -> drop (no repos) end to end on the host clock."""
+    import numpy as np
+    import torch
+    import fork_attention_decode_amd as fa
+    import workloads as W
+    from tests.harness import build_device_pool, to_torch
+    n_ctx, n_rep = 131072, 32
+    log("select: building a 131,072-token sequence")
+    sc = W.drop_scenario(requests=1, ctx=n_ctx, frac=0.0, hq=32, hkv=8, d=128, seed=3, repos=False)
+    pool, _ = build_device_pool(sc)
+    seq = 0
+    n_tok = pool.info(seq)[0]
+    qb = W.to_bf16_bits(np.random.default_rng(50).standard_normal((n_rep, 32, 128)))
+    q_rep = to_torch(qb, "bf16")
+    ws = torch.empty(fa.kv_score_workspace_size(pool.handle, seq, n_rep, 32), dtype=torch.uint8, device="cuda")
+    scores = torch.empty(n_tok, dtype=torch.float32, device="cuda")
+    keep = torch.empty(n_tok, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    budget = int(0.6 * n_tok)
+
+    def score():
+        fa.kv_score(pool.handle, seq, q_rep.data_ptr(), n_rep, 32, sc.sm_scale, scores.data_ptr(), ws.data_ptr(),
+                    ws.numel(), st)
+
+    def select():
+        fa.kv_select_keep(scores.data_ptr(), n_tok, budget, keep.data_ptr(), st)
+
+    for _ in range(warmup):
+        score()
+        select()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        score()
+        e[1].record()
+        select()
+        e[2].record()
+    torch.cuda.synchronize()
+    sc_us = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e3
+    se_us = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e3
+    k_bytes = n_tok * 8 * 128 * 2
+    alg = 2 * k_bytes  # every key's logits twice: normalisers, then scores
+    t0 = time.perf_counter()
+    mask = pool.select_and_drop(seq, q_rep, sc.sm_scale, budget, repos=False)
+    torch.cuda.synchronize()
+    e2e_ms = (time.perf_counter() - t0) * 1e3
+    return {
+        "workload": "agentkv_select (one 131,072-token sequence, 32 / 8 heads, d = 128, bf16; 32 representative "
+                    "queries; keep 60 %)",
+        "score_us_mean": float(np.mean(sc_us)), "score_us_p10": float(np.percentile(sc_us, 10)),
+        "score_us_p90": float(np.percentile(sc_us, 90)),
+        "algorithmic_bytes": alg,
+        "score_GBps": alg / (float(np.mean(sc_us)) * 1e-6) / 1e9,
+        "score_frac_of_8TBps": alg / (float(np.mean(sc_us)) * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        "note": "algorithmic bytes = the sequence's K read twice (normalisers, then scores); the normaliser pass "
+                "runs the decode path, which also reads V",
+        "select_us_mean": float(np.mean(se_us)),
+        "select_drop_end_to_end_ms": e2e_ms, "kept": int(mask.sum()), "reps": reps,
+    }
+
+
 def bench_octopus(steps, warmup):
     import workloads as W
     from tests.harness import build_device_pool, to_torch
@@ -384,6 +450,7 @@ def main():
     ap.add_argument("--only-decode", action="store_true", help="skip the prefill / DAG / AKV objects")
     ap.add_argument("--only-prefill", action="store_true", help="time the prefill object alone (profiling)")
     ap.add_argument("--only-akv", action="store_true", help="time the drop + repos object alone (profiling)")
+    ap.add_argument("--only-select", action="store_true", help="time the key scoring object alone (profiling)")
     ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy 256 MiB device to device once (a kernel of known "
@@ -410,6 +477,9 @@ def main():
         return
     if args.only_akv:
         print(json.dumps({"akv": bench_akv(max(20, args.steps // 4), 5)}))
+        return
+    if args.only_select:
+        print(json.dumps({"agentkv_select": bench_select(20, 3)}))
         return
     sc = W.WORKLOADS[args.workload]()
     log(f"workload {args.workload}: building {args.copies} pool copies")
@@ -478,6 +548,8 @@ def main():
         result["prefill"] = bench_prefill(args.prefill_reps, 3, 0.0 if args.no_cpu_baseline else 8.0)
         torch.cuda.empty_cache()
         result["octopus_dag"] = bench_octopus(max(20, args.steps // 4), 5)
+        torch.cuda.empty_cache()
+        result["agentkv_select"] = bench_select(20, 3)
         torch.cuda.empty_cache()
         result["akv"] = bench_akv(max(20, args.steps // 4), 5)
         torch.cuda.empty_cache()

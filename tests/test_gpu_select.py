@@ -116,3 +116,19 @@ def test_select_drop_then_decode(repos):
     check_close(out_to_f64(out, "bf16"), ro, 2e-2, 2e-3, "decode after select + drop")
     check_close(lse.double().cpu().numpy(), rl, 2e-3, 2e-3, "lse")
     print("[ok] select + drop + decode", flush=True)
+
+
+def test_scores_full_size():
+    """One 131,072-token sequence (32 / 8 heads, d = 128), 32 representative queries: every
+    score against the oracle, and the keep mask at 60 % against the oracle's selection
+    on the GPU scores."""
+    import torch
+    import fork_attention_decode_amd as fa
+    from oracle import select as sel
+    sc = W.fork_scenario(prefix=131072 - 16, branches=1, private=[16], hq=32, hkv=8, d=128, seed=3)
+    pool, got, ref = _scores(sc, 1, 32, 50, "scores, 131,072 tokens, 32 queries")
+    budget = int(0.6 * len(got))
+    keep = fa.select_keep(torch.from_numpy(got.astype(np.float32)).cuda(), budget)
+    torch.cuda.synchronize()
+    want = sel.select_keep(got.astype(np.float32).astype(np.float64), budget)
+    assert np.array_equal(keep.cpu().numpy().astype(bool), want)
