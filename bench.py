@@ -303,6 +303,7 @@ def bench_select(reps, warmup):
     ws = torch.empty(fa.kv_score_workspace_size(pool.handle, seq, n_rep, 32), dtype=torch.uint8, device="cuda")
     scores = torch.empty(n_tok, dtype=torch.float32, device="cuda")
     keep = torch.empty(n_tok, dtype=torch.uint8, device="cuda")
+    sel_ws = torch.empty(fa.kv_select_workspace_size(n_tok), dtype=torch.uint8, device="cuda")
     st = torch.cuda.current_stream().cuda_stream
     budget = int(0.6 * n_tok)
 
@@ -311,7 +312,7 @@ def bench_select(reps, warmup):
                     ws.numel(), st)
 
     def select():
-        fa.kv_select_keep(scores.data_ptr(), n_tok, budget, keep.data_ptr(), st)
+        fa.kv_select_keep(scores.data_ptr(), n_tok, budget, keep.data_ptr(), sel_ws.data_ptr(), sel_ws.numel(), st)
 
     for _ in range(warmup):
         score()

@@ -90,7 +90,8 @@ _SIGS = {
     "dag_attn_run": [_P, _P, _P, _i32, _i32, _i32, _i32, _P, C.c_int64, _i32, C.c_float, _P, _sz, _P],
     "kv_score_workspace_size": [_P, _i32, _i32, _i32, _psz],
     "kv_score": [_P, _i32, _P, _i32, _i32, C.c_float, _P, _P, _sz, _P],
-    "kv_select_keep": [_P, C.c_int64, C.c_int64, _P, _P],
+    "kv_select_workspace_size": [C.c_int64, _psz],
+    "kv_select_keep": [_P, C.c_int64, C.c_int64, _P, _P, _sz, _P],
     "kv_drop_keep": [_P, _i32, C.POINTER(C.c_uint8), C.c_int64, _i32, _P],
 }
 EXPORTED = sorted(list(_SIGS) + ["kv_status_str", "kv_last_error"])
@@ -292,8 +293,14 @@ def kv_score(pool: int, seq: int, q_rep: int, n_rep: int, n_q_heads: int, sm_sca
                                     stream or None), pool)
 
 
-def kv_select_keep(scores: int, n: int, budget: int, keep: int, stream: int = 0):
-    _check("kv_select_keep", lib.kv_select_keep(scores, n, budget, keep, stream or None))
+def kv_select_workspace_size(n: int) -> int:
+    out = C.c_size_t(0)
+    _check("kv_select_workspace_size", lib.kv_select_workspace_size(n, C.byref(out)))
+    return out.value
+
+
+def kv_select_keep(scores: int, n: int, budget: int, keep: int, workspace: int, ws_bytes: int, stream: int = 0):
+    _check("kv_select_keep", lib.kv_select_keep(scores, n, budget, keep, workspace or None, ws_bytes, stream or None))
 
 
 def kv_drop_keep(pool: int, seq: int, keep: np.ndarray, flags: int = 0, stream: int = 0):
@@ -355,13 +362,16 @@ def dag_attn_run(q: int, out: int, lse: int, T: int, n_q_heads: int, n_kv_heads:
 
 
 # ------------------------------------------------------------------ packed DAG prefill
-def select_keep(scores, budget: int, keep=None):
+def select_keep(scores, budget: int, keep=None, workspace=None):
     """keep (uint8 tensor): 1 for the `budget` highest scores, ties to the lower index."""
     import torch
     n = scores.numel()
     if keep is None:
         keep = torch.empty(max(n, 1), dtype=torch.uint8, device=scores.device)[:n]
-    kv_select_keep(scores.data_ptr(), n, budget, keep.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    if workspace is None:
+        workspace = torch.empty(kv_select_workspace_size(n), dtype=torch.uint8, device=scores.device)
+    kv_select_keep(scores.data_ptr(), n, budget, keep.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                   torch.cuda.current_stream().cuda_stream)
     return keep
 
 

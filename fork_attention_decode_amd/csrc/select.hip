@@ -8,18 +8,26 @@
 //
 // score(t) = mean over the n_rep x Hq (representative query, head) pairs of the softmax
 // probability of own token t in that query's attention over the sequence's visible
-// context.  Two passes over the keys:
-//   1. the normalisers: the decode path (fork_attn_decode) over the representative
-//      queries gives each (query, head) its log-sum-exp over the whole visible context;
-//   2. score_kernel streams each own page's K block once per KV head and computes
-//      S = Q K^T for all of the head's rows (query x head-of-group) on
-//      v_mfma_f32_16x16x32_bf16 with the keys as N: each lane then holds one key, so the
-//      sum over rows of exp2(S c2 - lse2) stays in the lane plus two shuffles.
-// select_kernel: one workgroup, radix select of the budget-th largest score on an
-// order-preserving integer image of the floats (4 passes of 8 bits), then ties kept in
-// index order through a block-wide scan.
+// context.  Two passes over the keys, each streaming a page's K block once per KV head
+// and computing S = Q K^T for all of the head's rows (query x head-of-group) on
+// v_mfma_f32_16x16x32_bf16, a wave taking 4 pages at a time and issuing the MFMAs of one
+// 16-row tile beside the exponentials of the tile before:
+//   1. norm_kernel (keys as the A operand, so a lane holds 4 keys of one row): every lane
+//      keeps an online (max, sum) per row tile over the visible chunks (own pages, then
+//      mounts), rescaled lazily, reduced over the lanes and waves of the workgroup into
+//      one partial per row; norm_merge_kernel folds the workgroups' partials into each
+//      row's log2 normaliser;
+//   2. score_kernel (keys as B, so a lane holds one key of 4 rows): over the own pages,
+//      the sum over rows of exp2(S c2 - lse2) stays in the lane plus two shuffles.
+// Keep selection: radix select of the budget-th largest score on an order-preserving
+// integer image of the floats (4 passes of 8 bits over many workgroups), then ties kept
+// in index order (a slice's ties start after the earlier slices' count of the last
+// digit).
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
+#include <cstddef>
 #include <string>
 #include <vector>
 
@@ -40,77 +48,261 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxScoreRows = 256;  // representative queries x query heads per KV head
-constexpr int kPagesPerWg = 16;
+constexpr int kGroup = 4;           // chunks a wave takes at once
+constexpr int kChunksPerWg = 128;
+constexpr float kEmpty = -1e30f;    // running max of an empty (max, sum) state
 
 struct ScoreParams {
   const bf16_t* q;        // [n_rep][hq][D] representative queries (rotated)
-  const float* lse;       // [n_rep][hq] natural-log normalisers over the visible context
   const bf16_t* k_pages;  // pool K, head-major blocks
-  const int32_t* pages;   // own logical page -> page id [n_lp]
-  float* partial;         // [hkv][n_tok] per-KV-head sums over that head's rows
-  int32_t n_rep, hq, hkv, G, pool_pages, n_lp;
+  const int32_t* chunks;  // [n_ch][2]: page id, lo | hi << 8 (valid slots); own pages first
+  float* part;            // normaliser partials [hkv][RP][2][nx]: log2-domain max, sum
+  float* lse2;            // [hkv][RP] log2 normaliser of each row (+inf for padding rows)
+  float* partial;         // [hkv][n_tok] per-KV-head score sums over that head's rows
+  int32_t n_rep, hq, hkv, G, pool_pages, n_ch, n_lp, RP, nx;
   int64_t n_tok;
   float c2;  // sm_scale * log2(e)
 };
 
-// grid (ceil(n_lp / kPagesPerWg), hkv); rows of KV head h: r = rep * G + g (query head
-// h * G + g), padded with zero queries and +inf normalisers to whole 16-row tiles
+// stage the representative queries of KV head h in A-operand order: unit (row r, f, g)
+// = Q[r][32 f + 8 g .. + 8] at lane r % 16 + 16 g of tile r / 16; rows past R are zero
 template <int D>
-__global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
-  constexpr int NF = D / 32;  // 32-dim k-steps
-  __shared__ __attribute__((aligned(16))) char qa[kMaxScoreRows * D * 2];  // A fragments [tile][f][lane]
-  __shared__ __attribute__((aligned(16))) float lse2[kMaxScoreRows];
-  const int h = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ void stage_q(const ScoreParams& p, int h, int n_tiles, int row0, char* qa) {
+  constexpr int NF = D / 32;
   const int R = p.n_rep * p.G;
-  const int RT = (R + 15) / 16;
-  // stage Q in operand order: unit (row r, f, g) = Q[r][32 f + 8 g .. + 8] at lane r % 16 + 16 g
-  for (int u = threadIdx.x; u < RT * 16 * NF * 4; u += 256) {
+  for (int u = threadIdx.x; u < n_tiles * 16 * NF * 4; u += blockDim.x) {
     const int g = u & 3, f = (u >> 2) % NF, r = (u >> 2) / NF;
     i32x4 val = {0, 0, 0, 0};
-    if (r < R) {
-      const int rep = r / p.G, qh = h * p.G + r % p.G;
+    if (row0 + r < R) {
+      const int rep = (row0 + r) / p.G, qh = h * p.G + (row0 + r) % p.G;
       val = *reinterpret_cast<const i32x4*>(p.q + ((size_t)rep * p.hq + qh) * D + 32 * f + 8 * g);
     }
     *reinterpret_cast<i32x4*>(qa + (((r >> 4) * NF + f) * 64 + (r & 15) + 16 * g) * 16) = val;
   }
-  for (int r = threadIdx.x; r < RT * 16; r += 256) {
-    float v = INFINITY;  // padding rows and rows without visible keys add nothing
-    if (r < R) {
-      const float l = p.lse[(size_t)(r / p.G) * p.hq + h * p.G + r % p.G];
-      if (l > -INFINITY) v = l * 1.4426950408889634f;
+}
+
+// (m, l) <- the log-sum-exp union of (m, l) and (mo, lo); empty states are (kEmpty, 0)
+__device__ __forceinline__ void lse_combine(float& m, float& l, float mo, float lo) {
+  const float mn = fmaxf(m, mo);
+  l = l * __builtin_amdgcn_exp2f(m - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
+  m = mn;
+}
+
+// K fragments of the P chunks c .. c + P - 1 of KV head h (lane t + 16 g holds
+// K[t][32 f + 8 g .. + 8]); ch is the workgroup's chunk list in LDS, indexed from its
+// first chunk.  Chunks at or past n report an empty slot range and load chunk n - 1
+// again (an L2 hit), so the loads stay unconditional.
+template <int D, int P>
+__device__ __forceinline__ void load_group(const ScoreParams& p, const int* ch, int h, int c, int n, int lane,
+                                           bf16x8 (&kf)[P][D / 32], int (&lohi)[P]) {
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp) {
+    const int cc = min(c + pp, n - 1);
+    lohi[pp] = c + pp < n ? ch[2 * cc + 1] : 0;
+    const bf16_t* blk = p.k_pages + ((size_t)h * p.pool_pages + ch[2 * cc]) * 16 * D;
+#pragma unroll
+    for (int f = 0; f < D / 32; ++f)
+      kf[pp][f] = __builtin_bit_cast(
+          bf16x8, __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(blk + (f * 64 + lane) * 8)));
+  }
+}
+
+// S tiles of row tile T against the P chunks: keys as A (acc[pp][i] = key 4 (lane / 16) + i,
+// row 16 T + lane % 16) or keys as B (acc[pp][i] = row 16 T + 4 (lane / 16) + i, key
+// lane % 16)
+template <int D, int P, bool KeysA>
+__device__ __forceinline__ void s_tile(const char* qa, int T, int lane, const bf16x8 (&kf)[P][D / 32],
+                                       f32x4 (&acc)[P]) {
+  constexpr int NF = D / 32;
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const bf16x8 q = *reinterpret_cast<const bf16x8*>(qa + ((T * NF + f) * 64 + lane) * 16);
+#pragma unroll
+    for (int pp = 0; pp < P; ++pp)
+      acc[pp] = KeysA ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[pp][f], q, acc[pp], 0, 0, 0)
+                      : __builtin_amdgcn_mfma_f32_16x16x32_bf16(q, kf[pp][f], acc[pp], 0, 0, 0);
+  }
+}
+
+// all RT row tiles of one group: the MFMAs of tile T + 1 are issued beside the vector
+// work of tile T (one wave keeps both units busy), one tile step per scheduling region
+template <int D, int RT, int P, bool KeysA, class F>
+__device__ __forceinline__ void group_tiles(const char* qa, int lane, const bf16x8 (&kf)[P][D / 32], F&& valu) {
+  f32x4 acc[2][P];
+  s_tile<D, P, KeysA>(qa, 0, lane, kf, acc[0]);
+#pragma unroll
+  for (int T = 0; T < RT; ++T) {
+    if (T + 1 < RT) s_tile<D, P, KeysA>(qa, T + 1, lane, kf, acc[(T + 1) & 1]);
+    valu(T, acc[T & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// a wave's groups c0, c0 + 4 P, ... below n (indices into the LDS chunk list)
+template <int D, int P, class F>
+__device__ __forceinline__ void for_groups(const ScoreParams& p, const int* ch, int h, int c0, int n, int lane,
+                                           F&& body) {
+  for (int c = c0; c < n; c += 4 * P) {
+    bf16x8 kf[P][D / 32];
+    int lohi[P];
+    load_group<D, P>(p, ch, h, c, n, lane, kf, lohi);
+    body(c, kf, lohi);
+  }
+}
+
+// the workgroup's chunks C0 .. C1 - 1 into LDS
+__device__ __forceinline__ void stage_chunks(const ScoreParams& p, int C0, int C1, int* ch) {
+  for (int i = threadIdx.x; i < 2 * (C1 - C0); i += blockDim.x) ch[i] = p.chunks[2 * C0 + i];
+}
+
+// pass 1: grid (nx, hkv); RT 16-row tiles cover the head's rows row0 .. row0 + 16 RT.
+// The keys are the MFMA's A operand here (the pool's K block is laid out for either
+// side), so each lane holds 4 keys of one row per tile and keeps one (max, sum) per
+// tile.  Each wave takes groups of kGroup consecutive chunks: every Q fragment read
+// from LDS feeds kGroup MFMAs.
+template <int D, int RT>
+__global__ __launch_bounds__(256) void norm_kernel(ScoreParams p, int row0) {
+  constexpr int NF = D / 32, P = kGroup;
+  static_assert(RT <= 8, "row tiles per launch");
+  __shared__ __attribute__((aligned(16))) char qa[RT * 16 * D * 2];
+  __shared__ float red[4][2][RT * 16];
+  __shared__ int ch[2 * kChunksPerWg];
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int C0 = blockIdx.x * kChunksPerWg;
+  const int C1 = min(C0 + kChunksPerWg, p.n_ch);
+  stage_q<D>(p, h, RT, row0, qa);
+  stage_chunks(p, C0, C1, ch);
+  __syncthreads();
+  float m[RT], l[RT];
+#pragma unroll
+  for (int T = 0; T < RT; ++T) m[T] = kEmpty, l[T] = 0.f;
+  const int key0 = 4 * (lane >> 4);
+  const float c2 = p.c2;
+  for_groups<D, P>(p, ch, h, wave * P, C1 - C0, lane, [&](int c, const bf16x8(&kf)[P][NF], const int(&lohi)[P]) {
+    bool full = true;
+#pragma unroll
+    for (int pp = 0; pp < P; ++pp) full = full && lohi[pp] == (16 << 8);
+    group_tiles<D, RT, P, true>(qa, lane, kf, [&](int T, f32x4(&acc)[P]) {
+      // acc[pp][i]: key 4 (lane / 16) + i of chunk C0 + c + pp, row 16 T + lane % 16
+      if (!full) {
+#pragma unroll
+        for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool valid = key0 + i >= (lohi[pp] & 0xff) && key0 + i < (lohi[pp] >> 8);
+            acc[pp][i] = valid ? acc[pp][i] : -INFINITY;
+          }
+      }
+      // lazy rescale: the sum is taken against the running max as it stands, and only a
+      // lane whose keys reach 2^64 times that (the first keys, against an empty state)
+      // takes the max of the group and rescales
+      float sum = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[pp][i], c2, -m[T]));
+      if (sum <= 0x1p64f) {
+        l[T] += sum;
+      } else {
+        float mx = acc[0][0];
+#pragma unroll
+        for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[pp][i]);
+        const float mn = fmaxf(m[T], mx * c2);
+        sum = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[pp][i], c2, -mn));
+        l[T] = __builtin_fmaf(l[T], __builtin_amdgcn_exp2f(m[T] - mn), sum);
+        m[T] = mn;
+      }
+    });
+  });
+  // row 16 T + lane % 16 is held by the 4 lanes lane % 16 + 16 k
+#pragma unroll
+  for (int T = 0; T < RT; ++T) {
+    lse_combine(m[T], l[T], __shfl_xor(m[T], 16), __shfl_xor(l[T], 16));
+    lse_combine(m[T], l[T], __shfl_xor(m[T], 32), __shfl_xor(l[T], 32));
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int T = 0; T < RT; ++T) {
+      red[wave][0][16 * T + lane] = m[T];
+      red[wave][1][16 * T + lane] = l[T];
     }
-    lse2[r] = v;
   }
   __syncthreads();
+  for (int r = threadIdx.x; r < RT * 16; r += 256) {
+    float M = red[0][0][r], L = red[0][1][r];
+    for (int w = 1; w < 4; ++w) lse_combine(M, L, red[w][0][r], red[w][1][r]);
+    float* dst = p.part + ((size_t)(h * p.RP + row0 + r) * 2) * p.nx + blockIdx.x;
+    dst[0] = M;
+    dst[p.nx] = L;
+  }
+}
 
-  const int L0 = blockIdx.x * kPagesPerWg;
-  const int L1 = min(L0 + kPagesPerWg, p.n_lp);
-  for (int L = L0 + wave; L < L1; L += 4) {
-    const bf16_t* blk = p.k_pages + ((size_t)h * p.pool_pages + p.pages[L]) * 16 * D;
-    bf16x8 kf[NF];  // B operand: lane t + 16 g holds K[t][32 f + 8 g .. + 8]
+// one wave per (KV head, row): lanes stride over the nx workgroup partials
+__global__ __launch_bounds__(256) void norm_merge_kernel(ScoreParams p) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // h * RP + r
+  if (row >= p.hkv * p.RP) return;
+  const float* src = p.part + (size_t)row * 2 * p.nx;
+  float M = kEmpty, L = 0.f;
+  for (int x = lane; x < p.nx; x += 64) lse_combine(M, L, src[x], src[p.nx + x]);
 #pragma unroll
-    for (int f = 0; f < NF; ++f)
-      kf[f] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(blk + (f * 64 + lane) * 8)));
-    float s = 0.f;
-    for (int T = 0; T < RT; ++T) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int off = 1; off < 64; off <<= 1) lse_combine(M, L, __shfl_xor(M, off), __shfl_xor(L, off));
+  if (lane == 0) {
+    const bool pad = row % p.RP >= p.n_rep * p.G;
+    p.lse2[row] = (pad || L <= 0.f) ? INFINITY : M + __log2f(L);  // no visible key: adds nothing
+  }
+}
+
+// pass 2: grid (ceil(n_lp / kChunksPerWg), hkv) over the own pages (the first n_lp
+// chunks); rows of KV head h: r = rep * G + g (query head h * G + g), padded with zero
+// queries and +inf normalisers to RT whole 16-row tiles
+template <int D, int RT>
+__global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
+  constexpr int NF = D / 32, P = kGroup;
+  __shared__ __attribute__((aligned(16))) char qa[RT * 16 * D * 2];  // A fragments [tile][f][lane]
+  __shared__ __attribute__((aligned(16))) float lse2[RT * 16];
+  __shared__ int ch[2 * kChunksPerWg];
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int C0 = blockIdx.x * kChunksPerWg;
+  const int C1 = min(C0 + kChunksPerWg, p.n_lp);
+  stage_q<D>(p, h, RT, 0, qa);
+  stage_chunks(p, C0, C1, ch);
+  for (int r = threadIdx.x; r < RT * 16; r += 256) lse2[r] = p.lse2[h * p.RP + r];
+  __syncthreads();
+
+  const float c2 = p.c2;
+  for_groups<D, P>(p, ch, h, wave * P, C1 - C0, lane, [&](int c, const bf16x8(&kf)[P][NF], const int(&)[P]) {
+    float s[P];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(qa + ((T * NF + f) * 64 + lane) * 16);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[f], acc, 0, 0, 0);
-      }
-      // acc[i]: row 16 T + 4 (lane / 16) + i, key lane % 16
+    for (int pp = 0; pp < P; ++pp) s[pp] = 0.f;
+    group_tiles<D, RT, P, false>(qa, lane, kf, [&](int T, f32x4(&acc)[P]) {
+      // acc[pp][i]: row 16 T + 4 (lane / 16) + i, key lane % 16 of own page C0 + c + pp
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 16 * T + 4 * (lane >> 4));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], p.c2, -l4[i]));
+      for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[pp] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[pp][i], c2, -l4[i]));
+    });
+#pragma unroll
+    for (int pp = 0; pp < P; ++pp) {
+      float v = s[pp] + __shfl_xor(s[pp], 16);
+      v += __shfl_xor(v, 32);
+      const int64_t t = (int64_t)(C0 + c + pp) * 16 + lane;
+      if (lane < 16 && C0 + c + pp < C1 && t < p.n_tok) p.partial[(size_t)h * p.n_tok + t] = v;
     }
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    const int64_t t = (int64_t)L * 16 + lane;
-    if (lane < 16 && t < p.n_tok) p.partial[(size_t)h * p.n_tok + t] = s;
-  }
+  });
 }
 
 __global__ __launch_bounds__(256) void score_sum_kernel(const float* __restrict__ partial, float* __restrict__ scores,
@@ -122,67 +314,145 @@ __global__ __launch_bounds__(256) void score_sum_kernel(const float* __restrict_
   scores[t] = s * inv;
 }
 
-// order-preserving image of a float (NaN lowest)
+// order-preserving image of a float (NaN lowest; -0 and +0 equal)
 __device__ __forceinline__ uint32_t key_of(float x) {
   if (x != x) return 0u;
-  const uint32_t b = __float_as_uint(x);
+  const uint32_t b = __float_as_uint(x == 0.f ? 0.f : x);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// one workgroup of 1024 threads; 1 <= budget < n
-__global__ __launch_bounds__(1024) void select_kernel(const float* __restrict__ scores, int64_t n, int64_t budget,
-                                                      uint8_t* __restrict__ keep) {
-  __shared__ int64_t hist[256];
-  __shared__ uint32_t s_prefix;
-  __shared__ int64_t s_remaining;
-  __shared__ int64_t s_wave[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t prefix = 0, mask = 0;
-  int64_t remaining = budget;  // still to take among the keys that match prefix under mask
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = tid; b < 256; b += 1024) hist[b] = 0;
-    __syncthreads();
-    for (int64_t t = tid; t < n; t += 1024) {
-      const uint32_t u = key_of(scores[t]);
-      if ((u & mask) == prefix) atomicAdd((unsigned long long*)&hist[(u >> shift) & 255], 1ull);
+// Radix select over many workgroups with no atomics or fences between them: digit pass
+// k (one launch) writes every workgroup's 256-bin histogram of its slice as plain
+// stores, and each workgroup of the next launch first sums those histograms itself to
+// find digit k (all of them get the same answer; workgroup 0 also records it).
+struct SelState {
+  uint32_t prefix, remaining;  // after a digit: the key prefix and how many keys still to take
+};
+constexpr int kSelThreads = 1024;
+constexpr int kSelMaxWg = 256;
+constexpr int kSelPerWg = 4096;
+constexpr int kSelUnroll = 4;  // keys a thread loads before it histograms them
+
+struct SelWs {
+  uint32_t* hist;  // [4][n_wg][256]
+  SelState* st;    // [5]: st[k] after digit k - 1 (st[0] unused: the budget is an argument)
+};
+
+// digit k from the n_wg histograms of pass k under state `in`; returns the new state
+__device__ SelState sel_digit(const uint32_t* __restrict__ hist, int n_wg, SelState in, int shift,
+                              uint32_t* lds) {
+  __shared__ SelState s_out;
+  __shared__ uint32_t part[kSelThreads / 256][256];
+  const int tid = threadIdx.x, lane = tid & 63, bin = tid & 255, q = tid >> 8;
+  uint32_t c = 0;
+  for (int w = q; w < n_wg; w += kSelThreads / 256) c += hist[(size_t)w * 256 + bin];
+  part[q][bin] = c;
+  __syncthreads();
+  if (tid < 256) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < kSelThreads / 256; ++j) sum += part[j][tid];
+    lds[tid] = sum;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // lane l takes bins 255 - 4 l .. 252 - 4 l, so lanes run from the top bin down
+    uint32_t v[4], local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) local += (v[j] = lds[255 - 4 * lane - j]);
+    uint32_t incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
     }
-    __syncthreads();
-    if (tid == 0) {
-      int64_t above = 0;
-      int digit = 0;
-      for (int b = 255; b >= 0; --b) {
-        if (above + hist[b] >= remaining) {
-          digit = b;
+    const uint32_t excl = incl - local;
+    if (excl < in.remaining && incl >= in.remaining) {
+      uint32_t above = excl;
+      int digit = 255 - 4 * lane;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (above + v[j] >= in.remaining) {
+          digit = 255 - 4 * lane - j;
           break;
         }
-        above += hist[b];
+        above += v[j];
       }
-      s_prefix = prefix | ((uint32_t)digit << shift);
-      s_remaining = remaining - above;
+      s_out = SelState{in.prefix | ((uint32_t)digit << shift), in.remaining - above};
     }
-    __syncthreads();
-    prefix = s_prefix;
-    remaining = s_remaining;
-    mask |= 255u << shift;
   }
-  // prefix is the budget-th largest key; keep every larger key and the first `remaining`
-  // keys equal to it in index order
-  int64_t carry = 0;
-  for (int64_t base = 0; base < n; base += 1024) {
+  __syncthreads();
+  return s_out;
+}
+
+// pass k (shift 24 - 8 k): histogram of digit k over the slice's keys matching the prefix
+__global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float* __restrict__ scores, int64_t n,
+                                                              int64_t slice, SelWs ws, int n_wg, int k,
+                                                              uint32_t budget) {
+  __shared__ uint32_t hist[256];
+  const int shift = 24 - 8 * k;
+  SelState st{0u, budget};
+  if (k > 0) {
+    const SelState in = k == 1 ? st : ws.st[k - 1];
+    st = sel_digit(ws.hist + (size_t)(k - 1) * n_wg * 256, n_wg, in, shift + 8, hist);
+    if (blockIdx.x == 0 && threadIdx.x == 0) ws.st[k] = st;
+  }
+  const uint32_t mask = k == 0 ? 0u : ~0u << (shift + 8);
+  __syncthreads();
+  if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t t0 = (int64_t)blockIdx.x * slice, t1 = min(t0 + slice, n);
+  for (int64_t base = t0 + threadIdx.x; base < t1; base += kSelUnroll * kSelThreads) {
+    float v[kSelUnroll];
+#pragma unroll
+    for (int j = 0; j < kSelUnroll; ++j) {
+      const int64_t t = base + (int64_t)j * kSelThreads;
+      v[j] = t < t1 ? scores[t] : __builtin_nanf("");
+    }
+#pragma unroll
+    for (int j = 0; j < kSelUnroll; ++j) {
+      const uint32_t u = key_of(v[j]);
+      if (base + (int64_t)j * kSelThreads < t1 && (u & mask) == st.prefix) atomicAdd(&hist[(u >> shift) & 255], 1u);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 256) ws.hist[((size_t)k * n_wg + blockIdx.x) * 256 + threadIdx.x] = hist[threadIdx.x];
+}
+
+// the last digit, then: keep every key above the prefix and the first `remaining` keys
+// equal to it in index order (a slice's ties start after those of the slices before
+// it: its count of the last digit in the last pass)
+__global__ __launch_bounds__(kSelThreads) void sel_write_kernel(const float* __restrict__ scores, int64_t n,
+                                                               int64_t slice, SelWs ws, int n_wg,
+                                                               uint8_t* __restrict__ keep) {
+  __shared__ uint32_t lds[256];
+  __shared__ uint32_t s_wave[kSelThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t* h3 = ws.hist + (size_t)3 * n_wg * 256;
+  const SelState st = sel_digit(h3, n_wg, ws.st[3], 0, lds);
+  if (blockIdx.x == 0 && tid == 0) ws.st[4] = st;
+  const uint32_t prefix = st.prefix, remaining = st.remaining;
+  uint32_t b = 0;
+  for (int w = tid; w < (int)blockIdx.x; w += kSelThreads) b += h3[(size_t)w * 256 + (prefix & 255)];
+  for (int off = 32; off > 0; off >>= 1) b += __shfl_xor(b, off);
+  if (lane == 0) s_wave[wave] = b;
+  __syncthreads();
+  uint32_t carry = 0;
+  for (int w = 0; w < kSelThreads / 64; ++w) carry += s_wave[w];
+  const int64_t t0 = (int64_t)blockIdx.x * slice, t1 = min(t0 + slice, n);
+  for (int64_t base = t0; base < t1; base += kSelThreads) {
     const int64_t t = base + tid;
-    const uint32_t u = t < n ? key_of(scores[t]) : 0u;
-    const bool tie = t < n && u == prefix;
+    const uint32_t u = t < t1 ? key_of(scores[t]) : 0u;
+    const bool tie = t < t1 && u == prefix;
     const uint64_t bal = __ballot(tie);
-    const int64_t before = __popcll(bal & ((1ull << lane) - 1ull));
+    const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
+    __syncthreads();  // every read of s_wave from the step before is done
     if (lane == 0) s_wave[wave] = __popcll(bal);
     __syncthreads();
-    int64_t wave_base = carry;
+    uint32_t wave_base = carry;
     for (int w = 0; w < wave; ++w) wave_base += s_wave[w];
-    if (t < n) keep[t] = (u > prefix || (tie && wave_base + before < remaining)) ? 1 : 0;
-    int64_t total = 0;
-    for (int w = 0; w < 16; ++w) total += s_wave[w];
-    carry += total;
-    __syncthreads();
+    if (t < t1) keep[t] = (u > prefix || (tie && wave_base + before < remaining)) ? 1 : 0;
+    for (int w = 0; w < kSelThreads / 64; ++w) carry += s_wave[w];
   }
 }
 
@@ -194,43 +464,92 @@ __global__ __launch_bounds__(256) void fill_kernel(uint8_t* __restrict__ keep, i
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct ScoreLayout {
-  size_t dec, out, lse, pages, partial, total;
+  size_t chunks, part, lse2, partial, total;
 };
 
-}  // namespace
 
-extern "C" {
+// visible chunks of the sequence: own pages (lo 0, hi the page's fill), then mounted runs
+static std::vector<int32_t> score_chunks(const Seq* S, int64_t PS) {
+  std::vector<int32_t> c;
+  c.reserve(2 * S->pages.size());
+  for (size_t L = 0; L < S->pages.size(); ++L) {
+    c.push_back(S->pages[L]);
+    c.push_back((int32_t)std::min<int64_t>(PS, S->n - (int64_t)L * PS) << 8);
+  }
+  for (const Mount& m : S->mounts)
+    for (size_t j = 0; j < m.pages.size(); ++j) {
+      const int64_t a = std::max<int64_t>(0, m.off - (int64_t)j * PS);
+      const int64_t b = std::min<int64_t>(PS, m.off + m.n - (int64_t)j * PS);
+      if (a < b) {
+        c.push_back(m.pages[j]);
+        c.push_back((int32_t)(a | b << 8));
+      }
+    }
+  return c;
+}
+
+// rows per KV head padded to 16 x a power of two (the normaliser's tile count)
+static int32_t score_tiles(int32_t rows) {
+  int32_t t = 1;
+  while (16 * t < rows) t *= 2;
+  return t;
+}
 
 static int score_layout(kv_pool_t* P, kv_seq_t seq, int32_t n_rep, int32_t hq, ScoreLayout* w, int64_t* n_tok,
-                        int32_t* n_lp) {
+                        int32_t* n_ch) {
   if (!P) FAIL(P, KV_ERR_INVALID, "null pool");
   Seq* S = fa_seq(P, seq);
   if (!S) FAIL(P, KV_ERR_NOT_FOUND, "no live sequence");
   const int32_t hkv = P->cfg.n_kv_heads;
   if (n_rep < 1 || hq < hkv || hq % hkv) FAIL(P, KV_ERR_INVALID, "bad representative query shape");
-  if (n_rep * (hq / hkv) > kMaxScoreRows)
+  if ((int64_t)n_rep * (hq / hkv) > kMaxScoreRows)
     FAIL(P, KV_ERR_UNSUPPORTED, "at most 256 representative rows (queries x query heads) per KV head");
-  std::vector<kv_seq_t> seqs((size_t)n_rep, seq);
-  size_t dec = 0;
-  if (int st = fork_attn_workspace_size(P, seqs.data(), n_rep, hq, &dec)) return st;
-  const size_t es = P->cfg.dtype == KV_F32 ? 4 : 2;
-  w->dec = 0;
-  w->out = align256(dec);
-  w->lse = align256(w->out + (size_t)n_rep * hq * P->cfg.head_dim * es);
-  w->pages = align256(w->lse + (size_t)n_rep * hq * 4);
-  w->partial = align256(w->pages + S->pages.size() * 4);
+  int64_t ch = (int64_t)S->pages.size();
+  for (const Mount& m : S->mounts) ch += (int64_t)m.pages.size();
+  if (ch > INT32_MAX / 2) FAIL(P, KV_ERR_INVALID, "too many visible pages");
+  const int64_t RP = 16 * score_tiles(n_rep * (hq / hkv));
+  const int64_t nx = (ch + kChunksPerWg - 1) / kChunksPerWg;
+  w->chunks = 0;
+  w->part = align256((size_t)ch * 8);
+  w->lse2 = align256(w->part + (size_t)hkv * RP * 2 * std::max<int64_t>(nx, 1) * 4);
+  w->partial = align256(w->lse2 + (size_t)hkv * RP * 4);
   w->total = w->partial + (size_t)hkv * S->n * 4;
   *n_tok = S->n;
-  *n_lp = (int32_t)S->pages.size();
+  *n_ch = (int32_t)ch;  // an upper bound: mount pages outside the mounted run add no chunk
   return KV_OK;
 }
+
+template <int D>
+static void launch_score(const ScoreParams& p, int RT, hipStream_t stream) {
+  const dim3 ngrid(p.nx, p.hkv);
+  switch (RT) {  // more than 8 tiles (128 rows) would spill: one launch per 128 rows
+    case 1: norm_kernel<D, 1><<<ngrid, 256, 0, stream>>>(p, 0); break;
+    case 2: norm_kernel<D, 2><<<ngrid, 256, 0, stream>>>(p, 0); break;
+    case 4: norm_kernel<D, 4><<<ngrid, 256, 0, stream>>>(p, 0); break;
+    default:
+      for (int r0 = 0; r0 < 16 * RT; r0 += 128) norm_kernel<D, 8><<<ngrid, 256, 0, stream>>>(p, r0);
+  }
+  norm_merge_kernel<<<(p.hkv * p.RP + 3) / 4, 256, 0, stream>>>(p);
+  const dim3 sgrid((p.n_lp + kChunksPerWg - 1) / kChunksPerWg, p.hkv);
+  switch (RT) {
+    case 1: score_kernel<D, 1><<<sgrid, 256, 0, stream>>>(p); break;
+    case 2: score_kernel<D, 2><<<sgrid, 256, 0, stream>>>(p); break;
+    case 4: score_kernel<D, 4><<<sgrid, 256, 0, stream>>>(p); break;
+    case 8: score_kernel<D, 8><<<sgrid, 256, 0, stream>>>(p); break;
+    default: score_kernel<D, 16><<<sgrid, 256, 0, stream>>>(p); break;
+  }
+}
+
+}  // namespace
+
+extern "C" {
 
 int kv_score_workspace_size(kv_pool_t* P, kv_seq_t seq, int32_t n_rep, int32_t n_q_heads, size_t* bytes) {
   if (!bytes) FAIL(P, KV_ERR_INVALID, "null bytes");
   ScoreLayout w;
   int64_t n_tok;
-  int32_t n_lp;
-  if (int st = score_layout(P, seq, n_rep, n_q_heads, &w, &n_tok, &n_lp)) return st;
+  int32_t n_ch;
+  if (int st = score_layout(P, seq, n_rep, n_q_heads, &w, &n_tok, &n_ch)) return st;
   *bytes = w.total;
   return KV_OK;
 }
@@ -239,8 +558,8 @@ int kv_score(kv_pool_t* P, kv_seq_t seq, const void* q_rep, int32_t n_rep, int32
              float* scores, void* workspace, size_t ws_bytes, hipStream_t stream) {
   ScoreLayout w;
   int64_t n_tok;
-  int32_t n_lp;
-  if (int st = score_layout(P, seq, n_rep, n_q_heads, &w, &n_tok, &n_lp)) return st;
+  int32_t n_ch_max;
+  if (int st = score_layout(P, seq, n_rep, n_q_heads, &w, &n_tok, &n_ch_max)) return st;
   if (!P->device) FAIL(P, KV_ERR_INVALID, "metadata-only pool has no KV data");
   if (P->cfg.dtype != KV_BF16 || (P->cfg.head_dim != 64 && P->cfg.head_dim != 128))
     FAIL(P, KV_ERR_UNSUPPORTED, "key scoring needs a bf16 pool with head_dim 64 or 128");
@@ -249,33 +568,33 @@ int kv_score(kv_pool_t* P, kv_seq_t seq, const void* q_rep, int32_t n_rep, int32
   if (ws_bytes < w.total) FAIL(P, KV_ERR_WORKSPACE, "score workspace too small");
   if (n_tok == 0) return KV_OK;
   char* ws = static_cast<char*>(workspace);
-  float* lse = reinterpret_cast<float*>(ws + w.lse);
-  std::vector<kv_seq_t> seqs((size_t)n_rep, seq);
-  if (int st = fork_attn_decode(P, seqs.data(), n_rep, n_q_heads, q_rep, ws + w.out, lse, sm_scale, ws + w.dec,
-                                w.out - w.dec, stream))
-    return st;
   Seq* S = fa_seq(P, seq);
-  hipError_t e = fa_upload(P, ws + w.pages, S->pages.data(), (size_t)n_lp * 4, stream);
-  if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("score page upload: ") + hipGetErrorString(e));
+  const std::vector<int32_t> chunks = score_chunks(S, P->cfg.page_size);
+  hipError_t e = fa_upload(P, ws + w.chunks, chunks.data(), chunks.size() * 4, stream);
+  if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("score chunk upload: ") + hipGetErrorString(e));
   ScoreParams p;
   p.q = static_cast<const bf16_t*>(q_rep);
-  p.lse = lse;
   p.k_pages = static_cast<const bf16_t*>(P->k);
-  p.pages = reinterpret_cast<const int32_t*>(ws + w.pages);
+  p.chunks = reinterpret_cast<const int32_t*>(ws + w.chunks);
+  p.part = reinterpret_cast<float*>(ws + w.part);
+  p.lse2 = reinterpret_cast<float*>(ws + w.lse2);
   p.partial = reinterpret_cast<float*>(ws + w.partial);
   p.n_rep = n_rep;
   p.hq = n_q_heads;
   p.hkv = P->cfg.n_kv_heads;
   p.G = n_q_heads / p.hkv;
   p.pool_pages = P->cfg.n_pages;
-  p.n_lp = n_lp;
+  p.n_ch = (int32_t)(chunks.size() / 2);
+  p.n_lp = (int32_t)S->pages.size();
+  const int RT = score_tiles(n_rep * p.G);
+  p.RP = 16 * RT;
+  p.nx = (p.n_ch + kChunksPerWg - 1) / kChunksPerWg;
   p.n_tok = n_tok;
   p.c2 = sm_scale * 1.4426950408889634f;
-  const dim3 grid((n_lp + kPagesPerWg - 1) / kPagesPerWg, p.hkv);
   if (P->cfg.head_dim == 128)
-    score_kernel<128><<<grid, 256, 0, stream>>>(p);
+    launch_score<128>(p, RT, stream);
   else
-    score_kernel<64><<<grid, 256, 0, stream>>>(p);
+    launch_score<64>(p, RT, stream);
   score_sum_kernel<<<(unsigned)((n_tok + 255) / 256), 256, 0, stream>>>(p.partial, scores, n_tok, p.hkv,
                                                                          1.f / (float)(n_rep * n_q_heads));
   e = hipGetLastError();
@@ -283,14 +602,43 @@ int kv_score(kv_pool_t* P, kv_seq_t seq, const void* q_rep, int32_t n_rep, int32
   return KV_OK;
 }
 
-int kv_select_keep(const float* scores, int64_t n, int64_t budget, uint8_t* keep, hipStream_t stream) {
+static int64_t sel_slice(int64_t n, int32_t* n_wg) {
+  const int64_t wg = std::max<int64_t>(1, std::min<int64_t>(kSelMaxWg, (n + kSelPerWg - 1) / kSelPerWg));
+  const int64_t slice = ((n + wg - 1) / wg + kSelThreads - 1) / kSelThreads * kSelThreads;
+  *n_wg = (int32_t)((n + slice - 1) / slice);
+  return slice;
+}
+
+static size_t sel_ws_bytes(int32_t n_wg) { return 256 + (size_t)4 * n_wg * 256 * 4; }
+
+int kv_select_workspace_size(int64_t n, size_t* bytes) {
+  if (!bytes || n < 0) return fa_set_err(nullptr, KV_ERR_INVALID, "bad select size query");
+  int32_t n_wg = 1;
+  if (n > 0) sel_slice(n, &n_wg);
+  *bytes = sel_ws_bytes(n_wg);
+  return KV_OK;
+}
+
+int kv_select_keep(const float* scores, int64_t n, int64_t budget, uint8_t* keep, void* workspace, size_t ws_bytes,
+                   hipStream_t stream) {
   if (n < 0) return fa_set_err(nullptr, KV_ERR_INVALID, "negative count");
+  if (n > INT32_MAX) return fa_set_err(nullptr, KV_ERR_UNSUPPORTED, "at most 2^31 - 1 scores");
   if (n == 0) return KV_OK;
   if (!scores || !keep) return fa_set_err(nullptr, KV_ERR_INVALID, "null pointer");
-  if (budget <= 0 || budget >= n)
+  if (budget <= 0 || budget >= n) {
     fill_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(keep, n, budget <= 0 ? 0 : 1);
-  else
-    select_kernel<<<1, 1024, 0, stream>>>(scores, n, budget, keep);
+  } else {
+    int32_t n_wg;
+    const int64_t slice = sel_slice(n, &n_wg);
+    if (!workspace) return fa_set_err(nullptr, KV_ERR_INVALID, "null workspace");
+    if (ws_bytes < sel_ws_bytes(n_wg)) return fa_set_err(nullptr, KV_ERR_WORKSPACE, "select workspace too small");
+    SelWs w;
+    w.st = static_cast<SelState*>(workspace);
+    w.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + 256);
+    for (int k = 0; k < 4; ++k)
+      sel_hist_kernel<<<n_wg, kSelThreads, 0, stream>>>(scores, n, slice, w, n_wg, k, (uint32_t)budget);
+    sel_write_kernel<<<n_wg, kSelThreads, 0, stream>>>(scores, n, slice, w, n_wg, keep);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("select launch: ") + hipGetErrorString(e));
   return KV_OK;

@@ -281,18 +281,23 @@ int dag_attn_run(const void* q, void* out, float* lse, int32_t T, int32_t n_q_he
  * sm_scale * q.k).  q_rep: device, pool dtype, [n_rep][n_q_heads][head_dim], rotated by
  * the caller.  scores: device float [n_tokens].  Needs a device bf16 pool (head_dim 64 or
  * 128; KV_ERR_UNSUPPORTED otherwise) and n_rep * n_q_heads / Hkv <= 256.  The workspace
- * (kv_score_workspace_size bytes, caller-owned device memory) holds a decode over the
- * representative queries (their normalisers) and per-KV-head partial sums; it replaces
- * the pool's cached decode plan.  Stream-ordered; scores are valid once the stream has
- * run the call. */
+ * (kv_score_workspace_size bytes, caller-owned device memory) holds the visible chunk
+ * list, the per-row normalisers and per-KV-head partial sums; the pool's cached decode
+ * plan is left alone.  Stream-ordered; scores are valid once the stream has run the
+ * call. */
 int kv_score_workspace_size(kv_pool_t* pool, kv_seq_t seq, int32_t n_rep, int32_t n_q_heads, size_t* bytes);
 int kv_score(kv_pool_t* pool, kv_seq_t seq, const void* q_rep, int32_t n_rep, int32_t n_q_heads, float sm_scale,
              float* scores, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* keep[t] = 1 for the `budget` highest scores (ties to the lower index), 0 for the rest;
- * budget <= 0 keeps nothing, budget >= n keeps everything.  scores: device float [n];
- * keep: device uint8 [n].  No workspace; stream-ordered. */
-int kv_select_keep(const float* scores, int64_t n, int64_t budget, uint8_t* keep, hipStream_t stream);
+ * budget <= 0 keeps nothing, budget >= n keeps everything.  scores: device float [n],
+ * n <= 2^31 - 1 (KV_ERR_UNSUPPORTED above); keep: device uint8 [n].  workspace:
+ * caller-owned device memory of kv_select_workspace_size(n) bytes (at most 1 MiB + 256), used
+ * by the calls on `stream` only: two calls in flight on different streams need two
+ * workspaces.  A NaN score ranks below every number.  Stream-ordered. */
+int kv_select_workspace_size(int64_t n, size_t* bytes);
+int kv_select_keep(const float* scores, int64_t n, int64_t budget, uint8_t* keep, void* workspace, size_t ws_bytes,
+                   hipStream_t stream);
 
 /* Drop the tokens whose keep entry is 0: kv_drop with the maximal spans of zeros.  keep:
  * HOST uint8 [n], n = the sequence's n_tokens (copy the device mask back first: the page

@@ -89,6 +89,27 @@ def test_select_keep_exact(n):
         assert np.array_equal(got, want), f"n={n} budget={budget}: {int((got != want).sum())} entries differ"
 
 
+@pytest.mark.parametrize("kind", ["all_equal", "signed_zeros"])
+def test_select_keep_ties_across_slices(kind):
+    # the threshold's ties span many workgroup slices and must still go in index order
+    import torch
+    import fork_attention_decode_amd as fa
+    from oracle import select as sel
+    rng = np.random.default_rng(51)
+    if kind == "all_equal":
+        n = 300_001
+        sc = np.full(n, 0.25, np.float32)
+    else:
+        n = 70_001
+        sc = rng.choice(np.array([-1.5, -0.0, 0.0, 0.5, 2.0], np.float32), size=n)
+    t = torch.from_numpy(sc).cuda()
+    for budget in (1, n // 2, n - 1):
+        print(f"[case] select {kind} n={n} budget={budget}", flush=True)
+        got = fa.select_keep(t, budget).cpu().numpy().astype(bool)
+        want = sel.select_keep(sc.astype(np.float64), budget)
+        assert np.array_equal(got, want), f"{kind} budget={budget}: {int((got != want).sum())} entries differ"
+
+
 @pytest.mark.parametrize("repos", [True, False])
 def test_select_drop_then_decode(repos):
     import torch
