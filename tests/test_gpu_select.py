@@ -1,12 +1,15 @@
 """GPU parity of key scoring (kv_score), keep selection (kv_select_keep) and the drop that
 follows (kv_drop_keep), against the fp64 oracle (oracle/select.py).
 
-Bars: scores within 1e-2 relative (+1e-9 absolute) of the fp64 scores: each probability
-is exp2(s c2 - lse2) with the normaliser from the decode path, whose LSE is held to 2e-3
-absolute, i.e. ~2e-3 relative on every probability; the fp32 dot products add ~1e-6.
-Keep masks are bit-exact against the oracle's selection applied to the GPU's own fp32
-scores (the decision is taken in the same precision on both sides).  After the drop, the
-page table is bit-exact and the decode is within the decode bars.
+Bars: scores within 2e-4 relative (+1e-9 absolute) of the fp64 scores, from the fp32
+arithmetic on the same bf16 inputs: each probability is exp2(s c2 - lse2); the exponent
+s c2 is a 128-term fp32 dot product of exact bf16 products (worst case 128 u times
+sum |q_i k_i| c2 ~ 10, i.e. ~8e-5 absolute in log2 units), and the normaliser is a sum
+of at most a few thousand terms per lane merged in a shallow tree (~1e-5 relative), so
+each probability, and their mean, is within ~1e-4 relative; measured errors are below
+1e-6.  Keep masks are bit-exact against the oracle's selection applied to the GPU's own
+fp32 scores (the decision is taken in the same precision on both sides).  After the
+drop, the page table is bit-exact and the decode is within the decode bars.
 """
 import numpy as np
 import pytest
@@ -16,7 +19,7 @@ from tests.harness import build_device_pool, check_close, oracle_decode, out_to_
 
 pytestmark = pytest.mark.gpu
 
-REL, ABS = 1e-2, 1e-9
+REL, ABS = 2e-4, 1e-9
 
 
 def _q_rep(n_rep, hq, d, seed):
