@@ -88,6 +88,9 @@ _SIGS = {
                          _sz, _P],
     "dag_attn_prepare": [_P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, C.c_int64, _i32, _P, _sz, _P],
     "dag_attn_run": [_P, _P, _P, _i32, _i32, _i32, _i32, _P, C.c_int64, _i32, C.c_float, _P, _sz, _P],
+    "dag_attn_backward_workspace_size": [_i32, _i32, _i32, _i32, C.c_int64, _psz],
+    "dag_attn_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, C.c_int64, _i32,
+                          C.c_float, _P, _sz, _P],
     "kv_score_workspace_size": [_P, _i32, _i32, _i32, _psz],
     "kv_score": [_P, _i32, _P, _i32, _i32, C.c_float, _P, _P, _sz, _P],
     "kv_select_workspace_size": [C.c_int64, _psz],
@@ -361,6 +364,21 @@ def dag_attn_run(q: int, out: int, lse: int, T: int, n_q_heads: int, n_kv_heads:
                                             sm_scale, workspace or None, ws_bytes, stream or None))
 
 
+def dag_attn_backward_workspace_size(T: int, n_q_heads: int, n_kv_heads: int, block: int, nnz: int) -> int:
+    out = C.c_size_t(0)
+    _check("dag_attn_backward_workspace_size",
+           lib.dag_attn_backward_workspace_size(T, n_q_heads, n_kv_heads, block, nnz, C.byref(out)))
+    return out.value
+
+
+def dag_attn_backward(q: int, k: int, v: int, out: int, dout: int, lse: int, dq: int, dk: int, dv: int, T: int,
+                      n_q_heads: int, n_kv_heads: int, head_dim: int, row_ptr: int, col: int, kind: int, nnz: int,
+                      block: int, sm_scale: float, workspace: int, ws_bytes: int, stream: int = 0):
+    _check("dag_attn_backward", lib.dag_attn_backward(q, k, v, out, dout, lse, dq, dk, dv, T, n_q_heads, n_kv_heads,
+                                                      head_dim, row_ptr, col, kind, nnz, block, sm_scale,
+                                                      workspace or None, ws_bytes, stream or None))
+
+
 # ------------------------------------------------------------------ packed DAG prefill
 def select_keep(scores, budget: int, keep=None, workspace=None):
     """keep (uint8 tensor): 1 for the `budget` highest scores, ties to the lower index."""
@@ -408,6 +426,29 @@ def prefill(q, k, v, mask: DagMask, sm_scale: float, out=None, lse=None, workspa
                      mask.block, sm_scale, workspace.data_ptr(), workspace.numel(),
                      torch.cuda.current_stream().cuda_stream)
     return out, lse
+
+
+def prefill_backward(q, k, v, out, dout, lse, mask: DagMask, sm_scale: float, workspace=None):
+    """Gradients of `prefill` over `mask`: q / out / dout [T, Hq, 128], k / v [T, Hkv, 128]
+    bf16, lse [Hq, T] fp32 from the forward.  Returns (dq [T, Hq, 128], dk, dv [T, Hkv,
+    128]) fp32."""
+    import torch
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    for t in (q, k, v, out, dout, lse):
+        assert t.is_contiguous()
+    assert T == mask.T and q.dtype == torch.bfloat16 and dout.dtype == torch.bfloat16 and lse.dtype == torch.float32
+    dq = torch.empty((T, hq, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((T, hkv, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty((T, hkv, d), dtype=torch.float32, device=q.device)
+    need = dag_attn_backward_workspace_size(T, hq, hkv, mask.block, mask.nnz)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    dag_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), T, hq, hkv, d, mask.row_ptr.data_ptr(),
+                      mask.col.data_ptr(), mask.kind.data_ptr(), mask.nnz, mask.block, sm_scale,
+                      workspace.data_ptr(), workspace.numel(), torch.cuda.current_stream().cuda_stream)
+    return dq, dk, dv
 
 
 # ------------------------------------------------------------------ torch-backed holder

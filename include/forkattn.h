@@ -267,6 +267,32 @@ int dag_attn_run(const void* q, void* out, float* lse, int32_t T, int32_t n_q_he
                  int32_t block, float sm_scale, const void* workspace, size_t ws_bytes,
                  hipStream_t stream);
 
+/* Gradients of dag_attn_prefill over the same CSR (Octopus "Packed DAG-GRPO": the packed
+ * episode is trained through the same block-sparse attention, so only DAG-visible pairs
+ * carry gradient).  For query head h (KV head g = h / (Hq / Hkv)) and a visible pair
+ * (i, j): P_ij = exp(sm_scale q_i.k_j - lse_i), D_i = dout_i.out_i,
+ * dS_ij = P_ij (dout_i.v_j - D_i); dq_i = sm_scale sum_j dS_ij k_j,
+ * dk_j = sm_scale sum over the group's heads and i of dS_ij q_i,
+ * dv_j = sum over the group's heads and i of P_ij dout_i.
+ *   q, out, dout: DEVICE bf16 [T][Hq][d]; k, v: DEVICE bf16 [T][Hkv][d]; lse: DEVICE fp32
+ *   [Hq][T], natural log, as written by the forward (out and lse must be the forward's
+ *   outputs for these q, k, v and mask).  dq: DEVICE fp32 [T][Hq][d]; dk, dv: DEVICE
+ *   fp32 [T][Hkv][d]; every element is written (keys no query sees get 0).
+ *   row_ptr / col / kind: DEVICE CSR as for the forward (entries whose column is
+ *   outside [0, nb) are skipped).  workspace: DEVICE, at least
+ *   dag_attn_backward_workspace_size() bytes (per 64-token block and query head a 66,048 B
+ *   record of Q / dout images, per block and KV head a 49,152 B record of K / V images,
+ *   and the mask's transpose).
+ * Errors as for dag_attn_prefill (d = 128, block = 64).  Stream-ordered. */
+int dag_attn_backward_workspace_size(int32_t T, int32_t n_q_heads, int32_t n_kv_heads,
+                                     int32_t block, int64_t nnz, size_t* bytes);
+int dag_attn_backward(const void* q, const void* k, const void* v, const void* out,
+                      const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                      int32_t T, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                      const int32_t* row_ptr, const int32_t* col, const uint8_t* kind,
+                      int64_t nnz, int32_t block, float sm_scale, void* workspace,
+                      size_t ws_bytes, hipStream_t stream);
+
 /* ---- errors ---- */
 /* ---- key scoring and keep selection in front of Drop ----
  * AgentKV (rit.work), section "Как AgentKV выбирает и освобождает записи кэша": before a

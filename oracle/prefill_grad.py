@@ -15,6 +15,11 @@ For query head h (KV head g = h // G), scale c, and a visible pair (i, j):
   dv_j = sum_{h in g} sum_i P_ij do_i.
 Reading: o_i and lse_i are the oracle's own fp64 forward values (the library takes the
 caller's forward outputs instead; they differ by the forward's rounding).
+
+The `magnitudes` forms return, beside each gradient, the same sums taken over the
+magnitudes of their terms, |dS_ij| + P_ij d_i with d_i = sum_d |do_i o_i| for dq and dk
+and P_ij for dv: a rounding of relative size u in every term of a gradient's sum (or in
+D_i) moves it by at most u times that magnitude.
 """
 from __future__ import annotations
 
@@ -24,12 +29,14 @@ from oracle.prefill import _segment_of, visible_mask_row
 
 
 def _row(q, k, v, do, segments, edges, scale, i, seg_of):
-    """Per-row quantities for query i over its visible keys: (idx, P [Hq, n], dS [Hq, n])."""
+    """Per-row quantities for query i over its visible keys: (idx, P [Hq, n], dS [Hq, n],
+    W [Hq, n] = |dS| + P sum_d |do_i o_i|)."""
     T, hq, d = q.shape
     g = hq // k.shape[1]
     idx = np.nonzero(visible_mask_row(segments, edges, T, int(i), seg_of))[0]
     P = np.zeros((hq, len(idx)))
     dS = np.zeros((hq, len(idx)))
+    W = np.zeros((hq, len(idx)))
     for h in range(hq):
         kk, vv = k[idx, h // g, :], v[idx, h // g, :]
         s = scale * (kk @ q[i, h])
@@ -40,38 +47,46 @@ def _row(q, k, v, do, segments, edges, scale, i, seg_of):
         dp = vv @ do[i, h]
         P[h] = p
         dS[h] = p * (dp - float(do[i, h] @ o))
-    return idx, P, dS
+        W[h] = np.abs(dS[h]) + p * float(np.abs(do[i, h] * o).sum())
+    return idx, P, dS, W
 
 
-def grads(q, k, v, do, segments, edges, scale: float):
+def grads(q, k, v, do, segments, edges, scale: float, magnitudes: bool = False):
     """Full gradients (small T): q [T, Hq, d], k/v [T, Hkv, d], do [T, Hq, d] (fp64) ->
-    dq [T, Hq, d], dk [T, Hkv, d], dv [T, Hkv, d]."""
+    dq [T, Hq, d], dk [T, Hkv, d], dv [T, Hkv, d] (then their magnitudes, if asked)."""
     T, hq, d = q.shape
     g = hq // k.shape[1]
     seg_of = _segment_of(segments, T)
     dq = np.zeros_like(q, dtype=np.float64)
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)
+    mq, mk, mv = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
     for i in range(T):
-        idx, P, dS = _row(q, k, v, do, segments, edges, scale, i, seg_of)
+        idx, P, dS, W = _row(q, k, v, do, segments, edges, scale, i, seg_of)
         for h in range(hq):
             dq[i, h] = scale * (dS[h] @ k[idx, h // g, :])
             dk[idx, h // g, :] += scale * np.outer(dS[h], q[i, h])
             dv[idx, h // g, :] += np.outer(P[h], do[i, h])
-    return dq, dk, dv
+            if magnitudes:
+                mq[i, h] = scale * (W[h] @ np.abs(k[idx, h // g, :]))
+                mk[idx, h // g, :] += scale * np.outer(W[h], np.abs(q[i, h]))
+                mv[idx, h // g, :] += np.outer(P[h], np.abs(do[i, h]))
+    return (dq, dk, dv, mq, mk, mv) if magnitudes else (dq, dk, dv)
 
 
 def dq_rows(q, k, v, do, segments, edges, scale: float, rows):
-    """dq for the listed query rows only -> [len(rows), Hq, d]."""
+    """dq for the listed query rows only -> ([len(rows), Hq, d], its magnitudes)."""
     T, hq, d = q.shape
     g = hq // k.shape[1]
     seg_of = _segment_of(segments, T)
     out = np.zeros((len(rows), hq, d))
+    mag = np.zeros((len(rows), hq, d))
     for r, i in enumerate(rows):
-        idx, _, dS = _row(q, k, v, do, segments, edges, scale, i, seg_of)
+        idx, _, dS, W = _row(q, k, v, do, segments, edges, scale, i, seg_of)
         for h in range(hq):
             out[r, h] = scale * (dS[h] @ k[idx, h // g, :])
-    return out
+            mag[r, h] = scale * (W[h] @ np.abs(k[idx, h // g, :]))
+    return out, mag
 
 
 def seen_by(segments, edges, T: int, j: int) -> np.ndarray:
@@ -101,22 +116,24 @@ def seen_by(segments, edges, T: int, j: int) -> np.ndarray:
 
 
 def dkdv_keys(q, k, v, do, segments, edges, scale: float, keys):
-    """dk, dv for the listed keys only -> [len(keys), Hkv, d] each; each key's gradient
-    sums over the queries that see it, with each such row's full softmax."""
+    """dk, dv for the listed keys only -> [len(keys), Hkv, d] each, then their magnitudes;
+    each key's gradient sums over the queries that see it, with each such row's full
+    softmax."""
     T, hq, d = q.shape
     hkv = k.shape[1]
     g = hq // hkv
     seg_of = _segment_of(segments, T)
-    dk = np.zeros((len(keys), hkv, d))
-    dv = np.zeros((len(keys), hkv, d))
+    dk, dv, mk, mv = (np.zeros((len(keys), hkv, d)) for _ in range(4))
     rows = {}
     for r, j in enumerate(keys):
         for i in seen_by(segments, edges, T, int(j)):
             if i not in rows:
                 rows[i] = _row(q, k, v, do, segments, edges, scale, i, seg_of)
-            idx, P, dS = rows[i]
+            idx, P, dS, W = rows[i]
             pos = int(np.searchsorted(idx, j))
             for h in range(hq):
                 dk[r, h // g] += scale * dS[h, pos] * q[i, h]
                 dv[r, h // g] += P[h, pos] * do[i, h]
-    return dk, dv
+                mk[r, h // g] += scale * W[h, pos] * np.abs(q[i, h])
+                mv[r, h // g] += P[h, pos] * np.abs(do[i, h])
+    return dk, dv, mk, mv

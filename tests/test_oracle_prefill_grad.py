@@ -93,11 +93,16 @@ def test_sampled_routines_match_full_and_seen_by():
     q, k, v, do = _data(T, hq, hkv, d, 5)
     dq, dk, dv = pg.grads(q, k, v, do, seg, edg, 0.6)
     rows = [0, 5, 15, 16, 25, 30, 41]
-    assert np.allclose(pg.dq_rows(q, k, v, do, seg, edg, 0.6, rows), dq[rows], rtol=1e-12, atol=1e-14)
+    _, _, _, mq, mk, mv = pg.grads(q, k, v, do, seg, edg, 0.6, magnitudes=True)
+    rq, rmq = pg.dq_rows(q, k, v, do, seg, edg, 0.6, rows)
+    assert np.allclose(rq, dq[rows], rtol=1e-12, atol=1e-14) and np.allclose(rmq, mq[rows], rtol=1e-12)
     keys = [0, 15, 17, 19, 22, 26, 31, 41]
-    sk, sv = pg.dkdv_keys(q, k, v, do, seg, edg, 0.6, keys)
+    sk, sv, smk, smv = pg.dkdv_keys(q, k, v, do, seg, edg, 0.6, keys)
     assert np.allclose(sk, dk[keys], rtol=1e-12, atol=1e-14)
     assert np.allclose(sv, dv[keys], rtol=1e-12, atol=1e-14)
+    assert np.allclose(smk, mk[keys], rtol=1e-12) and np.allclose(smv, mv[keys], rtol=1e-12)
+    # a magnitude bounds its gradient
+    assert np.all(np.abs(dq) <= mq + 1e-12) and np.all(np.abs(dk) <= mk + 1e-12) and np.all(np.abs(dv) <= mv + 1e-12)
     dense = pf.visible_mask(seg, edg, T)
     for j in range(T):
         assert np.array_equal(pg.seen_by(seg, edg, T, j), np.nonzero(dense[:, j])[0]), j
