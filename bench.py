@@ -33,6 +33,7 @@ HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
 PREFILL_FLOPS = 27488461783040  # 4 * 128 * 1,677,762,560 visible pairs * 32 query heads
+PREFILL_BWD_FLOPS = 68721154457600  # 10 * 128 * pairs * heads: S again, dP, dV, dK, dQ (2.5 x the forward)
 
 
 def log(msg):
@@ -282,6 +283,63 @@ def bench_prefill(reps, warmup, cpu_budget=0.0):
     return out_obj
 
 
+def bench_prefill_bwd(reps, warmup):
+    """dag_attn_backward (the whole call: operand images, mask transpose, dK / dV and dQ
+    passes; HIP events on its stream) on the packed DAG workload, after one forward for
+    out and lse; the upstream gradient is a seeded N(0, 1) draw in bf16."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import fork_attention_decode_amd as fa
+    from tests.harness import to_torch
+    log("prefill backward: generating the packed DAG workload")
+    pi = W.dag_prefill()
+    mask = fa.DagMask(pi.segments, pi.edges, pi.T, pi.block)
+    q, k, v = (to_torch(x, "bf16") for x in (pi.q, pi.k, pi.v))
+    do = to_torch(W.to_bf16_bits(np.random.default_rng(67).standard_normal((pi.T, 32, 128))), "bf16")
+    pi.q = pi.k = pi.v = None
+    out, lse = fa.prefill(q, k, v, mask, pi.sm_scale)
+    hq, hkv = q.shape[1], k.shape[1]
+    dq = torch.empty((pi.T, hq, 128), dtype=torch.float32, device=q.device)
+    dk = torch.empty((pi.T, hkv, 128), dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
+    ws = torch.empty(fa.dag_attn_backward_workspace_size(pi.T, hq, hkv, 64, mask.nnz), dtype=torch.uint8,
+                     device=q.device)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        fa.dag_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), pi.T, hq, hkv, 128,
+                             mask.row_ptr.data_ptr(), mask.col.data_ptr(), mask.kind.data_ptr(), mask.nnz, 64,
+                             pi.sm_scale, ws.data_ptr(), ws.numel(), st)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    log(f"prefill backward: timing {reps} calls")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        run()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    t = float(np.mean(ms)) * 1e-3
+    tflops = PREFILL_BWD_FLOPS / t / 1e12
+    return {
+        "workload": "packed_dag_prefill backward (same mask and shapes as the forward; dq fp32 [T][32][128], "
+                    "dk / dv fp32 [T][8][128])",
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "dag_attn_backward (whole call)", "algorithmic_flops_per_call": PREFILL_BWD_FLOPS,
+                     "call_ms_mean": t * 1e3, "call_ms_p10": float(np.percentile(ms, 10)),
+                     "call_ms_p90": float(np.percentile(ms, 90))},
+        "note": "algorithmic FLOPs = 10 x 128 per visible (query, key) pair per query head (S recomputed, dP, dV, "
+                "dK, dQ); the dQ pass recomputes S and dP once more, so the matrix cores execute 14 x 128",
+        "reps": reps,
+    }
+
+
 def bench_select(reps, warmup):
     """Key scoring + keep selection (AgentKV's choice of entries before a compression) on
     one 131,072-token sequence (32 / 8 heads, d = 128, bf16) with 32 representative
@@ -452,6 +510,7 @@ def main():
     ap.add_argument("--only-prefill", action="store_true", help="time the prefill object alone (profiling)")
     ap.add_argument("--only-akv", action="store_true", help="time the drop + repos object alone (profiling)")
     ap.add_argument("--only-select", action="store_true", help="time the key scoring object alone (profiling)")
+    ap.add_argument("--only-prefill-bwd", action="store_true", help="time the prefill backward alone (profiling)")
     ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy 256 MiB device to device once (a kernel of known "
@@ -481,6 +540,9 @@ def main():
         return
     if args.only_select:
         print(json.dumps({"agentkv_select": bench_select(20, 3)}))
+        return
+    if args.only_prefill_bwd:
+        print(json.dumps({"prefill_backward": bench_prefill_bwd(5, 1)}))
         return
     sc = W.WORKLOADS[args.workload]()
     log(f"workload {args.workload}: building {args.copies} pool copies")
@@ -547,6 +609,8 @@ def main():
 
     if not args.only_decode:
         result["prefill"] = bench_prefill(args.prefill_reps, 3, 0.0 if args.no_cpu_baseline else 8.0)
+        torch.cuda.empty_cache()
+        result["prefill_backward"] = bench_prefill_bwd(5, 1)
         torch.cuda.empty_cache()
         result["octopus_dag"] = bench_octopus(max(20, args.steps // 4), 5)
         torch.cuda.empty_cache()

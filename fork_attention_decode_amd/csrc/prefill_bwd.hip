@@ -16,16 +16,17 @@
 //     and K transposed.  The TP order pairs query (or key) 4 k + r of two 16-row tiles
 //     with the lanes and registers where an accumulator tile holds them, so P and dS
 //     feed the next products straight from the accumulators, with no shuffles;
-//   * dkdv_kernel: one workgroup per (64-key block, KV head), 4 waves of 16 keys, K and V
-//     fragments held in registers; it walks the key block's column of the mask (a CSC
-//     built on the device, rows ascending) and, for each visible query block and each of
-//     the G query heads, stages that block's record in LDS and computes S = Q K^T,
-//     P, dP = dO V^T, dS, then dV += P^T dO and dK += dS^T Q: dK and dV of the G heads
-//     accumulate in registers, with no atomics;
-//   * dq_kernel: one workgroup per (64-query block, query head), 4 waves of 16 queries,
-//     Q and dO fragments in registers; it walks the block's CSR row, stages the key
-//     block's K / V / K^T and computes S^T = K Q^T, P^T, dP^T = V dO^T, dS^T and
-//     dQ += dS K;
+//   * dkdv_kernel: one workgroup per (two 64-key blocks, KV head), 8 waves of 16 keys, K
+//     and V fragments held in registers; it walks the union of the two blocks' columns
+//     of the mask (a CSC over column pairs built on the device, rows ascending) and, for
+//     each listed query block and each of the G query heads, stages that block's record
+//     in LDS (double-buffered: the next record's loads are in flight while the current
+//     one computes) and computes S = Q K^T, P, dP = dO V^T, dS, then dV += P^T dO and
+//     dK += dS^T Q: dK and dV of the G heads accumulate in registers, with no atomics;
+//   * dq_kernel: one workgroup per (64-query block, 2 query heads of a KV head), 8 waves
+//     of 16 queries, Q and dO fragments in registers; it walks the block's CSR row,
+//     stages each key block's K / V / K^T (double-buffered) for both heads and computes
+//     S^T = K Q^T, P^T, dP^T = V dO^T, dS^T and dQ += dS K;
 //   * the mask kinds are those of the forward: kind 1 (the diagonal block) hides key >
 //     query, keys >= T are hidden, a row with lse = -inf contributes nothing.
 #include <hip/hip_runtime.h>
@@ -163,19 +164,21 @@ __device__ __forceinline__ int find_in_row(const int32_t* col, int a, int b, int
   return lo < b && col[lo] == c ? lo : -1;
 }
 
+// one workgroup per pair of key-block columns (2 c, 2 c + 1): query blocks in either
 __global__ __launch_bounds__(kThreads) void csc_count_kernel(const int32_t* __restrict__ row_ptr,
                                                              const int32_t* __restrict__ col, int32_t nb,
                                                              int32_t* __restrict__ count) {
   __shared__ int s_n;
-  const int c = blockIdx.x;
+  const int c0 = 2 * blockIdx.x;
   if (threadIdx.x == 0) s_n = 0;
   __syncthreads();
   int n = 0;
-  for (int r = threadIdx.x; r < nb; r += kThreads) n += find_in_row(col, row_ptr[r], row_ptr[r + 1], c) >= 0;
+  for (int r = threadIdx.x; r < nb; r += kThreads)
+    n += find_in_row(col, row_ptr[r], row_ptr[r + 1], c0) >= 0 || find_in_row(col, row_ptr[r], row_ptr[r + 1], c0 + 1) >= 0;
   for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
   if ((threadIdx.x & 63) == 0) atomicAdd(&s_n, n);
   __syncthreads();
-  if (threadIdx.x == 0) count[c] = s_n;
+  if (threadIdx.x == 0) count[blockIdx.x] = s_n;
 }
 
 // exclusive scan of nb counts into col_ptr[0..nb] (one workgroup)
@@ -206,35 +209,64 @@ __global__ __launch_bounds__(1024) void csc_scan_kernel(const int32_t* __restric
   if (tid == 0) col_ptr[nb] = s_carry;
 }
 
+// entries of column pair c in ascending query block: qb | present bits << 24 (bit i: column
+// 2 c + i lists qb) | diagonal bits << 26
 __global__ __launch_bounds__(kThreads) void csc_fill_kernel(const int32_t* __restrict__ row_ptr,
                                                             const int32_t* __restrict__ col,
                                                             const uint8_t* __restrict__ kind, int32_t nb,
                                                             const int32_t* __restrict__ col_ptr,
                                                             uint32_t* __restrict__ crow) {
   __shared__ int s_wave[kThreads / 64];
-  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int carry = col_ptr[c];
+  const int c0 = 2 * blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = col_ptr[blockIdx.x];
   for (int base = 0; base < nb; base += kThreads) {  // uniform trip count
     const int r = base + tid;
-    const int e = r < nb ? find_in_row(col, row_ptr[r], row_ptr[r + 1], c) : -1;
-    const uint64_t bal = __ballot(e >= 0);
+    int e0 = -1, e1 = -1;
+    if (r < nb) {
+      e0 = find_in_row(col, row_ptr[r], row_ptr[r + 1], c0);
+      e1 = find_in_row(col, row_ptr[r], row_ptr[r + 1], c0 + 1);
+    }
+    const bool any = e0 >= 0 || e1 >= 0;
+    const uint64_t bal = __ballot(any);
     const int before = __popcll(bal & ((1ull << lane) - 1ull));
     __syncthreads();
     if (lane == 0) s_wave[wave] = __popcll(bal);
     __syncthreads();
     int wb = carry;
     for (int w = 0; w < wave; ++w) wb += s_wave[w];
-    if (e >= 0) crow[wb + before] = (uint32_t)r | ((uint32_t)(kind[e] != 0) << 24);
+    if (any) {
+      uint32_t ent = (uint32_t)r | (e0 >= 0 ? 1u << 24 : 0u) | (e1 >= 0 ? 2u << 24 : 0u);
+      if (e0 >= 0 && kind[e0]) ent |= 1u << 26;
+      if (e1 >= 0 && kind[e1]) ent |= 2u << 26;
+      crow[wb + before] = ent;
+    }
     for (int w = 0; w < kThreads / 64; ++w) carry += s_wave[w];
   }
 }
 
-__device__ __forceinline__ void copy_rec(const char* __restrict__ src, char* dst, int bytes) {
-  const i32x4* s = reinterpret_cast<const i32x4*>(src);
-  i32x4* d = reinterpret_cast<i32x4*>(dst);
-#pragma unroll 4
-  for (int u = threadIdx.x; u < bytes / 16; u += kThreads) d[u] = s[u];
-}
+// a record staged through registers: the loads of the next stage are issued before the
+// current stage computes and written to the other LDS buffer after it
+template <int kUnits, int kThr>
+struct Stager {
+  static constexpr int kPer = (kUnits + kThr - 1) / kThr;
+  i32x4 r[kPer];
+  __device__ __forceinline__ void load(const char* __restrict__ src) {
+    const i32x4* s = reinterpret_cast<const i32x4*>(src);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = threadIdx.x + i * kThr;
+      if (kUnits % kThr == 0 || u < kUnits) r[i] = s[u];
+    }
+  }
+  __device__ __forceinline__ void store(char* dst) const {
+    i32x4* d = reinterpret_cast<i32x4*>(dst);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int u = threadIdx.x + i * kThr;
+      if (kUnits % kThr == 0 || u < kUnits) d[u] = r[i];
+    }
+  }
+};
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -263,32 +295,59 @@ struct BwdParams {
   float c2, scale;
 };
 
-// grid (Hkv, n_blocks): dK, dV of a 64-key block for one KV head
-__global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) char rec[kQRec];
-  const int g = blockIdx.x, kb = blockIdx.y, lane = threadIdx.x & 63;
+constexpr int kKeyBlocksPerWg = 2;                 // dK / dV workgroup: 2 key blocks, 8 waves
+constexpr int kDkdvThreads = 256 * kKeyBlocksPerWg;
+constexpr int kHeadsPerWg = 2;                     // dQ workgroup: up to 2 query heads, 8 waves
+constexpr int kDqThreads = 256 * kHeadsPerWg;
+
+// grid (Hkv, ceil(n_blocks / 2)): dK, dV of two 64-key blocks for one KV head; wave w takes
+// keys 16 (w % 4) .. + 15 of block 2 blockIdx.y + w / 4.  The workgroup walks the union
+// of the two columns; a wave whose column lacks the query block skips it.
+__global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char rec[2][kQRec];
+  const int g = blockIdx.x, lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const char* krec = p.krec + ((size_t)kb * p.hkv + g) * kKRec;
+  const int kbi = w >> 2, kt = w & 3;
+  const int kb = kKeyBlocksPerWg * blockIdx.y + kbi;
+  const bool live = kb < p.nb;
   bf16x8 kf[4], vf[4];  // the wave's 16 keys as the B operand (key = lane % 16)
+  if (live) {
+    const char* krec = p.krec + ((size_t)kb * p.hkv + g) * kKRec;
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    kf[f] = *reinterpret_cast<const bf16x8*>(krec + ((w * 4 + f) * 64 + lane) * 16);
-    vf[f] = *reinterpret_cast<const bf16x8*>(krec + kImg + ((w * 4 + f) * 64 + lane) * 16);
+    for (int f = 0; f < 4; ++f) {
+      kf[f] = *reinterpret_cast<const bf16x8*>(krec + ((kt * 4 + f) * 64 + lane) * 16);
+      vf[f] = *reinterpret_cast<const bf16x8*>(krec + kImg + ((kt * 4 + f) * 64 + lane) * 16);
+    }
   }
   f32x4 dk[8], dv[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) dk[n] = dv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int key_tok = kb * kB + w * 16 + (lane & 15);
-  const int e0 = p.col_ptr[kb], e1 = p.col_ptr[kb + 1];
-  for (int e = e0; e < e1; ++e) {
-    const uint32_t ent = p.crow[e];
+  const int key_tok = kb * kB + kt * 16 + (lane & 15);
+  const int e0 = p.col_ptr[blockIdx.y], e1 = p.col_ptr[blockIdx.y + 1];
+  // stages: (entry, head of the group), entries from the highest query block down, so
+  // workgroups whose lists share a tail (every prefix column reaches the last branch
+  // blocks) start on the same records and read them while they sit in the die's L2
+  const int n_st = (e1 - e0) * p.G;
+  auto ent_of = [&](int st) { return p.crow[e1 - 1 - st / p.G]; };
+  Stager<kQRec / 16, kDkdvThreads> stg;
+  auto src = [&](int st) {
+    const int qb = (int)(ent_of(st) & kRowMask);
+    return p.qrec + ((size_t)qb * p.hq + g * p.G + st % p.G) * kQRec;
+  };
+  if (n_st > 0) {
+    stg.load(src(0));
+    stg.store(rec[0]);
+  }
+  __syncthreads();
+  for (int st = 0; st < n_st; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < n_st) stg.load(src(st + 1));
+    const uint32_t ent = ent_of(st);
     const int qb = (int)(ent & kRowMask);
-    const bool diag = (ent >> 24) != 0;
-    for (int hh = 0; hh < p.G; ++hh) {
-      __syncthreads();  // every wave is done with the previous record
-      copy_rec(p.qrec + ((size_t)qb * p.hq + g * p.G + hh) * kQRec, rec, kQRec);
-      __syncthreads();
-      const float* lse2 = reinterpret_cast<const float*>(rec + 4 * kImg);
+    if (live && ((ent >> (24 + kbi)) & 1u)) {
+      const bool diag = (ent >> (26 + kbi)) & 1u;
+      const char* r = rec[cur];
+      const float* lse2 = reinterpret_cast<const float*>(r + 4 * kImg);
       const float* dd = lse2 + kB;
       f32x4 s[4], dp[4];
 #pragma unroll
@@ -297,80 +356,101 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
           const int u = ((t * 4 + f) * 64 + lane) * 16;
-          s[t] = mfma(*reinterpret_cast<const bf16x8*>(rec + u), kf[f], s[t]);
-          dp[t] = mfma(*reinterpret_cast<const bf16x8*>(rec + kImg + u), vf[f], dp[t]);
+          s[t] = mfma(*reinterpret_cast<const bf16x8*>(r + u), kf[f], s[t]);
+          dp[t] = mfma(*reinterpret_cast<const bf16x8*>(r + kImg + u), vf[f], dp[t]);
         }
       }
-      // s[t][r]: query 16 t + 4 (lane / 16) + r, key lane % 16 of the wave
+      // s[t][i]: query 16 t + 4 (lane / 16) + i, key lane % 16 of the wave
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int q0 = 16 * t + 4 * (lane >> 4);
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + q0);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + q0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool vis = key_tok < p.T && (!diag || key_tok <= qb * kB + q0 + r);
-          const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], p.c2, -l4[r])) : 0.f;
-          s[t][r] = pr;
-          dp[t][r] = pr * (dp[t][r] - d4[r]);
+        for (int i = 0; i < 4; ++i) {
+          const bool vis = key_tok < p.T && (!diag || key_tok <= qb * kB + q0 + i);
+          const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], p.c2, -l4[i])) : 0.f;
+          s[t][i] = pr;
+          dp[t][i] = pr * (dp[t][i] - d4[i]);
         }
       }
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8 ap = pack_pair(s[2 * st], s[2 * st + 1]);
-        const bf16x8 ads = pack_pair(dp[2 * st], dp[2 * st + 1]);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const bf16x8 ap = pack_pair(s[2 * h2], s[2 * h2 + 1]);
+        const bf16x8 ads = pack_pair(dp[2 * h2], dp[2 * h2 + 1]);
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
-          const int u = ((n * 2 + st) * 64 + lane) * 16;
-          dv[n] = mfma(ap, *reinterpret_cast<const bf16x8*>(rec + 3 * kImg + u), dv[n]);
-          dk[n] = mfma(ads, *reinterpret_cast<const bf16x8*>(rec + 2 * kImg + u), dk[n]);
+          const int u = ((n * 2 + h2) * 64 + lane) * 16;
+          dv[n] = mfma(ap, *reinterpret_cast<const bf16x8*>(r + 3 * kImg + u), dv[n]);
+          dk[n] = mfma(ads, *reinterpret_cast<const bf16x8*>(r + 2 * kImg + u), dk[n]);
         }
       }
     }
+    if (st + 1 < n_st) stg.store(rec[cur ^ 1]);
+    __syncthreads();  // stage st + 1 is in place; every wave is done with stage st
   }
-  // dk[n][r]: key 4 (lane / 16) + r of the wave, dim 16 n + lane % 16
+  // dk[n][i]: key 4 (lane / 16) + i of the wave, dim 16 n + lane % 16
+  if (!live) return;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int j = kb * kB + w * 16 + 4 * (lane >> 4) + r;
+  for (int i = 0; i < 4; ++i) {
+    const int j = kb * kB + kt * 16 + 4 * (lane >> 4) + i;
     if (j < p.T) {
       float* dkr = p.dk + ((size_t)j * p.hkv + g) * kD + (lane & 15);
       float* dvr = p.dv + ((size_t)j * p.hkv + g) * kD + (lane & 15);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        dkr[16 * n] = dk[n][r] * p.scale;
-        dvr[16 * n] = dv[n][r];
+        dkr[16 * n] = dk[n][i] * p.scale;
+        dvr[16 * n] = dv[n][i];
       }
     }
   }
 }
 
-// grid (Hq, n_blocks): dQ of a 64-query block for one query head
-__global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) char rec[kKRec];
-  const int h = blockIdx.x, qb = blockIdx.y, lane = threadIdx.x & 63;
+// grid (Hq / hw, n_blocks), hw = 2 query heads of one KV head per workgroup (1 when G is
+// odd): dQ of a 64-query block; wave w takes queries 16 (w % 4) .. + 15 of head
+// blockIdx.x hw + w / 4 (with hw = 1 the upper four waves only help stage).  Each key
+// block's record staged in LDS serves the workgroup's heads.
+__global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw) {
+  __shared__ __attribute__((aligned(16))) char rec[2][kKRec];
+  const int qb = blockIdx.y, lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = h / p.G;
+  const bool active = (w >> 2) < hw;
+  const int h = blockIdx.x * hw + (active ? w >> 2 : 0), qt = w & 3;
+  const int g = blockIdx.x * hw / p.G;
   const char* qrec = p.qrec + ((size_t)qb * p.hq + h) * kQRec;
   bf16x8 qf[4], df[4];  // the wave's 16 queries as the B operand (query = lane % 16)
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
-    qf[f] = *reinterpret_cast<const bf16x8*>(qrec + ((w * 4 + f) * 64 + lane) * 16);
-    df[f] = *reinterpret_cast<const bf16x8*>(qrec + kImg + ((w * 4 + f) * 64 + lane) * 16);
+    qf[f] = *reinterpret_cast<const bf16x8*>(qrec + ((qt * 4 + f) * 64 + lane) * 16);
+    df[f] = *reinterpret_cast<const bf16x8*>(qrec + kImg + ((qt * 4 + f) * 64 + lane) * 16);
   }
-  const float lq = reinterpret_cast<const float*>(qrec + 4 * kImg)[w * 16 + (lane & 15)];
-  const float dq_d = reinterpret_cast<const float*>(qrec + 4 * kImg)[kB + w * 16 + (lane & 15)];
-  const int q_tok = qb * kB + w * 16 + (lane & 15);
+  const float lq = reinterpret_cast<const float*>(qrec + 4 * kImg)[qt * 16 + (lane & 15)];
+  const float dq_d = reinterpret_cast<const float*>(qrec + 4 * kImg)[kB + qt * 16 + (lane & 15)];
+  const int q_tok = qb * kB + qt * 16 + (lane & 15);
   f32x4 dq[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) dq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
-  for (int e = e0; e < e1; ++e) {
+  Stager<kKRec / 16, kDqThreads> stg;
+  // stages: the row's entries whose column is inside [0, nb) (others are never followed)
+  auto col_ok = [&](int e) { return p.col[e] >= 0 && p.col[e] < p.nb; };
+  auto next_ok = [&](int e) {
+    while (e < e1 && !col_ok(e)) ++e;
+    return e;
+  };
+  int e = next_ok(e0);
+  if (e < e1) {
+    stg.load(p.krec + ((size_t)p.col[e] * p.hkv + g) * kKRec);
+    stg.store(rec[0]);
+  }
+  __syncthreads();
+  for (int cur = 0; e < e1; cur ^= 1) {
+    const int en = next_ok(e + 1);
+    if (en < e1) stg.load(p.krec + ((size_t)p.col[en] * p.hkv + g) * kKRec);
     const int kb = p.col[e];
-    if (kb < 0 || kb >= p.nb) continue;  // outside the mask's range: never followed (uniform)
     const bool diag = p.kind[e] != 0;
-    __syncthreads();
-    copy_rec(p.krec + ((size_t)kb * p.hkv + g) * kKRec, rec, kKRec);
-    __syncthreads();
+    const char* r = rec[cur];
+    if (active) {
     f32x4 s[4], dp[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -378,36 +458,41 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(BwdParams p) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         const int u = ((t * 4 + f) * 64 + lane) * 16;
-        s[t] = mfma(*reinterpret_cast<const bf16x8*>(rec + u), qf[f], s[t]);
-        dp[t] = mfma(*reinterpret_cast<const bf16x8*>(rec + kImg + u), df[f], dp[t]);
+        s[t] = mfma(*reinterpret_cast<const bf16x8*>(r + u), qf[f], s[t]);
+        dp[t] = mfma(*reinterpret_cast<const bf16x8*>(r + kImg + u), df[f], dp[t]);
       }
     }
-    // s[t][r]: key 16 t + 4 (lane / 16) + r, query lane % 16 of the wave
+    // s[t][i]: key 16 t + 4 (lane / 16) + i, query lane % 16 of the wave
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb * kB + 16 * t + 4 * (lane >> 4) + r;
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb * kB + 16 * t + 4 * (lane >> 4) + i;
         const bool vis = key < p.T && (!diag || key <= q_tok);
-        const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][r], p.c2, -lq)) : 0.f;
-        dp[t][r] = pr * (dp[t][r] - dq_d);
+        const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], p.c2, -lq)) : 0.f;
+        dp[t][i] = pr * (dp[t][i] - dq_d);
       }
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const bf16x8 ads = pack_pair(dp[2 * st], dp[2 * st + 1]);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const bf16x8 ads = pack_pair(dp[2 * h2], dp[2 * h2 + 1]);
 #pragma unroll
       for (int n = 0; n < 8; ++n)
-        dq[n] = mfma(ads, *reinterpret_cast<const bf16x8*>(rec + 2 * kImg + ((n * 2 + st) * 64 + lane) * 16), dq[n]);
+        dq[n] = mfma(ads, *reinterpret_cast<const bf16x8*>(r + 2 * kImg + ((n * 2 + h2) * 64 + lane) * 16), dq[n]);
     }
+    }
+    if (en < e1) stg.store(rec[cur ^ 1]);
+    __syncthreads();  // the next key block is in place; every wave is done with this one
+    e = en;
   }
-  // dq[n][r]: query 4 (lane / 16) + r of the wave, dim 16 n + lane % 16
+  // dq[n][i]: query 4 (lane / 16) + i of the wave, dim 16 n + lane % 16
+  if (!active) return;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = qb * kB + w * 16 + 4 * (lane >> 4) + r;
-    if (i < p.T) {
-      float* dqr = p.dq + ((size_t)i * p.hq + h) * kD + (lane & 15);
+  for (int i = 0; i < 4; ++i) {
+    const int qi = qb * kB + qt * 16 + 4 * (lane >> 4) + i;
+    if (qi < p.T) {
+      float* dqr = p.dq + ((size_t)qi * p.hq + h) * kD + (lane & 15);
 #pragma unroll
-      for (int n = 0; n < 8; ++n) dqr[16 * n] = dq[n][r] * p.scale;
+      for (int n = 0; n < 8; ++n) dqr[16 * n] = dq[n][i] * p.scale;
     }
   }
 }
@@ -476,9 +561,10 @@ extern "C" int dag_attn_backward(const void* q, const void* k, const void* v, co
   int32_t* count = reinterpret_cast<int32_t*>(ws + w.count);
   int32_t* col_ptr = reinterpret_cast<int32_t*>(ws + w.col_ptr);
   uint32_t* crow = reinterpret_cast<uint32_t*>(ws + w.crow);
-  csc_count_kernel<<<(unsigned)nb, kThreads, 0, stream>>>(row_ptr, col, (int32_t)nb, count);
-  csc_scan_kernel<<<1, 1024, 0, stream>>>(count, (int32_t)nb, col_ptr);
-  csc_fill_kernel<<<(unsigned)nb, kThreads, 0, stream>>>(row_ptr, col, kind, (int32_t)nb, col_ptr, crow);
+  const int32_t n_pair = (int32_t)((nb + 1) / 2);
+  csc_count_kernel<<<(unsigned)n_pair, kThreads, 0, stream>>>(row_ptr, col, (int32_t)nb, count);
+  csc_scan_kernel<<<1, 1024, 0, stream>>>(count, n_pair, col_ptr);
+  csc_fill_kernel<<<(unsigned)n_pair, kThreads, 0, stream>>>(row_ptr, col, kind, (int32_t)nb, col_ptr, crow);
   BwdParams p;
   p.qrec = ws + w.qrec;
   p.krec = ws + w.krec;
@@ -497,8 +583,9 @@ extern "C" int dag_attn_backward(const void* q, const void* k, const void* v, co
   p.nb = (int32_t)nb;
   p.scale = sm_scale;
   p.c2 = sm_scale * 1.4426950408889634f;
-  dkdv_kernel<<<dim3(n_kv_heads, (unsigned)nb), kThreads, 0, stream>>>(p);
-  dq_kernel<<<dim3(n_q_heads, (unsigned)nb), kThreads, 0, stream>>>(p);
+  dkdv_kernel<<<dim3(n_kv_heads, (unsigned)n_pair), kDkdvThreads, 0, stream>>>(p);
+  const int hw = p.G % kHeadsPerWg == 0 ? kHeadsPerWg : 1;
+  dq_kernel<<<dim3(n_q_heads / hw, (unsigned)nb), kDqThreads, 0, stream>>>(p, hw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill backward: ") + hipGetErrorString(e));
   return KV_OK;
