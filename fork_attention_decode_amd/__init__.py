@@ -88,6 +88,9 @@ _SIGS = {
                          _sz, _P],
     "dag_attn_prepare": [_P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, C.c_int64, _i32, _P, _sz, _P],
     "dag_attn_run": [_P, _P, _P, _i32, _i32, _i32, _i32, _P, C.c_int64, _i32, C.c_float, _P, _sz, _P],
+    "kv_window_plan": [_P, _pi32, _i32, _i32, _i32, _psz],
+    "kv_window_upload": [_P, _P, _sz, _P],
+    "kv_window_step": [_P, _i32, _P, _P, _P, _P, _P, C.c_float, _P],
     "dag_attn_backward_workspace_size": [_i32, _i32, _i32, _i32, C.c_int64, _psz],
     "dag_attn_backward": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, C.c_int64, _i32,
                           C.c_float, _P, _sz, _P],
@@ -364,6 +367,24 @@ def dag_attn_run(q: int, out: int, lse: int, T: int, n_q_heads: int, n_kv_heads:
                                             sm_scale, workspace or None, ws_bytes, stream or None))
 
 
+def kv_window_plan(pool: int, seqs, n_q_heads: int, n_steps: int) -> int:
+    s = np.ascontiguousarray(np.asarray(seqs, np.int32))
+    out = C.c_size_t(0)
+    _check("kv_window_plan", lib.kv_window_plan(pool, s.ctypes.data_as(_pi32), len(s), n_q_heads, n_steps,
+                                                C.byref(out)), pool)
+    return out.value
+
+
+def kv_window_upload(pool: int, workspace: int, ws_bytes: int, stream: int = 0):
+    _check("kv_window_upload", lib.kv_window_upload(pool, workspace or None, ws_bytes, stream or None), pool)
+
+
+def kv_window_step(pool: int, step: int, k: int, v: int, q: int, out: int, lse: int, sm_scale: float,
+                   stream: int = 0):
+    _check("kv_window_step", lib.kv_window_step(pool, step, k, v, q, out, lse or None, sm_scale, stream or None),
+           pool)
+
+
 def dag_attn_backward_workspace_size(T: int, n_q_heads: int, n_kv_heads: int, block: int, nnz: int) -> int:
     out = C.c_size_t(0)
     _check("dag_attn_backward_workspace_size",
@@ -603,6 +624,20 @@ class Pool:
         fork_attn_decode(self.handle, seqs, hq, q.data_ptr(), out.data_ptr(), lse.data_ptr(), sm_scale,
                          workspace.data_ptr(), workspace.numel(), self._stream())
         return out, lse
+
+    def window(self, seqs: Sequence[int], n_q_heads: int, n_steps: int):
+        """Reserve and plan a steady-state decode window (kv_window_plan + kv_window_upload);
+        returns the workspace tensor, which must stay alive while the window's steps run."""
+        import torch
+        need = kv_window_plan(self.handle, seqs, n_q_heads, n_steps)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        kv_window_upload(self.handle, ws.data_ptr(), ws.numel(), self._stream())
+        return ws
+
+    def window_step(self, step: int, k, v, q, sm_scale: float, out, lse):
+        """One window step: k / v [n, Hkv, d] new rows, q [n, Hq, d]; out / lse written."""
+        kv_window_step(self.handle, step, k.data_ptr(), v.data_ptr(), q.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                       sm_scale, self._stream())
 
     def plan_stats(self) -> dict:
         return fork_attn_plan_stats(self.handle)

@@ -28,6 +28,9 @@ using namespace fa;
 int fa_set_err(kv_pool* P, int code, const std::string& m);
 Seq* fa_seq(kv_pool* P, kv_seq_t s);
 hipError_t fa_upload(kv_pool* P, void* dst, const void* src, size_t bytes, hipStream_t s);
+void fa_take_page(kv_pool* P, int32_t p);
+void fa_unref_page(kv_pool* P, int32_t p);
+void fa_pos_append(std::vector<PosRun>& v, int64_t p0, int64_t n);
 #define FAIL(P, code, msg) return fa_set_err((P), (code), (msg))
 
 namespace {
@@ -52,7 +55,9 @@ void put(std::vector<char>& blob, size_t off, const std::vector<T>& v) {
 
 }  // namespace
 
-static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq) {
+// len_cap (optional): per query, the number of its sequence's own tokens to attend to
+// (a prefix of the own context); the cached plan is bypassed and left invalid.
+static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, const int64_t* len_cap = nullptr) {
   const kv_pool_config& C = P->cfg;
   if (n < 0 || (n > 0 && !seqs)) FAIL(P, KV_ERR_INVALID, "bad sequence list");
   if (hq < C.n_kv_heads || hq % C.n_kv_heads) FAIL(P, KV_ERR_INVALID, "n_q_heads must be a multiple of n_kv_heads");
@@ -60,7 +65,7 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq) {
   if (G > kMaxRows) FAIL(P, KV_ERR_UNSUPPORTED, "more than 64 query heads per KV head");
   const int32_t PS = C.page_size;
   DecodePlanCache& pc = P->plan;
-  if (pc.valid && pc.version == P->version && pc.n_q_heads == hq && (int32_t)pc.seqs.size() == n &&
+  if (!len_cap && pc.valid && pc.version == P->version && pc.n_q_heads == hq && (int32_t)pc.seqs.size() == n &&
       std::equal(pc.seqs.begin(), pc.seqs.end(), seqs))
     return KV_OK;
 
@@ -69,8 +74,9 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq) {
   for (int32_t i = 0; i < n; ++i) {
     Seq* S = fa_seq(P, seqs[i]);
     if (!S) FAIL(P, KV_ERR_NOT_FOUND, "no live sequence in the query list");
-    for (size_t L = 0; L < S->pages.size(); ++L)
-      ent.push_back({S->pages[L], 0, (int32_t)std::min<int64_t>(PS, S->n - (int64_t)L * PS), i});
+    const int64_t n_own = len_cap ? std::min<int64_t>(len_cap[i], S->n) : S->n;
+    for (size_t L = 0; (int64_t)L * PS < n_own; ++L)
+      ent.push_back({S->pages[L], 0, (int32_t)std::min<int64_t>(PS, n_own - (int64_t)L * PS), i});
     for (const Mount& m : S->mounts) {
       for (size_t j = 0; j < m.pages.size(); ++j) {
         const int64_t a = std::max<int64_t>(0, m.off - (int64_t)j * PS);
@@ -323,6 +329,175 @@ int fork_attn_decode(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, 
   int st = fork_attn_partials(P, seqs, n, hq, q, sm_scale, ws, ws_bytes, s);
   if (st) return st;
   return fork_attn_merge(P, seqs, n, hq, out, lse, ws, ws_bytes, s);
+}
+
+// ------------------------------------------------------------------ steady-state decode window
+// Agentrix (the ForkAttention section) and AgentKV run fork attention inside a captured
+// decode loop; a window reserves the slots of the next n_steps tokens of every sequence
+// (tail copy-on-write and new pages, in exactly the order n_steps rounds of one append
+// per sequence would take them) and plans each step's decode once, so a step is three
+// launches with fixed arguments: the new K / V into their reserved slots, the split-K
+// partials, the merge.
+
+int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, int32_t n_steps, size_t* ws_need) {
+  if (!P || !ws_need) FAIL(P, KV_ERR_INVALID, "null argument");
+  if (n < 1 || !seqs || n_steps < 1) FAIL(P, KV_ERR_INVALID, "bad window shape");
+  const int32_t PS = P->cfg.page_size;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!fa_seq(P, seqs[i])) FAIL(P, KV_ERR_NOT_FOUND, "no live sequence in the window");
+    for (int32_t j = 0; j < i; ++j)
+      if (seqs[j] == seqs[i]) FAIL(P, KV_ERR_INVALID, "a sequence appears twice in the window");
+  }
+  if (hq < P->cfg.n_kv_heads || hq % P->cfg.n_kv_heads) FAIL(P, KV_ERR_INVALID, "n_q_heads must be a multiple of n_kv_heads");
+  // capacity: copies of shared partial tails + pages the new tokens start
+  int64_t need = 0;
+  std::vector<int64_t> base((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    Seq* S = fa_seq(P, seqs[i]);
+    base[i] = S->n;
+    const int64_t have = (int64_t)S->pages.size();
+    if (S->n % PS && P->rc[S->pages[(size_t)(S->n / PS)]] > 1) ++need;
+    need += std::max<int64_t>(0, (S->n + n_steps + PS - 1) / PS - have);
+  }
+  if (need > P->free.count()) FAIL(P, KV_ERR_OOM, "not enough free pages for the window");
+  DecodeWindow& W = P->window;
+  W = DecodeWindow();
+  // 1. reservation, round by round (the page order of n_steps rounds of single appends)
+  std::vector<PageWrite> cow;
+  std::vector<std::vector<PageWrite>> writes((size_t)n_steps, std::vector<PageWrite>((size_t)n));
+  for (int32_t st = 0; st < n_steps; ++st)
+    for (int32_t i = 0; i < n; ++i) {
+      Seq* S = fa_seq(P, seqs[i]);
+      const int64_t L = S->n / PS, slot = S->n % PS;
+      if (L < (int64_t)S->pages.size()) {
+        if (P->rc[S->pages[(size_t)L]] > 1) {  // shared partial tail: copy before the first write
+          std::vector<int32_t> id;
+          P->free.peek_lowest(1, id);
+          const int32_t old = S->pages[(size_t)L];
+          fa_take_page(P, id[0]);
+          S->pages[(size_t)L] = id[0];
+          fa_unref_page(P, old);
+          cow.push_back({id[0], old, 0, 0, 0});
+        }
+      } else {
+        std::vector<int32_t> id;
+        P->free.peek_lowest(1, id);
+        fa_take_page(P, id[0]);
+        S->pages.push_back(id[0]);
+      }
+      writes[st][i] = {S->pages[(size_t)L], -1, (int32_t)slot, (int32_t)slot + 1, (int64_t)i};  // row i of k / v
+      fa_pos_append(S->pos, S->next_pos, 1);
+      S->next_pos += 1;
+      S->n += 1;
+    }
+  P->version++;
+  // 2. one plan per step over the contexts through that step's token
+  std::vector<int64_t> cap((size_t)n);
+  size_t off = 0;
+  W.off_cow = off;
+  off = align256(off + cow.size() * sizeof(PageWrite));
+  int64_t part_slots = 0;
+  std::vector<std::vector<char>> blobs((size_t)n_steps);
+  W.steps.resize((size_t)n_steps);
+  for (int32_t st = 0; st < n_steps; ++st) {
+    for (int32_t i = 0; i < n; ++i) cap[i] = base[i] + st + 1;
+    if (int e = build_plan(P, seqs, n, hq, cap.data())) {
+      P->plan.valid = false;
+      W = DecodeWindow();
+      return e;  // the page table keeps the reservation; the window is unusable
+    }
+    DecodePlanCache& pc = P->plan;
+    DecodeWindow::Step& ws = W.steps[st];
+    ws.off_plan = off;
+    ws.off_items = off + pc.off_items;
+    ws.off_mptr = off + pc.off_mptr;
+    ws.n_items = pc.n_items;
+    ws.n_out_rows = pc.n_out_rows;
+    ws.max_parts = pc.max_parts;
+    part_slots = std::max<int64_t>(part_slots, (int64_t)pc.n_out_rows * pc.max_parts);
+    blobs[st] = pc.blob;
+    off = align256(off + pc.blob.size());
+    ws.off_writes = off;
+    off = align256(off + (size_t)n * sizeof(PageWrite));
+  }
+  P->plan.valid = false;  // the cached plan was overwritten by the window's plans
+  W.off_plse = off;
+  off = align256(off + (size_t)part_slots * sizeof(float));
+  W.off_po = off;
+  off = align256(off + (size_t)part_slots * P->cfg.head_dim * sizeof(float));
+  W.ws_need = std::max<size_t>(off, 256);
+  W.blob.assign(W.off_plse, 0);
+  if (!cow.empty()) std::memcpy(W.blob.data() + W.off_cow, cow.data(), cow.size() * sizeof(PageWrite));
+  for (int32_t st = 0; st < n_steps; ++st) {
+    const DecodeWindow::Step& ws = W.steps[st];
+    std::memcpy(W.blob.data() + ws.off_plan, blobs[st].data(), blobs[st].size());
+    std::memcpy(W.blob.data() + ws.off_writes, writes[st].data(), (size_t)n * sizeof(PageWrite));
+  }
+  W.seqs.assign(seqs, seqs + n);
+  W.n_q_heads = hq;
+  W.n_steps = n_steps;
+  W.n_cow = (int32_t)cow.size();
+  W.version = P->version;
+  W.valid = true;
+  *ws_need = W.ws_need;
+  return KV_OK;
+}
+
+int kv_window_upload(kv_pool_t* P, void* workspace, size_t ws_bytes, hipStream_t s) {
+  if (!P) FAIL(P, KV_ERR_INVALID, "null pool");
+  if (!P->device) FAIL(P, KV_ERR_INVALID, "metadata-only pool has no KV data");
+  DecodeWindow& W = P->window;
+  if (!W.valid || W.version != P->version) FAIL(P, KV_ERR_INVALID, "no window planned since the last page-table change");
+  if (!workspace) FAIL(P, KV_ERR_INVALID, "null workspace");
+  if (ws_bytes < W.ws_need) FAIL(P, KV_ERR_WORKSPACE, "window workspace too small");
+  char* w = static_cast<char*>(workspace);
+  hipError_t e = fa_upload(P, w, W.blob.data(), W.blob.size(), s);
+  if (e == hipSuccess && W.n_cow > 0)
+    e = launch_page_write(P->cfg.dtype, P->cfg.head_dim, P->cfg.n_kv_heads, P->cfg.n_pages, P->k, P->v, P->k, P->v,
+                          reinterpret_cast<const PageWrite*>(w + W.off_cow), W.n_cow, s);
+  if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("window upload: ") + hipGetErrorString(e));
+  W.ws = workspace;
+  return KV_OK;
+}
+
+int kv_window_step(kv_pool_t* P, int32_t step, const void* k, const void* v, const void* q, void* out, float* lse,
+                   float sm_scale, hipStream_t s) {
+  if (!P) FAIL(P, KV_ERR_INVALID, "null pool");
+  DecodeWindow& W = P->window;
+  if (!W.valid || W.version != P->version || !W.ws)
+    FAIL(P, KV_ERR_INVALID, "no uploaded window since the last page-table change");
+  if (step < 0 || step >= W.n_steps) FAIL(P, KV_ERR_INVALID, "step outside the window");
+  if (!k || !v || !q || !out) FAIL(P, KV_ERR_INVALID, "null device pointer");
+  const DecodeWindow::Step& ws = W.steps[step];
+  char* w = static_cast<char*>(W.ws);
+  hipError_t e = launch_page_write(P->cfg.dtype, P->cfg.head_dim, P->cfg.n_kv_heads, P->cfg.n_pages, P->k, P->v, k,
+                                   v, reinterpret_cast<const PageWrite*>(w + ws.off_writes), (int)W.seqs.size(), s);
+  if (e == hipSuccess) {
+    DecodeParams dp;
+    dp.q = q;
+    dp.k_pages = P->k;
+    dp.v_pages = P->v;
+    dp.items = reinterpret_cast<const int32_t*>(w + ws.off_items);
+    dp.part_lse2 = reinterpret_cast<float*>(w + W.off_plse);
+    dp.part_o = reinterpret_cast<float*>(w + W.off_po);
+    dp.n_items = ws.n_items;
+    dp.n_pages = P->cfg.n_pages;
+    dp.scale_log2 = sm_scale * 1.4426950408889634f;
+    e = launch_decode(P->cfg.dtype, P->cfg.head_dim, dp, s);
+  }
+  if (e == hipSuccess) {
+    MergeParams mp;
+    mp.count = reinterpret_cast<const int32_t*>(w + ws.off_mptr);
+    mp.max_parts = ws.max_parts;
+    mp.part_lse2 = reinterpret_cast<const float*>(w + W.off_plse);
+    mp.part_o = reinterpret_cast<const float*>(w + W.off_po);
+    mp.out = out;
+    mp.lse = lse;
+    mp.n_rows = ws.n_out_rows;
+    e = launch_merge(P->cfg.dtype, P->cfg.head_dim, mp, s);
+  }
+  if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("window step: ") + hipGetErrorString(e));
+  return KV_OK;
 }
 
 }  // extern "C"

@@ -76,6 +76,8 @@ static void take_page(kv_pool* P, int32_t p) {
   P->free.take(p);
   P->rc[p] = 1;
 }
+void fa_take_page(kv_pool* P, int32_t p) { take_page(P, p); }
+void fa_unref_page(kv_pool* P, int32_t p) { unref_page(P, p); }
 
 void fa_pos_append(std::vector<PosRun>& v, int64_t p0, int64_t n) {
   if (n <= 0) return;

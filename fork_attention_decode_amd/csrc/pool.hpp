@@ -68,6 +68,23 @@ struct DecodePlanCache {
   int64_t stats[6] = {0, 0, 0, 0, 0, 0};
 };
 
+// A steady-state decode window: every sequence's next n_steps slots reserved up front and
+// one decode plan per step, so each step is a fixed set of kernel launches.
+struct DecodeWindow {
+  struct Step {
+    size_t off_plan = 0, off_items = 0, off_mptr = 0, off_writes = 0;
+    int32_t n_items = 0, n_out_rows = 0, max_parts = 1;
+  };
+  bool valid = false;
+  uint64_t version = 0;
+  std::vector<int32_t> seqs;
+  int32_t n_q_heads = 0, n_steps = 0, n_cow = 0;
+  size_t off_cow = 0, off_plse = 0, off_po = 0, ws_need = 0;
+  std::vector<Step> steps;
+  std::vector<char> blob;  // plans, step writes and tail copies, at their workspace offsets
+  void* ws = nullptr;
+};
+
 }  // namespace fa
 
 struct kv_pool {
@@ -98,4 +115,5 @@ struct kv_pool {
   int32_t ticket = 0;
   int32_t epoch = 0;
   fa::DecodePlanCache plan;
+  fa::DecodeWindow window;
 };

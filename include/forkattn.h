@@ -267,6 +267,31 @@ int dag_attn_run(const void* q, void* out, float* lse, int32_t T, int32_t n_q_he
                  int32_t block, float sm_scale, const void* workspace, size_t ws_bytes,
                  hipStream_t stream);
 
+/* Steady-state decode window (Agentrix, "ForkAttention": the fork kernels run inside the
+ * captured decode loop; AgentKV runs compaction and fork attention in graph-captured
+ * decode).  Every step appends one token to each of n sequences and decodes all of them:
+ *   kv_window_plan: reserves each sequence's next n_steps slots now -- the page table
+ *     changes as if n_steps rounds of one kv_append per sequence (in list order) had
+ *     run: a shared partial tail is copied, new pages are taken lowest-first, positions
+ *     continue from next_pos -- and plans the decode of every step (contexts through
+ *     that step's token) on the host; *ws_need = workspace bytes.  Works on
+ *     metadata-only pools too (page table only).  Sequences must be distinct; n_q_heads
+ *     as for fork_attn_decode.  KV_ERR_OOM leaves everything unchanged.
+ *   kv_window_upload: uploads the plans into `workspace` (DEVICE, >= ws_need bytes,
+ *     caller-owned, used by every step) and enqueues the tail copies.
+ *   kv_window_step(step): writes k, v (DEVICE [n][Hkv][d], pool dtype, keys rotated for
+ *     their reserved positions) into the step's slots and decodes q (DEVICE
+ *     [n][Hq][d]) into out / lse as fork_attn_decode would over the contexts through
+ *     this step; three kernels with fixed arguments, so steps 0 .. n_steps - 1 can be
+ *     captured in a HIP graph once and replayed.  Steps run in order on one stream.
+ * Any other page-table change ends the window (its calls then return KV_ERR_INVALID;
+ * replays of a captured graph are not checked). */
+int kv_window_plan(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n, int32_t n_q_heads,
+                   int32_t n_steps, size_t* ws_need);
+int kv_window_upload(kv_pool_t* pool, void* workspace, size_t ws_bytes, hipStream_t stream);
+int kv_window_step(kv_pool_t* pool, int32_t step, const void* k, const void* v, const void* q,
+                   void* out, float* lse, float sm_scale, hipStream_t stream);
+
 /* Gradients of dag_attn_prefill over the same CSR (Octopus "Packed DAG-GRPO": the packed
  * episode is trained through the same block-sparse attention, so only DAG-visible pairs
  * carry gradient).  For query head h (KV head g = h / (Hq / Hkv)) and a visible pair

@@ -1,0 +1,102 @@
+"""Steady-state decode window (kv_window_plan / kv_window_upload / kv_window_step) on the
+GPU: every step appends one token to each branch and decodes all branches.
+
+- each step's outputs against the fp64 oracle, which appends the same tokens one round
+  at a time and decodes over the materialised contexts (bf16 outputs max-abs 2e-2 and
+  mean-abs 2e-3, LSE max-abs 2e-3, as for fork_attn_decode);
+- the window's steps captured once in a HIP graph and replayed on a second, identical
+  pool give the eager outputs bit for bit;
+- the page table after the window equals the oracle's (block tables, positions).
+The branches share a partial tail page (the prefix is not page-aligned), so the first
+step writes into copies, and the window crosses page boundaries.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from tests.harness import build_device_pool, check_close, out_to_f64, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(sc, n, n_steps, seed):
+    rng = np.random.default_rng(seed)
+    d, hkv, hq = sc.head_dim, sc.n_kv_heads, sc.n_q_heads
+    k = [W.to_bf16_bits(rng.standard_normal((n, hkv, d)) / np.sqrt(d)) for _ in range(n_steps)]
+    v = [W.to_bf16_bits(rng.standard_normal((n, hkv, d))) for _ in range(n_steps)]
+    q = [W.to_bf16_bits(rng.standard_normal((n, hq, d))) for _ in range(n_steps)]
+    return k, v, q
+
+
+def _run(fa, pool, seqs, sc, n_steps, kt, vt, qt, outs, lses, graph):
+    import torch
+    ws = pool.window(seqs, sc.n_q_heads, n_steps)
+    torch.cuda.synchronize()
+    if not graph:
+        for s in range(n_steps):
+            pool.window_step(s, kt[s], vt[s], qt[s], sc.sm_scale, outs[s], lses[s])
+        torch.cuda.synchronize()
+        return ws
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for s in range(n_steps):
+            pool.window_step(s, kt[s], vt[s], qt[s], sc.sm_scale, outs[s], lses[s])
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    return ws, g
+
+
+def test_window_steps_oracle_graph_and_page_table():
+    import torch
+    import fork_attention_decode_amd as fa
+    from oracle import attention as att, pagetable as pt
+    sc = W.fork_scenario(prefix=517, branches=4, private=[0, 3, 16, 30], hq=8, hkv=2, d=128, seed=73)
+    sc.n_pages += 48
+    seqs, n_steps = [1, 2, 3, 4], 20
+    n = len(seqs)
+    print(f"[case] window: {n} branches, {n_steps} steps, shared partial tail", flush=True)
+    kb, vb, qb = _inputs(sc, n, n_steps, 74)
+    kt = [to_torch(x, "bf16") for x in kb]
+    vt = [to_torch(x, "bf16") for x in vb]
+    qt = [to_torch(x, "bf16") for x in qb]
+    res = {}
+    keep = []
+    for mode in ("eager", "graph"):
+        pool, _ = build_device_pool(sc)
+        outs = [torch.empty((n, sc.n_q_heads, sc.head_dim), dtype=torch.bfloat16, device="cuda")
+                for _ in range(n_steps)]
+        lses = [torch.empty((n, sc.n_q_heads), dtype=torch.float32, device="cuda") for _ in range(n_steps)]
+        keep.append(_run(fa, pool, seqs, sc, n_steps, kt, vt, qt, outs, lses, mode == "graph"))
+        res[mode] = (pool, [o.clone() for o in outs], [l.clone() for l in lses])
+    for s in range(n_steps):
+        assert torch.equal(res["eager"][1][s], res["graph"][1][s]) and torch.equal(res["eager"][2][s],
+                                                                                   res["graph"][2][s]), s
+    print("[ok] graph replay equals the eager steps", flush=True)
+
+    table, _ = pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, sc.dtype))
+    f = W.bf16_bits_to_f64
+    for s in range(n_steps):
+        for i, b in enumerate(seqs):
+            table.append(b, 1, k=f(kb[s][i:i + 1]), v=f(vb[s][i:i + 1]))
+        ro, rl = att.decode(table, seqs, f(qb[s]), sc.sm_scale)
+        o = out_to_f64(res["eager"][1][s], "bf16")
+        check_close(o, ro, 2e-2, 2e-3, f"window step {s}")
+        check_close(res["eager"][2][s].double().cpu().numpy(), rl, 2e-3, 2e-3, f"window step {s} lse")
+    print(f"[ok] {n_steps} steps against the oracle", flush=True)
+    pool = res["eager"][0]
+    for b in seqs:
+        assert list(pool.block_table(b)) == table.block_table(b), b
+        assert np.array_equal(pool.positions(b), table.positions(b)), b
+    print("[ok] page table after the window", flush=True)
+    # a second window continues from the first (the pool's own decode sees the same context)
+    pool = res["eager"][0]
+    kb2, vb2, qb2 = _inputs(sc, n, 3, 75)
+    outs = [torch.empty((n, sc.n_q_heads, sc.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    lses = [torch.empty((n, sc.n_q_heads), dtype=torch.float32, device="cuda") for _ in range(3)]
+    _run(fa, pool, seqs, sc, 3, [to_torch(x, "bf16") for x in kb2], [to_torch(x, "bf16") for x in vb2],
+         [to_torch(x, "bf16") for x in qb2], outs, lses, False)
+    o_dec, l_dec = pool.decode(seqs, to_torch(qb2[2], "bf16"), sc.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_dec, outs[2]) and torch.equal(l_dec, lses[2])
+    print("[ok] second window; its last step equals fork_attn_decode over the same context", flush=True)

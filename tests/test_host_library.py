@@ -267,3 +267,51 @@ def test_error_paths_leave_state():
     with pytest.raises(fa.ForkAttnError) as e:
         fa.fork_attn_decode(pool.handle, [0], 1, 1, 1, 0, 1.0, 1, 1)
     assert e.value.status in (fa.KV_ERR_INVALID, fa.KV_ERR_NOT_FOUND)
+
+
+@pytest.mark.parametrize("make,n_steps", [
+    (lambda: W.fork_scenario(prefix=517, branches=5, private=[0, 3, 16, 30, 1], hq=8, hkv=2, d=128, seed=71), 20),
+    (lambda: W.dag_scenario(root=300, threads=3, private=90, mounts_per_thread=2, mount_len=33, hq=8, hkv=2, d=128,
+                            seed=72), 37),
+])
+def test_window_reservation_equals_rounds_of_appends(make, n_steps):
+    # kv_window_plan changes the page table exactly as n_steps rounds of one append per
+    # sequence (in list order): shared partial tails copied first, pages lowest-first
+    sc = make()
+    sc.n_pages += 64
+    ora, _ = pt.replay(sc, with_data=False)
+    pool = fa.Pool(sc.n_kv_heads, sc.head_dim, sc.n_pages, page_size=sc.page_size, rope_theta=sc.rope_theta,
+                   metadata_only=True)
+    for op in sc.ops:
+        if op[0] == "create":
+            pool.seq_create()
+        elif op[0] == "append":
+            blk = sc.blocks[op[2]]
+            pool.append(op[1], n=len(blk.pos), positions=blk.pos)
+        elif op[0] == "fork":
+            pool.fork(op[1])
+        elif op[0] == "mount":
+            pool.mount(*op[1:])
+    live = [i for i, s in enumerate(ora.seqs) if s.live]
+    seqs = [i for i in live if i != 0][::-1]  # not in creation order
+    need = fa.kv_window_plan(pool.handle, seqs, sc.n_q_heads, n_steps)
+    assert need > 0
+    for _ in range(n_steps):
+        for b in seqs:
+            ora.append(b, 1)
+    _cmp(pool.handle, ora, live)
+
+
+def test_window_oom_and_duplicates_leave_state():
+    pool = fa.Pool(1, 2, 6, page_size=4, metadata_only=True)
+    a = pool.seq_create()
+    pool.append(a, n=5)
+    b = pool.fork(a)
+    before = [list(fa.kv_block_table(pool.handle, s)) for s in (a, b)]
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.kv_window_plan(pool.handle, [a, b], 2, 8)  # 2 tail copies + 2 x 2 new pages > 4 free
+    assert e.value.status == fa.KV_ERR_OOM
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.kv_window_plan(pool.handle, [a, a], 2, 1)
+    assert e.value.status == fa.KV_ERR_INVALID
+    assert [list(fa.kv_block_table(pool.handle, s)) for s in (a, b)] == before
