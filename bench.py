@@ -340,6 +340,60 @@ def bench_prefill_bwd(reps, warmup):
     }
 
 
+def bench_window(n_steps=16, replays=20):
+    """Steady-state decode on the shared-prefix workload: a window of n_steps steps (each
+    appends one token to all 16 branches and decodes them) captured once in a HIP graph and
+    replayed; HIP events around the replays.  A replay rewrites the same reserved slots
+    with the same rows, so every replay does the window's full work."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from tests.harness import build_device_pool, to_torch
+    sc = W.shared_prefix_fork()
+    sc.n_pages += 64
+    log("window: building the shared-prefix pool")
+    pool, _ = build_device_pool(sc)
+    seqs = list(sc.queries)
+    n, hq, hkv, d = len(seqs), sc.n_q_heads, sc.n_kv_heads, sc.head_dim
+    rng = np.random.default_rng(81)
+    kt = [to_torch(W.to_bf16_bits(rng.standard_normal((n, hkv, d)) / np.sqrt(d)), "bf16") for _ in range(n_steps)]
+    vt = [to_torch(W.to_bf16_bits(rng.standard_normal((n, hkv, d))), "bf16") for _ in range(n_steps)]
+    qt = [to_torch(W.to_bf16_bits(rng.standard_normal((n, hq, d))), "bf16") for _ in range(n_steps)]
+    out = torch.empty((n, hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((n, hq), dtype=torch.float32, device="cuda")
+    t0 = time.perf_counter()
+    ws = pool.window(seqs, hq, n_steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        for st in range(n_steps):
+            pool.window_step(st, kt[st], vt[st], qt[st], sc.sm_scale, out, lse)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(replays):
+        g.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    us_step = ev[0].elapsed_time(ev[1]) * 1e3 / (replays * n_steps)
+    del ws
+    return {
+        "workload": "shared_prefix_fork_decode steady state (16 branches, 32,768-token prefix + 2,048 private each; "
+                    "every step appends one token per branch, then decodes all 16)",
+        "steps_per_window": n_steps,
+        "us_per_step": us_step,
+        "branch_tokens_per_s": n / (us_step * 1e-6),
+        "host_plan_upload_ms_per_window": (t1 - t0) * 1e3,
+        "host_capture_ms_per_window": (t2 - t1) * 1e3,
+        "timed": "HIP events around back-to-back replays of the captured window (page write + decode + merge per "
+                 "step)",
+    }
+
+
 def bench_select(reps, warmup):
     """Key scoring + keep selection (AgentKV's choice of entries before a compression) on
     one 131,072-token sequence (32 / 8 heads, d = 128, bf16) with 32 representative
@@ -511,6 +565,7 @@ def main():
     ap.add_argument("--only-akv", action="store_true", help="time the drop + repos object alone (profiling)")
     ap.add_argument("--only-select", action="store_true", help="time the key scoring object alone (profiling)")
     ap.add_argument("--only-prefill-bwd", action="store_true", help="time the prefill backward alone (profiling)")
+    ap.add_argument("--only-window", action="store_true", help="time the steady-state decode window alone")
     ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy 256 MiB device to device once (a kernel of known "
@@ -540,6 +595,9 @@ def main():
         return
     if args.only_select:
         print(json.dumps({"agentkv_select": bench_select(20, 3)}))
+        return
+    if args.only_window:
+        print(json.dumps({"decode_window": bench_window()}))
         return
     if args.only_prefill_bwd:
         print(json.dumps({"prefill_backward": bench_prefill_bwd(5, 1)}))
@@ -609,6 +667,8 @@ def main():
 
     if not args.only_decode:
         result["prefill"] = bench_prefill(args.prefill_reps, 3, 0.0 if args.no_cpu_baseline else 8.0)
+        torch.cuda.empty_cache()
+        result["decode_window"] = bench_window()
         torch.cuda.empty_cache()
         result["prefill_backward"] = bench_prefill_bwd(5, 1)
         torch.cuda.empty_cache()

@@ -299,7 +299,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, const int32_t
   };
 
   f32x4 o[NDB];
-  float m = -INFINITY, l = 0.f;
+  float m = -1e30f, l = 0.f;  // finite: an item whose slot ranges are all empty stays (m, 0)
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -326,7 +326,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, const int32_t
   if (active) {
     l = row_sum4(l);
     if (orow >= 0) {
-      const float inv = 1.f / l;
+      const float inv = l > 0.f ? 1.f / l : 0.f;  // an item with no visible key leaves (0, -inf)
       float* dst = p.part_o + (size_t)slot * D + 4 * g;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[db] * inv;

@@ -85,7 +85,14 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
       }
     }
   }
-  std::stable_sort(ent.begin(), ent.end(), [](const Entry& x, const Entry& y) { return x.page < y.page; });
+  {  // stable counting sort by page id (readers of a page keep query order)
+    std::vector<int32_t> at((size_t)C.n_pages + 1, 0);
+    for (const Entry& e : ent) at[(size_t)e.page + 1]++;
+    for (size_t p = 1; p < at.size(); ++p) at[p] += at[p - 1];
+    std::vector<Entry> sorted(ent.size());
+    for (const Entry& e : ent) sorted[(size_t)at[(size_t)e.page]++] = e;
+    ent.swap(sorted);
+  }
 
   // 2. chunks grouped into segments by reader multiset
   std::vector<Segment> segs;
@@ -361,7 +368,9 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
   }
   if (need > P->free.count()) FAIL(P, KV_ERR_OOM, "not enough free pages for the window");
   DecodeWindow& W = P->window;
+  std::vector<char> keep = std::move(W.blob);  // reuse the host buffer of the previous window
   W = DecodeWindow();
+  W.blob = std::move(keep);
   // 1. reservation, round by round (the page order of n_steps rounds of single appends)
   std::vector<PageWrite> cow;
   std::vector<std::vector<PageWrite>> writes((size_t)n_steps, std::vector<PageWrite>((size_t)n));
@@ -391,22 +400,46 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
       S->n += 1;
     }
   P->version++;
-  // 2. one plan per step over the contexts through that step's token
+  // 2. one plan over the contexts through the window's last token; step s is that plan
+  // with each reserved page's slot range cut at the sequence's length after step s (the
+  // same items, partial slots and merge counts; a chunk past the cut is empty)
   std::vector<int64_t> cap((size_t)n);
+  for (int32_t i = 0; i < n; ++i) cap[i] = base[i] + n_steps;
+  if (int e = build_plan(P, seqs, n, hq, cap.data())) {
+    P->plan.valid = false;
+    W = DecodeWindow();
+    return e;  // the page table keeps the reservation; the window is unusable
+  }
+  DecodePlanCache& pc = P->plan;
+  // the chunk records of reserved pages: (record int, query index, logical page)
+  std::vector<int64_t> owner((size_t)P->cfg.n_pages, -1);  // page -> i * 2^32 + logical page
+  for (int32_t i = 0; i < n; ++i) {
+    Seq* S = fa_seq(P, seqs[i]);
+    for (int64_t L = base[i] / PS; L < (int64_t)S->pages.size(); ++L)
+      owner[(size_t)S->pages[(size_t)L]] = ((int64_t)i << 32) | L;
+  }
+  struct Patch {
+    size_t at;
+    int32_t i;
+    int64_t L;
+  };
+  std::vector<Patch> patches;
+  {
+    const int32_t* recs = reinterpret_cast<const int32_t*>(pc.blob.data() + pc.off_items);
+    for (int32_t it = 0; it < pc.n_items; ++it) {
+      const int32_t* rec = recs + (size_t)it * kRecInts;
+      for (int32_t c = 0; c < rec[0]; ++c) {
+        const int64_t o = owner[(size_t)rec[kRecChunk + 2 * c]];
+        if (o >= 0) patches.push_back({(size_t)it * kRecInts + kRecChunk + 2 * c + 1, (int32_t)(o >> 32), o & 0xffffffff});
+      }
+    }
+  }
   size_t off = 0;
   W.off_cow = off;
   off = align256(off + cow.size() * sizeof(PageWrite));
-  int64_t part_slots = 0;
-  std::vector<std::vector<char>> blobs((size_t)n_steps);
+  const size_t plan_bytes = pc.blob.size();
   W.steps.resize((size_t)n_steps);
   for (int32_t st = 0; st < n_steps; ++st) {
-    for (int32_t i = 0; i < n; ++i) cap[i] = base[i] + st + 1;
-    if (int e = build_plan(P, seqs, n, hq, cap.data())) {
-      P->plan.valid = false;
-      W = DecodeWindow();
-      return e;  // the page table keeps the reservation; the window is unusable
-    }
-    DecodePlanCache& pc = P->plan;
     DecodeWindow::Step& ws = W.steps[st];
     ws.off_plan = off;
     ws.off_items = off + pc.off_items;
@@ -414,25 +447,32 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
     ws.n_items = pc.n_items;
     ws.n_out_rows = pc.n_out_rows;
     ws.max_parts = pc.max_parts;
-    part_slots = std::max<int64_t>(part_slots, (int64_t)pc.n_out_rows * pc.max_parts);
-    blobs[st] = pc.blob;
-    off = align256(off + pc.blob.size());
+    off = align256(off + plan_bytes);
     ws.off_writes = off;
     off = align256(off + (size_t)n * sizeof(PageWrite));
   }
-  P->plan.valid = false;  // the cached plan was overwritten by the window's plans
+  const int64_t part_slots = (int64_t)pc.n_out_rows * pc.max_parts;
   W.off_plse = off;
   off = align256(off + (size_t)part_slots * sizeof(float));
   W.off_po = off;
   off = align256(off + (size_t)part_slots * P->cfg.head_dim * sizeof(float));
   W.ws_need = std::max<size_t>(off, 256);
-  W.blob.assign(W.off_plse, 0);
+  W.blob.resize(W.off_plse);  // alignment gaps are never read
   if (!cow.empty()) std::memcpy(W.blob.data() + W.off_cow, cow.data(), cow.size() * sizeof(PageWrite));
   for (int32_t st = 0; st < n_steps; ++st) {
     const DecodeWindow::Step& ws = W.steps[st];
-    std::memcpy(W.blob.data() + ws.off_plan, blobs[st].data(), blobs[st].size());
+    char* plan = W.blob.data() + ws.off_plan;
+    std::memcpy(plan, pc.blob.data(), plan_bytes);
+    int32_t* recs = reinterpret_cast<int32_t*>(plan + pc.off_items);
+    for (const Patch& q : patches) {
+      const int64_t len = base[q.i] + st + 1 - q.L * PS;  // valid slots of the page after step st
+      const int32_t lohi = recs[q.at], lo = lohi & 0xff, hi = lohi >> 8;
+      const int32_t nh = (int32_t)std::min<int64_t>(hi, std::max<int64_t>(lo, len));
+      recs[q.at] = nh > lo ? (lo | nh << 8) : 0;
+    }
     std::memcpy(W.blob.data() + ws.off_writes, writes[st].data(), (size_t)n * sizeof(PageWrite));
   }
+  P->plan.valid = false;  // the cached plan now describes the window's last step only
   W.seqs.assign(seqs, seqs + n);
   W.n_q_heads = hq;
   W.n_steps = n_steps;

@@ -6,7 +6,8 @@ GPU: every step appends one token to each branch and decodes all branches.
   mean-abs 2e-3, LSE max-abs 2e-3, as for fork_attn_decode);
 - the window's steps captured once in a HIP graph and replayed on a second, identical
   pool give the eager outputs bit for bit;
-- the page table after the window equals the oracle's (block tables, positions).
+- the page table after the window equals the oracle's (block tables, positions), and a
+  second window continues from it.
 The branches share a partial tail page (the prefix is not page-aligned), so the first
 step writes into copies, and the window crosses page boundaries.
 """
@@ -89,14 +90,47 @@ def test_window_steps_oracle_graph_and_page_table():
         assert list(pool.block_table(b)) == table.block_table(b), b
         assert np.array_equal(pool.positions(b), table.positions(b)), b
     print("[ok] page table after the window", flush=True)
-    # a second window continues from the first (the pool's own decode sees the same context)
-    pool = res["eager"][0]
+    # a second window continues from the first
     kb2, vb2, qb2 = _inputs(sc, n, 3, 75)
     outs = [torch.empty((n, sc.n_q_heads, sc.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
     lses = [torch.empty((n, sc.n_q_heads), dtype=torch.float32, device="cuda") for _ in range(3)]
     _run(fa, pool, seqs, sc, 3, [to_torch(x, "bf16") for x in kb2], [to_torch(x, "bf16") for x in vb2],
          [to_torch(x, "bf16") for x in qb2], outs, lses, False)
-    o_dec, l_dec = pool.decode(seqs, to_torch(qb2[2], "bf16"), sc.sm_scale)
-    torch.cuda.synchronize()
-    assert torch.equal(o_dec, outs[2]) and torch.equal(l_dec, lses[2])
-    print("[ok] second window; its last step equals fork_attn_decode over the same context", flush=True)
+    for s in range(3):
+        for i, b in enumerate(seqs):
+            table.append(b, 1, k=f(kb2[s][i:i + 1]), v=f(vb2[s][i:i + 1]))
+        ro, rl = att.decode(table, seqs, f(qb2[s]), sc.sm_scale)
+        check_close(out_to_f64(outs[s], "bf16"), ro, 2e-2, 2e-3, f"second window step {s}")
+        check_close(lses[s].double().cpu().numpy(), rl, 2e-3, 2e-3, f"second window step {s} lse")
+    print("[ok] a second window continues from the first", flush=True)
+
+
+def test_long_window_items_past_the_cut():
+    # page-aligned prefix, a branch with no private tokens: its window pages form a
+    # private segment split into several work items, and at early steps the last items
+    # lie wholly past the cut (every slot range empty)
+    import torch
+    import fork_attention_decode_amd as fa
+    from oracle import attention as att, pagetable as pt
+    sc = W.fork_scenario(prefix=512, branches=2, private=[0, 5], hq=8, hkv=2, d=128, seed=76)
+    sc.n_pages += 40
+    seqs, n_steps = [1, 2], 200
+    n = len(seqs)
+    print(f"[case] window: {n} branches, {n_steps} steps from a page-aligned fork", flush=True)
+    kb, vb, qb = _inputs(sc, n, n_steps, 77)
+    pool, _ = build_device_pool(sc)
+    outs = [torch.empty((n, sc.n_q_heads, sc.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(n_steps)]
+    lses = [torch.empty((n, sc.n_q_heads), dtype=torch.float32, device="cuda") for _ in range(n_steps)]
+    _run(fa, pool, seqs, sc, n_steps, [to_torch(x, "bf16") for x in kb], [to_torch(x, "bf16") for x in vb],
+         [to_torch(x, "bf16") for x in qb], outs, lses, False)
+    table, _ = pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, sc.dtype))
+    f = W.bf16_bits_to_f64
+    check = {0, 1, 15, 16, 17, 100, 199}
+    for s in range(n_steps):
+        for i, b in enumerate(seqs):
+            table.append(b, 1, k=f(kb[s][i:i + 1]), v=f(vb[s][i:i + 1]))
+        if s in check:
+            ro, rl = att.decode(table, seqs, f(qb[s]), sc.sm_scale)
+            check_close(out_to_f64(outs[s], "bf16"), ro, 2e-2, 2e-3, f"long window step {s}")
+            check_close(lses[s].double().cpu().numpy(), rl, 2e-3, 2e-3, f"long window step {s} lse")
+    print(f"[ok] steps {sorted(check)} against the oracle", flush=True)
