@@ -394,6 +394,66 @@ def bench_window(n_steps=16, replays=20):
     }
 
 
+def bench_restore(reps=20, n_seg=4, seg_len=128):
+    """Restore of n_seg segments of seg_len tokens (own positions) into one branch of the
+    shared-prefix workload: kv_append per segment, then kv_causal_attend over the restored
+    tokens (HIP events around kv_causal_attend on its stream)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import fork_attention_decode_amd as fa
+    from tests.harness import build_device_pool, to_torch
+    sc = W.shared_prefix_fork()
+    sc.n_pages += 64
+    log("restore: building the shared-prefix pool")
+    pool, _ = build_device_pool(sc)
+    seq, hq, hkv, d = sc.queries[0], sc.n_q_heads, sc.n_kv_heads, sc.head_dim
+    rng = np.random.default_rng(83)
+    for i in range(n_seg):
+        k = to_torch(W.to_bf16_bits(rng.standard_normal((seg_len, hkv, d)) / np.sqrt(d)), "bf16")
+        v = to_torch(W.to_bf16_bits(rng.standard_normal((seg_len, hkv, d))), "bf16")
+        pool.append(seq, k=k, v=v, positions=np.arange(100000 * (i + 1), 100000 * (i + 1) + seg_len))
+    n = n_seg * seg_len
+    q = to_torch(W.to_bf16_bits(rng.standard_normal((n, hq, d))), "bf16")
+    t0 = time.perf_counter()
+    need = fa.kv_causal_attend_workspace_size(pool.handle, seq, n, hq)  # plans (cached for the calls below)
+    host_plan_ms = (time.perf_counter() - t0) * 1e3
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((n, hq), dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        fa.kv_causal_attend(pool.handle, seq, n, hq, q.data_ptr(), out.data_ptr(), lse.data_ptr(), sc.sm_scale,
+                            ws.data_ptr(), ws.numel(), st)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        run()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ctx = int(pool.info(seq)[0])
+    kv_bytes = ctx * hkv * d * 2 * 2
+    return {
+        "workload": f"restore {n_seg} segments x {seg_len} tokens (own positions) into a branch of the shared-prefix "
+                    f"workload, then causal attention of the {n} restored tokens over the {ctx}-token context",
+        "us_mean": float(np.mean(ms)) * 1e3, "us_p10": float(np.percentile(ms, 10)) * 1e3,
+        "host_plan_ms": host_plan_ms,
+        "context_kv_bytes": kv_bytes,
+        "streamed_kv_bytes": kv_bytes * (n // 16),
+        "streamed_GBps": kv_bytes * (n // 16) / (float(np.mean(ms)) * 1e-3) / 1e9,
+        "rows": n * hq,
+        "note": "the attention runs as one split-K decode of n x Hq rows: every context page is streamed once per "
+                "group of 64 / G = 16 restored tokens, so it reads the context n / 16 times; the plan (host) is "
+                "built once and cached, the events enclose the kernels",
+    }
+
+
 def bench_select(reps, warmup):
     """Key scoring + keep selection (AgentKV's choice of entries before a compression) on
     one 131,072-token sequence (32 / 8 heads, d = 128, bf16) with 32 representative
@@ -566,6 +626,7 @@ def main():
     ap.add_argument("--only-select", action="store_true", help="time the key scoring object alone (profiling)")
     ap.add_argument("--only-prefill-bwd", action="store_true", help="time the prefill backward alone (profiling)")
     ap.add_argument("--only-window", action="store_true", help="time the steady-state decode window alone")
+    ap.add_argument("--only-restore", action="store_true", help="time the segment restore alone")
     ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy 256 MiB device to device once (a kernel of known "
@@ -595,6 +656,9 @@ def main():
         return
     if args.only_select:
         print(json.dumps({"agentkv_select": bench_select(20, 3)}))
+        return
+    if args.only_restore:
+        print(json.dumps({"restore": bench_restore()}))
         return
     if args.only_window:
         print(json.dumps({"decode_window": bench_window()}))
@@ -669,6 +733,8 @@ def main():
         result["prefill"] = bench_prefill(args.prefill_reps, 3, 0.0 if args.no_cpu_baseline else 8.0)
         torch.cuda.empty_cache()
         result["decode_window"] = bench_window()
+        torch.cuda.empty_cache()
+        result["restore"] = bench_restore()
         torch.cuda.empty_cache()
         result["prefill_backward"] = bench_prefill_bwd(5, 1)
         torch.cuda.empty_cache()

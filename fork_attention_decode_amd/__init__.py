@@ -88,6 +88,8 @@ _SIGS = {
                          _sz, _P],
     "dag_attn_prepare": [_P, _P, _i32, _i32, _i32, _i32, _P, _P, _P, C.c_int64, _i32, _P, _sz, _P],
     "dag_attn_run": [_P, _P, _P, _i32, _i32, _i32, _i32, _P, C.c_int64, _i32, C.c_float, _P, _sz, _P],
+    "kv_causal_attend_workspace_size": [_P, _i32, C.c_int64, _i32, _psz],
+    "kv_causal_attend": [_P, _i32, C.c_int64, _i32, _P, _P, _P, C.c_float, _P, _sz, _P],
     "kv_window_plan": [_P, _pi32, _i32, _i32, _i32, _psz],
     "kv_window_upload": [_P, _P, _sz, _P],
     "kv_window_step": [_P, _i32, _P, _P, _P, _P, _P, C.c_float, _P],
@@ -367,6 +369,19 @@ def dag_attn_run(q: int, out: int, lse: int, T: int, n_q_heads: int, n_kv_heads:
                                             sm_scale, workspace or None, ws_bytes, stream or None))
 
 
+def kv_causal_attend_workspace_size(pool: int, seq: int, n: int, n_q_heads: int) -> int:
+    out = C.c_size_t(0)
+    _check("kv_causal_attend_workspace_size",
+           lib.kv_causal_attend_workspace_size(pool, seq, n, n_q_heads, C.byref(out)), pool)
+    return out.value
+
+
+def kv_causal_attend(pool: int, seq: int, n: int, n_q_heads: int, q: int, out: int, lse: int, sm_scale: float,
+                     workspace: int, ws_bytes: int, stream: int = 0):
+    _check("kv_causal_attend", lib.kv_causal_attend(pool, seq, n, n_q_heads, q, out, lse or None, sm_scale,
+                                                    workspace or None, ws_bytes, stream or None), pool)
+
+
 def kv_window_plan(pool: int, seqs, n_q_heads: int, n_steps: int) -> int:
     s = np.ascontiguousarray(np.asarray(seqs, np.int32))
     out = C.c_size_t(0)
@@ -623,6 +638,19 @@ class Pool:
             lse = torch.empty((n, hq), dtype=torch.float32, device=q.device)
         fork_attn_decode(self.handle, seqs, hq, q.data_ptr(), out.data_ptr(), lse.data_ptr(), sm_scale,
                          workspace.data_ptr(), workspace.numel(), self._stream())
+        return out, lse
+
+    def causal_attend(self, seq: int, q, sm_scale: float):
+        """Attention of the sequence's last q.shape[0] tokens (kv_causal_attend); returns
+        (out, lse)."""
+        import torch
+        n, hq, d = q.shape
+        need = kv_causal_attend_workspace_size(self.handle, seq, n, hq)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        out = torch.empty_like(q)
+        lse = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+        kv_causal_attend(self.handle, seq, n, hq, q.data_ptr(), out.data_ptr(), lse.data_ptr(), sm_scale,
+                         ws.data_ptr(), ws.numel(), self._stream())
         return out, lse
 
     def window(self, seqs: Sequence[int], n_q_heads: int, n_steps: int):

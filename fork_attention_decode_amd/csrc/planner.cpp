@@ -65,8 +65,8 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
   if (G > kMaxRows) FAIL(P, KV_ERR_UNSUPPORTED, "more than 64 query heads per KV head");
   const int32_t PS = C.page_size;
   DecodePlanCache& pc = P->plan;
-  if (!len_cap && pc.valid && pc.version == P->version && pc.n_q_heads == hq && (int32_t)pc.seqs.size() == n &&
-      std::equal(pc.seqs.begin(), pc.seqs.end(), seqs))
+  if (!len_cap && pc.valid && pc.causal_n == 0 && pc.version == P->version && pc.n_q_heads == hq &&
+      (int32_t)pc.seqs.size() == n && std::equal(pc.seqs.begin(), pc.seqs.end(), seqs))
     return KV_OK;
 
   // 1. visible runs
@@ -243,6 +243,7 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
   pc.stats[4] = unique_tokens * C.n_kv_heads * 2 * D * (int64_t)es;
   pc.stats[5] = n_out;
   pc.valid = true;
+  pc.causal_n = len_cap ? -1 : 0;
   pc.version = P->version;
   pc.seqs.assign(seqs, seqs + n);
   pc.n_q_heads = hq;
@@ -537,6 +538,78 @@ int kv_window_step(kv_pool_t* P, int32_t step, const void* k, const void* v, con
     e = launch_merge(P->cfg.dtype, P->cfg.head_dim, mp, s);
   }
   if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("window step: ") + hipGetErrorString(e));
+  return KV_OK;
+}
+
+// ------------------------------------------------------------------ causal attention of a sequence's last tokens
+// AgentKV restores an evicted or edited span of a sequence with one prefill in which each
+// segment keeps its own positions: the caller appends the segments' K / V (kv_append with
+// their positions) and then attends the last n tokens, token j over the context through
+// itself (every earlier own token, then the mounts), as n rows of one split-K decode.
+
+static int causal_plan(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t hq) {
+  Seq* S = fa_seq(P, seq);
+  if (!S) FAIL(P, KV_ERR_NOT_FOUND, "no live sequence");
+  if (n < 1 || n > S->n) FAIL(P, KV_ERR_INVALID, "the attended tokens must be the sequence's last n (n >= 1)");
+  if (n * hq > (int64_t)1 << 30) FAIL(P, KV_ERR_UNSUPPORTED, "too many query rows");
+  DecodePlanCache& pc = P->plan;
+  if (pc.valid && pc.causal_n == n && pc.version == P->version && pc.n_q_heads == hq && !pc.seqs.empty() &&
+      pc.seqs[0] == seq)
+    return KV_OK;  // planned for the same sequence state
+  std::vector<kv_seq_t> seqs((size_t)n, seq);
+  std::vector<int64_t> cap((size_t)n);
+  for (int64_t j = 0; j < n; ++j) cap[(size_t)j] = S->n - n + j + 1;
+  const int st = build_plan(P, seqs.data(), (int32_t)n, hq, cap.data());
+  if (st == KV_OK) pc.causal_n = n;
+  return st;
+}
+
+int kv_causal_attend_workspace_size(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t n_q_heads, size_t* bytes) {
+  if (!P || !bytes) FAIL(P, KV_ERR_INVALID, "null argument");
+  if (int st = causal_plan(P, seq, n, n_q_heads)) return st;
+  *bytes = P->plan.ws_need;
+  return KV_OK;
+}
+
+int kv_causal_attend(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t n_q_heads, const void* q, void* out, float* lse,
+                     float sm_scale, void* workspace, size_t ws_bytes, hipStream_t s) {
+  if (!P) FAIL(P, KV_ERR_INVALID, "null pool");
+  if (!P->device) FAIL(P, KV_ERR_INVALID, "metadata-only pool has no KV data");
+  if (!q || !out || !workspace) FAIL(P, KV_ERR_INVALID, "null device pointer");
+  if (int st = causal_plan(P, seq, n, n_q_heads)) return st;
+  DecodePlanCache& pc = P->plan;  // cached for the same sequence state (never a decode plan)
+  if (ws_bytes < pc.ws_need) FAIL(P, KV_ERR_WORKSPACE, "causal attention workspace too small");
+  char* w = static_cast<char*>(workspace);
+  hipError_t e = hipSuccess;
+  if (pc.ws != workspace) {
+    e = fa_upload(P, w, pc.blob.data(), pc.blob.size(), s);
+    if (e == hipSuccess) pc.ws = workspace;
+  }
+  if (e == hipSuccess) {
+    DecodeParams dp;
+    dp.q = q;
+    dp.k_pages = P->k;
+    dp.v_pages = P->v;
+    dp.items = reinterpret_cast<const int32_t*>(w + pc.off_items);
+    dp.part_lse2 = reinterpret_cast<float*>(w + pc.off_plse);
+    dp.part_o = reinterpret_cast<float*>(w + pc.off_po);
+    dp.n_items = pc.n_items;
+    dp.n_pages = P->cfg.n_pages;
+    dp.scale_log2 = sm_scale * 1.4426950408889634f;
+    e = launch_decode(P->cfg.dtype, P->cfg.head_dim, dp, s);
+  }
+  if (e == hipSuccess) {
+    MergeParams mp;
+    mp.count = reinterpret_cast<const int32_t*>(w + pc.off_mptr);
+    mp.max_parts = pc.max_parts;
+    mp.part_lse2 = reinterpret_cast<const float*>(w + pc.off_plse);
+    mp.part_o = reinterpret_cast<const float*>(w + pc.off_po);
+    mp.out = out;
+    mp.lse = lse;
+    mp.n_rows = pc.n_out_rows;
+    e = launch_merge(P->cfg.dtype, P->cfg.head_dim, mp, s);
+  }
+  if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("causal attention: ") + hipGetErrorString(e));
   return KV_OK;
 }
 

@@ -66,6 +66,7 @@ struct DecodePlanCache {
   int32_t n_items = 0, n_out_rows = 0, max_parts = 1;
   std::vector<char> blob;  // host image of the plan part of the workspace
   int64_t stats[6] = {0, 0, 0, 0, 0, 0};
+  int64_t causal_n = 0;  // 0: a decode plan; n > 0: causal rows of the last n tokens; -1: other caps
 };
 
 // A steady-state decode window: every sequence's next n_steps slots reserved up front and

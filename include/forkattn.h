@@ -292,6 +292,22 @@ int kv_window_upload(kv_pool_t* pool, void* workspace, size_t ws_bytes, hipStrea
 int kv_window_step(kv_pool_t* pool, int32_t step, const void* k, const void* v, const void* q,
                    void* out, float* lse, float sm_scale, hipStream_t stream);
 
+/* Causal attention of a sequence's last n tokens (AgentKV restores an evicted or edited
+ * span with one prefill in which each segment keeps its own positions: append the
+ * segments' K / V with kv_append and their positions, then call this).  Token j of the
+ * n (0-based, query q[j]) attends to the sequence's own tokens up to and including
+ * itself, then to the mounts, exactly as fork_attn_decode would for a sequence that
+ * ended at that token.  q: DEVICE [n][Hq][d] (pool dtype, rotated by the caller); out:
+ * DEVICE [n][Hq][d]; lse: DEVICE fp32 [n][Hq] or NULL.  workspace: DEVICE, at least
+ * kv_causal_attend_workspace_size bytes for the same sequence state, n and n_q_heads.
+ * The attention runs as n rows of one split-K decode (every context page is read once
+ * per group of 64 / G rows).  1 <= n <= the sequence's length.  Stream-ordered. */
+int kv_causal_attend_workspace_size(kv_pool_t* pool, kv_seq_t seq, int64_t n, int32_t n_q_heads,
+                                    size_t* bytes);
+int kv_causal_attend(kv_pool_t* pool, kv_seq_t seq, int64_t n, int32_t n_q_heads, const void* q,
+                     void* out, float* lse, float sm_scale, void* workspace, size_t ws_bytes,
+                     hipStream_t stream);
+
 /* Gradients of dag_attn_prefill over the same CSR (Octopus "Packed DAG-GRPO": the packed
  * episode is trained through the same block-sparse attention, so only DAG-visible pairs
  * carry gradient).  For query head h (KV head g = h / (Hq / Hkv)) and a visible pair

@@ -82,3 +82,22 @@ def decode(table, seqs, q: np.ndarray, scale: float):
         k, v = table.materialise(sid)
         o[i], lse[i] = attend_heads(np.asarray(q[i], np.float64), k, v, scale)
     return o, lse
+
+
+def causal_last(table, sid: int, q: np.ndarray, scale: float):
+    """Attention of the last n own tokens of sequence `sid` (n = q.shape[0]) of an oracle
+    ``PageTable`` (with data): token j of the n attends to the own tokens up to and
+    including itself, then to the mounts (AgentKV page, restoring an evicted or edited
+    span with one prefill; each token sees what a decode at that token would see).
+
+    q [n, Hq, d] (fp64) -> (o [n, Hq, d], lse [n, Hq])."""
+    n, hq, d = q.shape
+    k, v = table.materialise(sid)  # own tokens, then mounts
+    n_own = table.info(sid)[0]
+    o = np.zeros((n, hq, d))
+    lse = np.zeros((n, hq))
+    for j in range(n):
+        end = n_own - n + j + 1
+        idx = np.concatenate([np.arange(end), np.arange(n_own, k.shape[0])]).astype(np.int64)
+        o[j], lse[j] = attend_heads(np.asarray(q[j], np.float64), k[idx], v[idx], scale)
+    return o, lse

@@ -170,3 +170,44 @@ def test_repos_closed_form_from_raw_draws():
         assert np.max(np.abs(k[:r] - exp)) < 2 ** -8 * 4 / np.sqrt(32) * 1.01
         assert np.array_equal(v[:r], W.storage_to_f64(sc.blocks[2 * i].v, "bf16")[kept])
         assert list(table.positions(i)) == list(range(r)) + [r]
+
+
+def test_causal_last_pins():
+    # the attention of a sequence's last n tokens (oracle/attention.causal_last):
+    # fresh sequence = causal self-attention (torch SDPA, float64); last row = decode;
+    # with a mount: own prefix causal and the mounted keys visible to every row
+    torch = pytest.importorskip("torch")
+    from oracle import attention as att, pagetable as pt
+    rng = np.random.default_rng(91)
+    hkv, hq, d, P = 2, 4, 8, 4
+    t = pt.PageTable(64, P, hkv, d, with_data=True)
+    a = t.create()
+    k, v = rng.standard_normal((23, hkv, d)), rng.standard_normal((23, hkv, d))
+    t.append(a, 23, k=k, v=v)
+    q = rng.standard_normal((23, hq, d))
+    o, lse = att.causal_last(t, a, q, 0.4)
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]                       # [1, Hq, n, d]
+    tk = torch.from_numpy(np.repeat(k, hq // hkv, axis=1)).permute(1, 0, 2)[None]
+    tv = torch.from_numpy(np.repeat(v, hq // hkv, axis=1)).permute(1, 0, 2)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=0.4)
+    assert np.allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+    od, ld = att.decode(t, [a], q[-1:], 0.4)
+    assert np.allclose(o[-1], od[0]) and np.allclose(lse[-1], ld[0])
+    # mount: b = fork-free second sequence mounting 5 tokens of a
+    b = t.create()
+    kb, vb = rng.standard_normal((9, hkv, d)), rng.standard_normal((9, hkv, d))
+    t.append(b, 9, k=kb, v=vb)
+    t.mount(b, a, 3, 5)
+    qb = rng.standard_normal((4, hq, d))
+    o2, _ = att.causal_last(t, b, qb, 0.4)
+    keys = np.concatenate([kb, k[3:8]])
+    vals = np.concatenate([vb, v[3:8]])
+    for j in range(4):
+        vis = np.zeros(len(keys), bool)
+        vis[:9 - 4 + j + 1] = True
+        vis[9:] = True
+        s = torch.einsum("hd,nhd->hn", torch.from_numpy(qb[j]),
+                         torch.from_numpy(np.repeat(keys, hq // hkv, axis=1))) * 0.4
+        s = s.masked_fill(~torch.from_numpy(vis)[None], float("-inf"))
+        want = torch.einsum("hn,nhd->hd", torch.softmax(s, -1), torch.from_numpy(np.repeat(vals, hq // hkv, axis=1)))
+        assert np.allclose(o2[j], want.numpy(), rtol=1e-12, atol=1e-12), j
