@@ -315,3 +315,37 @@ def test_window_oom_and_duplicates_leave_state():
         fa.kv_window_plan(pool.handle, [a, a], 2, 1)
     assert e.value.status == fa.KV_ERR_INVALID
     assert [list(fa.kv_block_table(pool.handle, s)) for s in (a, b)] == before
+
+
+def test_new_entry_points_reject_bad_arguments():
+    # window, causal attention and the prefill backward fail with a status, before any
+    # device work, on metadata-only pools and bad shapes
+    pool = fa.Pool(1, 2, 8, page_size=4, metadata_only=True)
+    a = pool.seq_create()
+    pool.append(a, n=6)
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.kv_window_upload(pool.handle, 1, 1 << 20)  # nothing planned
+    assert e.value.status == fa.KV_ERR_INVALID
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.kv_window_step(pool.handle, 0, 1, 1, 1, 1, 0, 1.0)
+    assert e.value.status == fa.KV_ERR_INVALID
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.kv_causal_attend_workspace_size(pool.handle, a, 7, 2)  # more tokens than the sequence holds
+    assert e.value.status == fa.KV_ERR_INVALID
+    assert fa.kv_causal_attend_workspace_size(pool.handle, a, 6, 2) > 0  # metadata pools can plan
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.kv_causal_attend(pool.handle, a, 6, 2, 1, 1, 0, 1.0, 1, 1 << 20)
+    assert e.value.status == fa.KV_ERR_INVALID  # no KV data
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.dag_attn_backward_workspace_size(64, 3, 2, 64, 1)  # Hq not a multiple of Hkv
+    assert e.value.status == fa.KV_ERR_INVALID
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.dag_attn_backward(1, 1, 1, 1, 1, 1, 1, 1, 1, 64, 4, 2, 64, 1, 1, 1, 1, 64, 1.0, 1, 1 << 30)
+    assert e.value.status == fa.KV_ERR_UNSUPPORTED  # head_dim 64
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.dag_attn_backward(1, 1, 1, 1, 1, 1, 1, 1, 1, 64, 4, 2, 128, 1, 1, 1, 1, 64, 0.0, 1, 1 << 30)
+    assert e.value.status == fa.KV_ERR_INVALID  # scale
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.dag_attn_backward(1, 1, 1, 1, 1, 1, 1, 1, 1, 64, 4, 2, 128, 1, 1, 1, 1, 64, 1.0, 1, 16)
+    assert e.value.status == fa.KV_ERR_WORKSPACE
+    assert pool.info(a)[0] == 6
