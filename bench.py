@@ -515,7 +515,7 @@ def bench_select(reps, warmup):
         "score_GBps": alg / (float(np.mean(sc_us)) * 1e-6) / 1e9,
         "score_frac_of_8TBps": alg / (float(np.mean(sc_us)) * 1e-6) / 1e9 / HBM_PEAK_GBPS,
         "note": "algorithmic bytes = the sequence's K read twice (normaliser pass, then score pass); the events "
-                "enclose the whole kv_score call, including the upload of its chunk list",
+                "enclose the whole kv_score call (its chunk list is uploaded by the first call only)",
         "select_us_mean": float(np.mean(se_us)),
         "select_drop_end_to_end_ms": e2e_ms, "kept": int(mask.sum()), "reps": reps,
     }

@@ -117,4 +117,11 @@ struct kv_pool {
   int32_t epoch = 0;
   fa::DecodePlanCache plan;
   fa::DecodeWindow window;
+  // key scoring: the chunk list last uploaded (sequence, page-table version, workspace)
+  struct ScoreChunks {
+    uint64_t version = 0;
+    kv_seq_t seq = -1;
+    void* ws = nullptr;
+    int32_t n_ch = 0;
+  } score_chunks;
 };

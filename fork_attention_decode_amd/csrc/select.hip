@@ -569,9 +569,17 @@ int kv_score(kv_pool_t* P, kv_seq_t seq, const void* q_rep, int32_t n_rep, int32
   if (n_tok == 0) return KV_OK;
   char* ws = static_cast<char*>(workspace);
   Seq* S = fa_seq(P, seq);
-  const std::vector<int32_t> chunks = score_chunks(S, P->cfg.page_size);
-  hipError_t e = fa_upload(P, ws + w.chunks, chunks.data(), chunks.size() * 4, stream);
-  if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("score chunk upload: ") + hipGetErrorString(e));
+  auto& sc = P->score_chunks;  // the list is uploaded again only when the page table or workspace changed
+  if (sc.version != P->version || sc.seq != seq || sc.ws != workspace) {
+    const std::vector<int32_t> chunks = score_chunks(S, P->cfg.page_size);
+    hipError_t e = fa_upload(P, ws + w.chunks, chunks.data(), chunks.size() * 4, stream);
+    if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("score chunk upload: ") + hipGetErrorString(e));
+    sc.version = P->version;
+    sc.seq = seq;
+    sc.ws = workspace;
+    sc.n_ch = (int32_t)(chunks.size() / 2);
+  }
+  hipError_t e = hipSuccess;
   ScoreParams p;
   p.q = static_cast<const bf16_t*>(q_rep);
   p.k_pages = static_cast<const bf16_t*>(P->k);
@@ -584,7 +592,7 @@ int kv_score(kv_pool_t* P, kv_seq_t seq, const void* q_rep, int32_t n_rep, int32
   p.hkv = P->cfg.n_kv_heads;
   p.G = n_q_heads / p.hkv;
   p.pool_pages = P->cfg.n_pages;
-  p.n_ch = (int32_t)(chunks.size() / 2);
+  p.n_ch = sc.n_ch;
   p.n_lp = (int32_t)S->pages.size();
   const int RT = score_tiles(n_rep * p.G);
   p.RP = 16 * RT;

@@ -349,9 +349,11 @@ int dag_attn_backward(const void* q, const void* k, const void* v, const void* o
  * the caller.  scores: device float [n_tokens].  Needs a device bf16 pool (head_dim 64 or
  * 128; KV_ERR_UNSUPPORTED otherwise) and n_rep * n_q_heads / Hkv <= 256.  The workspace
  * (kv_score_workspace_size bytes, caller-owned device memory) holds the visible chunk
- * list, the per-row normalisers and per-KV-head partial sums; the pool's cached decode
- * plan is left alone.  Stream-ordered; scores are valid once the stream has run the
- * call. */
+ * list, the per-row normalisers and per-KV-head partial sums; the chunk list stays in
+ * it between calls and is uploaded again only after a page-table change, for another
+ * sequence or another workspace (so do not write the workspace between calls); the
+ * pool's cached decode plan is left alone.  Stream-ordered; scores are valid once the
+ * stream has run the call. */
 int kv_score_workspace_size(kv_pool_t* pool, kv_seq_t seq, int32_t n_rep, int32_t n_q_heads, size_t* bytes);
 int kv_score(kv_pool_t* pool, kv_seq_t seq, const void* q_rep, int32_t n_rep, int32_t n_q_heads, float sm_scale,
              float* scores, void* workspace, size_t ws_bytes, hipStream_t stream);
