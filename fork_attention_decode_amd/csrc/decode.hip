@@ -432,7 +432,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lds[ring_slots<T, D>() * 2 * kPage * D * sizeof(T)];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  decode_item<T, D>(p, p.items + (size_t)blockIdx.x * kRecInts, wave, lane, lds);
+  const int it = blockIdx.x;
+  decode_item<T, D>(p, it < p.n_head ? p.items + (size_t)it * kRecInts : p.tail + (size_t)(it - p.n_head) * kRecInts,
+                    wave, lane, lds);
 }
 
 // ---------------------------------------------------------------- page writes (append)

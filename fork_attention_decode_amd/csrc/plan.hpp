@@ -49,10 +49,12 @@ struct DecodeParams {
   const void* q;            // [n_seqs][Hq][d]
   const void* k_pages;
   const void* v_pages;
-  const int32_t* items;     // [n_items][kRecInts]
+  const int32_t* items;     // [n_head][kRecInts]: items 0 .. n_head - 1
+  const int32_t* tail;      // [n_items - n_head][kRecInts]: the rest (a decode window's per-step items)
   float* part_lse2;         // [n_partials] log2-domain log-sum-exp of the partial
   float* part_o;            // [n_partials][d] normalised partial output
   int32_t n_items;
+  int32_t n_head;
   int32_t n_pages;          // pool capacity: head h's blocks start at h * n_pages
   float scale_log2;         // sm_scale * log2(e)
 };

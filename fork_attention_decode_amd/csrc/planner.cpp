@@ -299,6 +299,8 @@ int fork_attn_partials(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq
   dp.k_pages = P->k;
   dp.v_pages = P->v;
   dp.items = reinterpret_cast<const int32_t*>(w + pc.off_items);
+  dp.tail = dp.items;
+  dp.n_head = pc.n_items;
   dp.part_lse2 = reinterpret_cast<float*>(w + pc.off_plse);
   dp.part_o = reinterpret_cast<float*>(w + pc.off_po);
   dp.n_items = pc.n_items;
@@ -419,36 +421,49 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
     for (int64_t L = base[i] / PS; L < (int64_t)S->pages.size(); ++L)
       owner[(size_t)S->pages[(size_t)L]] = ((int64_t)i << 32) | L;
   }
+  // items that read a reserved page form the per-step tail (their slot ranges change
+  // with the step); the rest, and the merge counts, are shared by every step
+  const int32_t* recs0 = reinterpret_cast<const int32_t*>(pc.blob.data() + pc.off_items);
+  std::vector<int32_t> head, tail;
+  for (int32_t it = 0; it < pc.n_items; ++it) {
+    const int32_t* rec = recs0 + (size_t)it * kRecInts;
+    bool mine = false;
+    for (int32_t c = 0; c < rec[0] && !mine; ++c) mine = owner[(size_t)rec[kRecChunk + 2 * c]] >= 0;
+    (mine ? tail : head).push_back(it);
+  }
   struct Patch {
-    size_t at;
+    size_t at;  // int offset in the tail records
     int32_t i;
     int64_t L;
   };
   std::vector<Patch> patches;
-  {
-    const int32_t* recs = reinterpret_cast<const int32_t*>(pc.blob.data() + pc.off_items);
-    for (int32_t it = 0; it < pc.n_items; ++it) {
-      const int32_t* rec = recs + (size_t)it * kRecInts;
-      for (int32_t c = 0; c < rec[0]; ++c) {
-        const int64_t o = owner[(size_t)rec[kRecChunk + 2 * c]];
-        if (o >= 0) patches.push_back({(size_t)it * kRecInts + kRecChunk + 2 * c + 1, (int32_t)(o >> 32), o & 0xffffffff});
-      }
+  for (size_t t = 0; t < tail.size(); ++t) {
+    const int32_t* rec = recs0 + (size_t)tail[t] * kRecInts;
+    for (int32_t c = 0; c < rec[0]; ++c) {
+      const int64_t o = owner[(size_t)rec[kRecChunk + 2 * c]];
+      if (o >= 0) patches.push_back({t * kRecInts + kRecChunk + 2 * c + 1, (int32_t)(o >> 32), o & 0xffffffff});
     }
   }
+  const size_t rec_bytes = (size_t)kRecInts * sizeof(int32_t);
   size_t off = 0;
   W.off_cow = off;
   off = align256(off + cow.size() * sizeof(PageWrite));
-  const size_t plan_bytes = pc.blob.size();
+  const size_t off_head = off;
+  off = align256(off + head.size() * rec_bytes);
+  const size_t off_mptr = off;
+  const size_t mptr_bytes = (size_t)pc.n_out_rows * sizeof(int32_t);
+  off = align256(off + mptr_bytes);
   W.steps.resize((size_t)n_steps);
   for (int32_t st = 0; st < n_steps; ++st) {
     DecodeWindow::Step& ws = W.steps[st];
-    ws.off_plan = off;
-    ws.off_items = off + pc.off_items;
-    ws.off_mptr = off + pc.off_mptr;
+    ws.off_items = off_head;
+    ws.off_mptr = off_mptr;
+    ws.n_head = (int32_t)head.size();
     ws.n_items = pc.n_items;
     ws.n_out_rows = pc.n_out_rows;
     ws.max_parts = pc.max_parts;
-    off = align256(off + plan_bytes);
+    ws.off_plan = off;  // this step's tail records
+    off = align256(off + tail.size() * rec_bytes);
     ws.off_writes = off;
     off = align256(off + (size_t)n * sizeof(PageWrite));
   }
@@ -460,11 +475,14 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
   W.ws_need = std::max<size_t>(off, 256);
   W.blob.resize(W.off_plse);  // alignment gaps are never read
   if (!cow.empty()) std::memcpy(W.blob.data() + W.off_cow, cow.data(), cow.size() * sizeof(PageWrite));
+  for (size_t h = 0; h < head.size(); ++h)
+    std::memcpy(W.blob.data() + off_head + h * rec_bytes, recs0 + (size_t)head[h] * kRecInts, rec_bytes);
+  std::memcpy(W.blob.data() + off_mptr, pc.blob.data() + pc.off_mptr, mptr_bytes);
   for (int32_t st = 0; st < n_steps; ++st) {
     const DecodeWindow::Step& ws = W.steps[st];
-    char* plan = W.blob.data() + ws.off_plan;
-    std::memcpy(plan, pc.blob.data(), plan_bytes);
-    int32_t* recs = reinterpret_cast<int32_t*>(plan + pc.off_items);
+    int32_t* recs = reinterpret_cast<int32_t*>(W.blob.data() + ws.off_plan);
+    for (size_t t = 0; t < tail.size(); ++t)
+      std::memcpy(recs + t * kRecInts, recs0 + (size_t)tail[t] * kRecInts, rec_bytes);
     for (const Patch& q : patches) {
       const int64_t len = base[q.i] + st + 1 - q.L * PS;  // valid slots of the page after step st
       const int32_t lohi = recs[q.at], lo = lohi & 0xff, hi = lohi >> 8;
@@ -519,6 +537,8 @@ int kv_window_step(kv_pool_t* P, int32_t step, const void* k, const void* v, con
     dp.k_pages = P->k;
     dp.v_pages = P->v;
     dp.items = reinterpret_cast<const int32_t*>(w + ws.off_items);
+    dp.tail = reinterpret_cast<const int32_t*>(w + ws.off_plan);
+    dp.n_head = ws.n_head;
     dp.part_lse2 = reinterpret_cast<float*>(w + W.off_plse);
     dp.part_o = reinterpret_cast<float*>(w + W.off_po);
     dp.n_items = ws.n_items;
@@ -591,6 +611,8 @@ int kv_causal_attend(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t n_q_heads, c
     dp.k_pages = P->k;
     dp.v_pages = P->v;
     dp.items = reinterpret_cast<const int32_t*>(w + pc.off_items);
+    dp.tail = dp.items;
+    dp.n_head = pc.n_items;
     dp.part_lse2 = reinterpret_cast<float*>(w + pc.off_plse);
     dp.part_o = reinterpret_cast<float*>(w + pc.off_po);
     dp.n_items = pc.n_items;

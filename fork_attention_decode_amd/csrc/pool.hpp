@@ -73,8 +73,10 @@ struct DecodePlanCache {
 // one decode plan per step, so each step is a fixed set of kernel launches.
 struct DecodeWindow {
   struct Step {
-    size_t off_plan = 0, off_items = 0, off_mptr = 0, off_writes = 0;
-    int32_t n_items = 0, n_out_rows = 0, max_parts = 1;
+    size_t off_plan = 0;   // this step's tail item records
+    size_t off_items = 0;  // the head item records (shared by every step)
+    size_t off_mptr = 0, off_writes = 0;
+    int32_t n_head = 0, n_items = 0, n_out_rows = 0, max_parts = 1;
   };
   bool valid = false;
   uint64_t version = 0;
