@@ -50,7 +50,7 @@ constexpr int kImg = kB * kD * 2;          // bytes of one 64 x 128 bf16 image (
 constexpr int kQRec = 4 * kImg + 2 * kB * 4;  // Q OPO, dO OPO, Q TP, dO TP, lse2[64], D[64]
 constexpr int kKRec = 3 * kImg;            // K OPO, V OPO, K TP
 constexpr int kThreads = 256;
-constexpr unsigned kRowMask = 0xffffffu;   // CSC entry: query block | kind << 24
+constexpr unsigned kRowMask = 0xffffffu;   // CSC entry: query block | listed bits << 24 | diagonal bits << 26
 
 // OPO unit of element (r, 8 c8 .. 8 c8 + 7) of a 64 x 128 block: fragment (r / 16, c8 / 4),
 // lane r % 16 + 16 (c8 % 4)
@@ -152,7 +152,9 @@ __global__ __launch_bounds__(kThreads) void k_prep_kernel(const bf16_t* __restri
   for (int u = tid; u < kB * 16; u += kThreads) k_tp[u] = reinterpret_cast<const i32x4*>(tp)[u];
 }
 
-// CSC of the block mask, rows ascending within a column: one workgroup per column
+// The mask's transpose over pairs of key-block columns, query blocks ascending within a
+// pair (count, scan, fill), found by a binary search of each column in every CSR row.
+
 // index of column c in the ascending col[a..b), or -1
 __device__ __forceinline__ int find_in_row(const int32_t* col, int a, int b, int c) {
   int lo = a, hi = b;
