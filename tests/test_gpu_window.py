@@ -134,3 +134,31 @@ def test_long_window_items_past_the_cut():
             check_close(out_to_f64(outs[s], "bf16"), ro, 2e-2, 2e-3, f"long window step {s}")
             check_close(lses[s].double().cpu().numpy(), rl, 2e-3, 2e-3, f"long window step {s} lse")
     print(f"[ok] steps {sorted(check)} against the oracle", flush=True)
+
+
+def test_one_step_window_and_an_empty_sequence():
+    # a window of one step over a fork and a new, empty root (its first token opens its
+    # first page)
+    import torch
+    import fork_attention_decode_amd as fa
+    from oracle import attention as att, pagetable as pt
+    sc = W.fork_scenario(prefix=48, branches=1, private=[5], hq=8, hkv=2, d=128, seed=78)
+    sc.n_pages += 8
+    sc.ops.append(("create",))  # sequence 2, no tokens
+    seqs = [2, 1]
+    n = len(seqs)
+    print("[case] one-step window over an empty root and a fork", flush=True)
+    kb, vb, qb = _inputs(sc, n, 1, 79)
+    pool, _ = build_device_pool(sc)
+    outs = [torch.empty((n, sc.n_q_heads, sc.head_dim), dtype=torch.bfloat16, device="cuda")]
+    lses = [torch.empty((n, sc.n_q_heads), dtype=torch.float32, device="cuda")]
+    _run(fa, pool, seqs, sc, 1, [to_torch(kb[0], "bf16")], [to_torch(vb[0], "bf16")], [to_torch(qb[0], "bf16")],
+         outs, lses, False)
+    table, _ = pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, sc.dtype))
+    f = W.bf16_bits_to_f64
+    for i, b in enumerate(seqs):
+        table.append(b, 1, k=f(kb[0][i:i + 1]), v=f(vb[0][i:i + 1]))
+    ro, rl = att.decode(table, seqs, f(qb[0]), sc.sm_scale)
+    check_close(out_to_f64(outs[0], "bf16"), ro, 2e-2, 2e-3, "one-step window")
+    check_close(lses[0].double().cpu().numpy(), rl, 2e-3, 2e-3, "one-step window lse")
+    print("[ok] one-step window", flush=True)

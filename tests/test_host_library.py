@@ -348,4 +348,5 @@ def test_new_entry_points_reject_bad_arguments():
     with pytest.raises(fa.ForkAttnError) as e:
         fa.dag_attn_backward(1, 1, 1, 1, 1, 1, 1, 1, 1, 64, 4, 2, 128, 1, 1, 1, 1, 64, 1.0, 1, 16)
     assert e.value.status == fa.KV_ERR_WORKSPACE
+    fa.dag_attn_backward(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 4, 2, 128, 0, 0, 0, 0, 64, 1.0, 0, 0)  # T = 0: nothing to do
     assert pool.info(a)[0] == 6
