@@ -240,7 +240,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // with buffer loads straight into LDS (each wave loads a quarter of every chunk); wave w
 // computes rows [16 w, 16 w + 16) from LDS, two chunks per step; NB - 2 chunks stay in
 // flight; one workgroup barrier per step.
-template <typename T, int D>
+template <typename T, int D, int kPolicy>
 __device__ __forceinline__ void decode_item(const DecodeParams& p, const int32_t* __restrict__ rec, int wave,
                                             int lane, char* ring) {
   using TR = Tr<T, D>;
@@ -283,7 +283,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, const int32_t
 #pragma unroll
     for (int i = 0; i < LPW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
-                                               lane * 16 + i * 1024, 0, 0, kCachePolicyNT);
+                                               lane * 16 + i * 1024, 0, 0, kPolicy);
   };
   auto lohi_of = [&](int j) {
     if (j >= n) return 0;  // empty slot range: every key masked
@@ -427,13 +427,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   if (p.lse && half == 0 && lane == 0) p.lse[row] = S > 0.f ? (M + __log2f(S)) * 0.69314718055994531f : -INFINITY;
 }
 
-template <typename T, int D>
+// kPolicy: kCachePolicyNT for a single pass over the pages; 0 (cached) where the same
+// pages are streamed again by other items of the launch
+template <typename T, int D, int kPolicy>
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lds[ring_slots<T, D>() * 2 * kPage * D * sizeof(T)];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int it = blockIdx.x;
-  decode_item<T, D>(p, it < p.n_head ? p.items + (size_t)it * kRecInts : p.tail + (size_t)(it - p.n_head) * kRecInts,
+  decode_item<T, D, kPolicy>(p, it < p.n_head ? p.items + (size_t)it * kRecInts : p.tail + (size_t)(it - p.n_head) * kRecInts,
                     wave, lane, lds);
 }
 
@@ -486,7 +488,10 @@ __global__ __launch_bounds__(256) void page_write_kernel(T* __restrict__ kp, T* 
 template <typename T, int D>
 static hipError_t decode_t(const DecodeParams& p, hipStream_t s) {
   if (p.n_items == 0) return hipSuccess;
-  decode_kernel<T, D><<<p.n_items, 256, 0, s>>>(p);
+  if (p.cached)
+    decode_kernel<T, D, 0><<<p.n_items, 256, 0, s>>>(p);
+  else
+    decode_kernel<T, D, kCachePolicyNT><<<p.n_items, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -55,6 +55,7 @@ struct DecodeParams {
   float* part_o;            // [n_partials][d] normalised partial output
   int32_t n_items;
   int32_t n_head;
+  int32_t cached;           // 1: cached loads (the launch streams the same pages several times)
   int32_t n_pages;          // pool capacity: head h's blocks start at h * n_pages
   float scale_log2;         // sm_scale * log2(e)
 };

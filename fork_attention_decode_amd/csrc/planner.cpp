@@ -301,6 +301,7 @@ int fork_attn_partials(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq
   dp.items = reinterpret_cast<const int32_t*>(w + pc.off_items);
   dp.tail = dp.items;
   dp.n_head = pc.n_items;
+  dp.cached = 0;
   dp.part_lse2 = reinterpret_cast<float*>(w + pc.off_plse);
   dp.part_o = reinterpret_cast<float*>(w + pc.off_po);
   dp.n_items = pc.n_items;
@@ -539,6 +540,7 @@ int kv_window_step(kv_pool_t* P, int32_t step, const void* k, const void* v, con
     dp.items = reinterpret_cast<const int32_t*>(w + ws.off_items);
     dp.tail = reinterpret_cast<const int32_t*>(w + ws.off_plan);
     dp.n_head = ws.n_head;
+    dp.cached = 0;
     dp.part_lse2 = reinterpret_cast<float*>(w + W.off_plse);
     dp.part_o = reinterpret_cast<float*>(w + W.off_po);
     dp.n_items = ws.n_items;
@@ -613,6 +615,7 @@ int kv_causal_attend(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t n_q_heads, c
     dp.items = reinterpret_cast<const int32_t*>(w + pc.off_items);
     dp.tail = dp.items;
     dp.n_head = pc.n_items;
+    dp.cached = 1;  // every context page is streamed once per group of 64 / G restored tokens
     dp.part_lse2 = reinterpret_cast<float*>(w + pc.off_plse);
     dp.part_o = reinterpret_cast<float*>(w + pc.off_po);
     dp.n_items = pc.n_items;
