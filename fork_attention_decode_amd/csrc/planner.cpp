@@ -48,6 +48,8 @@ struct Segment {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+constexpr size_t kMaxCutRanges = 4;  // slot ranges of one page cut into shared chunks
+
 template <typename T>
 void put(std::vector<char>& blob, size_t off, const std::vector<T>& v) {
   if (!v.empty()) std::memcpy(blob.data() + off, v.data(), v.size() * sizeof(T));
@@ -137,11 +139,32 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
       }
       std::sort(cuts.begin(), cuts.end());
       cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
-      for (size_t c = 0; c + 1 < cuts.size(); ++c) {
+      if (cuts.size() <= kMaxCutRanges + 1) {
+        // a few slot ranges: one chunk per range, read by every reader that covers it
+        for (size_t c = 0; c + 1 < cuts.size(); ++c) {
+          key.clear();
+          for (size_t e = a; e < b; ++e)
+            if (ent[e].lo <= cuts[c] && ent[e].hi >= cuts[c + 1]) key.push_back(ent[e].reader);
+          if (!key.empty()) emit(ent[a].page, cuts[c], cuts[c + 1], key);
+        }
+      } else {
+        // many ranges (a causal diagonal page: each of its own tokens reads up to itself):
+        // the readers of the most common range share one chunk, every other reader reads
+        // its own range alone, instead of one reader set per distinct range
+        std::map<std::pair<int32_t, int32_t>, int32_t> freq;
+        for (size_t e = a; e < b; ++e) ++freq[{ent[e].lo, ent[e].hi}];
+        std::pair<int32_t, int32_t> top = freq.begin()->first;
+        for (const auto& f : freq)
+          if (f.second > freq[top]) top = f.first;
         key.clear();
         for (size_t e = a; e < b; ++e)
-          if (ent[e].lo <= cuts[c] && ent[e].hi >= cuts[c + 1]) key.push_back(ent[e].reader);
-        if (!key.empty()) emit(ent[a].page, cuts[c], cuts[c + 1], key);
+          if (ent[e].lo == top.first && ent[e].hi == top.second) key.push_back(ent[e].reader);
+        emit(ent[a].page, top.first, top.second, key);
+        for (size_t e = a; e < b; ++e)
+          if (!(ent[e].lo == top.first && ent[e].hi == top.second)) {
+            key.assign(1, ent[e].reader);
+            emit(ent[a].page, ent[e].lo, ent[e].hi, key);
+          }
       }
     }
     a = b;
