@@ -84,20 +84,22 @@ def decode(table, seqs, q: np.ndarray, scale: float):
     return o, lse
 
 
-def causal_last(table, sid: int, q: np.ndarray, scale: float):
+def causal_last(table, sid: int, q, scale: float, rows=None):
     """Attention of the last n own tokens of sequence `sid` (n = q.shape[0]) of an oracle
     ``PageTable`` (with data): token j of the n attends to the own tokens up to and
     including itself, then to the mounts (AgentKV page, restoring an evicted or edited
     span with one prefill; each token sees what a decode at that token would see).
 
-    q [n, Hq, d] (fp64) -> (o [n, Hq, d], lse [n, Hq])."""
+    q [n, Hq, d] (fp64; anything indexable by row) -> (o [n, Hq, d], lse [n, Hq]), or
+    only the listed rows j, in their order, when `rows` is given."""
     n, hq, d = q.shape
     k, v = table.materialise(sid)  # own tokens, then mounts
     n_own = table.info(sid)[0]
-    o = np.zeros((n, hq, d))
-    lse = np.zeros((n, hq))
-    for j in range(n):
+    rows = list(range(n)) if rows is None else [int(j) for j in rows]
+    o = np.zeros((len(rows), hq, d))
+    lse = np.zeros((len(rows), hq))
+    for r, j in enumerate(rows):
         end = n_own - n + j + 1
         idx = np.concatenate([np.arange(end), np.arange(n_own, k.shape[0])]).astype(np.int64)
-        o[j], lse[j] = attend_heads(np.asarray(q[j], np.float64), k[idx], v[idx], scale)
+        o[r], lse[r] = attend_heads(np.asarray(q[j], np.float64), k[idx], v[idx], scale)
     return o, lse

@@ -9,7 +9,10 @@ GPU: every step appends one token to each branch and decodes all branches.
 - the page table after the window equals the oracle's (block tables, positions), and a
   second window continues from it.
 The branches share a partial tail page (the prefix is not page-aligned), so the first
-step writes into copies, and the window crosses page boundaries.
+step writes into copies, and the window crosses page boundaries.  The timed steady-state
+workload runs at full size too: 16 branches over a 32,768-token prefix + 2,048 private
+tokens each, a 16-step window captured in one HIP graph and replayed once; its first
+and last steps against the oracle.
 """
 import numpy as np
 import pytest
@@ -162,3 +165,33 @@ def test_one_step_window_and_an_empty_sequence():
     check_close(out_to_f64(outs[0], "bf16"), ro, 2e-2, 2e-3, "one-step window")
     check_close(lses[0].double().cpu().numpy(), rl, 2e-3, 2e-3, "one-step window lse")
     print("[ok] one-step window", flush=True)
+
+
+def test_window_full_size():
+    import torch
+    import fork_attention_decode_amd as fa
+    from oracle import attention as att, pagetable as pt
+    sc = W.shared_prefix_fork()
+    sc.n_pages += 64
+    seqs, n_steps = list(sc.queries), 16
+    n = len(seqs)
+    print(f"[case] window, full size: {n} branches, {n_steps} steps in one graph", flush=True)
+    kb, vb, qb = _inputs(sc, n, n_steps, 80)
+    pool, _ = build_device_pool(sc)
+    outs = [torch.empty((n, sc.n_q_heads, sc.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(n_steps)]
+    lses = [torch.empty((n, sc.n_q_heads), dtype=torch.float32, device="cuda") for _ in range(n_steps)]
+    keep = _run(fa, pool, seqs, sc, n_steps, [to_torch(x, "bf16") for x in kb], [to_torch(x, "bf16") for x in vb],
+                [to_torch(x, "bf16") for x in qb], outs, lses, True)
+    table, _ = pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, sc.dtype))
+    f = W.bf16_bits_to_f64
+    for s in range(n_steps):
+        for i, b in enumerate(seqs):
+            table.append(b, 1, k=f(kb[s][i:i + 1]), v=f(vb[s][i:i + 1]))
+        if s in (0, n_steps - 1):
+            ro, rl = att.decode(table, seqs, f(qb[s]), sc.sm_scale)
+            check_close(out_to_f64(outs[s], "bf16"), ro, 2e-2, 2e-3, f"full-size window step {s}")
+            check_close(lses[s].double().cpu().numpy(), rl, 2e-3, 2e-3, f"full-size window step {s} lse")
+            print(f"[ok] full-size window step {s}", flush=True)
+    for b in seqs:
+        assert list(pool.block_table(b)) == table.block_table(b), b
+    del keep

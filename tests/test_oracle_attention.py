@@ -193,6 +193,9 @@ def test_causal_last_pins():
     assert np.allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
     od, ld = att.decode(t, [a], q[-1:], 0.4)
     assert np.allclose(o[-1], od[0]) and np.allclose(lse[-1], ld[0])
+    rows = [22, 0, 7]  # a sample of rows gives those rows of the full result
+    os_, ls_ = att.causal_last(t, a, q, 0.4, rows=rows)
+    assert np.array_equal(os_, o[rows]) and np.array_equal(ls_, lse[rows])
     # mount: b = fork-free second sequence mounting 5 tokens of a
     b = t.create()
     kb, vb = rng.standard_normal((9, hkv, d)), rng.standard_normal((9, hkv, d))
