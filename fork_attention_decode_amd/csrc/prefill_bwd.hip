@@ -299,8 +299,8 @@ struct BwdParams {
 
 constexpr int kKeyBlocksPerWg = 2;                 // dK / dV workgroup: 2 key blocks, 8 waves
 constexpr int kDkdvThreads = 256 * kKeyBlocksPerWg;
-constexpr int kHeadsPerWg = 2;                     // dQ workgroup: up to 2 query heads, 8 waves
-constexpr int kDqThreads = 256 * kHeadsPerWg;
+constexpr int kHeadsPerWg = 4;                     // dQ workgroup: up to 4 query heads, 8 waves of 32 queries
+constexpr int kDqThreads = 512;
 
 // grid (Hkv, ceil(n_blocks / 2)): dK, dV of two 64-key blocks for one KV head; wave w takes
 // keys 16 (w % 4) .. + 15 of block 2 blockIdx.y + w / 4.  The workgroup walks the union
@@ -408,30 +408,39 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p) {
   }
 }
 
-// grid (Hq / hw, n_blocks), hw = 2 query heads of one KV head per workgroup (1 when G is
-// odd): dQ of a 64-query block; wave w takes queries 16 (w % 4) .. + 15 of head
-// blockIdx.x hw + w / 4 (with hw = 1 the upper four waves only help stage).  Each key
-// block's record staged in LDS serves the workgroup's heads.
+// grid (Hq / hw, n_blocks), hw = 4, 2 or 1 query heads of one KV head per workgroup (the
+// largest that divides G): dQ of a 64-query block; wave w takes queries 32 (w % 2) .. + 31
+// (two 16-query tiles) of head blockIdx.x hw + w / 2 (waves past the hw heads only help
+// stage).  Each key block's record staged in LDS serves the workgroup's heads, and each
+// K / V fragment read from LDS feeds the products of both tiles.
 __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw) {
   __shared__ __attribute__((aligned(16))) char rec[2][kKRec];
   const int qb = blockIdx.y, lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool active = (w >> 2) < hw;
-  const int h = blockIdx.x * hw + (active ? w >> 2 : 0), qt = w & 3;
+  const bool active = (w >> 1) < hw;
+  const int h = blockIdx.x * hw + (active ? w >> 1 : 0), qt0 = 2 * (w & 1);
   const int g = blockIdx.x * hw / p.G;
   const char* qrec = p.qrec + ((size_t)qb * p.hq + h) * kQRec;
-  bf16x8 qf[4], df[4];  // the wave's 16 queries as the B operand (query = lane % 16)
+  bf16x8 qf[2][4], df[2][4];  // tile u's 16 queries as the B operand (query = lane % 16)
+  float lq[2], dq_d[2];
+  int q_tok[2];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    qf[f] = *reinterpret_cast<const bf16x8*>(qrec + ((qt * 4 + f) * 64 + lane) * 16);
-    df[f] = *reinterpret_cast<const bf16x8*>(qrec + kImg + ((qt * 4 + f) * 64 + lane) * 16);
+  for (int u = 0; u < 2; ++u) {
+    const int qt = qt0 + u;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      qf[u][f] = *reinterpret_cast<const bf16x8*>(qrec + ((qt * 4 + f) * 64 + lane) * 16);
+      df[u][f] = *reinterpret_cast<const bf16x8*>(qrec + kImg + ((qt * 4 + f) * 64 + lane) * 16);
+    }
+    lq[u] = reinterpret_cast<const float*>(qrec + 4 * kImg)[qt * 16 + (lane & 15)];
+    dq_d[u] = reinterpret_cast<const float*>(qrec + 4 * kImg)[kB + qt * 16 + (lane & 15)];
+    q_tok[u] = qb * kB + qt * 16 + (lane & 15);
   }
-  const float lq = reinterpret_cast<const float*>(qrec + 4 * kImg)[qt * 16 + (lane & 15)];
-  const float dq_d = reinterpret_cast<const float*>(qrec + 4 * kImg)[kB + qt * 16 + (lane & 15)];
-  const int q_tok = qb * kB + qt * 16 + (lane & 15);
-  f32x4 dq[8];
+  f32x4 dq[2][8];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) dq[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) dq[u][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
   Stager<kKRec / 16, kDqThreads> stg;
   // stages: the row's entries whose column is inside [0, nb) (others are never followed)
@@ -453,50 +462,65 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw) {
     const bool diag = p.kind[e] != 0;
     const char* r = rec[cur];
     if (active) {
-    f32x4 s[4], dp[4];
+    f32x4 s[2][4], dp[2][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      s[t] = dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) s[u][t] = dp[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const int u = ((t * 4 + f) * 64 + lane) * 16;
-        s[t] = mfma(*reinterpret_cast<const bf16x8*>(r + u), qf[f], s[t]);
-        dp[t] = mfma(*reinterpret_cast<const bf16x8*>(r + kImg + u), df[f], dp[t]);
+        const int o = ((t * 4 + f) * 64 + lane) * 16;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(r + o);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(r + kImg + o);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          s[u][t] = mfma(kf, qf[u][f], s[u][t]);
+          dp[u][t] = mfma(vf, df[u][f], dp[u][t]);
+        }
       }
     }
-    // s[t][i]: key 16 t + 4 (lane / 16) + i, query lane % 16 of the wave
+    // s[u][t][i]: key 16 t + 4 (lane / 16) + i, query lane % 16 of tile u
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb * kB + 16 * t + 4 * (lane >> 4) + i;
-        const bool vis = key < p.T && (!diag || key <= q_tok);
-        const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], p.c2, -lq)) : 0.f;
-        dp[t][i] = pr * (dp[t][i] - dq_d);
-      }
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb * kB + 16 * t + 4 * (lane >> 4) + i;
+          const bool vis = key < p.T && (!diag || key <= q_tok[u]);
+          const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][i], p.c2, -lq[u])) : 0.f;
+          dp[u][t][i] = pr * (dp[u][t][i] - dq_d[u]);
+        }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      const bf16x8 ads = pack_pair(dp[2 * h2], dp[2 * h2 + 1]);
+      bf16x8 ads[2];
 #pragma unroll
-      for (int n = 0; n < 8; ++n)
-        dq[n] = mfma(ads, *reinterpret_cast<const bf16x8*>(r + 2 * kImg + ((n * 2 + h2) * 64 + lane) * 16), dq[n]);
+      for (int u = 0; u < 2; ++u) ads[u] = pack_pair(dp[u][2 * h2], dp[u][2 * h2 + 1]);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const bf16x8 kt = *reinterpret_cast<const bf16x8*>(r + 2 * kImg + ((n * 2 + h2) * 64 + lane) * 16);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) dq[u][n] = mfma(ads[u], kt, dq[u][n]);
+      }
     }
     }
     if (en < e1) stg.store(rec[cur ^ 1]);
     __syncthreads();  // the next key block is in place; every wave is done with this one
     e = en;
   }
-  // dq[n][i]: query 4 (lane / 16) + i of the wave, dim 16 n + lane % 16
+  // dq[u][n][i]: query 4 (lane / 16) + i of tile u, dim 16 n + lane % 16
   if (!active) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qi = qb * kB + qt * 16 + 4 * (lane >> 4) + i;
-    if (qi < p.T) {
-      float* dqr = p.dq + ((size_t)qi * p.hq + h) * kD + (lane & 15);
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int n = 0; n < 8; ++n) dqr[16 * n] = dq[n][i] * p.scale;
+    for (int i = 0; i < 4; ++i) {
+      const int qi = qb * kB + (qt0 + u) * 16 + 4 * (lane >> 4) + i;
+      if (qi < p.T) {
+        float* dqr = p.dq + ((size_t)qi * p.hq + h) * kD + (lane & 15);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) dqr[16 * n] = dq[u][n][i] * p.scale;
+      }
     }
-  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -586,7 +610,7 @@ extern "C" int dag_attn_backward(const void* q, const void* k, const void* v, co
   p.scale = sm_scale;
   p.c2 = sm_scale * 1.4426950408889634f;
   dkdv_kernel<<<dim3(n_kv_heads, (unsigned)n_pair), kDkdvThreads, 0, stream>>>(p);
-  const int hw = p.G % kHeadsPerWg == 0 ? kHeadsPerWg : 1;
+  const int hw = p.G % kHeadsPerWg == 0 ? kHeadsPerWg : (p.G % 2 == 0 ? 2 : 1);
   dq_kernel<<<dim3(n_q_heads / hw, (unsigned)nb), kDqThreads, 0, stream>>>(p, hw);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill backward: ") + hipGetErrorString(e));
