@@ -23,9 +23,10 @@
 //     in LDS (double-buffered: the next record's loads are in flight while the current
 //     one computes) and computes S = Q K^T, P, dP = dO V^T, dS, then dV += P^T dO and
 //     dK += dS^T Q: dK and dV of the G heads accumulate in registers, with no atomics;
-//   * dq_kernel: one workgroup per (64-query block, 2 query heads of a KV head), 8 waves
-//     of 16 queries, Q and dO fragments in registers; it walks the block's CSR row,
-//     stages each key block's K / V / K^T (double-buffered) for both heads and computes
+//   * dq_kernel: one workgroup per (64-query block, 4 query heads of a KV head), 8 waves
+//     of 32 queries (two 16-query tiles, so each K / V fragment read from LDS feeds two
+//     MFMAs), Q and dO fragments in registers; it walks the block's CSR row, stages each
+//     key block's K / V / K^T (double-buffered) once for the 4 heads and computes
 //     S^T = K Q^T, P^T, dP^T = V dO^T, dS^T and dQ += dS K;
 //   * the mask kinds are those of the forward: kind 1 (the diagonal block) hides key >
 //     query, keys >= T are hidden, a row with lse = -inf contributes nothing.
