@@ -63,9 +63,9 @@ def test_plain_causal(T):
     _check(pi, o, lse, list(range(T)), f"causal T={T}")
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (4, 2), (2, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (4, 2), (2, 2), (6, 2), (8, 1)])
 def test_small_dag_heads(hq, hkv):
-    # G = 4, 8 (two head groups per workgroup set), 2 and 1 (idle waves)
+    # G = 4, 8 (two head groups per workgroup set), 2, 1 and 3 (idle waves)
     pi = W.prefill_inputs(prefix=192, branches=3, branch_len=[128, 256, 100], n_edges=3, edge_len=64, hq=hq,
                           hkv=hkv, seed=32)
     _, o, lse = _run(pi, f"small DAG Hq={hq} Hkv={hkv}")

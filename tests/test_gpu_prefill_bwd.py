@@ -78,9 +78,9 @@ def test_plain_causal(T):
     _full_check(pi, 62, f"backward causal T={T}")
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 2), (2, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 2), (2, 2), (6, 2), (8, 1)])
 def test_small_dag_heads(hq, hkv):
-    # G = 4, 2 and 1; ragged last branch, 3 edges
+    # G = 4, 2, 1, 3 (odd: one head per dQ workgroup) and 8; ragged last branch, 3 edges
     pi = W.prefill_inputs(prefix=192, branches=3, branch_len=[128, 256, 100], n_edges=3, edge_len=64, hq=hq,
                           hkv=hkv, seed=63)
     _full_check(pi, 64, f"backward small DAG Hq={hq} Hkv={hkv}")
