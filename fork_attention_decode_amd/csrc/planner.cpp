@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <cstring>
 #include <map>
+#include <unordered_map>
 
 using namespace fa;
 
@@ -87,13 +88,17 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
       }
     }
   }
-  {  // stable counting sort by page id (readers of a page keep query order)
-    std::vector<int32_t> at((size_t)C.n_pages + 1, 0);
-    for (const Entry& e : ent) at[(size_t)e.page + 1]++;
-    for (size_t p = 1; p < at.size(); ++p) at[p] += at[p - 1];
+  {  // stable radix sort by page id, 16 bits a pass (readers of a page keep query order);
+     // the cost follows the entries, not the pool's page count
     std::vector<Entry> sorted(ent.size());
-    for (const Entry& e : ent) sorted[(size_t)at[(size_t)e.page]++] = e;
-    ent.swap(sorted);
+    std::vector<int32_t> at((size_t)1 << 16 | 1);
+    for (int shift = 0; shift < 32 && (shift == 0 || (C.n_pages - 1) >> shift); shift += 16) {
+      std::fill(at.begin(), at.end(), 0);
+      for (const Entry& e : ent) at[((uint32_t)e.page >> shift & 0xffffu) + 1]++;
+      for (size_t d = 1; d < at.size(); ++d) at[d] += at[d - 1];
+      for (const Entry& e : ent) sorted[(size_t)at[(uint32_t)e.page >> shift & 0xffffu]++] = e;
+      ent.swap(sorted);
+    }
   }
 
   // 2. chunks grouped into segments by reader multiset
@@ -439,11 +444,11 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
   }
   DecodePlanCache& pc = P->plan;
   // the chunk records of reserved pages: (record int, query index, logical page)
-  std::vector<int64_t> owner((size_t)P->cfg.n_pages, -1);  // page -> i * 2^32 + logical page
+  std::unordered_map<int32_t, int64_t> owner;  // reserved page -> i * 2^32 + logical page
   for (int32_t i = 0; i < n; ++i) {
     Seq* S = fa_seq(P, seqs[i]);
     for (int64_t L = base[i] / PS; L < (int64_t)S->pages.size(); ++L)
-      owner[(size_t)S->pages[(size_t)L]] = ((int64_t)i << 32) | L;
+      owner[S->pages[(size_t)L]] = ((int64_t)i << 32) | L;
   }
   // items that read a reserved page form the per-step tail (their slot ranges change
   // with the step); the rest, and the merge counts, are shared by every step
@@ -452,7 +457,7 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
   for (int32_t it = 0; it < pc.n_items; ++it) {
     const int32_t* rec = recs0 + (size_t)it * kRecInts;
     bool mine = false;
-    for (int32_t c = 0; c < rec[0] && !mine; ++c) mine = owner[(size_t)rec[kRecChunk + 2 * c]] >= 0;
+    for (int32_t c = 0; c < rec[0] && !mine; ++c) mine = owner.count(rec[kRecChunk + 2 * c]) != 0;
     (mine ? tail : head).push_back(it);
   }
   struct Patch {
@@ -464,8 +469,10 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
   for (size_t t = 0; t < tail.size(); ++t) {
     const int32_t* rec = recs0 + (size_t)tail[t] * kRecInts;
     for (int32_t c = 0; c < rec[0]; ++c) {
-      const int64_t o = owner[(size_t)rec[kRecChunk + 2 * c]];
-      if (o >= 0) patches.push_back({t * kRecInts + kRecChunk + 2 * c + 1, (int32_t)(o >> 32), o & 0xffffffff});
+      const auto f = owner.find(rec[kRecChunk + 2 * c]);
+      if (f == owner.end()) continue;
+      const int64_t o = f->second;
+      patches.push_back({t * kRecInts + kRecChunk + 2 * c + 1, (int32_t)(o >> 32), o & 0xffffffff});
     }
   }
   const size_t rec_bytes = (size_t)kRecInts * sizeof(int32_t);
