@@ -62,6 +62,7 @@ _SIGS = {
     "kv_pool_destroy": [_P],
     "kv_seq_create": [_P, _pi32],
     "kv_append": [_P, _i32, _i64, _P, _P, _pi64, _P],
+    "kv_append_batch": [_P, _pi32, _i32, _P, _P, _P],
     "kv_write": [_P, _i32, _i64, _i64, _P, _P, _P],
     "kv_fork": [_P, _i32, _pi32],
     "kv_mount": [_P, _i32, _i32, _i64, _i64],
@@ -174,6 +175,12 @@ def kv_append(pool: int, seq: int, n: int, k: int = 0, v: int = 0, positions=Non
     pos = None if positions is None else _i64arr(positions)
     _check("kv_append", lib.kv_append(pool, seq, n, k or None, v or None,
                                       None if pos is None else _ptr(pos, C.c_int64), stream or None), pool)
+
+
+def kv_append_batch(pool: int, seqs: Sequence[int], k: int = 0, v: int = 0, stream: int = 0):
+    s = np.ascontiguousarray(np.asarray(seqs, np.int32))
+    _check("kv_append_batch", lib.kv_append_batch(pool, _ptr(s, C.c_int32), len(s), k or None, v or None,
+                                                  stream or None), pool)
 
 
 def kv_write(pool: int, seq: int, start: int, n: int, k: int = 0, v: int = 0, stream: int = 0):
@@ -539,6 +546,14 @@ class Pool:
         else:
             assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape
             kv_append(self.handle, seq, k.shape[0], k.data_ptr(), v.data_ptr(), positions, self._stream())
+
+    def append_batch(self, seqs, k=None, v=None):
+        """One token onto each listed sequence (row i of k / v for seqs[i])."""
+        if k is None:
+            kv_append_batch(self.handle, seqs, 0, 0, 0)
+        else:
+            assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.shape[0] == len(seqs)
+            kv_append_batch(self.handle, seqs, k.data_ptr(), v.data_ptr(), self._stream())
 
     def write(self, seq: int, start: int, k=None, v=None, n: Optional[int] = None):
         if k is None:

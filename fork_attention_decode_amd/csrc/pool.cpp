@@ -14,6 +14,7 @@
 #include "pool.hpp"
 
 #include <algorithm>
+#include <unordered_map>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -366,6 +367,90 @@ int kv_append(kv_pool_t* P, kv_seq_t seq, int64_t n, const void* k, const void* 
   Seq* S = fa_seq(P, seq);
   if (!S) FAIL(P, KV_ERR_NOT_FOUND, "no live sequence");
   return write_tokens(P, seq, S->n, n, k, v, positions, true, s);
+}
+
+// One token onto each of n distinct sequences, exactly as n single-token appends in list
+// order would do it (a shared partial tail page is copied, a full tail takes a new page,
+// both lowest free id first), with one upload and one page-write launch.  The page
+// decisions run first on a copy of the refcounts (two forks sharing a tail page: the
+// first copies it, the second then owns it alone and writes in place), so a failure
+// leaves the pool unchanged.
+int kv_append_batch(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, const void* k, const void* v, hipStream_t s) {
+  if (!P) FAIL(P, KV_ERR_INVALID, "null pool");
+  if (n < 0 || (n > 0 && !seqs)) FAIL(P, KV_ERR_INVALID, "bad sequence list");
+  if (n == 0) return KV_OK;
+  if (n > P->cfg.n_pages) FAIL(P, KV_ERR_INVALID, "more sequences than pool pages");
+  if (P->device && (!k || !v)) FAIL(P, KV_ERR_INVALID, "null k / v");
+  std::vector<Seq*> S((size_t)n);
+  for (int32_t i = 0; i < n; ++i)
+    if (!(S[(size_t)i] = fa_seq(P, seqs[i]))) FAIL(P, KV_ERR_NOT_FOUND, "no live sequence in the list");
+  {
+    std::vector<kv_seq_t> sorted(seqs, seqs + n);
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+      FAIL(P, KV_ERR_INVALID, "a sequence appears twice in the list");
+  }
+  const int32_t PS = P->cfg.page_size;
+  enum { kInPlace = 0, kCopy = 1, kNew = 2 };
+  std::vector<uint8_t> how((size_t)n);
+  std::unordered_map<int32_t, int32_t> rc_delta;  // refcount changes of earlier copies in the list
+  int32_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* q = S[(size_t)i];
+    const int64_t L = q->n / PS;
+    if (L < (int64_t)q->pages.size()) {
+      const int32_t pg = q->pages[(size_t)L];
+      const bool shared = P->rc[pg] + rc_delta[pg] > 1;
+      if (shared) --rc_delta[pg];
+      how[(size_t)i] = shared ? kCopy : kInPlace;
+    } else {
+      how[(size_t)i] = kNew;
+    }
+    need += how[(size_t)i] != kInPlace;
+  }
+  if (need > P->free.count()) FAIL(P, KV_ERR_OOM, "not enough free pages");
+  std::vector<int32_t> ids;
+  P->free.peek_lowest(need, ids);
+  if (P->device) {
+    std::vector<PageWrite> writes((size_t)n);
+    int32_t j = 0;
+    for (int32_t i = 0; i < n; ++i) {
+      const Seq* q = S[(size_t)i];
+      const int64_t L = q->n / PS;
+      const int32_t slot = (int32_t)(q->n % PS);
+      PageWrite& w = writes[(size_t)i];
+      w.dst_page = how[(size_t)i] == kInPlace ? q->pages[(size_t)L] : ids[(size_t)j++];
+      w.src_page = how[(size_t)i] == kCopy ? q->pages[(size_t)L] : -1;
+      w.lo = slot;
+      w.hi = slot + 1;
+      w.tok_base = i;  // row i of k / v
+    }
+    char* area = P->ws + fa_ws_plan_offset(&P->cfg);
+    hipError_t e = fa_upload(P, area, writes.data(), writes.size() * sizeof(PageWrite), s);
+    if (e == hipSuccess)
+      e = launch_page_write(P->cfg.dtype, P->cfg.head_dim, P->cfg.n_kv_heads, P->cfg.n_pages, P->k, P->v, k, v,
+                            reinterpret_cast<const PageWrite*>(area), n, s);
+    if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("page write: ") + hipGetErrorString(e));
+  }
+  int32_t j = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    Seq* q = S[(size_t)i];
+    const size_t L = (size_t)(q->n / PS);
+    if (how[(size_t)i] == kCopy) {
+      const int32_t old = q->pages[L];
+      take_page(P, ids[(size_t)j]);
+      q->pages[L] = ids[(size_t)j++];
+      unref_page(P, old);
+    } else if (how[(size_t)i] == kNew) {
+      take_page(P, ids[(size_t)j]);
+      q->pages.push_back(ids[(size_t)j++]);
+    }
+    fa_pos_append(q->pos, q->next_pos, 1);
+    q->next_pos += 1;
+    q->n += 1;
+  }
+  P->version++;
+  return KV_OK;
 }
 
 int kv_write(kv_pool_t* P, kv_seq_t seq, int64_t start, int64_t n, const void* k, const void* v,

@@ -116,6 +116,17 @@ int kv_seq_create(kv_pool_t* pool, kv_seq_t* out);
 int kv_append(kv_pool_t* pool, kv_seq_t seq, int64_t n, const void* k, const void* v,
               const int64_t* positions, hipStream_t stream);
 
+/* Append one token to each of n distinct live sequences in one call (the decode step's
+ * append: Octopus forks keep decoding side by side; AKV "Append").  k, v: DEVICE arrays
+ * [n][Hkv][d] in the pool dtype, row i for seqs[i], keys already rotated; each token
+ * takes its sequence's next_pos.  The page table ends exactly as after n single-token
+ * kv_append calls in list order (a shared partial tail page is copied first; a full
+ * tail takes a new page; lowest free id first), with one upload and one kernel launch.
+ * KV_ERR_INVALID for a sequence listed twice or n > n_pages, KV_ERR_NOT_FOUND for a
+ * dead handle, KV_ERR_OOM if the pool cannot hold the result (nothing changes). */
+int kv_append_batch(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n, const void* k, const void* v,
+                    hipStream_t stream);
+
 /* Overwrite tokens [start, start + n) of the sequence's own context in place
  * (positions unchanged).  Every touched page whose refcount > 1 is copied first, so a
  * shared snapshot is never written (Agentrix: local edits create new versions while

@@ -135,3 +135,41 @@ def test_octopus_dag_full_size():
     pool, o, lse = _run(sc, "Octopus DAG decode, full size")
     assert pool.plan_stats()["unique_kv_bytes"] == 536870912
     _check(sc, o, lse, "Octopus DAG decode, full size")
+
+
+def test_append_batch_contents_and_decode():
+    # kv_append_batch, a few steps of one token per branch (a shared partial tail copied
+    # by the first fork, then owned by the second; page boundaries crossed): every page's
+    # K / V against the oracle's pages after the same single appends, and a decode after
+    import torch
+    from oracle import attention as att, pagetable as pt
+    sc = W.fork_scenario(prefix=37, branches=3, private=[0, 0, 14], hq=8, hkv=2, d=128, seed=5)
+    sc.n_pages += 16
+    print("[case] kv_append_batch: contents and a decode", flush=True)
+    pool, _ = build_device_pool(sc)
+    ora, _ = pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, "bf16"))
+    seqs = [2, 1, 3, 0]
+    rng = np.random.default_rng(6)
+    f = W.bf16_bits_to_f64
+    for _ in range(5):
+        kb = W.to_bf16_bits(rng.standard_normal((len(seqs), 2, 128)) / np.sqrt(128))
+        vb = W.to_bf16_bits(rng.standard_normal((len(seqs), 2, 128)))
+        pool.append_batch(seqs, to_torch(kb, "bf16"), to_torch(vb, "bf16"))
+        for i, b in enumerate(seqs):
+            ora.append(b, 1, k=f(kb[i:i + 1]), v=f(vb[i:i + 1]))
+    torch.cuda.synchronize()
+    for s in seqs:
+        assert list(pool.block_table(s)) == ora.block_table(s), s
+        for L, page in enumerate(ora.block_table(s)):
+            n_valid = min(16, ora.seqs[s].n - 16 * L)
+            for h in range(2):
+                k, v = pool.read_page(page, h)
+                assert np.array_equal(f(k[:n_valid]), ora.kdata[page][:n_valid, h]), (s, L, h)
+                assert np.array_equal(f(v[:n_valid]), ora.vdata[page][:n_valid, h]), (s, L, h)
+    qb = W.to_bf16_bits(rng.standard_normal((len(seqs), 8, 128)))
+    out, lse = pool.decode(seqs, to_torch(qb, "bf16"), sc.sm_scale)
+    torch.cuda.synchronize()
+    ro, rl = att.decode(ora, seqs, f(qb), sc.sm_scale)
+    check_close(out_to_f64(out, "bf16"), ro, BF16_MAX, BF16_MEAN, "decode after kv_append_batch")
+    check_close(lse.double().cpu().numpy(), rl, LSE_MAX, LSE_MAX, "decode after kv_append_batch lse")
+    print("[ok] kv_append_batch", flush=True)

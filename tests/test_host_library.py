@@ -302,6 +302,63 @@ def test_window_reservation_equals_rounds_of_appends(make, n_steps):
     _cmp(pool.handle, ora, live)
 
 
+@pytest.mark.parametrize("make", [
+    lambda: W.fork_scenario(prefix=517, branches=5, private=[0, 3, 16, 30, 1], hq=8, hkv=2, d=128, seed=73),
+    lambda: W.dag_scenario(root=300, threads=3, private=90, mounts_per_thread=2, mount_len=33, hq=8, hkv=2, d=128,
+                           seed=74),
+])
+def test_append_batch_equals_single_appends_in_list_order(make):
+    # kv_append_batch = one single-token append per listed sequence, in list order: forks
+    # sharing a partial tail (the first copies it, the next then owns it alone), full tails
+    # taking new pages, an empty root, repeated steps crossing page boundaries
+    sc = make()
+    sc.n_pages += 96
+    ora, _ = pt.replay(sc, with_data=False)
+    pool = fa.Pool(sc.n_kv_heads, sc.head_dim, sc.n_pages, page_size=sc.page_size, rope_theta=sc.rope_theta,
+                   metadata_only=True)
+    for op in sc.ops:
+        if op[0] == "create":
+            pool.seq_create()
+        elif op[0] == "append":
+            blk = sc.blocks[op[2]]
+            pool.append(op[1], n=len(blk.pos), positions=blk.pos)
+        elif op[0] == "fork":
+            pool.fork(op[1])
+        elif op[0] == "mount":
+            pool.mount(*op[1:])
+    assert pool.seq_create() == ora.create()  # an empty root
+    live = [i for i, s in enumerate(ora.seqs) if s.live]
+    seqs = live[::-1]
+    for _ in range(19):
+        pool.append_batch(seqs)
+        for b in seqs:
+            ora.append(b, 1)
+        _cmp(pool.handle, ora, live)
+
+
+def test_append_batch_rejections_leave_state():
+    pool = fa.Pool(1, 2, 6, page_size=4, metadata_only=True)
+    a = pool.seq_create()
+    pool.append(a, n=5)
+    b = pool.fork(a)
+    c = pool.fork(a)
+    pool.append(a, n=3)  # 4-token pages: a copies the shared tail (3 pages in use)
+    state = lambda: ([list(fa.kv_block_table(pool.handle, s)) for s in (a, b, c)], pool.free_pages())
+    before = state()
+    for bad, status in (([b, b], fa.KV_ERR_INVALID), ([b, 99], fa.KV_ERR_NOT_FOUND), (list(range(7)), fa.KV_ERR_INVALID)):
+        with pytest.raises(fa.ForkAttnError) as e:
+            fa.kv_append_batch(pool.handle, bad)
+        assert e.value.status == status, bad
+        assert state() == before
+    pool.append(c, n=3)  # c copies the shared tail too, b then owns the original alone
+    pool.append(b, n=4)  # b fills it in place and takes a new page: one page left
+    before = state()  # a and c are at page boundaries: the batch needs two new pages
+    with pytest.raises(fa.ForkAttnError) as e:
+        fa.kv_append_batch(pool.handle, [a, b, c])
+    assert e.value.status == fa.KV_ERR_OOM
+    assert state() == before
+
+
 def test_window_oom_and_duplicates_leave_state():
     pool = fa.Pool(1, 2, 6, page_size=4, metadata_only=True)
     a = pool.seq_create()
