@@ -381,7 +381,14 @@ def bench_window(n_steps=16, replays=20):
     torch.cuda.synchronize()
     us_step = ev[0].elapsed_time(ev[1]) * 1e3 / (replays * n_steps)
     del ws
+    # each unique KV byte once per step (the shared prefix once, each branch's own tokens
+    # once, the window's new tokens included), averaged over the window's steps
+    ctx_tokens = 32768 + n * 2048 + n * (n_steps + 1) / 2
+    step_bytes = ctx_tokens * hkv * d * 2 * 2
     return {
+        "algorithmic_bytes_per_step": step_bytes,
+        "step_GBps": step_bytes / (us_step * 1e-6) / 1e9,
+        "step_frac_of_8TBps": step_bytes / (us_step * 1e-6) / 8e12,
         "workload": "shared_prefix_fork_decode steady state (16 branches, 32,768-token prefix + 2,048 private each; "
                     "every step appends one token per branch, then decodes all 16)",
         "steps_per_window": n_steps,
@@ -439,6 +446,9 @@ def bench_restore(reps=20, n_seg=4, seg_len=128):
     ms = np.array([a.elapsed_time(b) for a, b in ev])
     ctx = int(pool.info(seq)[0])
     kv_bytes = ctx * hkv * d * 2 * 2
+    # 4 d FLOPs per visible (restored token, key) pair per query head; token j sees ctx - n + j + 1 keys
+    flops = 4 * d * hq * sum(ctx - n + j + 1 for j in range(n))
+    tflops = flops / (float(np.mean(ms)) * 1e-3) / 1e12
     return {
         "workload": f"restore {n_seg} segments x {seg_len} tokens (own positions) into a branch of the shared-prefix "
                     f"workload, then causal attention of the {n} restored tokens over the {ctx}-token context",
@@ -448,6 +458,8 @@ def bench_restore(reps=20, n_seg=4, seg_len=128):
         "streamed_kv_bytes": kv_bytes * (n // 16),
         "streamed_GBps": kv_bytes * (n // 16) / (float(np.mean(ms)) * 1e-3) / 1e9,
         "rows": n * hq,
+        "roofline": {"bound": "mfma", "unit": "TFLOP/s", "peak": 2500.0, "algorithmic_flops_per_call": flops,
+                     "achieved": tflops, "frac": tflops / 2500.0},
         "note": "the attention runs as one split-K decode of n x Hq rows: every context page is streamed once per "
                 "group of 64 / G = 16 restored tokens, so it reads the context n / 16 times; the plan (host) is "
                 "built once and cached, the events enclose the kernels",
