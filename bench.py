@@ -645,8 +645,8 @@ def main():
                          "traffic to scale hardware byte counters against)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on "
-              f"a single MI355X; decode shards by KV head with no exchange across GPUs).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the library runs on one "
+              f"MI355X; decode would shard by KV head with no exchange across GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

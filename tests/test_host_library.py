@@ -407,3 +407,15 @@ def test_new_entry_points_reject_bad_arguments():
     assert e.value.status == fa.KV_ERR_WORKSPACE
     fa.dag_attn_backward(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 4, 2, 128, 0, 0, 0, 0, 64, 1.0, 0, 0)  # T = 0: nothing to do
     assert pool.info(a)[0] == 6
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the bench measures one GPU; a request for several exits with a message, before any
+    # GPU work
+    import subprocess
+    import sys
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
