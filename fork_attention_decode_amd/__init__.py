@@ -78,6 +78,7 @@ _SIGS = {
     "kv_free_pages": [_P, _pi32],
     "kv_pool_read_page": [_P, _i32, _i32, _P, _P, _P],
     "kv_pool_sync_status": [_P, _P, _pi32],
+    "kv_pool_set_compute_units": [_P, _i32],
     "fork_attn_workspace_size": [_P, _pi32, _i32, _i32, _psz],
     "fork_attn_decode": [_P, _pi32, _i32, _i32, _P, _P, _P, C.c_float, _P, _sz, _P],
     "fork_attn_plan_stats": [_P, _pi64, _i32],
@@ -260,6 +261,10 @@ def kv_pool_read_page(pool: int, page: int, head: int, k_out: np.ndarray, v_out:
                                                       stream or None), pool)
 
 
+def kv_pool_set_compute_units(pool: int, n_cu: int) -> None:
+    _check("kv_pool_set_compute_units", lib.kv_pool_set_compute_units(pool, n_cu), pool)
+
+
 def kv_pool_sync_status(pool: int, stream: int = 0) -> int:
     n = C.c_int32()
     _check("kv_pool_sync_status", lib.kv_pool_sync_status(pool, stream or None, C.byref(n)), pool)
@@ -324,9 +329,9 @@ def kv_drop_keep(pool: int, seq: int, keep: np.ndarray, flags: int = 0, stream: 
 
 
 def fork_attn_plan_stats(pool: int) -> dict:
-    out = np.zeros(6, np.int64)
-    _check("fork_attn_plan_stats", lib.fork_attn_plan_stats(pool, _ptr(out, C.c_int64), 6), pool)
-    keys = ["segments", "items", "chunks", "partials", "unique_kv_bytes", "rows"]
+    out = np.zeros(7, np.int64)
+    _check("fork_attn_plan_stats", lib.fork_attn_plan_stats(pool, _ptr(out, C.c_int64), 7), pool)
+    keys = ["segments", "items", "chunks", "partials", "unique_kv_bytes", "rows", "longest_item_chunks"]
     return dict(zip(keys, (int(x) for x in out)))
 
 

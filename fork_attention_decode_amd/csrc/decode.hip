@@ -32,14 +32,6 @@ typedef __bf16 bf16_t;
 typedef bf16_t bf16x8 __attribute__((__vector_size__(8 * sizeof(bf16_t))));
 typedef bf16_t bf16x4 __attribute__((__vector_size__(4 * sizeof(bf16_t))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-
-// Streaming (non-temporal) loads of KV data that is read once per decode.
-template <typename V, typename R>
-__device__ __forceinline__ V nt_load(const void* p) {
-  return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const R*>(p)));
-}
 
 template <typename T, int D> struct Tr;
 
@@ -49,12 +41,6 @@ template <int D> struct Tr<bf16_t, D> {
   using KF = bf16x8;
   using VF = bf16x4;
   using PF = bf16x4;
-  __device__ static KF load_k(const bf16_t* blk, int f, int lane) {
-    return nt_load<KF, i32x4>(blk + (f * 64 + lane) * 8);
-  }
-  __device__ static VF load_v(const bf16_t* blk, int db, int lane) {
-    return nt_load<VF, i32x2>(blk + (db * 16 + (lane & 15)) * 16 + 4 * (lane >> 4));
-  }
   __device__ static KF load_q(const bf16_t* row, int f, int lane) {
     return *reinterpret_cast<const KF*>(row + 32 * f + 8 * (lane >> 4));
   }
@@ -74,9 +60,6 @@ template <int D> struct Tr<bf16_t, D> {
     }
     return v;
   }
-  __device__ static f32x4 pv(f32x4 c, VF v, PF p) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v, p, c, 0, 0, 0);
-  }
   // two chunks at once: K index 8 g + e is key 4 g + e of chunk e / 4
   __device__ static f32x4 pv2(f32x4 c, VF v0, VF v1, PF p0, PF p1) {
     const KF a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -91,12 +74,6 @@ template <int D> struct Tr<float, D> {
   using KF = f32x4;
   using VF = f32x4;
   using PF = f32x4;
-  __device__ static KF load_k(const float* blk, int f, int lane) {
-    return nt_load<KF, i32x4>(blk + (f * 64 + lane) * 4);
-  }
-  __device__ static VF load_v(const float* blk, int db, int lane) {
-    return nt_load<VF, i32x4>(blk + (db * 16 + (lane & 15)) * 16 + 4 * (lane >> 4));
-  }
   __device__ static KF load_q(const float* row, int f, int lane) {
     const int g = lane >> 4;
     KF r;

@@ -270,6 +270,9 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
   pc.stats[3] = n_part;
   pc.stats[4] = unique_tokens * C.n_kv_heads * 2 * D * (int64_t)es;
   pc.stats[5] = n_out;
+  int64_t longest = 0;
+  for (const Item& it : items) longest = std::max<int64_t>(longest, it.n_chunks);
+  pc.stats[6] = longest;
   pc.valid = true;
   pc.causal_n = len_cap ? -1 : 0;
   pc.version = P->version;
@@ -292,7 +295,7 @@ int fork_attn_workspace_size(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int3
 int fork_attn_plan_stats(kv_pool_t* P, int64_t* out, int32_t n) {
   if (!P || !out || n < 0) FAIL(P, KV_ERR_INVALID, "null argument");
   if (!P->plan.valid) FAIL(P, KV_ERR_INVALID, "no plan yet");
-  for (int32_t i = 0; i < n && i < 6; ++i) out[i] = P->plan.stats[i];
+  for (int32_t i = 0; i < n && i < 7; ++i) out[i] = P->plan.stats[i];
   return KV_OK;
 }
 
@@ -594,8 +597,8 @@ int kv_window_step(kv_pool_t* P, int32_t step, const void* k, const void* v, con
 }
 
 // ------------------------------------------------------------------ causal attention of a sequence's last tokens
-// AgentKV restores an evicted or edited span of a sequence with one prefill in which each
-// segment keeps its own positions: the caller appends the segments' K / V (kv_append with
+// AKV page, section "AKV 如何工作": segmented batch attention restores an evicted state
+// with one prefill, each segment keeping its own positions: the caller appends the segments' K / V (kv_append with
 // their positions) and then attends the last n tokens, token j over the context through
 // itself (every earlier own token, then the mounts), as n rows of one split-K decode.
 

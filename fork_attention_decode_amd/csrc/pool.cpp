@@ -237,6 +237,14 @@ int kv_pool_create(const kv_pool_config* c, void* k, void* v, void* ws, size_t w
   return KV_OK;
 }
 
+int kv_pool_set_compute_units(kv_pool_t* P, int32_t n_cu) {
+  if (!P) FAIL(nullptr, KV_ERR_INVALID, "null pool");
+  if (n_cu < 1) FAIL(P, KV_ERR_INVALID, "compute unit count must be >= 1");
+  P->n_cu = n_cu;
+  P->plan.valid = false;  // the cached decode plan was cut for the old count
+  return KV_OK;
+}
+
 int kv_pool_destroy(kv_pool_t* P) {
   if (!P) FAIL(nullptr, KV_ERR_INVALID, "null pool");
   for (auto& slot : P->stage) {
@@ -371,10 +379,11 @@ int kv_append(kv_pool_t* P, kv_seq_t seq, int64_t n, const void* k, const void* 
 
 // One token onto each of n distinct sequences, exactly as n single-token appends in list
 // order would do it (a shared partial tail page is copied, a full tail takes a new page,
-// both lowest free id first), with one upload and one page-write launch.  The page
+// both lowest free id first), with one upload and at most two page-write launches.  The page
 // decisions run first on a copy of the refcounts (two forks sharing a tail page: the
 // first copies it, the second then owns it alone and writes in place), so a failure
-// leaves the pool unchanged.
+// leaves the pool unchanged.  Copies are written in a launch of their own before the
+// in-place and new-page writes.
 int kv_append_batch(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, const void* k, const void* v, hipStream_t s) {
   if (!P) FAIL(P, KV_ERR_INVALID, "null pool");
   if (n < 0 || (n > 0 && !seqs)) FAIL(P, KV_ERR_INVALID, "bad sequence list");
@@ -412,13 +421,19 @@ int kv_append_batch(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, const void* k
   std::vector<int32_t> ids;
   P->free.peek_lowest(need, ids);
   if (P->device) {
+    // A page can be the source of one sequence's copy and, once that copy has dropped its
+    // reference, the in-place target of a later sequence in the list (a fork rewound into
+    // the shared tail).  The copies therefore run in a first launch and every other write
+    // in a second, so a copy reads the page as it was before this call.
     std::vector<PageWrite> writes((size_t)n);
-    int32_t j = 0;
+    int32_t j = 0, n_copy = 0;
+    for (int32_t i = 0; i < n; ++i) n_copy += how[(size_t)i] == kCopy;
+    int32_t at_copy = 0, at_rest = n_copy;
     for (int32_t i = 0; i < n; ++i) {
       const Seq* q = S[(size_t)i];
       const int64_t L = q->n / PS;
       const int32_t slot = (int32_t)(q->n % PS);
-      PageWrite& w = writes[(size_t)i];
+      PageWrite& w = writes[(size_t)(how[(size_t)i] == kCopy ? at_copy++ : at_rest++)];
       w.dst_page = how[(size_t)i] == kInPlace ? q->pages[(size_t)L] : ids[(size_t)j++];
       w.src_page = how[(size_t)i] == kCopy ? q->pages[(size_t)L] : -1;
       w.lo = slot;
@@ -427,9 +442,13 @@ int kv_append_batch(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, const void* k
     }
     char* area = P->ws + fa_ws_plan_offset(&P->cfg);
     hipError_t e = fa_upload(P, area, writes.data(), writes.size() * sizeof(PageWrite), s);
-    if (e == hipSuccess)
+    const PageWrite* dw = reinterpret_cast<const PageWrite*>(area);
+    if (e == hipSuccess && n_copy > 0)
+      e = launch_page_write(P->cfg.dtype, P->cfg.head_dim, P->cfg.n_kv_heads, P->cfg.n_pages, P->k, P->v, k, v, dw,
+                            n_copy, s);
+    if (e == hipSuccess && n > n_copy)
       e = launch_page_write(P->cfg.dtype, P->cfg.head_dim, P->cfg.n_kv_heads, P->cfg.n_pages, P->k, P->v, k, v,
-                            reinterpret_cast<const PageWrite*>(area), n, s);
+                            dw + n_copy, n - n_copy, s);
     if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("page write: ") + hipGetErrorString(e));
   }
   int32_t j = 0;

@@ -65,7 +65,7 @@ struct DecodePlanCache {
   size_t off_items = 0, off_mptr = 0, off_plse = 0, off_po = 0;
   int32_t n_items = 0, n_out_rows = 0, max_parts = 1;
   std::vector<char> blob;  // host image of the plan part of the workspace
-  int64_t stats[6] = {0, 0, 0, 0, 0, 0};
+  int64_t stats[7] = {0, 0, 0, 0, 0, 0, 0};
   int64_t causal_n = 0;  // 0: a decode plan; n > 0: causal rows of the last n tokens; -1: other caps
 };
 

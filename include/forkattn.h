@@ -121,7 +121,9 @@ int kv_append(kv_pool_t* pool, kv_seq_t seq, int64_t n, const void* k, const voi
  * [n][Hkv][d] in the pool dtype, row i for seqs[i], keys already rotated; each token
  * takes its sequence's next_pos.  The page table ends exactly as after n single-token
  * kv_append calls in list order (a shared partial tail page is copied first; a full
- * tail takes a new page; lowest free id first), with one upload and one kernel launch.
+ * tail takes a new page; lowest free id first), with one upload and at most two kernel
+ * launches (the tail copies first, so a page copied for one sequence and then written in
+ * place by a later one in the list is copied as it was before the call).
  * KV_ERR_INVALID for a sequence listed twice or n > n_pages, KV_ERR_NOT_FOUND for a
  * dead handle, KV_ERR_OOM if the pool cannot hold the result (nothing changes). */
 int kv_append_batch(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n, const void* k, const void* v,
@@ -220,9 +222,18 @@ int fork_attn_partials(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n_seqs, in
 int fork_attn_merge(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n_seqs, int32_t n_q_heads,
                     void* out, float* lse, void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Decode plans cut the chunk lists into work items so that one launch holds about two
+ * items per compute unit (up to 128 chunks each); the count is the device's at
+ * kv_pool_create (256 on MI355X) or 256 for a metadata-only pool.  Set another count for
+ * a decode that shares the device with other work, or to plan long items over short
+ * contexts.  Invalidates the cached decode plan (the next call plans again).
+ * KV_ERR_INVALID for n_cu < 1. */
+int kv_pool_set_compute_units(kv_pool_t* pool, int32_t n_cu);
+
 /* Plan statistics of the last fork_attn_decode / fork_attn_workspace_size call:
  * out[0] segments, out[1] work items, out[2] chunks, out[3] partial rows,
- * out[4] unique KV bytes streamed (algorithmic), out[5] query rows. */
+ * out[4] unique KV bytes streamed (algorithmic), out[5] query rows, out[6] the largest
+ * chunk count of one work item. */
 int fork_attn_plan_stats(kv_pool_t* pool, int64_t* out, int32_t n);
 
 /* ---- packed DAG prefill (Octopus Packed DAG-GRPO, forward) ----
@@ -303,8 +314,9 @@ int kv_window_upload(kv_pool_t* pool, void* workspace, size_t ws_bytes, hipStrea
 int kv_window_step(kv_pool_t* pool, int32_t step, const void* k, const void* v, const void* q,
                    void* out, float* lse, float sm_scale, hipStream_t stream);
 
-/* Causal attention of a sequence's last n tokens (AgentKV restores an evicted or edited
- * span with one prefill in which each segment keeps its own positions: append the
+/* Causal attention of a sequence's last n tokens (AKV page, section "AKV 如何工作":
+ * segmented batch attention restores an evicted state with one prefill in which each
+ * segment keeps its own positions: append the
  * segments' K / V with kv_append and their positions, then call this).  Token j of the
  * n (0-based, query q[j]) attends to the sequence's own tokens up to and including
  * itself, then to the mounts, exactly as fork_attn_decode would for a sequence that

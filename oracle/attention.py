@@ -71,35 +71,70 @@ def merge(parts):
     return O / L, M + np.log(L)
 
 
-def decode(table, seqs, q: np.ndarray, scale: float):
+def magnitudes(q, k, v, scale: float):
+    """Sizes of the terms of one row's attention, for error bars (no new arithmetic of the
+    method): a[e] = sum_j pi_j |v_je| with pi the softmax weights, and the largest score
+    magnitude s_abs = scale * max_j sum_i |q_i k_ji|.  q [d], k [n, d], v [n, d]."""
+    q = np.asarray(q, np.float64)
+    if k.shape[0] == 0:
+        return np.zeros(q.shape[-1]), 0.0
+    k = np.asarray(k, np.float64)
+    s = scale * (k @ q)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    return p @ np.abs(np.asarray(v, np.float64)), float(abs(scale) * (np.abs(k) @ np.abs(q)).max())
+
+
+def decode(table, seqs, q: np.ndarray, scale: float, with_magnitudes: bool = False):
     """Decode for every listed sequence of an oracle ``PageTable`` (with data).
 
-    q [n, Hq, d] (fp64) -> (o [n, Hq, d], lse [n, Hq])."""
+    q [n, Hq, d] (fp64) -> (o [n, Hq, d], lse [n, Hq]); with_magnitudes adds the
+    ``magnitudes`` of every row: a [n, Hq, d] and s_abs [n, Hq]."""
     n, hq, d = q.shape
     o = np.zeros((n, hq, d))
     lse = np.zeros((n, hq))
+    a = np.zeros((n, hq, d))
+    s_abs = np.zeros((n, hq))
     for i, sid in enumerate(seqs):
         k, v = table.materialise(sid)
-        o[i], lse[i] = attend_heads(np.asarray(q[i], np.float64), k, v, scale)
+        qi = np.asarray(q[i], np.float64)
+        o[i], lse[i] = attend_heads(qi, k, v, scale)
+        if with_magnitudes:
+            g = hq // k.shape[1]
+            for h in range(hq):
+                a[i, h], s_abs[i, h] = magnitudes(qi[h], k[:, h // g, :], v[:, h // g, :], scale)
+    if with_magnitudes:
+        return o, lse, a, s_abs
     return o, lse
 
 
-def causal_last(table, sid: int, q, scale: float, rows=None):
+def causal_last(table, sid: int, q, scale: float, rows=None, with_magnitudes: bool = False):
     """Attention of the last n own tokens of sequence `sid` (n = q.shape[0]) of an oracle
     ``PageTable`` (with data): token j of the n attends to the own tokens up to and
-    including itself, then to the mounts (AgentKV page, restoring an evicted or edited
-    span with one prefill; each token sees what a decode at that token would see).
+    including itself, then to the mounts (AKV page, section "AKV 如何工作": segmented
+    batch attention restores an evicted or edited state with one prefill, each segment
+    keeping its own positions; each token sees what a decode at that token would see).
 
     q [n, Hq, d] (fp64; anything indexable by row) -> (o [n, Hq, d], lse [n, Hq]), or
-    only the listed rows j, in their order, when `rows` is given."""
+    only the listed rows j, in their order, when `rows` is given; with_magnitudes adds
+    the rows' ``magnitudes`` (a, s_abs) as in ``decode``."""
     n, hq, d = q.shape
     k, v = table.materialise(sid)  # own tokens, then mounts
     n_own = table.info(sid)[0]
     rows = list(range(n)) if rows is None else [int(j) for j in rows]
     o = np.zeros((len(rows), hq, d))
     lse = np.zeros((len(rows), hq))
+    a = np.zeros((len(rows), hq, d))
+    s_abs = np.zeros((len(rows), hq))
+    g = hq // k.shape[1]
     for r, j in enumerate(rows):
         end = n_own - n + j + 1
         idx = np.concatenate([np.arange(end), np.arange(n_own, k.shape[0])]).astype(np.int64)
-        o[r], lse[r] = attend_heads(np.asarray(q[j], np.float64), k[idx], v[idx], scale)
+        qj = np.asarray(q[j], np.float64)
+        o[r], lse[r] = attend_heads(qj, k[idx], v[idx], scale)
+        if with_magnitudes:
+            for h in range(hq):
+                a[r, h], s_abs[r, h] = magnitudes(qj[h], k[idx][:, h // g, :], v[idx][:, h // g, :], scale)
+    if with_magnitudes:
+        return o, lse, a, s_abs
     return o, lse

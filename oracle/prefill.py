@@ -87,24 +87,59 @@ def block_pairs(segments, edges, T: int, block: int) -> np.ndarray:
     return need
 
 
-def attend_rows(q, k, v, segments, edges, rows, scale: float):
+def attend_rows(q, k, v, segments, edges, rows, scale: float, with_magnitudes: bool = False):
     """Dense masked attention for the listed query rows.
 
-    q [T, Hq, d], k/v [T, Hkv, d] (fp64) -> o [len(rows), Hq, d], lse [len(rows), Hq]."""
+    q [T, Hq, d] (fp64, or anything that yields fp64 rows when indexed), k/v [T, Hkv, d]
+    (fp64) -> o [len(rows), Hq, d], lse [len(rows), Hq]; with_magnitudes adds, per row and
+    head, a = sum_j pi_j |v_j| [len(rows), Hq, d] and s_abs = scale * max_j sum_i |q_i k_ji|
+    [len(rows), Hq] over the visible keys (sizes of the terms, for error bars).
+
+    A row's visible keys are its segment's fixed ranges (ancestors, edge sources) and its
+    own segment up to itself; rows of one segment are evaluated together as one masked
+    product, key range by key range (every key of a range is read in place)."""
     T, hq, d = q.shape
     hkv = k.shape[1]
     g = hq // hkv
     seg_of = _segment_of(segments, T)
+    kt = np.ascontiguousarray(np.transpose(k, (1, 0, 2)))  # [Hkv, T, d]
+    vt = np.ascontiguousarray(np.transpose(v, (1, 0, 2)))
+    rows = [int(i) for i in rows]
     o = np.zeros((len(rows), hq, d))
     lse = np.zeros((len(rows), hq))
+    a_out = np.zeros((len(rows), hq, d)) if with_magnitudes else None
+    s_out = np.zeros((len(rows), hq)) if with_magnitudes else None
+    by_seg = {}
     for r, i in enumerate(rows):
-        idx = np.nonzero(visible_mask_row(segments, edges, T, int(i), seg_of))[0]
-        for h in range(hq):
-            kk = k[idx, h // g, :]
-            s = scale * (kk @ q[i, h])
-            m = s.max()
-            p = np.exp(s - m)
-            l = p.sum()
-            o[r, h] = (p @ v[idx, h // g, :]) / l
-            lse[r, h] = m + np.log(l)
+        by_seg.setdefault(int(seg_of[i]), []).append(r)
+    for s, rs in by_seg.items():
+        st = int(segments[s][0])
+        for c0 in range(0, len(rs), 64):  # a group of rows of one segment
+            grp = rs[c0:c0 + 64]
+            ii = np.array([rows[r] for r in grp])
+            ranges = list(visible_ranges(segments, edges, s)) + [(st, int(ii.max()) + 1)]
+            qg = np.stack([np.asarray(q[int(i)], np.float64) for i in ii])  # [R, Hq, d]
+            for hk in range(hkv):
+                qh = qg[:, hk * g:(hk + 1) * g, :].reshape(-1, d)  # [R * G, d]
+                parts = [scale * (qh @ kt[hk, a:b].T) for a, b in ranges]
+                own = parts[-1].reshape(len(grp), g, -1)
+                later = np.arange(st, ranges[-1][1])[None, :] > ii[:, None]  # [R, keys]: key after the query
+                own[np.broadcast_to(later[:, None, :], own.shape)] = -np.inf  # causal
+                m = np.max([p.max(axis=1) for p in parts], axis=0)  # [R * G]
+                ps = [np.exp(p - m[:, None]) for p in parts]
+                l = np.sum([p.sum(axis=1) for p in ps], axis=0)
+                oh = sum(p @ vt[hk, a:b] for p, (a, b) in zip(ps, ranges)) / l[:, None]
+                o[grp, hk * g:(hk + 1) * g] = oh.reshape(len(grp), g, d)
+                lse[grp, hk * g:(hk + 1) * g] = (m + np.log(l)).reshape(len(grp), g)
+                if with_magnitudes:
+                    ah = sum(p @ np.abs(vt[hk, a:b]) for p, (a, b) in zip(ps, ranges)) / l[:, None]
+                    a_out[grp, hk * g:(hk + 1) * g] = ah.reshape(len(grp), g, d)
+                    sa = []
+                    for (a, b), p in zip(ranges, parts):
+                        t = abs(scale) * (np.abs(qh) @ np.abs(kt[hk, a:b]).T)
+                        t[~np.isfinite(p)] = 0.0  # masked keys are not read
+                        sa.append(t.max(axis=1))
+                    s_out[grp, hk * g:(hk + 1) * g] = np.max(sa, axis=0).reshape(len(grp), g)
+    if with_magnitudes:
+        return o, lse, a_out, s_out
     return o, lse

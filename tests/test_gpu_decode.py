@@ -1,32 +1,39 @@
 """GPU parity of fork_attn_decode (HIP path through the C ABI) against the fp64 oracle.
 
-Tolerances: bf16 outputs max-abs 2e-2 and mean-abs 2e-3 against the fp64 oracle
-(fp32 accumulation in the kernels); fp32 pools max-abs 1e-4; LSE (fp32) max-abs 2e-3.
-Integer state (block tables, refcounts) bit-exact.  Every case prints its name first.
+Bars: every output element and LSE within the decode error model's bars
+(tests/harness.py: decode_bars, derived from the kernel's arithmetic: bf16 P, fp32
+sums), and within the coarse gate (bf16 max-abs 2e-2 / mean-abs 2e-3, fp32 pools
+max-abs 1e-4, LSE 2e-3).  Planted-key cases (one key singled out per row, so the row's
+output is that key's value: a closed form) cover every chunk slot of the longest work
+items, at small size with a one-compute-unit plan and at full size.  Integer state
+(block tables, refcounts) bit-exact.  Every case prints its name first.
 """
 import numpy as np
 import pytest
 
 import workloads as W
-from tests.harness import build_device_pool, check_close, oracle_decode, out_to_f64, subscenario, to_torch
+from tests.harness import (build_device_pool, check_close, check_decode_model, oracle_decode, out_to_f64,
+                           plant_queries, subscenario, to_torch)
 
 pytestmark = pytest.mark.gpu
 
 BF16_MAX, BF16_MEAN, F32_MAX, LSE_MAX = 2e-2, 2e-3, 1e-4, 2e-3
 
 
-def _run(sc, label):
+def _run(sc, label, q=None, n_cu=None):
     import torch
+    import fork_attention_decode_amd as fa
     print(f"[case] {label}: {sc.name} Hq={sc.n_q_heads} Hkv={sc.n_kv_heads} d={sc.head_dim} {sc.dtype}", flush=True)
     pool, _ = build_device_pool(sc)
-    q = to_torch(sc.q, sc.dtype)
-    out, lse = pool.decode(sc.queries, q, sc.sm_scale)
+    if n_cu is not None:
+        fa.kv_pool_set_compute_units(pool.handle, n_cu)
+    out, lse = pool.decode(sc.queries, to_torch(sc.q if q is None else q, sc.dtype), sc.sm_scale)
     torch.cuda.synchronize()
     return pool, out_to_f64(out, sc.dtype), lse.double().cpu().numpy()
 
 
-def _check(sc, o, lse, label, rows=None):
-    ro, rl = oracle_decode(sc, rows)
+def _check(sc, o, lse, label, rows=None, q=None):
+    ro, rl, a, s_abs = oracle_decode(sc, rows, with_magnitudes=True, q=q)
     if rows is not None:
         o, lse = o[rows], lse[rows]
     if sc.dtype == "bf16":
@@ -34,7 +41,17 @@ def _check(sc, o, lse, label, rows=None):
     else:
         mx, mn = check_close(o, ro, F32_MAX, F32_MAX, label)
     check_close(lse, rl, LSE_MAX, LSE_MAX, label + " lse")
-    print(f"[ok] {label}: max-abs {mx:.3g} mean-abs {mn:.3g}", flush=True)
+    wo, wl = check_decode_model(o, lse, ro, rl, a, s_abs, sc.head_dim, sc.dtype, label)
+    print(f"[ok] {label}: max-abs {mx:.3g} mean-abs {mn:.3g}; error / model bar: O {wo:.3f}, LSE {wl:.3f}",
+          flush=True)
+
+
+def _check_planted(sc, o, vp, label):
+    """Closed form: a planted row's output is the planted key's value (bf16 values are
+    exact in the output type; the other keys carry ~e^-20 of the weight)."""
+    err = np.abs(o - vp)
+    bad = err > 2.0 ** -8 * np.abs(vp) + 1e-6
+    assert not bad.any(), f"{label}: {int(bad.sum())} planted elements differ from v_j, rows {np.argwhere(bad)[:4, :2].tolist()}"
 
 
 def test_tiny_fork_fp32():
@@ -133,8 +150,40 @@ def test_shared_prefix_full_size():
 def test_octopus_dag_full_size():
     sc = W.octopus_dag()
     pool, o, lse = _run(sc, "Octopus DAG decode, full size")
-    assert pool.plan_stats()["unique_kv_bytes"] == 536870912
+    st = pool.plan_stats()
+    assert st["unique_kv_bytes"] == 536870912 and st["longest_item_chunks"] == 128
     _check(sc, o, lse, "Octopus DAG decode, full size")
+
+
+def test_long_items_planted_keys_small():
+    # a one-compute-unit plan cuts the 128-page shared prefix into one 128-chunk item per
+    # KV head, so chunk slots 64..127 (the second chunk-metadata register) are read at
+    # small size; every row singles out a key in a different chunk slot, half of them in
+    # slots 64..127, the rest in the low slots and the private tails
+    sc = W.fork_scenario(prefix=2048, branches=3, private=[40, 0, 300], hq=8, hkv=2, d=128, seed=12)
+    n, hq = len(sc.queries), sc.n_q_heads
+    ctx = [2048 + 40, 2048, 2048 + 300]
+    idx = [[16 * (64 + 5 * (4 * i + h // 2)) + h if h % 2 == 0 else (16 * (21 * i + 3 * h) + 5) % ctx[i]
+            for h in range(hq)] for i in range(n)]
+    idx[1][6] = 16 * 127 + 15  # the last slot of the last chunk
+    idx[0][7], idx[2][5] = 2048 + 39, 2048 + 299  # the private tails' last tokens
+    qs, vp, idx = plant_queries(sc, None, idx=idx)
+    pool, o, lse = _run(sc, "planted keys over 128-chunk items", q=qs, n_cu=1)
+    assert pool.plan_stats()["longest_item_chunks"] == 128
+    _check_planted(sc, o, vp, "planted keys over 128-chunk items")
+    _check(sc, o, lse, "planted keys over 128-chunk items", q=qs)
+
+
+@pytest.mark.parametrize("make", [W.shared_prefix_fork, W.octopus_dag], ids=["shared_prefix", "octopus_dag"])
+def test_planted_keys_full_size(make):
+    # every row (branch, query head) of the full-size workload singles out one key drawn
+    # uniformly from its context: a page missing from a work item, read twice, or read
+    # from the wrong place moves that row's output by O(1)
+    sc = make()
+    qs, vp, idx = plant_queries(sc, np.random.default_rng(99))
+    pool, o, lse = _run(sc, f"planted keys, {sc.name}, full size", q=qs)
+    _check_planted(sc, o, vp, f"planted keys, {sc.name}")
+    _check(sc, o, lse, f"planted keys, {sc.name}", q=qs)
 
 
 def test_append_batch_contents_and_decode():
@@ -169,7 +218,53 @@ def test_append_batch_contents_and_decode():
     qb = W.to_bf16_bits(rng.standard_normal((len(seqs), 8, 128)))
     out, lse = pool.decode(seqs, to_torch(qb, "bf16"), sc.sm_scale)
     torch.cuda.synchronize()
-    ro, rl = att.decode(ora, seqs, f(qb), sc.sm_scale)
+    ro, rl, a, s_abs = att.decode(ora, seqs, f(qb), sc.sm_scale, with_magnitudes=True)
     check_close(out_to_f64(out, "bf16"), ro, BF16_MAX, BF16_MEAN, "decode after kv_append_batch")
     check_close(lse.double().cpu().numpy(), rl, LSE_MAX, LSE_MAX, "decode after kv_append_batch lse")
+    check_decode_model(out_to_f64(out, "bf16"), lse.double().cpu().numpy(), ro, rl, a, s_abs, 128, "bf16",
+                       "decode after kv_append_batch")
     print("[ok] kv_append_batch", flush=True)
+
+
+@pytest.mark.parametrize("order", ["copier_first", "writer_first"])
+def test_append_batch_rewound_fork_in_shared_tail(order):
+    # a has 40 tokens, b = fork(a) rewound to 36 (page 2 shared; a's tokens 36..39 sit in
+    # its slots 4..7).  append_batch lists both: whichever comes first copies page 2, the
+    # other then owns it alone and writes in place into a slot the copy reads.  Every
+    # page's contents must equal the oracle's after the same single appends.
+    import torch
+    import fork_attention_decode_amd as fa
+    from oracle import pagetable as pt
+    print(f"[case] kv_append_batch after a rewind into the shared tail ({order})", flush=True)
+    hkv, d = 2, 128
+    f = W.bf16_bits_to_f64
+    rng = np.random.default_rng(17)
+    pool = fa.Pool(hkv, d, 16)
+    ora = pt.PageTable(16, 16, hkv, d, with_data=True)
+    a = pool.seq_create()
+    ora.create()
+    kb = W.to_bf16_bits(rng.standard_normal((40, hkv, d)) / np.sqrt(d))
+    vb = W.to_bf16_bits(rng.standard_normal((40, hkv, d)))
+    pool.append(a, to_torch(kb, "bf16"), to_torch(vb, "bf16"))
+    ora.append(a, 40, k=f(kb), v=f(vb))
+    b = pool.fork(a)
+    ora.fork(a)
+    pool.rewind(b, 36)
+    ora.rewind(b, 36)
+    seqs = [a, b] if order == "copier_first" else [b, a]
+    for _ in range(3):
+        kn = W.to_bf16_bits(rng.standard_normal((2, hkv, d)) / np.sqrt(d))
+        vn = W.to_bf16_bits(rng.standard_normal((2, hkv, d)))
+        pool.append_batch(seqs, to_torch(kn, "bf16"), to_torch(vn, "bf16"))
+        for i, s in enumerate(seqs):
+            ora.append(s, 1, k=f(kn[i:i + 1]), v=f(vn[i:i + 1]))
+        torch.cuda.synchronize()
+    for s in (a, b):
+        assert list(pool.block_table(s)) == ora.block_table(s), s
+        for L, page in enumerate(ora.block_table(s)):
+            n_valid = min(16, ora.seqs[s].n - 16 * L)
+            for h in range(hkv):
+                k, v = pool.read_page(page, h)
+                assert np.array_equal(f(k[:n_valid]), ora.kdata[page][:n_valid, h]), (s, L, h)
+                assert np.array_equal(f(v[:n_valid]), ora.vdata[page][:n_valid, h]), (s, L, h)
+    print("[ok] kv_append_batch after a rewind into the shared tail", flush=True)

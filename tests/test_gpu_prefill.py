@@ -2,15 +2,17 @@
 the fp64 token-level oracle.
 
 Bars: bf16 outputs max-abs 2e-2 and mean-abs 2e-3 against the fp64 oracle, LSE (natural
-log, fp32) max-abs 2e-3.  Small cases compare every row; the full-size packed workload
-(81,920 tokens) compares the first and last token of every segment, the tokens at both
-ends of every edge target range and every 64-row block boundary of a seeded sample.
+log, fp32) max-abs 2e-3, and every element within the attention error model's bars
+(tests/harness.py: decode_bars; bf16 P, fp32 sums, here with accumulator chains of up to
+4,096 steps: gamma = 2^-12).  Small cases compare every row; the full-size packed
+workload (81,920 tokens) compares every row of 64 seeded query blocks and of the first and
+last block of every segment.
 """
 import numpy as np
 import pytest
 
 import workloads as W
-from tests.harness import check_close, to_torch
+from tests.harness import check_close, check_decode_model, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -45,14 +47,17 @@ def _oracle_rows(pi, rows):
     from oracle import prefill as pf
     k = W.bf16_bits_to_f64(pi.k)
     v = W.bf16_bits_to_f64(pi.v)
-    return pf.attend_rows(_Rows(pi.q), k, v, pi.segments, pi.edges, rows, pi.sm_scale)
+    return pf.attend_rows(_Rows(pi.q), k, v, pi.segments, pi.edges, rows, pi.sm_scale, with_magnitudes=True)
 
 
 def _check(pi, o, lse, rows, label):
-    ro, rl = _oracle_rows(pi, rows)
+    ro, rl, a, s_abs = _oracle_rows(pi, rows)
     mx, mn = check_close(o[rows], ro, BF16_MAX, BF16_MEAN, label)
     check_close(lse[:, rows].T, rl, LSE_MAX, LSE_MAX, label + " lse")
-    print(f"[ok] {label}: {len(rows)} rows, max-abs {mx:.3g} mean-abs {mn:.3g}", flush=True)
+    wo, wl = check_decode_model(o[rows], lse[:, rows].T, ro, rl, a, s_abs, pi.head_dim, "bf16", label,
+                                gamma=2.0 ** -12)
+    print(f"[ok] {label}: {len(rows)} rows, max-abs {mx:.3g} mean-abs {mn:.3g}; error / model bar: O {wo:.3f}, "
+          f"LSE {wl:.3f}", flush=True)
 
 
 @pytest.mark.parametrize("T", [1, 37, 64, 300])
@@ -83,21 +88,17 @@ def test_dag_many_edges_long_rows():
 
 def test_packed_dag_full_size():
     """16,384-token prefix + 8 x 8,192 branches, 12 edges of 2,048 tokens (81,920 tokens,
-    32 / 8 heads); sampled rows against the oracle, block counts exact."""
+    32 / 8 heads); every row of 64 seeded query blocks and of the first and last block of
+    each segment against the oracle, block counts exact."""
     pi = W.dag_prefill()
     mask, o, lse = _run(pi, "packed DAG prefill, full size")
     row_ptr, col, kind = mask.host
     assert mask.nnz == 410240 and int((kind == 1).sum()) == 1280
     rng = np.random.default_rng(7)
-    rows = set()
+    blocks = {int(b) for b in rng.choice(pi.T // 64, size=64, replace=False)}
     for st, ln, _ in pi.segments:
-        rows |= {int(st), int(st + ln - 1)}
-    for _, _, _, dst in pi.edges:
-        st, ln, _ = pi.segments[dst]
-        rows |= {int(st), int(st + 63), int(st + ln - 64)}
-    for qb in rng.choice(pi.T // 64, size=12, replace=False):
-        rows |= {int(64 * qb), int(64 * qb + 31), int(64 * qb + 32), int(64 * qb + 63)}
-    rows = sorted(rows)
+        blocks |= {int(st) // 64, int(st + ln - 1) // 64}
+    rows = sorted(r for b in blocks for r in range(64 * b, min(pi.T, 64 * b + 64)))
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     _check(pi, o, lse, rows, "packed DAG prefill, full size")
 

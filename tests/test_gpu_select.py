@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import workloads as W
-from tests.harness import build_device_pool, check_close, oracle_decode, out_to_f64, to_torch
+from tests.harness import build_device_pool, check_close, check_decode_both, oracle_decode, out_to_f64, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -127,8 +127,13 @@ def test_select_drop_then_decode(repos):
     keep = pool.select_and_drop(1, to_torch(qb, "bf16"), sc.sm_scale, budget, repos=repos)
     torch.cuda.synchronize()
     assert int(keep.sum()) == budget
-    # the oracle replays the same scenario, then drops the spans of the GPU's keep mask
-    sc.ops = sc.ops + [("drop", 1, sel.drop_spans(keep.astype(bool)), repos)]
+    # several keep sets are correct where fp32 scores tie to within their rounding: the
+    # GPU's set must be one of them by the oracle's fp64 scores (no dropped key scores
+    # above a kept one by more than the score bar), and the oracle then drops its spans
+    ref = sel.key_scores(_oracle_table(sc)[0], 1, W.bf16_bits_to_f64(qb), sc.sm_scale)
+    kb = keep.astype(bool)
+    assert ref[~kb].max() <= ref[kb].min() + 2 * (REL * ref[kb].min() + ABS), "keep set not a top-k of the scores"
+    sc.ops = sc.ops + [("drop", 1, sel.drop_spans(kb), repos)]
     table, _ = _oracle_table(sc)
     assert list(pool.block_table(1)) == table.block_table(1)
     assert np.array_equal(pool.positions(1), table.positions(1))
@@ -136,9 +141,8 @@ def test_select_drop_then_decode(repos):
         assert pool.refcount(p) == table.rc[p], f"refcount of page {p}"
     out, lse = pool.decode(sc.queries, to_torch(sc.q, "bf16"), sc.sm_scale)
     torch.cuda.synchronize()
-    ro, rl = oracle_decode(sc)
-    check_close(out_to_f64(out, "bf16"), ro, 2e-2, 2e-3, "decode after select + drop")
-    check_close(lse.double().cpu().numpy(), rl, 2e-3, 2e-3, "lse")
+    check_decode_both(out_to_f64(out, "bf16"), lse.double().cpu().numpy(), oracle_decode(sc, with_magnitudes=True),
+                      sc.head_dim, "bf16", "decode after select + drop", rerotated_keys=repos)
     print("[ok] select + drop + decode", flush=True)
 
 

@@ -419,3 +419,29 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
+
+
+def test_append_batch_copy_source_written_in_place_by_a_later_sequence():
+    # a has 40 tokens (pages of 16), b = fork(a) rewound to 36: page 2 is shared, a's
+    # token 36 sits in its slot 4.  append_batch([a, b]): a copies page 2 (its token goes
+    # to slot 8 of the copy), after which b owns page 2 alone and writes slot 4 in place.
+    # The same decisions as two single appends in list order.
+    pool = fa.Pool(1, 2, 16, metadata_only=True)
+    ora = pt.PageTable(16, 16)
+    a = pool.seq_create()
+    assert ora.create() == a
+    pool.append(a, n=40)
+    ora.append(a, 40)
+    b = pool.fork(a)
+    assert ora.fork(a) == b
+    pool.rewind(b, 36)
+    ora.rewind(b, 36)
+    shared = list(fa.kv_block_table(pool.handle, a))[2]
+    assert fa.kv_page_refcount(pool.handle, shared) == 2
+    pool.append_batch([a, b])
+    ora.append(a, 1)
+    ora.append(b, 1)
+    _cmp(pool.handle, ora, [a, b])
+    ta, tb = list(fa.kv_block_table(pool.handle, a)), list(fa.kv_block_table(pool.handle, b))
+    assert ta[:2] == tb[:2] and ta[2] != shared and tb[2] == shared  # a copied, b wrote in place
+    assert fa.kv_page_refcount(pool.handle, shared) == 1
