@@ -13,7 +13,8 @@ import numpy as np
 import pytest
 
 import workloads as W
-from tests.harness import (build_device_pool, check_close, check_decode_both, oracle_decode, out_to_f64,
+from tests.harness import (build_device_pool, check_close, check_decode_both, check_decode_model, oracle_decode,
+                           out_to_f64,
                            plant_queries, subscenario, to_torch)
 
 pytestmark = pytest.mark.gpu
@@ -213,6 +214,10 @@ def test_akv_drop_repos_full_size():
     for req, (sub, qs, vp) in planted.items():
         bad = np.abs(o[req] - vp[0]) > 2.0 ** -8 * np.abs(vp[0]) + 1e-6
         assert not bad.any(), f"planted keys of request {req}: {int(bad.sum())} elements differ from v_j"
-        check_decode_both(o[[req]], l[[req]], oracle_decode(sub, with_magnitudes=True, q=qs), 128, "bf16",
-                          f"planted keys, request {req}", rerotated_keys=True)
+        # planted scores are ~40: the keys' one-ulp rounding moves them by up to 2^-7 x 40,
+        # so only the error model (which scales with the scores) applies, not the fixed
+        # 2e-3 LSE gate
+        ro, rl, a, s_abs = oracle_decode(sub, with_magnitudes=True, q=qs)
+        check_decode_model(o[[req]], l[[req]], ro, rl, a, s_abs, 128, "bf16", f"planted keys, request {req}",
+                           rerotated_keys=True)
     print("[ok] planted keys of requests 0 and 11", flush=True)

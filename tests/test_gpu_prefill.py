@@ -4,7 +4,7 @@ the fp64 token-level oracle.
 Bars: bf16 outputs max-abs 2e-2 and mean-abs 2e-3 against the fp64 oracle, LSE (natural
 log, fp32) max-abs 2e-3, and every element within the attention error model's bars
 (tests/harness.py: decode_bars; bf16 P, fp32 sums, here with accumulator chains of up to
-4,096 steps: gamma = 2^-12).  Small cases compare every row; the full-size packed
+4,096 steps: gamma = 2^-12, and a row sum over the rounded P).  Small cases compare every row; the full-size packed
 workload (81,920 tokens) compares every row of 64 seeded query blocks and of the first and
 last block of every segment.
 """
@@ -55,7 +55,7 @@ def _check(pi, o, lse, rows, label):
     mx, mn = check_close(o[rows], ro, BF16_MAX, BF16_MEAN, label)
     check_close(lse[:, rows].T, rl, LSE_MAX, LSE_MAX, label + " lse")
     wo, wl = check_decode_model(o[rows], lse[:, rows].T, ro, rl, a, s_abs, pi.head_dim, "bf16", label,
-                                gamma=2.0 ** -12)
+                                gamma=2.0 ** -12, rounded_p_sum=True)
     print(f"[ok] {label}: {len(rows)} rows, max-abs {mx:.3g} mean-abs {mn:.3g}; error / model bar: O {wo:.3f}, "
           f"LSE {wl:.3f}", flush=True)
 

@@ -64,8 +64,8 @@ def test_bars_scale_with_the_terms():
     b2, l2 = decode_bars(o, np.zeros((1, 1)), 2 * a, np.full((1, 1), 10.0), 128, "bf16")
     b3, l3 = decode_bars(o, np.zeros((1, 1)), a, np.full((1, 1), 20.0), 128, "bf16")
     assert np.all(b2 > b1) and np.all(b3 > b1) and np.all(l3 > l1) and np.all(l2 == l1)
-    assert np.allclose(b1, (2.0 ** -9 + np.expm1(2 * 130 * 2.0 ** -24 * 10) + 2.0 ** -15) * 0.5
-                       + 2.0 ** -9 * 0.1 + 1e-7)
+    assert np.allclose(b1, (2.0 ** -8 + np.expm1(2 * 130 * 2.0 ** -24 * 10) + 2.0 ** -15) * 0.5
+                       + 2.0 ** -8 * 0.1 + 1e-7)
 
 
 def test_planted_queries_single_out_their_key():
