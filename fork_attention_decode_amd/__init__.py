@@ -81,6 +81,7 @@ _SIGS = {
     "kv_pool_set_compute_units": [_P, _i32],
     "fork_attn_workspace_size": [_P, _pi32, _i32, _i32, _psz],
     "fork_attn_decode": [_P, _pi32, _i32, _i32, _P, _P, _P, C.c_float, _P, _sz, _P],
+    "fork_attn_decode_static": [_P, _pi32, _i32, _i32, _P, _P, _P, C.c_float, _P],
     "fork_attn_plan_stats": [_P, _pi64, _i32],
     "fork_attn_partials": [_P, _pi32, _i32, _i32, _P, C.c_float, _P, _sz, _P],
     "fork_attn_merge": [_P, _pi32, _i32, _i32, _P, _P, _P, _sz, _P],
@@ -285,6 +286,16 @@ def fork_attn_decode(pool: int, seqs: Sequence[int], n_q_heads: int, q: int, out
     _check("fork_attn_decode", lib.fork_attn_decode(pool, _ptr(s, C.c_int32), len(s), n_q_heads, q, out,
                                                     lse or None, sm_scale, workspace, ws_bytes, stream or None),
            pool)
+
+
+FORKATTN_STATIC_WORKSPACE_BYTES = 32 << 20
+
+
+def fork_attn_decode_static(pool: int, seqs: Sequence[int], n_q_heads: int, q: int, out: int, lse: int,
+                            sm_scale: float, stream: int = 0):
+    s = np.ascontiguousarray(np.asarray(seqs, np.int32))
+    _check("fork_attn_decode_static", lib.fork_attn_decode_static(pool, _ptr(s, C.c_int32), len(s), n_q_heads, q, out,
+                                                                  lse or None, sm_scale, stream or None), pool)
 
 
 def fork_attn_partials(pool: int, seqs: Sequence[int], n_q_heads: int, q: int, sm_scale: float, workspace: int,

@@ -20,6 +20,7 @@
 #include "pool.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <map>
 #include <unordered_map>
@@ -274,6 +275,8 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
   for (const Item& it : items) longest = std::max<int64_t>(longest, it.n_chunks);
   pc.stats[6] = longest;
   pc.valid = true;
+  static std::atomic<uint64_t> plan_serial{0};
+  pc.serial = ++plan_serial;
   pc.causal_n = len_cap ? -1 : 0;
   pc.version = P->version;
   pc.seqs.assign(seqs, seqs + n);
@@ -317,14 +320,9 @@ static int prepare(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, vo
   return KV_OK;
 }
 
-int fork_attn_partials(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, const void* q, float sm_scale,
-                       void* ws, size_t ws_bytes, hipStream_t s) {
-  if (P && n == 0) return KV_OK;
-  if (!q) FAIL(P, KV_ERR_INVALID, "null q");
-  int st = prepare(P, seqs, n, hq, ws, ws_bytes, s);
-  if (st) return st;
-  DecodePlanCache& pc = P->plan;
-  char* w = (char*)ws;
+// The two launches of a planned decode whose plan sits in the device buffer w.
+static hipError_t launch_partials(kv_pool_t* P, const void* q, float sm_scale, char* w, hipStream_t s) {
+  const DecodePlanCache& pc = P->plan;
   DecodeParams dp;
   dp.q = q;
   dp.k_pages = P->k;
@@ -338,7 +336,29 @@ int fork_attn_partials(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq
   dp.n_items = pc.n_items;
   dp.n_pages = P->cfg.n_pages;
   dp.scale_log2 = sm_scale * 1.4426950408889634f;
-  hipError_t e = launch_decode(P->cfg.dtype, P->cfg.head_dim, dp, s);
+  return launch_decode(P->cfg.dtype, P->cfg.head_dim, dp, s);
+}
+
+static hipError_t launch_merge_of(kv_pool_t* P, void* out, float* lse, char* w, hipStream_t s) {
+  const DecodePlanCache& pc = P->plan;
+  MergeParams mp;
+  mp.count = reinterpret_cast<const int32_t*>(w + pc.off_mptr);
+  mp.max_parts = pc.max_parts;
+  mp.part_lse2 = reinterpret_cast<const float*>(w + pc.off_plse);
+  mp.part_o = reinterpret_cast<const float*>(w + pc.off_po);
+  mp.out = out;
+  mp.lse = lse;
+  mp.n_rows = pc.n_out_rows;
+  return launch_merge(P->cfg.dtype, P->cfg.head_dim, mp, s);
+}
+
+int fork_attn_partials(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, const void* q, float sm_scale,
+                       void* ws, size_t ws_bytes, hipStream_t s) {
+  if (P && n == 0) return KV_OK;
+  if (!q) FAIL(P, KV_ERR_INVALID, "null q");
+  int st = prepare(P, seqs, n, hq, ws, ws_bytes, s);
+  if (st) return st;
+  hipError_t e = launch_partials(P, q, sm_scale, (char*)ws, s);
   if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("decode launch: ") + hipGetErrorString(e));
   return KV_OK;
 }
@@ -349,20 +369,42 @@ int fork_attn_merge(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, v
   if (!out) FAIL(P, KV_ERR_INVALID, "null out");
   int st = prepare(P, seqs, n, hq, ws, ws_bytes, s);
   if (st) return st;
-  DecodePlanCache& pc = P->plan;
-  char* w = (char*)ws;
-  MergeParams mp;
-  mp.count = reinterpret_cast<const int32_t*>(w + pc.off_mptr);
-  mp.max_parts = pc.max_parts;
-  mp.part_lse2 = reinterpret_cast<const float*>(w + pc.off_plse);
-  mp.part_o = reinterpret_cast<const float*>(w + pc.off_po);
-  mp.out = out;
-  mp.lse = lse;
-  mp.n_rows = pc.n_out_rows;
-  hipError_t e = launch_merge(P->cfg.dtype, P->cfg.head_dim, mp, s);
+  hipError_t e = launch_merge_of(P, out, lse, (char*)ws, s);
   if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
   return KV_OK;
 }
+
+}  // extern "C"
+
+// fork_attn_decode into a library-held device buffer `w` of cap bytes that every call on
+// the device shares: *held names the plan the buffer holds (0 = none); the plan is
+// uploaded again unless it is this pool's current one.  The upload copies from pageable
+// host memory (no staging buffer to allocate).  Used by the no-allocation entry point.
+int fa_decode_shared_buffer(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, const void* q, void* out,
+                            float* lse, float sm_scale, char* w, size_t cap, uint64_t* held, hipStream_t s) {
+  if (!P) FAIL(P, KV_ERR_INVALID, "null pool");
+  if (n == 0) return KV_OK;
+  if (!P->device) FAIL(P, KV_ERR_INVALID, "metadata-only pool has no KV data");
+  if (!q || !out) FAIL(P, KV_ERR_INVALID, "null device pointer");
+  int st = build_plan(P, seqs, n, hq);
+  if (st) return st;
+  DecodePlanCache& pc = P->plan;
+  if (pc.ws_need > cap)
+    FAIL(P, KV_ERR_WORKSPACE, "decode needs " + std::to_string(pc.ws_need) + " bytes of workspace, more than the " +
+                                  std::to_string(cap) + "-byte static buffer");
+  hipError_t e = hipSuccess;
+  if (*held != pc.serial) {
+    *held = 0;
+    e = hipMemcpyAsync(w, pc.blob.data(), pc.blob.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) *held = pc.serial;
+  }
+  if (e == hipSuccess) e = launch_partials(P, q, sm_scale, w, s);
+  if (e == hipSuccess) e = launch_merge_of(P, out, lse, w, s);
+  if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("decode (static buffer): ") + hipGetErrorString(e));
+  return KV_OK;
+}
+
+extern "C" {
 
 int fork_attn_decode(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, const void* q, void* out,
                      float* lse, float sm_scale, void* ws, size_t ws_bytes, hipStream_t s) {

@@ -67,6 +67,7 @@ struct DecodePlanCache {
   std::vector<char> blob;  // host image of the plan part of the workspace
   int64_t stats[7] = {0, 0, 0, 0, 0, 0, 0};
   int64_t causal_n = 0;  // 0: a decode plan; n > 0: causal rows of the last n tokens; -1: other caps
+  uint64_t serial = 0;   // unique across pools and rebuilds: names this plan's contents
 };
 
 // A steady-state decode window: every sequence's next n_steps slots reserved up front and

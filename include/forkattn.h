@@ -230,6 +230,21 @@ int fork_attn_merge(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n_seqs, int32
  * KV_ERR_INVALID for n_cu < 1. */
 int kv_pool_set_compute_units(kv_pool_t* pool, int32_t n_cu);
 
+/* fork_attn_decode without a workspace, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, hosts that forbid allocation).  The
+ * plan and the partials live in a device array the library holds for the process
+ * lifetime, one per device (FORKATTN_STATIC_WORKSPACE_BYTES = 32 MiB each); the call
+ * itself allocates nothing (the plan is copied from host memory the pool already holds).
+ * Same arguments, results and errors as fork_attn_decode, plus KV_ERR_WORKSPACE when the
+ * decode needs more than that many bytes of workspace (fork_attn_workspace_size tells).
+ * Call with the pool's device current.  Every call on a device shares its array and
+ * leaves its contents behind: calls that overlap on one device (other host threads,
+ * other streams) race and must be serialised by the caller; the plan is uploaded again
+ * whenever the array holds another pool's or an older plan. */
+#define FORKATTN_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+int fork_attn_decode_static(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n_seqs, int32_t n_q_heads,
+                            const void* q, void* out, float* lse, float sm_scale, hipStream_t stream);
+
 /* Plan statistics of the last fork_attn_decode / fork_attn_workspace_size call:
  * out[0] segments, out[1] work items, out[2] chunks, out[3] partial rows,
  * out[4] unique KV bytes streamed (algorithmic), out[5] query rows, out[6] the largest
