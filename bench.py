@@ -4,11 +4,13 @@ Step (the headline `value`): one fork_attn_decode over every branch of the share
 fork workload -- 16 branches x 32 query heads, 8 KV heads, d = 128, bf16, a 32,768-token
 shared prefix + 2,048 private tokens per branch, page 16 -- with every input resident
 in HBM.  `value` = branch-tokens/s (branches decoded per second of wall clock over the
-timed steps).  `roofline` prices the dominant kernel (decode_kernel, launched by
-fork_attn_partials) against MI355X's 8 TB/s HBM with its algorithmic bytes (each unique
-KV byte once + Q), timed with HIP events on the launch stream.  Steps rotate over
-several identical pool copies so no step finds its KV in the last-level cache left by
-the previous one.
+timed steps).  `roofline` prices the same step (decode_kernel from fork_attn_partials +
+merge_kernel from fork_attn_merge) against MI355X's 8 TB/s HBM with its algorithmic
+bytes (each unique KV byte once + Q read + O written), timed with HIP events on the
+replaying stream; `roofline.kernel_only` prices the decode kernel alone.  `ceilings`
+holds the achievable read rate and matrix-core rate measured by the library's probe
+kernels.  Steps rotate over several identical pool copies so no step finds its KV in
+the last-level cache left by the previous one.
 
 Further objects in the same line (each timed the same way, on its own workload):
   prefill       the packed DAG prefill attention kernel (dag_attn_run) on the
@@ -17,7 +19,9 @@ Further objects in the same line (each timed the same way, on its own workload):
   octopus_dag   decode over the Octopus-style DAG (mounted sibling blocks);
   akv           drop + repos compaction of 16 x 131,072-token requests (40 % dropped),
                 then decode over the compacted requests.
-cpu_baseline times the fp64 oracle on a bounded sample of the headline workload.
+cpu_baseline times the fp64 oracle on a bounded sample of the headline workload, and in
+full on the tiny fork workload; the Octopus leg times it over every thread and the AKV
+leg over one request.
 """
 import argparse
 import json
@@ -41,15 +45,18 @@ def log(msg):
 
 
 def measured_traffic():
-    """HBM bytes per decode_kernel launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE runs, or None once the kernel sources differ from the profiled ones."""
+    """HBM bytes per decode step and per decode_kernel launch from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs ({"step": ..., "decode_kernel": ...}), or None
+    once the kernel or planner sources differ from the profiled ones."""
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
         h = hashlib.sha256()
         for f in rec["source_files"]:
             h.update(open(os.path.join(ROOT, f), "rb").read())
-        return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return {"step": rec["traffic_bytes_per_step"], "decode_kernel": rec["traffic_bytes_per_decode_launch"]}
     except (OSError, KeyError, ValueError):
         return None
 
@@ -134,19 +141,23 @@ class DecodeBench:
         torch.cuda.synchronize()
         return g
 
-    def run_graph(self, steps):  # -> wall seconds of `steps` graph-replayed steps, decode-kernel us
-        """The step loop as one graph replay (no per-launch host work), then the decode
-        kernel's launch duration: HIP events on the launching stream around a replay of
-        `steps` back-to-back decode kernels, divided by `steps` (ROCm cannot record timing
-        events inside a graph)."""
+    def run_graph(self, steps):  # -> wall s of `steps` graph-replayed steps, step us (events), decode-kernel us
+        """The step loop as one graph replay (no per-launch host work), bracketed by the
+        host clock and by HIP events on the replaying stream; then the decode kernel's
+        launch duration: HIP events around a replay of `steps` back-to-back decode kernels,
+        divided by `steps` (ROCm cannot record timing events inside a graph)."""
         torch = self.torch
         g = self.capture(steps)
         g.replay()
         torch.cuda.synchronize()
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        ea.record()
         g.replay()
+        eb.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        step_us = ea.elapsed_time(eb) * 1e3 / steps
         gd = self.capture(steps, merge=False)
         gd.replay()
         torch.cuda.synchronize()
@@ -156,7 +167,7 @@ class DecodeBench:
         b.record()
         torch.cuda.synchronize()
         del g, gd
-        return wall, a.elapsed_time(b) * 1e3 / steps
+        return wall, step_us, a.elapsed_time(b) * 1e3 / steps
 
     def settle(self, seconds):
         """Untimed steps for `seconds` of wall clock before the warmup: the first few
@@ -533,19 +544,96 @@ def bench_select(reps, warmup):
     }
 
 
-def bench_octopus(steps, warmup):
+def bench_octopus(steps, warmup, cpu_timing=False):
+    """Decode over the Octopus-style DAG: eager steps with per-launch events, then the
+    timed steps as one graph replay (as the headline), two pool copies rotated (each
+    537 MB of KV, beyond the last-level cache).  cpu_timing: the fp64 oracle over every
+    thread of the same workload, timed once."""
     import workloads as W
     from tests.harness import build_device_pool, to_torch
     log("octopus_dag: building 2 pool copies")
     sc = W.octopus_dag()
     pools = [build_device_pool(sc)[0] for _ in range(2)]
-    d = DecodeBench(pools, sc, to_torch(sc.q, sc.dtype)).summary(steps, warmup)
+    db = DecodeBench(pools, sc, to_torch(sc.q, sc.dtype))
+    d = db.summary(steps, warmup)
+    wall, step_us, k_us = db.run_graph(steps)
+    d["graph"] = {"branch_tokens_per_s": db.n / (wall / steps), "us_per_step_wall": wall * 1e6 / steps,
+                  "step_us_events": step_us, "decode_kernel_us": k_us,
+                  "step_GBps": db.step_bytes / (step_us * 1e-6) / 1e9,
+                  "step_frac_of_8TBps": db.step_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                  "decode_kernel_frac_of_8TBps": db.kernel_bytes / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                  "step_algorithmic_bytes": db.step_bytes}
+    d["branch_tokens_per_s"] = d["graph"]["branch_tokens_per_s"]
+    d["timed"] = "graph replay of the timed steps (as the headline); eager per-launch events in the other fields"
     d["workload"] = ("octopus_dag_decode (65,536-token root, 8 threads x 8,192 private tokens, each mounting "
                      "the last 4,096 tokens of 2 siblings)")
+    del db, pools
+    if cpu_timing:
+        d["oracle_full"] = oracle_full_timing(sc, "every thread of the Octopus DAG workload")
     return d
 
 
-def bench_akv(steps, warmup):
+def oracle_full_timing(sc, what):
+    """The fp64 oracle over every query of a scenario once: page-table replay, then the
+    materialising decode of each query (timed apart)."""
+    import workloads as W
+    from oracle import attention as att, pagetable as pt
+    t0 = time.perf_counter()
+    table, _ = pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, sc.dtype))
+    t1 = time.perf_counter()
+    q = W.storage_to_f64(sc.q, sc.dtype)
+    att.decode(table, sc.queries, q, sc.sm_scale)
+    t2 = time.perf_counter()
+    return {"kind": "oracle", "what": what, "queries": len(sc.queries), "decode_s": t2 - t1, "replay_s": t1 - t0,
+            "branch_tokens_per_s": len(sc.queries) / (t2 - t1), "cores": len(os.sched_getaffinity(0))}
+
+
+def measure_ceilings():
+    """Achievable ceilings on this GPU, by the library's probe kernels: a streaming read of
+    2 GiB and of 268,435,456 B (the shared-prefix decode's KV, in one launch), and a
+    register-only bf16 matrix-core loop (clock implied at 4,096 FLOP / clock / CU)."""
+    import numpy as np
+    import torch
+    import fork_attention_decode_amd as fa
+    st = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    out = {}
+    for label, nbytes in (("read_2GiB", 2 << 30), ("read_268MB", 268435456)):
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2 if nbytes < (1 << 30) else 1)]
+        for b in bufs:
+            b.fill_(1)
+        for b in bufs:
+            fa.kv_probe_stream_read(b.data_ptr(), nbytes, sink.data_ptr(), st)
+        ms = []
+        for i in range(10):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fa.kv_probe_stream_read(bufs[i % len(bufs)].data_ptr(), nbytes, sink.data_ptr(), st)
+            e.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(e))
+        out[label] = {"GBps": nbytes / (float(np.median(ms)) * 1e-3) / 1e9, "us_median": float(np.median(ms)) * 1e3}
+        del bufs
+    n_iter, n_wg = 2000, 2048
+    flops = 4 * 8 * n_iter * 32768 * n_wg
+    fa.kv_probe_mfma_loop(200, n_wg, sink.data_ptr(), st)
+    ms = []
+    for _ in range(5):
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fa.kv_probe_mfma_loop(n_iter, n_wg, sink.data_ptr(), st)
+        e.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(e))
+    tf = flops / (float(np.median(ms)) * 1e-3) / 1e12
+    out["mfma_bf16"] = {"TFLOPs": tf, "implied_clock_GHz": tf * 1e12 / (256 * 4096) / 1e9,
+                        "us_median": float(np.median(ms)) * 1e3}
+    out["note"] = ("probe kernels of the library (kv_probe_stream_read, kv_probe_mfma_loop), HIP events, median of "
+                   "10 / 5 launches; the vendor peaks are 8,000 GB/s and 2,500 TFLOP/s")
+    return out
+
+
+def bench_akv(steps, warmup, cpu_timing=False):
     """Drop + repos of every request (the compaction kernels timed back to back behind a
     device sleep that covers the host planning), then decode over the compacted pool."""
     import numpy as np
@@ -617,6 +705,10 @@ def bench_akv(steps, warmup):
                              "host_planning_ms_total": host_s * 1e3, "host_hidden_behind_device": covered,
                              "timed": "plan upload + compaction kernel per request, HIP events"},
               "note": "one pool, no rotation: its 5.15 GB of KV exceed the last-level cache"})
+    if cpu_timing:
+        from tests.harness import subscenario
+        d["oracle_one_request"] = oracle_full_timing(subscenario(sc, [0]),
+                                                     "one request (drop + repos replayed, then its decode)")
     return d
 
 
@@ -689,10 +781,11 @@ def main():
     launch = "hip_graph"
     try:
         log(f"timed region: {args.steps} steps as one HIP graph replay")
-        wall, k_us = db.run_graph(args.steps)
+        wall, step_us, k_us = db.run_graph(args.steps)
     except RuntimeError as e:  # no graph capture here: the eager loop is the timed region
         log(f"graph capture unavailable ({e}); timing the eager loop")
         launch, wall, k_us = "eager", wall_eager, float(np.mean(k_ms)) * 1e3
+        step_us = float(np.mean(s_ms)) * 1e3
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=q.device)
         torch.empty_like(src).copy_(src)
@@ -700,6 +793,9 @@ def main():
     ms_step = wall * 1e3 / args.steps
     t_kernel = k_us * 1e-6
     achieved = db.kernel_bytes / t_kernel / 1e9
+    step_achieved = db.step_bytes / (step_us * 1e-6) / 1e9
+    traffic = measured_traffic() if args.workload == "shared_prefix_fork_decode" else None
+    ceilings = measure_ceilings() if not args.only_decode else None
     n_br, hq, d = q.shape
     result = {
         "metric": METRIC,
@@ -717,17 +813,28 @@ def main():
         "config": {"workload": args.workload, "branches": n_br, "q_heads": hq, "kv_heads": sc.n_kv_heads,
                    "head_dim": d, "page_size": sc.page_size, "pool_copies_rotated": args.copies,
                    "settle_s": args.settle, "settle_steps": db.settled_steps, "launch": launch},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic() if args.workload == "shared_prefix_fork_decode" else None,
-                     "kernel": "decode_kernel (fork_attn_partials)",
-                     "algorithmic_bytes_per_launch": db.kernel_bytes,
-                     "kernel_us_mean": t_kernel * 1e6,
-                     "kernel_timing": ("HIP events around a graph replay of back-to-back launches" if launch ==
-                                       "hip_graph" else "HIP events around each launch"),
-                     "kernel_us_eager_events_mean": float(np.mean(k_ms)) * 1e3,
-                     "kernel_us_eager_events_p10": float(np.percentile(k_ms, 10)) * 1e3,
-                     "kernel_us_eager_events_p90": float(np.percentile(k_ms, 90)) * 1e3},
+        "roofline": {"bound": "hbm", "achieved": step_achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": step_achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic["step"] if traffic else None,
+                     "kernel": "decode step = decode_kernel (fork_attn_partials) + merge_kernel (fork_attn_merge)",
+                     "algorithmic_bytes_per_step": db.step_bytes,
+                     "algorithmic_bytes_note": "unique KV (each shared page once) + Q read + O written",
+                     "step_us_mean": step_us,
+                     "timing": ("HIP events around the graph replay of the timed steps" if launch == "hip_graph"
+                                else "HIP events around each eager step"),
+                     "frac_of_measured_read_ceiling": (step_achieved / ceilings["read_268MB"]["GBps"]
+                                                       if ceilings else None),
+                     "kernel_only": {"kernel": "decode_kernel (fork_attn_partials)",
+                                     "algorithmic_bytes_per_launch": db.kernel_bytes,
+                                     "achieved": achieved, "frac": achieved / HBM_PEAK_GBPS,
+                                     "traffic": traffic["decode_kernel"] if traffic else None,
+                                     "kernel_us_mean": t_kernel * 1e6,
+                                     "kernel_timing": ("HIP events around a graph replay of back-to-back launches"
+                                                       if launch == "hip_graph" else "HIP events around each launch"),
+                                     "kernel_us_eager_events_mean": float(np.mean(k_ms)) * 1e3,
+                                     "kernel_us_eager_events_p10": float(np.percentile(k_ms, 10)) * 1e3,
+                                     "kernel_us_eager_events_p90": float(np.percentile(k_ms, 90)) * 1e3}},
+        "ceilings": ceilings,
         "step": {"us_per_step_timed": ms_step * 1e3, "us_per_step_eager_wall": wall_eager * 1e6 / args.steps,
                  "achieved_GBps_timed": db.step_bytes / (ms_step * 1e-3) / 1e9,
                  "frac_of_peak_timed": db.step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -750,15 +857,21 @@ def main():
         torch.cuda.empty_cache()
         result["prefill_backward"] = bench_prefill_bwd(5, 1)
         torch.cuda.empty_cache()
-        result["octopus_dag"] = bench_octopus(max(20, args.steps // 4), 5)
+        result["octopus_dag"] = bench_octopus(max(20, args.steps // 4), 5, cpu_timing=not args.no_cpu_baseline)
         torch.cuda.empty_cache()
         result["agentkv_select"] = bench_select(20, 3)
         torch.cuda.empty_cache()
-        result["akv"] = bench_akv(max(20, args.steps // 4), 5)
+        result["akv"] = bench_akv(max(20, args.steps // 4), 5, cpu_timing=not args.no_cpu_baseline)
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sc, args.cpu_budget)
+        if not args.only_decode:
+            result["cpu_baseline"]["oracle_full_tiny_fork"] = oracle_full_timing(
+                W.tiny_fork(), "every branch of the tiny fp32 fork workload")
+    if ceilings and "prefill" in result:
+        r = result["prefill"]["roofline"]
+        r["frac_of_measured_mfma_ceiling"] = r["achieved"] / ceilings["mfma_bf16"]["TFLOPs"]
     print(json.dumps(result))
 
 

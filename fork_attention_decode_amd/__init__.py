@@ -79,6 +79,8 @@ _SIGS = {
     "kv_pool_read_page": [_P, _i32, _i32, _P, _P, _P],
     "kv_pool_sync_status": [_P, _P, _pi32],
     "kv_pool_set_compute_units": [_P, _i32],
+    "kv_probe_stream_read": [_P, _sz, _P, _P],
+    "kv_probe_mfma_loop": [_i32, _i32, _P, _P],
     "fork_attn_workspace_size": [_P, _pi32, _i32, _i32, _psz],
     "fork_attn_decode": [_P, _pi32, _i32, _i32, _P, _P, _P, C.c_float, _P, _sz, _P],
     "fork_attn_decode_static": [_P, _pi32, _i32, _i32, _P, _P, _P, C.c_float, _P],
@@ -264,6 +266,14 @@ def kv_pool_read_page(pool: int, page: int, head: int, k_out: np.ndarray, v_out:
 
 def kv_pool_set_compute_units(pool: int, n_cu: int) -> None:
     _check("kv_pool_set_compute_units", lib.kv_pool_set_compute_units(pool, n_cu), pool)
+
+
+def kv_probe_stream_read(buf: int, nbytes: int, sink: int, stream: int = 0) -> None:
+    _check("kv_probe_stream_read", lib.kv_probe_stream_read(buf, nbytes, sink, stream or None), None)
+
+
+def kv_probe_mfma_loop(n_iter: int, n_workgroups: int, sink: int, stream: int = 0) -> None:
+    _check("kv_probe_mfma_loop", lib.kv_probe_mfma_loop(n_iter, n_workgroups, sink, stream or None), None)
 
 
 def kv_pool_sync_status(pool: int, stream: int = 0) -> int:

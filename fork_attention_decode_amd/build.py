@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libforkattn.so")
 SOURCES = ["pool.cpp", "planner.cpp", "drop.cpp", "dagmask.cpp", "decode.hip", "compact.hip", "prefill.hip",
-           "prefill_bwd.hip", "select.hip", "noalloc.hip"]
+           "prefill_bwd.hip", "select.hip", "noalloc.hip", "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU forms (v_pk_*_f32) are disabled for every device pass: the kernels
 # use plain fp32 VALU arithmetic only.

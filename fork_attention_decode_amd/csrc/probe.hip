@@ -1,0 +1,84 @@
+// Measurement probes for gfx950: the ceilings the attention kernels are priced against
+// besides the vendor peaks -- a pure streaming read of HBM and a register-only
+// bf16 matrix-core loop (at whatever clock the chip holds under that load).
+#include <hip/hip_runtime.h>
+#include <string>
+
+#include "../../include/forkattn.h"
+
+int fa_set_err(struct kv_pool* P, int code, const std::string& m);
+
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+// Every 16-byte word of the buffer read once (non-temporal), grid-stride; the xor of
+// everything read goes to sink so no load can be dropped.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf, size_t n16,
+                                                          unsigned* __restrict__ sink) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {  // four independent loads in flight per lane
+    const u32x4 a = __builtin_nontemporal_load(buf + i);
+    const u32x4 b = __builtin_nontemporal_load(buf + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(buf + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(buf + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(buf + i);
+  const unsigned x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == 0x9e3779b9u) sink[threadIdx.x] = x;  // practically never taken; keeps the loads live
+}
+
+// n_iter rounds of eight independent 32x32x16 bf16 matrix instructions per wave with
+// register operands (no memory traffic inside the loop).
+__global__ __launch_bounds__(256) void mfma_loop_kernel(int n_iter, float* __restrict__ sink) {
+  bf16x8 a, b;
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(1.0f + 1e-3f * (threadIdx.x & 7));
+    b[e] = (__bf16)(0.5f);
+  }
+  f32x16 c[8];
+  for (int k = 0; k < 8; ++k)
+    for (int e = 0; e < 16; ++e) c[k][e] = 0.f;
+  for (int it = 0; it < n_iter; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[k], 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int k = 0; k < 8; ++k)
+    for (int e = 0; e < 16; ++e) s += c[k][e];
+  if (s == 1234.5f) sink[threadIdx.x] = s;  // practically never taken; keeps the chain live
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_probe_stream_read(const void* buf, size_t bytes, void* sink, hipStream_t stream) {
+  if (!buf || !sink || bytes < 16 || (reinterpret_cast<uintptr_t>(buf) & 15))
+    return fa_set_err(nullptr, KV_ERR_INVALID, "stream probe: null or unaligned buffer");
+  int dev = 0, ncu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) {
+    stream_read_kernel<<<8 * (ncu > 0 ? ncu : 256), 256, 0, stream>>>(static_cast<const u32x4*>(buf), bytes / 16,
+                                                                       static_cast<unsigned*>(sink));
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("stream probe: ") + hipGetErrorString(e));
+  return KV_OK;
+}
+
+int kv_probe_mfma_loop(int32_t n_iter, int32_t n_workgroups, void* sink, hipStream_t stream) {
+  if (!sink || n_iter < 1 || n_workgroups < 1) return fa_set_err(nullptr, KV_ERR_INVALID, "mfma probe: bad arguments");
+  mfma_loop_kernel<<<n_workgroups, 256, 0, stream>>>(n_iter, static_cast<float*>(sink));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("mfma probe: ") + hipGetErrorString(e));
+  return KV_OK;
+}
+
+}  // extern "C"

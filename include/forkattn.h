@@ -372,6 +372,20 @@ int dag_attn_backward(const void* q, const void* k, const void* v, const void* o
                       int64_t nnz, int32_t block, float sm_scale, void* workspace,
                       size_t ws_bytes, hipStream_t stream);
 
+/* ---- measurement probes (ceilings to price the kernels against, besides the vendor
+ * peaks; not part of the attention path) ----
+ * kv_probe_stream_read: one launch that reads every 16-byte word of `buf` (DEVICE,
+ *   16-byte aligned, `bytes` long, multiple of 16 read) once with non-temporal loads;
+ *   time it with events on `stream` for the achievable HBM read rate.  sink: DEVICE, at
+ *   least 1 KiB, written only in a practically impossible case (keeps the loads live).
+ * kv_probe_mfma_loop: n_workgroups workgroups of 4 waves, each wave issuing n_iter x 8
+ *   independent v_mfma_f32_32x32x16_bf16 with register operands: 4 * 8 * n_iter * 32768
+ *   FLOPs per workgroup; time it for the achievable dense bf16 matrix-core rate at the
+ *   clock the chip holds under that load.  sink: DEVICE, at least 1 KiB of floats.
+ * Both: KV_ERR_INVALID for bad arguments, KV_ERR_HIP for launch failures. */
+int kv_probe_stream_read(const void* buf, size_t bytes, void* sink, hipStream_t stream);
+int kv_probe_mfma_loop(int32_t n_iter, int32_t n_workgroups, void* sink, hipStream_t stream);
+
 /* ---- errors ---- */
 /* ---- key scoring and keep selection in front of Drop ----
  * AgentKV (rit.work), section "Как AgentKV выбирает и освобождает записи кэша": before a
