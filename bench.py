@@ -391,7 +391,25 @@ def bench_window(n_steps=16, replays=20):
     ev[1].record()
     torch.cuda.synchronize()
     us_step = ev[0].elapsed_time(ev[1]) * 1e3 / (replays * n_steps)
-    del ws
+    del ws, g
+    # the same steps without a window: kv_append_batch then fork_attn_decode, eager; after
+    # the first step the decode plan is patched (no replanning) -- host time of each call
+    import fork_attention_decode_amd as fa
+    st = torch.cuda.current_stream().cuda_stream
+    wsd = torch.empty(fa.fork_attn_workspace_size(pool.handle, seqs, hq) + (1 << 20), dtype=torch.uint8,
+                      device="cuda")
+    app_us, dec_us = [], []
+    for step in range(n_steps):
+        h0 = time.perf_counter()
+        pool.append_batch(seqs, kt[step], vt[step])
+        h1 = time.perf_counter()
+        fa.fork_attn_decode(pool.handle, seqs, hq, qt[step].data_ptr(), out.data_ptr(), lse.data_ptr(), sc.sm_scale,
+                            wsd.data_ptr(), wsd.numel(), st)
+        h2 = time.perf_counter()
+        app_us.append((h1 - h0) * 1e6)
+        dec_us.append((h2 - h1) * 1e6)
+    torch.cuda.synchronize()
+    patched = pool.plan_stats()["patched_changes"]
     # each unique KV byte once per step (the shared prefix once, each branch's own tokens
     # once, the window's new tokens included), averaged over the window's steps
     ctx_tokens = 32768 + n * 2048 + n * (n_steps + 1) / 2
@@ -407,6 +425,12 @@ def bench_window(n_steps=16, replays=20):
         "branch_tokens_per_s": n / (us_step * 1e-6),
         "host_plan_upload_ms_per_window": (t1 - t0) * 1e3,
         "host_capture_ms_per_window": (t2 - t1) * 1e3,
+        "eager_steps": {"append_batch_host_us_median": float(np.median(app_us[1:])),
+                        "decode_host_us_median": float(np.median(dec_us[1:])),
+                        "decode_host_us_first": dec_us[0], "plan_patches": patched,
+                        "note": "kv_append_batch + fork_attn_decode per step without a window, host wall time of each "
+                                "call from Python (ctypes included); the first decode replans, later ones patch the "
+                                "cached plan"},
         "timed": "HIP events around back-to-back replays of the captured window (page write + decode + merge per "
                  "step)",
     }
@@ -634,8 +658,9 @@ def measure_ceilings():
 
 
 def bench_akv(steps, warmup, cpu_timing=False):
-    """Drop + repos of every request (the compaction kernels timed back to back behind a
-    device sleep that covers the host planning), then decode over the compacted pool."""
+    """Drop + repos of every request in one kv_drop_batch call (its plan upload and
+    compaction launch timed with HIP events behind a device sleep that covers the host
+    planning), then decode over the compacted pool."""
     import numpy as np
     import torch
     import workloads as W
@@ -676,20 +701,19 @@ def bench_akv(steps, warmup, cpu_timing=False):
     c1.record()
     torch.cuda.synchronize()
     cycles_per_ms = 50_000_000 / max(c0.elapsed_time(c1), 1e-3)
-    dev_ms, host_ms, covered = [], [], True
-    for _, sid, spans, repos in drops:
-        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(int(cycles_per_ms * 150))  # 150 ms of device time
-        ea.record()
-        t0 = time.perf_counter()
-        pool.drop(sid, spans, repos=repos)
-        host_ms.append((time.perf_counter() - t0) * 1e3)
-        eb.record()
-        torch.cuda.synchronize()
-        dev_ms.append(ea.elapsed_time(eb))
-        covered &= host_ms[-1] < 140.0
-    comp_ms = float(np.sum(dev_ms))
-    host_s = float(np.sum(host_ms)) * 1e-3
+    # all 16 drops in one kv_drop_batch call: one plan upload, one compaction launch
+    assert all(op[3] for op in drops)
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(cycles_per_ms * 400))  # 400 ms of device time
+    ea.record()
+    t0 = time.perf_counter()
+    pool.drop_batch([op[1] for op in drops], [op[2] for op in drops], repos=True)
+    host_s = time.perf_counter() - t0
+    eb.record()
+    torch.cuda.synchronize()
+    comp_ms = ea.elapsed_time(eb)
+    covered = host_s < 0.38
+    dev_ms = [comp_ms]
     assert pool.sync_status() == 0
     for op in tail:
         blk = sc.blocks[op[2]]
@@ -699,11 +723,11 @@ def bench_akv(steps, warmup, cpu_timing=False):
     d = DecodeBench([pool], sc, to_torch(sc.q, sc.dtype)).summary(steps, warmup)
     d.update({"workload": "akv_drop_repos (16 x 131,072 tokens, 40 % dropped as 2,048-8,192-token spans, repos, "
                           "then 1 decode token each)",
-              "compaction": {"device_ms_total": comp_ms, "device_ms_per_request": dev_ms, "moved_tokens": moved,
+              "compaction": {"device_ms_total": comp_ms, "moved_tokens": moved, "call": "kv_drop_batch (16 drops)",
                              "algorithmic_bytes": comp_bytes, "GBps": comp_bytes / (comp_ms * 1e-3) / 1e9,
                              "frac_of_8TBps": comp_bytes / (comp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                              "host_planning_ms_total": host_s * 1e3, "host_hidden_behind_device": covered,
-                             "timed": "plan upload + compaction kernel per request, HIP events"},
+                             "timed": "plan upload + compaction kernel of the one call, HIP events"},
               "note": "one pool, no rotation: its 5.15 GB of KV exceed the last-level cache"})
     if cpu_timing:
         from tests.harness import subscenario
@@ -731,6 +755,7 @@ def main():
     ap.add_argument("--only-prefill-bwd", action="store_true", help="time the prefill backward alone (profiling)")
     ap.add_argument("--only-window", action="store_true", help="time the steady-state decode window alone")
     ap.add_argument("--only-restore", action="store_true", help="time the segment restore alone")
+    ap.add_argument("--only-octopus", action="store_true", help="time the Octopus DAG decode alone (profiling)")
     ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, copy 256 MiB device to device once (a kernel of known "
@@ -747,29 +772,26 @@ def main():
     from tests.harness import build_device_pool, to_torch
 
     torch.cuda.set_device(0)
-    if args.only_prefill:
-        pf = bench_prefill(args.prefill_reps, 3)
+
+    def calibration():  # a device-to-device copy of 256 MiB: scales hardware byte counters
         if args.copy_calibration:
             src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
             torch.empty_like(src).copy_(src)
             torch.cuda.synchronize()
-        print(json.dumps({"prefill": pf}))
-        return
-    if args.only_akv:
-        print(json.dumps({"akv": bench_akv(max(20, args.steps // 4), 5)}))
-        return
-    if args.only_select:
-        print(json.dumps({"agentkv_select": bench_select(20, 3)}))
-        return
-    if args.only_restore:
-        print(json.dumps({"restore": bench_restore()}))
-        return
-    if args.only_window:
-        print(json.dumps({"decode_window": bench_window()}))
-        return
-    if args.only_prefill_bwd:
-        print(json.dumps({"prefill_backward": bench_prefill_bwd(5, 1)}))
-        return
+
+    single = [(args.only_prefill, "prefill", lambda: bench_prefill(args.prefill_reps, 3)),
+              (args.only_akv, "akv", lambda: bench_akv(max(20, args.steps // 4), 5)),
+              (args.only_select, "agentkv_select", lambda: bench_select(20, 3)),
+              (args.only_restore, "restore", lambda: bench_restore()),
+              (args.only_window, "decode_window", lambda: bench_window()),
+              (args.only_prefill_bwd, "prefill_backward", lambda: bench_prefill_bwd(5, 1)),
+              (args.only_octopus, "octopus_dag", lambda: bench_octopus(max(20, args.steps // 4), 5))]
+    for on, key, fn in single:
+        if on:
+            res = fn()
+            calibration()
+            print(json.dumps({key: res}))
+            return
     sc = W.WORKLOADS[args.workload]()
     log(f"workload {args.workload}: building {args.copies} pool copies")
     pools = [build_device_pool(sc)[0] for _ in range(args.copies)]
@@ -786,10 +808,7 @@ def main():
         log(f"graph capture unavailable ({e}); timing the eager loop")
         launch, wall, k_us = "eager", wall_eager, float(np.mean(k_ms)) * 1e3
         step_us = float(np.mean(s_ms)) * 1e3
-    if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=q.device)
-        torch.empty_like(src).copy_(src)
-        torch.cuda.synchronize()
+    calibration()
     ms_step = wall * 1e3 / args.steps
     t_kernel = k_us * 1e-6
     achieved = db.kernel_bytes / t_kernel / 1e9

@@ -67,6 +67,7 @@ _SIGS = {
     "kv_fork": [_P, _i32, _pi32],
     "kv_mount": [_P, _i32, _i32, _i64, _i64],
     "kv_drop": [_P, _i32, _pi64, _pi64, _i32, _i32, _pi64, _P],
+    "kv_drop_batch": [_P, _pi32, _i32, _pi64, _pi64, _pi64, _i32, _pi64, _P],
     "kv_repos": [_P, _i32, _P],
     "kv_rewind": [_P, _i32, _i64],
     "kv_commit": [_P, _i32],
@@ -211,6 +212,28 @@ def kv_drop(pool: int, seq: int, spans: Sequence[Tuple[int, int]], flags: int = 
     return kept[:kv_seq_info(pool, seq)[0]].copy()
 
 
+def kv_drop_batch(pool: int, seqs: Sequence[int], spans_per_seq, flags: int = 0, stream: int = 0):
+    """Drops of several sequences in one call; spans_per_seq[i] = [(begin, len), ...] of
+    seqs[i].  Returns the compaction index of each sequence (list of arrays)."""
+    s = np.ascontiguousarray(np.asarray(seqs, np.int32))
+    n_tok = [kv_seq_info(pool, int(q))[0] for q in s]
+    off = np.zeros(len(s) + 1, np.int64)
+    for i, sp in enumerate(spans_per_seq):
+        off[i + 1] = off[i] + len(sp)
+    flat = [x for sp in spans_per_seq for x in sp]
+    b = _i64arr([x[0] for x in flat]) if flat else np.zeros(1, np.int64)
+    L = _i64arr([x[1] for x in flat]) if flat else np.zeros(1, np.int64)
+    kept = np.zeros(max(1, sum(n_tok)), np.int64)
+    _check("kv_drop_batch", lib.kv_drop_batch(pool, _ptr(s, C.c_int32), len(s), _ptr(off, C.c_int64),
+                                              _ptr(b, C.c_int64), _ptr(L, C.c_int64), flags,
+                                              _ptr(kept, C.c_int64), stream or None), pool)
+    out, at = [], 0
+    for q, n in zip(s, n_tok):
+        out.append(kept[at:at + kv_seq_info(pool, int(q))[0]].copy())
+        at += n
+    return out
+
+
 def kv_repos(pool: int, seq: int, stream: int = 0):
     _check("kv_repos", lib.kv_repos(pool, seq, stream or None), pool)
 
@@ -350,9 +373,10 @@ def kv_drop_keep(pool: int, seq: int, keep: np.ndarray, flags: int = 0, stream: 
 
 
 def fork_attn_plan_stats(pool: int) -> dict:
-    out = np.zeros(7, np.int64)
-    _check("fork_attn_plan_stats", lib.fork_attn_plan_stats(pool, _ptr(out, C.c_int64), 7), pool)
-    keys = ["segments", "items", "chunks", "partials", "unique_kv_bytes", "rows", "longest_item_chunks"]
+    out = np.zeros(8, np.int64)
+    _check("fork_attn_plan_stats", lib.fork_attn_plan_stats(pool, _ptr(out, C.c_int64), 8), pool)
+    keys = ["segments", "items", "chunks", "partials", "unique_kv_bytes", "rows", "longest_item_chunks",
+            "patched_changes"]
     return dict(zip(keys, (int(x) for x in out)))
 
 
@@ -596,6 +620,10 @@ class Pool:
     def drop(self, seq: int, spans, repos: bool = False) -> np.ndarray:
         st = 0 if self.k_pages is None else self._stream()
         return kv_drop(self.handle, seq, spans, KV_DROP_REPOS if repos else 0, st)
+
+    def drop_batch(self, seqs, spans_per_seq, repos: bool = False):
+        st = 0 if self.k_pages is None else self._stream()
+        return kv_drop_batch(self.handle, seqs, spans_per_seq, KV_DROP_REPOS if repos else 0, st)
 
     def score(self, seq: int, q_rep, sm_scale: float, workspace=None):
         """Mean attention of the representative queries q_rep (torch [n_rep, Hq, d] on the

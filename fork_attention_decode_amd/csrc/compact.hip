@@ -5,9 +5,10 @@
 // values unchanged.  AgentKV (rit.work): kept entries are compacted physically and the
 // freed pages go back to the allocator.
 //
-// One workgroup per batch of kCompactBatch consecutive destination pages (all KV heads),
-// batches taken in start order by a ticket (a device-wide atomic on one address: one per
-// batch, since they serialise across the dies).
+// One workgroup per destination page (all KV heads); the launch holds the pages of one
+// or more drops, each drop's pages in ascending order.  The page's slots find their
+// sources through the drop's runs (consecutive kept tokens with one rotation offset) and
+// the sequence's block table before the drop.
 // Phase 1 gathers the page's kept tokens from their old slots into registers: each
 // thread holds a few 16-byte K slot pairs (i, i + d/2) -- rotated by the token's offset
 // with fp32 cos/sin rows computed on the host in fp64 (an fp32 angle at 131K positions
@@ -18,13 +19,14 @@
 // a CU and hide each other's latency.
 //
 // In-place hazard: kept tokens only move to lower slots, so a page rewritten in place
-// may still be a source of lower destination pages (at most two: a source page's kept
-// tokens are consecutive).  After phase 1 a workgroup publishes "sources read" (its
-// loads have returned), and a page rewritten in place waits for exactly the lower
-// entries that read it.  The hazard is write-after-read, so relaxed device-scope flags
-// order it (acquire / release would write back or invalidate the die's L2 on every
-// poll).  A workgroup only ever waits for entries started before it, all of which are
-// resident and never wait for it, so every wait ends.
+// may still be a source of lower destination pages of its drop (at most two: a source
+// page's kept tokens are consecutive).  After phase 1 a workgroup publishes "sources
+// read" (its loads have returned), and a page rewritten in place waits for exactly the
+// lower entries that read it.  The hazard is write-after-read, so relaxed device-scope
+// flags order it (acquire / release would write back or invalidate the die's L2 on every
+// poll).  Workgroups are dispatched in launch order on each die, so an entry only waits
+// for entries dispatched before it, which never wait for it: every wait ends (a bounded
+// spin counts a time-out instead of hanging if that order ever failed).
 #include <hip/hip_runtime.h>
 #include "plan.hpp"
 
@@ -44,31 +46,34 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
   constexpr int BLK = 16 * D;                  // elements per (page, head) block
   typedef T vec_t __attribute__((__vector_size__(16)));
   const int hkv = p.n_kv_heads;
-  __shared__ int s_b;
   __shared__ int s_loc[16], s_rot[16];
   __shared__ int s_run[16][3], s_nrun;  // runs of the page: first slot, length, source location of the first
-  if (threadIdx.x == 0) s_b = (int)((unsigned)atomicAdd(p.ticket, 1) - (unsigned)p.ticket_base);
-  __syncthreads();
-  const int b = s_b;
-  if (b < 0 || b * kCompactBatch >= p.n_pages) {  // ticket out of step with the host: count it, touch nothing
-    if (threadIdx.x == 0) atomicAdd(p.errors, 1);
-    return;
-  }
+  const int k = blockIdx.x;
+  if (k >= p.n_pages) return;
   T* kp = reinterpret_cast<T*>(p.k_pages);
   T* vp = reinterpret_cast<T*>(p.v_pages);
   const size_t np = (size_t)p.pool_pages;  // head-major pool: block (page, h) at h * np + page
-  const int k_end = min((b + 1) * kCompactBatch, p.n_pages);
-  for (int k = b * kCompactBatch; k < k_end; ++k) {  // this batch's list entries, in order
   const CompactPage cp = p.pages[k];
+  const int first_slot = cp.slots & 0xff, n_slots = (cp.slots >> 8) & 0xff;
+  const CompactJob jb = p.jobs[(unsigned)cp.slots >> 16];  // the drop this entry belongs to
   const size_t dst = (size_t)cp.dst_page * BLK;
-  const bool keep_rest = cp.first_slot > 0 || cp.n_slots < 16;
+  const bool keep_rest = first_slot > 0 || n_slots < 16;
   // the page's 16 source locations and rotation rows, once, so that every gather below
   // issues its loads independently instead of behind a dependent index load
   if (threadIdx.x < 16) {
     const int t = threadIdx.x;
-    const bool mine = t >= cp.first_slot && t < cp.n_slots;
-    s_loc[t] = mine ? p.src_loc[cp.tok_base + t] : -1;
-    s_rot[t] = mine ? p.rot[cp.tok_base + t] : -1;
+    int loc = -1, rot = -1;
+    if (t >= first_slot && t < n_slots) {
+      const int j = (jb.first + (k - jb.list_base)) * 16 + t;  // destination slot in the sequence
+      int q = cp.run0;
+      CompactRun run = p.runs[q];
+      while (j >= run.j0 + run.len) run = p.runs[++q];
+      const int src = run.s0 + (j - run.j0);
+      loc = p.tab[jb.tab_base + (src >> 4) - jb.first] * 16 + (src & 15);
+      rot = run.rot;
+    }
+    s_loc[t] = loc;
+    s_rot[t] = rot;
   }
   __syncthreads();
   // runs: maximal slot ranges whose sources are consecutive slots of one source page
@@ -180,7 +185,8 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
   // ---- publish "sources read", then wait for the lower entries that read this page
   if (threadIdx.x == 0) {
     __hip_atomic_store(&p.done[k], p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (int i = cp.wait_lo; i < cp.wait_hi && i < k; ++i) {
+    const int wait_lo = cp.wait & 0x3fffffff, wait_hi = wait_lo + ((unsigned)cp.wait >> 30);
+    for (int i = wait_lo; i < wait_hi && i < k; ++i) {
       int spins = 0;
       while (__hip_atomic_load(&p.done[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != p.epoch) {
         __builtin_amdgcn_s_sleep(4);
@@ -216,13 +222,11 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
         row[w4] = u32x4{vr[i][4 * w4], vr[i][4 * w4 + 1], vr[i][4 * w4 + 2], vr[i][4 * w4 + 3]};
     }
   }
-  __syncthreads();  // s_loc / s_rot / s_run are refilled for the next entry
-  }
 }
 
 template <typename T, int D, int UK, int UV>
 static hipError_t compact_t(const CompactParams& p, hipStream_t s) {
-  compact_kernel<T, D, UK, UV><<<(p.n_pages + kCompactBatch - 1) / kCompactBatch, 256, 0, s>>>(p);
+  compact_kernel<T, D, UK, UV><<<p.n_pages, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

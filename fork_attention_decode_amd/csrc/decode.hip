@@ -461,6 +461,19 @@ __global__ __launch_bounds__(256) void page_write_kernel(T* __restrict__ kp, T* 
   }
 }
 
+// ---------------------------------------------------------------- plan patches
+__global__ __launch_bounds__(256) void plan_patch_kernel(int32_t* __restrict__ ws, const int32_t* __restrict__ patches,
+                                                         int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) ws[patches[2 * i]] = patches[2 * i + 1];
+}
+
+hipError_t launch_plan_patch(void* ws, const int32_t* patches, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  plan_patch_kernel<<<(n + 255) / 256, 256, 0, s>>>(static_cast<int32_t*>(ws), patches, n);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 template <typename T, int D>
 static hipError_t decode_t(const DecodeParams& p, hipStream_t s) {

@@ -73,41 +73,49 @@ struct MergeParams {
   int32_t max_parts;
 };
 
-// Drop / repos compaction: one record per destination page to (re)write.  Slots
-// [first_slot, n_slots) of dst_page receive the kept tokens tok_base + slot; when the
-// page is rewritten in place its old tokens may be sources of lower destination pages
-// (kept tokens only move down), so the page is written only after the list entries
-// [wait_lo, wait_hi) that read it have read their sources (an empty range: nothing to
-// wait for).  A source page's kept tokens are consecutive in the kept order, so at most
-// two destination pages read it.
+// Drop / repos compaction.  A launch holds the drops of one or more sequences ("jobs");
+// every destination page of every job is one list entry, jobs in order, pages in
+// ascending logical order within a job.
+//   CompactJob: entries [list_base, list_base + n_list) rewrite logical pages first,
+//     first + 1, ... of one sequence; tab[tab_base + q - first] is that sequence's page
+//     id of logical page q before the drop (q >= first), where the kept tokens are read.
+//   CompactRun: destination slots [j0, j0 + len) of the job's sequence receive its old
+//     tokens s0, s0 + 1, ... with rotation row rot of cos_sin (-1: no rotation).
+//   CompactPage: slots [first_slot, n_slots) of dst_page are (re)written (slots = first_slot
+//     | n_slots << 8 | job << 16, job = index of its CompactJob); run0 = the run holding the
+//     first of them.  A page rewritten in place
+//     may still be a source of lower entries of its job (kept tokens only move down, and a
+//     page's kept tokens reach at most two destination pages), so it is written only after
+//     entries [wait & 0x3fffffff, + (wait >> 30)) have read their sources.
+struct CompactJob {
+  int32_t list_base;
+  int32_t n_list;
+  int32_t first;
+  int32_t tab_base;
+};
+struct CompactRun {
+  int32_t j0, s0, len, rot;
+};
 struct CompactPage {
   int32_t dst_page;
-  int32_t first_slot;
-  int32_t n_slots;
-  int32_t tok_base;
-  int32_t wait_lo;
-  int32_t wait_hi;
-  int32_t pad[2];
+  int32_t run0;
+  int32_t slots;
+  int32_t wait;
 };
-
-// Destination pages per compaction workgroup (one start-order ticket per batch).  One:
-// with more, a reader page's gather waits behind the earlier pages of its batch, which
-// chains the in-place waits (measured 1.2x / 1.8x / 2.7x slower at 2 / 4 / 8).
-constexpr int kCompactBatch = 1;
 
 struct CompactParams {
   void* k_pages;
   void* v_pages;
+  const CompactJob* jobs;
   const CompactPage* pages;
-  const int32_t* src_loc;    // [token] old page * 16 + old slot of the kept token
-  const int32_t* rot;        // [token] row of cos_sin, -1 = no rotation
+  const CompactRun* runs;
+  const int32_t* tab;
   const float* cos_sin;      // [n_rot][d/2][2] cos, sin of (offset * theta^(-2i/d))
-  int32_t* ticket;           // monotone counter: order in which workgroups start
   int32_t* done;             // [list entry] = epoch once that entry has read its sources
   int32_t* errors;           // incremented if a wait gives up (never expected)
-  int32_t ticket_base;
   int32_t epoch;
-  int32_t n_pages;           // destination pages in this launch
+  int32_t n_jobs;
+  int32_t n_pages;           // list entries (destination pages) in this launch
   int32_t n_kv_heads;
   int32_t pool_pages;        // pool capacity: head h's blocks start at h * pool_pages
 };
@@ -117,6 +125,9 @@ hipError_t launch_page_write(int dtype, int d, int hkv, int pool_pages, void* k_
                              int n_writes, hipStream_t s);
 hipError_t launch_decode(int dtype, int d, const DecodeParams& p, hipStream_t s);
 hipError_t launch_merge(int dtype, int d, const MergeParams& p, hipStream_t s);
+// ws[patches[2 i]] = patches[2 i + 1] for i < n (int offsets into a decode workspace;
+// distinct offsets)
+hipError_t launch_plan_patch(void* ws, const int32_t* patches, int n, hipStream_t s);
 hipError_t launch_compact(int dtype, int d, const CompactParams& p, hipStream_t s);
 bool compact_supported(int dtype, int d, int hkv);  // the kernel's register budget
 

@@ -33,6 +33,10 @@ hipError_t fa_upload(kv_pool* P, void* dst, const void* src, size_t bytes, hipSt
 void fa_take_page(kv_pool* P, int32_t p);
 void fa_unref_page(kv_pool* P, int32_t p);
 void fa_pos_append(std::vector<PosRun>& v, int64_t p0, int64_t n);
+void fa_changed(kv_pool* P, int32_t kind, kv_seq_t seq, int64_t n0, int64_t n1);
+hipError_t fa_upload(kv_pool* P, void* dst, const void* src, size_t bytes, hipStream_t s);
+size_t fa_ws_plan_offset(const kv_pool_config* c);
+size_t fa_pool_ws_need(const kv_pool_config* c);
 #define FAIL(P, code, msg) return fa_set_err((P), (code), (msg))
 
 namespace {
@@ -59,6 +63,77 @@ void put(std::vector<char>& blob, size_t off, const std::vector<T>& v) {
 
 }  // namespace
 
+static std::atomic<uint64_t> g_plan_serial{0};
+
+// Bring the cached decode plan up to date with the journal's changes without replanning:
+// possible when every change to a listed sequence is an append that wrote only into pages
+// the sequence owns alone -- its tail page (already its query's private chunk) grows, and
+// new pages join the last work item of the query's private segment for every KV head.
+// Records are patched in the host image; the changed ints are queued for the device.
+// false: replan (the image may be half patched; the replan rewrites all of it).
+static bool patch_plan(kv_pool* P) {
+  DecodePlanCache& pc = P->plan;
+  const ChangeJournal& J = P->journal;
+  const kv_pool_config& C = P->cfg;
+  const int32_t PS = C.page_size, H = C.n_kv_heads;
+  if (!pc.patchable || J.broken || J.base != pc.version || J.base + J.ev.size() != P->version) return false;
+  int32_t* recs = reinterpret_cast<int32_t*>(pc.blob.data() + pc.off_items);
+  const int32_t base_int = (int32_t)(pc.off_items / sizeof(int32_t));
+  auto set = [&](int32_t rec, int32_t at, int32_t val) {
+    recs[(size_t)rec * kRecInts + at] = val;
+    pc.pending.push_back(base_int + rec * kRecInts + at);
+    pc.pending.push_back(val);
+  };
+  const size_t es = C.dtype == KV_F32 ? 4 : 2;
+  for (const ChangeJournal::Event& e : J.ev) {
+    if (e.kind == ChangeJournal::kContent) continue;
+    int32_t i = -1;
+    for (size_t q = 0; q < pc.seqs.size(); ++q)
+      if (pc.seqs[q] == e.seq) i = pc.q_seq[q] >= 0 ? (int32_t)q : -2;
+    if (i == -1) continue;  // a sequence no query reads
+    if (i < 0 || e.kind != ChangeJournal::kAppend || e.n0 != pc.q_own_n[i]) return false;
+    const Seq* S = fa_seq(P, e.seq);
+    if (!S || (int64_t)S->pages.size() * PS < e.n1) return false;
+    int64_t L = e.n0 / PS;
+    if (e.n0 % PS) {  // the tail page grows
+      if (S->pages[(size_t)L] != pc.q_tail_page[i]) return false;
+      for (int32_t h = 0; h < H; ++h) {
+        const int32_t r = pc.tail_rec[(size_t)i * H + h], sl = pc.tail_slot[(size_t)i * H + h];
+        if (r < 0) return false;
+        const int32_t at = kRecChunk + 2 * sl + 1;
+        const int32_t lo = recs[(size_t)r * kRecInts + at] & 0xff;
+        set(r, at, lo | (int32_t)std::min<int64_t>(PS, e.n1 - L * PS) << 8);
+      }
+      ++L;
+    }
+    for (; L * PS < e.n1; ++L) {  // new pages
+      const int32_t page = S->pages[(size_t)L];
+      const int32_t lohi = (int32_t)std::min<int64_t>(PS, e.n1 - L * PS) << 8;
+      for (int32_t h = 0; h < H; ++h) {
+        const int32_t r = pc.last_rec[(size_t)i * H + h];
+        if (r < 0) return false;
+        const int32_t nc = recs[(size_t)r * kRecInts];
+        if (nc >= kMaxItemChunks) return false;
+        set(r, kRecChunk + 2 * nc, page);
+        set(r, kRecChunk + 2 * nc + 1, lohi);
+        set(r, 0, nc + 1);
+        pc.tail_rec[(size_t)i * H + h] = r;
+        pc.tail_slot[(size_t)i * H + h] = nc;
+        pc.stats[6] = std::max<int64_t>(pc.stats[6], nc + 1);
+      }
+      pc.q_tail_page[i] = page;
+      pc.stats[2] += 1;
+    }
+    pc.q_own_n[i] = (int32_t)e.n1;
+    pc.stats[4] += (e.n1 - e.n0) * H * 2 * C.head_dim * (int64_t)es;
+  }
+  pc.version = P->version;
+  pc.serial = ++g_plan_serial;
+  pc.stats[7] += 1;
+  P->journal.reset(P->version);
+  return true;
+}
+
 // len_cap (optional): per query, the number of its sequence's own tokens to attend to
 // (a prefix of the own context); the cached plan is bypassed and left invalid.
 static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, const int64_t* len_cap = nullptr) {
@@ -69,9 +144,10 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
   if (G > kMaxRows) FAIL(P, KV_ERR_UNSUPPORTED, "more than 64 query heads per KV head");
   const int32_t PS = C.page_size;
   DecodePlanCache& pc = P->plan;
-  if (!len_cap && pc.valid && pc.causal_n == 0 && pc.version == P->version && pc.n_q_heads == hq &&
-      (int32_t)pc.seqs.size() == n && std::equal(pc.seqs.begin(), pc.seqs.end(), seqs))
+  if (!len_cap && pc.valid && pc.causal_n == 0 && pc.n_q_heads == hq && (int32_t)pc.seqs.size() == n &&
+      std::equal(pc.seqs.begin(), pc.seqs.end(), seqs) && (pc.version == P->version || patch_plan(P)))
     return KV_OK;
+  pc.pending.clear();
 
   // 1. visible runs
   std::vector<Entry> ent;
@@ -228,13 +304,29 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
   const int64_t n_part_slots = (int64_t)n_out * max_parts;
   int64_t n_part = 0;
   std::vector<int32_t> fill((size_t)n_out, 0);
-  std::vector<int32_t> recs(items.size() * kRecInts, 0);
+  std::vector<int32_t>& mptr = row_count;  // uploaded as the per-row partial count
+
+  // 4. workspace image: [item records | per-row partial counts] is uploaded, then the
+  // partials.  Records are written straight into the host image (chunk slots past a
+  // record's count are never read, so they are not cleared)
+  const int D = C.head_dim;
+  size_t off = 0;
+  pc.off_items = off; off = align256(off + items.size() * kRecInts * sizeof(int32_t));
+  pc.off_mptr = off; off = align256(off + mptr.size() * sizeof(int32_t));
+  const size_t plan_bytes = off;
+  pc.off_plse = off; off = align256(off + (size_t)n_part_slots * sizeof(float));
+  pc.off_po = off; off = align256(off + (size_t)n_part_slots * D * sizeof(float));
+  pc.max_parts = max_parts;
+  pc.ws_need = std::max<size_t>(off, 256);
+  pc.blob.resize(plan_bytes);
+  int32_t* recs = reinterpret_cast<int32_t*>(pc.blob.data() + pc.off_items);
   for (size_t i = 0; i < items.size(); ++i) {
     const Item& it = items[i];
-    int32_t* rec = recs.data() + i * kRecInts;
+    int32_t* rec = recs + i * kRecInts;
     rec[0] = it.n_chunks;
     rec[1] = it.kv_head;
     rec[2] = it.rows;
+    rec[3] = 0;
     for (int32_t r = 0; r < kMaxRows; ++r) {
       rec[kRecRow + r] = r < it.rows ? it.orow[r] : -1;
       rec[kRecSlot + r] = r < it.rows ? it.orow[r] * max_parts + fill[it.orow[r]]++ : 0;
@@ -246,22 +338,45 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
       rec[kRecChunk + 2 * c + 1] = ch.lohi;
     }
   }
-  std::vector<int32_t>& mptr = row_count;  // uploaded as the per-row partial count
-
-  // 4. workspace image: [item records | per-row partial counts] is uploaded, then the
-  // partials
-  const int D = C.head_dim;
-  size_t off = 0;
-  pc.off_items = off; off = align256(off + recs.size() * sizeof(int32_t));
-  pc.off_mptr = off; off = align256(off + mptr.size() * sizeof(int32_t));
-  const size_t plan_bytes = off;
-  pc.off_plse = off; off = align256(off + (size_t)n_part_slots * sizeof(float));
-  pc.off_po = off; off = align256(off + (size_t)n_part_slots * D * sizeof(float));
-  pc.max_parts = max_parts;
-  pc.ws_need = std::max<size_t>(off, 256);
-  pc.blob.assign(plan_bytes, 0);
-  put(pc.blob, pc.off_items, recs);
   put(pc.blob, pc.off_mptr, mptr);
+  // what a later patch needs (decode plans): each query's tail page chunk and the last
+  // item of its private segment, per KV head
+  pc.patchable = !len_cap;
+  pc.pending.clear();
+  if (pc.patchable) {
+    const int32_t H = C.n_kv_heads;
+    pc.q_seq.assign(seqs, seqs + n);
+    for (int32_t i = 0; i < n; ++i)
+      for (int32_t j = 0; j < i; ++j)
+        if (seqs[j] == seqs[i]) pc.q_seq[i] = pc.q_seq[j] = -1;
+    pc.q_own_n.assign((size_t)n, 0);
+    pc.q_tail_page.assign((size_t)n, -1);
+    for (int32_t i = 0; i < n; ++i) {
+      const Seq* S = fa_seq(P, seqs[i]);
+      pc.q_own_n[i] = (int32_t)S->n;
+      if (S->n % PS) pc.q_tail_page[i] = S->pages[(size_t)(S->n / PS)];
+    }
+    pc.tail_rec.assign((size_t)n * H, -1);
+    pc.tail_slot.assign((size_t)n * H, -1);
+    pc.last_rec.assign((size_t)n * H, -1);
+    std::vector<int32_t> last_begin((size_t)n * H, -1);
+    for (size_t r = 0; r < items.size(); ++r) {
+      const Item& it = items[r];
+      if (it.seg->readers.size() != 1) continue;
+      const int32_t q = it.seg->readers[0];
+      const size_t at = (size_t)q * H + it.kv_head;
+      if (it.chunk_begin > last_begin[at]) {
+        last_begin[at] = it.chunk_begin;
+        pc.last_rec[at] = (int32_t)r;
+      }
+      if (pc.q_tail_page[q] >= 0)
+        for (int32_t c = 0; c < it.n_chunks; ++c)
+          if (it.seg->chunks[it.chunk_begin + c].page == pc.q_tail_page[q]) {
+            pc.tail_rec[at] = (int32_t)r;
+            pc.tail_slot[at] = c;
+          }
+    }
+  }
   pc.n_items = (int32_t)items.size();
   pc.n_out_rows = n_out;
   const size_t es = C.dtype == KV_F32 ? 4 : 2;
@@ -274,14 +389,15 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
   int64_t longest = 0;
   for (const Item& it : items) longest = std::max<int64_t>(longest, it.n_chunks);
   pc.stats[6] = longest;
+  pc.stats[7] = 0;
   pc.valid = true;
-  static std::atomic<uint64_t> plan_serial{0};
-  pc.serial = ++plan_serial;
+  pc.serial = ++g_plan_serial;
   pc.causal_n = len_cap ? -1 : 0;
   pc.version = P->version;
   pc.seqs.assign(seqs, seqs + n);
   pc.n_q_heads = hq;
   pc.ws = nullptr;  // not uploaded yet
+  if (!len_cap) P->journal.reset(P->version);
   return KV_OK;
 }
 
@@ -298,7 +414,7 @@ int fork_attn_workspace_size(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int3
 int fork_attn_plan_stats(kv_pool_t* P, int64_t* out, int32_t n) {
   if (!P || !out || n < 0) FAIL(P, KV_ERR_INVALID, "null argument");
   if (!P->plan.valid) FAIL(P, KV_ERR_INVALID, "no plan yet");
-  for (int32_t i = 0; i < n && i < 7; ++i) out[i] = P->plan.stats[i];
+  for (int32_t i = 0; i < n && i < 8; ++i) out[i] = P->plan.stats[i];
   return KV_OK;
 }
 
@@ -312,10 +428,36 @@ static int prepare(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, vo
   if (st) return st;
   DecodePlanCache& pc = P->plan;
   if (ws_bytes < pc.ws_need) FAIL(P, KV_ERR_WORKSPACE, "decode workspace too small");
+  hipError_t e = hipSuccess;
+  if (pc.ws == ws && !pc.pending.empty()) {
+    // the workspace holds this plan before its latest patches: send only the changed ints
+    // (the last value of each), scattered by a small kernel, through the pool's plan area
+    std::unordered_map<int32_t, size_t> last;
+    for (size_t k = 0; k < pc.pending.size(); k += 2) last[pc.pending[k]] = k;
+    std::vector<int32_t> list;
+    list.reserve(last.size() * 2);
+    for (size_t k = 0; k < pc.pending.size(); k += 2)
+      if (last[pc.pending[k]] == k) {
+        list.push_back(pc.pending[k]);
+        list.push_back(pc.pending[k + 1]);
+      }
+    pc.pending.clear();
+    const size_t area = fa_pool_ws_need(&P->cfg) - fa_ws_plan_offset(&P->cfg);
+    if (list.size() * sizeof(int32_t) <= area) {
+      char* at = P->ws + fa_ws_plan_offset(&P->cfg);
+      e = fa_upload(P, at, list.data(), list.size() * sizeof(int32_t), s);
+      if (e == hipSuccess)
+        e = launch_plan_patch(ws, reinterpret_cast<const int32_t*>(at), (int)(list.size() / 2), s);
+      if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("plan patch: ") + hipGetErrorString(e));
+    } else {
+      pc.ws = nullptr;  // too many changes for the plan area: upload the whole plan
+    }
+  }
   if (pc.ws != ws) {
-    hipError_t e = fa_upload(P, ws, pc.blob.data(), pc.blob.size(), s);
+    e = fa_upload(P, ws, pc.blob.data(), pc.blob.size(), s);
     if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("plan upload: ") + hipGetErrorString(e));
     pc.ws = ws;
+    pc.pending.clear();
   }
   return KV_OK;
 }
@@ -476,7 +618,7 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
       S->next_pos += 1;
       S->n += 1;
     }
-  P->version++;
+  fa_changed(P, ChangeJournal::kOther, -1, 0, 0);
   // 2. one plan over the contexts through the window's last token; step s is that plan
   // with each reserved page's slot range cut at the sequence's length after step s (the
   // same items, partial slots and merge counts; a chunk past the cut is empty)

@@ -78,6 +78,19 @@ static void take_page(kv_pool* P, int32_t p) {
   P->rc[p] = 1;
 }
 void fa_take_page(kv_pool* P, int32_t p) { take_page(P, p); }
+
+// One page-table change: a new version, logged for patching the cached decode plan.
+void fa_changed(kv_pool* P, int32_t kind, kv_seq_t seq, int64_t n0, int64_t n1) {
+  P->version++;
+  ChangeJournal& J = P->journal;
+  if (J.broken) return;
+  if (kind == ChangeJournal::kOther || J.ev.size() >= 65536) {
+    J.broken = true;
+    J.ev.clear();
+    return;
+  }
+  J.ev.push_back({seq, kind, n0, n1});
+}
 void fa_unref_page(kv_pool* P, int32_t p) { unref_page(P, p); }
 
 void fa_pos_append(std::vector<PosRun>& v, int64_t p0, int64_t n) {
@@ -119,12 +132,12 @@ hipError_t fa_upload(kv_pool* P, void* dst, const void* src, size_t bytes, hipSt
     if ((e = hipEventSynchronize(slot.ev)) != hipSuccess) return e;
     slot.pending = false;
   }
-  if (bytes > slot.bytes) {
-    if (slot.ptr) (void)hipHostFree(slot.ptr);
-    slot.ptr = nullptr;
-    slot.bytes = 0;
-    const size_t sz = std::max(bytes, (size_t)1 << 20);
-    if ((e = hipHostMalloc(&slot.ptr, sz, hipHostMallocDefault)) != hipSuccess) return e;
+  if (bytes > slot.bytes) {  // grow (at least double); the old buffer is freed with the pool
+    const size_t sz = std::max({bytes, 2 * slot.bytes, (size_t)1 << 20});
+    void* fresh = nullptr;
+    if ((e = hipHostMalloc(&fresh, sz, hipHostMallocDefault)) != hipSuccess) return e;
+    if (slot.ptr) P->retired.push_back(slot.ptr);
+    slot.ptr = fresh;
     slot.bytes = sz;
   }
   std::memcpy(slot.ptr, src, bytes);
@@ -135,7 +148,7 @@ hipError_t fa_upload(kv_pool* P, void* dst, const void* src, size_t bytes, hipSt
   return hipSuccess;
 }
 
-// Pool workspace: [0, 4096) counters (compaction ticket, wait time-outs), then one
+// Pool workspace: [0, 4096) counters (compaction wait time-outs at int 1), then one
 // read-done flag per page (zeroed at creation), then the plan area of append / write /
 // drop (overwritten by every such call, in stream order).
 static constexpr size_t kWsHeader = 4096;
@@ -147,7 +160,7 @@ size_t fa_ws_plan_offset(const kv_pool_config* c) {
 
 size_t fa_pool_ws_need(const kv_pool_config* c) {
   const size_t tokens = (size_t)c->n_pages * c->page_size;
-  return fa_ws_plan_offset(c) + tokens * 8 +
+  return fa_ws_plan_offset(c) + tokens * 16 +
          (size_t)c->n_pages * std::max(sizeof(CompactPage), sizeof(PageWrite)) +
          (size_t)kMaxRotations * (size_t)c->head_dim * 4 + 4 * 4096;
 }
@@ -252,6 +265,7 @@ int kv_pool_destroy(kv_pool_t* P) {
     if (slot.ptr) (void)hipHostFree(slot.ptr);
     if (slot.ev) (void)hipEventDestroy(slot.ev);
   }
+  for (void* p : P->retired) (void)hipHostFree(p);
   delete P;
   return KV_OK;
 }
@@ -260,7 +274,7 @@ int kv_seq_create(kv_pool_t* P, kv_seq_t* out) {
   if (!P || !out) FAIL(P, KV_ERR_INVALID, "null argument");
   P->seqs.emplace_back();
   *out = (kv_seq_t)P->seqs.size() - 1;
-  P->version++;
+  fa_changed(P, ChangeJournal::kTouch, *out, 0, 0);
   return KV_OK;
 }
 
@@ -274,7 +288,7 @@ int kv_fork(kv_pool_t* P, kv_seq_t parent, kv_seq_t* child) {
     for (int32_t p : m.pages) ref_page(P, p);
   P->seqs.push_back(std::move(c));
   *child = (kv_seq_t)P->seqs.size() - 1;
-  P->version++;
+  fa_changed(P, ChangeJournal::kTouch, *child, 0, 0);  // the parent's pages gain references only
   return KV_OK;
 }
 
@@ -292,7 +306,7 @@ int kv_mount(kv_pool_t* P, kv_seq_t dst, kv_seq_t src, int64_t b, int64_t n) {
   m.pos = pos_slice(s->pos, b, n);
   for (int32_t p : m.pages) ref_page(P, p);
   P->seqs[dst].mounts.push_back(std::move(m));
-  P->version++;
+  fa_changed(P, ChangeJournal::kTouch, dst, 0, 0);
   return KV_OK;
 }
 
@@ -365,7 +379,10 @@ static int write_tokens(kv_pool* P, kv_seq_t seq, int64_t start, int64_t n, cons
     }
     S->n += n;
   }
-  P->version++;
+  if (append && cow.empty())
+    fa_changed(P, ChangeJournal::kAppend, seq, S->n - n, S->n);
+  else
+    fa_changed(P, cow.empty() ? ChangeJournal::kContent : ChangeJournal::kOther, seq, 0, 0);
   return KV_OK;
 }
 
@@ -468,7 +485,13 @@ int kv_append_batch(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, const void* k
     q->next_pos += 1;
     q->n += 1;
   }
-  P->version++;
+  bool any_copy = false;
+  for (int32_t i = 0; i < n; ++i) any_copy |= how[(size_t)i] == kCopy;
+  if (any_copy) {
+    fa_changed(P, ChangeJournal::kOther, -1, 0, 0);
+  } else {  // one version step per appended sequence, as n single appends would take
+    for (int32_t i = 0; i < n; ++i) fa_changed(P, ChangeJournal::kAppend, seqs[i], S[(size_t)i]->n - 1, S[(size_t)i]->n);
+  }
   return KV_OK;
 }
 
@@ -490,7 +513,7 @@ int kv_rewind(kv_pool_t* P, kv_seq_t seq, int64_t n) {
   pos_truncate(S->pos, n);
   S->n = n;
   S->next_pos = n ? pos_last(S->pos) + 1 : 0;
-  P->version++;
+  fa_changed(P, ChangeJournal::kOther, seq, 0, 0);
   return KV_OK;
 }
 
@@ -512,7 +535,7 @@ int kv_release(kv_pool_t* P, kv_seq_t seq) {
   S->mounts.clear();
   S->pos.clear();
   S->live = false;
-  P->version++;
+  fa_changed(P, ChangeJournal::kOther, seq, 0, 0);
   return KV_OK;
 }
 

@@ -54,6 +54,27 @@ class FreeSet {
   int32_t hint_ = 0;  // no free id below word hint_
 };
 
+// Page-table changes since the cached decode plan, one per version step, so that a plan
+// can be patched instead of rebuilt when the only changes are appends that wrote into
+// pages their sequence owns alone (a decode step's one token per branch).
+struct ChangeJournal {
+  // kAppend: tokens appended with no page copied; kTouch: the sequence changed in another
+  // way; kContent: only token contents changed; kOther: anything the journal cannot follow
+  enum Kind : int32_t { kAppend = 0, kTouch = 1, kOther = 2, kContent = 3 };
+  struct Event {
+    int32_t seq, kind;
+    int64_t n0, n1;  // kAppend: token count before / after
+  };
+  uint64_t base = 0;  // pool version the journal starts at
+  bool broken = true;
+  std::vector<Event> ev;
+  void reset(uint64_t version) {
+    base = version;
+    broken = false;
+    ev.clear();
+  }
+};
+
 struct DecodePlanCache {
   bool valid = false;
   uint64_t version = 0;
@@ -65,9 +86,16 @@ struct DecodePlanCache {
   size_t off_items = 0, off_mptr = 0, off_plse = 0, off_po = 0;
   int32_t n_items = 0, n_out_rows = 0, max_parts = 1;
   std::vector<char> blob;  // host image of the plan part of the workspace
-  int64_t stats[7] = {0, 0, 0, 0, 0, 0, 0};
+  int64_t stats[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   int64_t causal_n = 0;  // 0: a decode plan; n > 0: causal rows of the last n tokens; -1: other caps
   uint64_t serial = 0;   // unique across pools and rebuilds: names this plan's contents
+  // patching (decode plans only): query of each listed sequence (-1 listed twice), per
+  // query its own token count and tail page, per (query, KV head) the record and chunk
+  // slot of the tail page's chunk and the record of the private segment's last item
+  bool patchable = false;
+  std::vector<int32_t> q_seq, q_own_n, q_tail_page;  // by query
+  std::vector<int32_t> tail_rec, tail_slot, last_rec;  // by query * Hkv + head
+  std::vector<int32_t> pending;                        // (int offset, value) pairs not yet on the device
 };
 
 // A steady-state decode window: every sequence's next n_steps slots reserved up front and
@@ -114,11 +142,14 @@ struct kv_pool {
   };
   static constexpr int kStageSlots = 8;
   StageSlot stage[kStageSlots];
+  // staging buffers outgrown by larger uploads, freed with the pool (freeing pinned
+  // memory waits for the whole device, so it never happens between operations)
+  std::vector<void*> retired;
   int stage_next = 0;
   // drop-kernel ordering state (see CompactParams)
-  int32_t ticket = 0;
   int32_t epoch = 0;
   fa::DecodePlanCache plan;
+  fa::ChangeJournal journal;
   fa::DecodeWindow window;
   // key scoring: the chunk list last uploaded (sequence, page-table version, workspace)
   struct ScoreChunks {

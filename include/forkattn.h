@@ -159,6 +159,22 @@ int kv_mount(kv_pool_t* pool, kv_seq_t dst, kv_seq_t src, int64_t src_begin, int
 int kv_drop(kv_pool_t* pool, kv_seq_t seq, const int64_t* begin, const int64_t* len,
             int32_t n_spans, int32_t flags, int64_t* kept_src_idx, hipStream_t stream);
 
+/* Drops of n distinct sequences in one call, ending exactly as n kv_drop calls in list
+ * order (same page tables, positions, compaction indices and page contents), with one
+ * plan upload and one kernel launch for all of them -- split into a few launches only
+ * where a later drop would write a page an earlier one still reads (sequences sharing
+ * pages) or the plans outgrow the pool workspace.  Sequence i's spans are
+ * begin / len[span_off[i] .. span_off[i + 1]) (HOST int64, span_off has n + 1 entries);
+ * flags as for kv_drop, for every listed sequence.  kept_src_idx: optional HOST int64,
+ * sequence i's compaction index at offset = the sum of the token counts (before the call)
+ * of the sequences listed before it.  Checks everything before changing anything:
+ * KV_ERR_INVALID for a sequence listed twice or a bad span, KV_ERR_NOT_FOUND for a dead
+ * handle, KV_ERR_OOM when the copies of all listed drops together (counted as if no
+ * earlier drop released a page) exceed the free pages. */
+int kv_drop_batch(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n, const int64_t* span_off,
+                  const int64_t* begin, const int64_t* len, int32_t flags, int64_t* kept_src_idx,
+                  hipStream_t stream);
+
 /* Repos alone: kv_drop with no spans and KV_DROP_REPOS. */
 int kv_repos(kv_pool_t* pool, kv_seq_t seq, hipStream_t stream);
 
@@ -248,7 +264,12 @@ int fork_attn_decode_static(kv_pool_t* pool, const kv_seq_t* seqs, int32_t n_seq
 /* Plan statistics of the last fork_attn_decode / fork_attn_workspace_size call:
  * out[0] segments, out[1] work items, out[2] chunks, out[3] partial rows,
  * out[4] unique KV bytes streamed (algorithmic), out[5] query rows, out[6] the largest
- * chunk count of one work item. */
+ * chunk count of one work item, out[7] how many times the plan was patched since it was
+ * last built (instead of replanning after page-table changes that were all appends into
+ * pages their sequence owns alone:
+ * the tail page's chunk grows and new pages join the last work item of the sequence's
+ * private segment, so a decode step after one kv_append_batch re-uploads a few ints
+ * instead of the plan). */
 int fork_attn_plan_stats(kv_pool_t* pool, int64_t* out, int32_t n);
 
 /* ---- packed DAG prefill (Octopus Packed DAG-GRPO, forward) ----

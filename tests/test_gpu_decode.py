@@ -12,8 +12,8 @@ import numpy as np
 import pytest
 
 import workloads as W
-from tests.harness import (build_device_pool, check_close, check_decode_model, oracle_decode, out_to_f64,
-                           plant_queries, subscenario, to_torch)
+from tests.harness import (build_device_pool, check_close, check_decode_both, check_decode_model, oracle_decode,
+                           out_to_f64, plant_queries, subscenario, to_torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -268,3 +268,36 @@ def test_append_batch_rewound_fork_in_shared_tail(order):
                 assert np.array_equal(f(k[:n_valid]), ora.kdata[page][:n_valid, h]), (s, L, h)
                 assert np.array_equal(f(v[:n_valid]), ora.vdata[page][:n_valid, h]), (s, L, h)
     print("[ok] kv_append_batch after a rewind into the shared tail", flush=True)
+
+
+def test_decode_steps_patch_the_plan():
+    # decode -> one token appended per branch -> decode ...: once every tail page is owned
+    # by its branch alone, each step's plan is patched (tail chunks grow, new pages join the
+    # private items) instead of rebuilt; every step against the oracle, and the plan after
+    # the last step equals a fresh plan's totals
+    import torch
+    import fork_attention_decode_amd as fa
+    from oracle import attention as att, pagetable as pt
+    sc = W.fork_scenario(prefix=517, branches=4, private=[0, 3, 16, 29], hq=8, hkv=2, d=128, seed=41)
+    sc.n_pages += 40
+    print("[case] decode steps with a patched plan", flush=True)
+    pool, _ = build_device_pool(sc)
+    ora, _ = pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, "bf16"))
+    seqs = list(sc.queries)
+    f = W.bf16_bits_to_f64
+    rng = np.random.default_rng(42)
+    patched = 0
+    for step in range(37):
+        qb = W.to_bf16_bits(rng.standard_normal((len(seqs), 8, 128)))
+        out, lse = pool.decode(seqs, to_torch(qb, "bf16"), sc.sm_scale)
+        torch.cuda.synchronize()
+        patched = max(patched, pool.plan_stats()["patched_changes"])
+        ref = att.decode(ora, seqs, f(qb), sc.sm_scale, with_magnitudes=True)
+        check_decode_both(out_to_f64(out, "bf16"), lse.double().cpu().numpy(), ref, 128, "bf16", f"step {step}")
+        kb = W.to_bf16_bits(rng.standard_normal((len(seqs), 2, 128)) / np.sqrt(128))
+        vb = W.to_bf16_bits(rng.standard_normal((len(seqs), 2, 128)))
+        pool.append_batch(seqs, to_torch(kb, "bf16"), to_torch(vb, "bf16"))
+        for i, b in enumerate(seqs):
+            ora.append(b, 1, k=f(kb[i:i + 1]), v=f(vb[i:i + 1]))
+    assert patched >= 30, patched
+    print(f"[ok] {patched} patched steps; plan {pool.plan_stats()}", flush=True)

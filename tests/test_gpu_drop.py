@@ -221,3 +221,31 @@ def test_akv_drop_repos_full_size():
         check_decode_model(o[[req]], l[[req]], ro, rl, a, s_abs, 128, "bf16", f"planted keys, request {req}",
                            rerotated_keys=True)
     print("[ok] planted keys of requests 0 and 11", flush=True)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_drop_batch_contents(shared):
+    # kv_drop_batch against the oracle's drops one after another in list order: independent
+    # requests (one launch), or forks sharing a prefix whose copies land on pages an
+    # earlier drop of the list released while still reading them (split launches)
+    import torch
+    if shared:
+        sc = W.fork_scenario(prefix=517, branches=3, private=[160, 300, 90], hq=4, hkv=2, d=128, seed=95)
+        sc.n_pages += 120
+        seqs = [2, 1, 3]
+        spans = [[(40, 33), (300, 100)], [(0, 5), (500, 20)], [(600, 7)]]
+    else:
+        sc = W.drop_scenario(requests=4, ctx=1100, frac=0.0, hq=4, hkv=2, d=128, seed=96, repos=True)
+        sc.ops = [op for op in sc.ops if op[0] != "drop" and not (op[0] == "append" and len(sc.blocks[op[2]].pos) == 1)]
+        seqs = [3, 0, 2, 1]
+        spans = [[(17, 300), (700, 64)], [(0, 16)], [], [(1000, 100)]]
+    print(f"[case] kv_drop_batch shared={shared}: {list(zip(seqs, spans))}", flush=True)
+    pool, _ = build_device_pool(sc)
+    ora, _ = _oracle(sc)
+    kept = pool.drop_batch(seqs, spans, repos=True)
+    torch.cuda.synchronize()
+    for s, sp, k in zip(seqs, spans, kept):
+        assert np.array_equal(k, ora.drop(s, sp, repos=True)), s
+    live = [i for i, s in enumerate(ora.seqs) if s.live]
+    _check_state(sc, pool, ora, live, exact_k=lambda s: s not in seqs)
+    print("[ok] kv_drop_batch", flush=True)

@@ -445,3 +445,97 @@ def test_append_batch_copy_source_written_in_place_by_a_later_sequence():
     ta, tb = list(fa.kv_block_table(pool.handle, a)), list(fa.kv_block_table(pool.handle, b))
     assert ta[:2] == tb[:2] and ta[2] != shared and tb[2] == shared  # a copied, b wrote in place
     assert fa.kv_page_refcount(pool.handle, shared) == 1
+
+
+@pytest.mark.parametrize("make", [
+    lambda: W.drop_scenario(requests=4, ctx=700, frac=0.4, span_min=17, span_max=120, hq=4, hkv=2, d=128, seed=91,
+                            repos=True),
+    lambda: W.fork_scenario(prefix=517, branches=4, private=[60, 200, 9, 0], hq=8, hkv=2, d=128, seed=92),
+    lambda: W.dag_scenario(root=300, threads=4, private=200, mounts_per_thread=2, mount_len=70, hq=8, hkv=2, d=128,
+                           seed=93),
+])
+@pytest.mark.parametrize("repos", [True, False])
+def test_drop_batch_equals_single_drops_in_list_order(make, repos):
+    # kv_drop_batch = one kv_drop per listed sequence, in list order: independent requests,
+    # forks sharing a prefix (a later drop may rewrite in place a page an earlier one
+    # released), mounted threads (copies); compaction indices, tables, refcounts, positions
+    sc = make()
+    sc.ops = [op for op in sc.ops if op[0] != "drop"]
+    sc.n_pages += 200
+    ora, _ = pt.replay(sc, with_data=False)
+    pool = fa.Pool(sc.n_kv_heads, sc.head_dim, sc.n_pages, page_size=sc.page_size, rope_theta=sc.rope_theta,
+                   metadata_only=True)
+    for op in sc.ops:
+        if op[0] == "create":
+            pool.seq_create()
+        elif op[0] == "append":
+            blk = sc.blocks[op[2]]
+            pool.append(op[1], n=len(blk.pos), positions=blk.pos)
+        elif op[0] == "fork":
+            pool.fork(op[1])
+        elif op[0] == "mount":
+            pool.mount(*op[1:])
+    live = [i for i, s in enumerate(ora.seqs) if s.live]
+    rng = np.random.default_rng(94)
+    seqs = list(rng.permutation(live))
+    spans = []
+    for s in seqs:
+        n = ora.seqs[s].n
+        sp = [(int(b), int(min(n - b, rng.integers(1, 40)))) for b in sorted(rng.integers(0, max(1, n), 3))] if n else []
+        spans.append(sp)
+    kept = pool.drop_batch(seqs, spans, repos=repos)
+    for s, sp, k in zip(seqs, spans, kept):
+        assert np.array_equal(k, ora.drop(s, sp, repos=repos)), s
+    _cmp(pool.handle, ora, live)
+
+
+def test_drop_batch_rejections_leave_state():
+    pool = fa.Pool(1, 2, 8, page_size=4, metadata_only=True)
+    a = pool.seq_create()
+    pool.append(a, n=9)
+    b = pool.fork(a)
+    c = pool.seq_create()
+    pool.append(c, n=6)
+    state = lambda: ([list(fa.kv_block_table(pool.handle, s)) for s in (a, b, c)], pool.free_pages(),
+                     [list(fa.kv_positions(pool.handle, s)) for s in (a, b, c)])
+    before = state()
+    for seqs, spans, status in (([a, a], [[(0, 1)], [(1, 1)]], fa.KV_ERR_INVALID),
+                                ([a, 9], [[(0, 1)], []], fa.KV_ERR_NOT_FOUND),
+                                ([c, a], [[(0, 1)], [(5, 9)]], fa.KV_ERR_INVALID),  # the second span is bad
+                                ([a, b], [[(0, 1)], [(0, 1)]], fa.KV_ERR_OOM)):    # copies of both exceed 1 free page
+        with pytest.raises(fa.ForkAttnError) as e:
+            pool.drop_batch(seqs, spans, repos=True)
+        assert e.value.status == status, (seqs, spans)
+        assert state() == before
+
+
+def test_patched_plan_totals_equal_a_fresh_plan():
+    # appends into pages a branch owns alone patch the cached decode plan; its totals
+    # (unique KV bytes, rows, segments, chunks) equal those of a plan built from scratch,
+    # and any other change (a drop) makes the next call replan
+    sc = W.fork_scenario(prefix=517, branches=4, private=[0, 3, 16, 29], hq=8, hkv=2, d=128, seed=41)
+    sc.n_pages += 80
+    pool = fa.Pool(sc.n_kv_heads, sc.head_dim, sc.n_pages, metadata_only=True)
+    for op in sc.ops:
+        if op[0] == "create":
+            pool.seq_create()
+        elif op[0] == "append":
+            pool.append(op[1], n=len(sc.blocks[op[2]].pos), positions=sc.blocks[op[2]].pos)
+        elif op[0] == "fork":
+            pool.fork(op[1])
+    seqs = list(sc.queries)
+    for step in range(45):
+        fa.fork_attn_workspace_size(pool.handle, seqs, 8)
+        pool.append_batch(seqs)
+    fa.fork_attn_workspace_size(pool.handle, seqs, 8)
+    patched = pool.plan_stats()
+    assert patched["patched_changes"] >= 40
+    fa.fork_attn_workspace_size(pool.handle, seqs[::-1], 8)  # another query list: a fresh plan
+    fa.fork_attn_workspace_size(pool.handle, seqs, 8)
+    fresh = pool.plan_stats()
+    assert fresh["patched_changes"] == 0
+    for key in ("unique_kv_bytes", "rows", "segments", "chunks"):
+        assert patched[key] == fresh[key], key
+    pool.drop(seqs[0], [(0, 3)])
+    fa.fork_attn_workspace_size(pool.handle, seqs, 8)
+    assert pool.plan_stats()["patched_changes"] == 0
