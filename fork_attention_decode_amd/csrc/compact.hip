@@ -24,15 +24,19 @@
 // read" (its loads have returned), and a page rewritten in place waits for exactly the
 // lower entries that read it.  The hazard is write-after-read, so relaxed device-scope
 // flags order it (acquire / release would write back or invalidate the die's L2 on every
-// poll).  Workgroups are dispatched in launch order on each die, so an entry only waits
-// for entries dispatched before it, which never wait for it: every wait ends (a bounded
-// spin counts a time-out instead of hanging if that order ever failed).
+// poll).  Workgroups are dispatched in launch order on each die, and on each die the
+// entries rise with the launch order, so the lowest unfinished entry is always resident
+// and waits only for finished ones: every wait ends (a bounded spin counts a time-out
+// instead of hanging if that order ever failed).
 #include <hip/hip_runtime.h>
 #include "plan.hpp"
 
 namespace fa {
 
 typedef __bf16 bf16_t;
+
+constexpr int kDies = 8;     // dies (XCDs) of MI355X that workgroups are dealt to in turn
+constexpr int kDieRun = 8;   // consecutive list entries per die
 
 template <typename T> __device__ inline float to_f(T x) { return (float)x; }
 template <typename T> __device__ inline T from_f(float x) { return (T)x; }
@@ -48,7 +52,13 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
   const int hkv = p.n_kv_heads;
   __shared__ int s_loc[16], s_rot[16];
   __shared__ int s_run[16][3], s_nrun;  // runs of the page: first slot, length, source location of the first
-  const int k = blockIdx.x;
+  // die-aware order: workgroups are handed to the chip's dies round robin, so runs of
+  // kDieRun consecutive list entries go to one die; neighbouring destination pages read
+  // the same source pages (a source page's kept tokens reach at most two), and the second
+  // read then hits that die's L2 instead of HBM.  On each die entries still start in
+  // ascending order.
+  const int die = blockIdx.x % kDies, on_die = blockIdx.x / kDies;
+  const int k = (die + kDies * (on_die / kDieRun)) * kDieRun + on_die % kDieRun;
   if (k >= p.n_pages) return;
   T* kp = reinterpret_cast<T*>(p.k_pages);
   T* vp = reinterpret_cast<T*>(p.v_pages);
@@ -113,13 +123,29 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
       const int run = s_rot[t];
       if (run >= 0) {
         const float* cs = p.cos_sin + (size_t)run * D;  // [D/2][2]
+        if constexpr (sizeof(T) == 2) {
+          // the slot's 8 dims are consecutive: their (cos, sin) pairs are 64 contiguous bytes
+          typedef float f32x4 __attribute__((ext_vector_type(4)));
+          const f32x4* c4 = reinterpret_cast<const f32x4*>(cs + 2 * (32 * fp + 8 * g));
+          f32x4 w[4];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int d = sizeof(T) == 2 ? 32 * fp + 8 * g + e : 16 * fp + 4 * e + g;
-          const float c = cs[2 * d], sn = cs[2 * d + 1];
-          const float x = to_f(ka[i][e]), y = to_f(kb[i][e]);
-          ka[i][e] = from_f<T>(x * c - y * sn);
-          kb[i][e] = from_f<T>(y * c + x * sn);
+          for (int q = 0; q < 4; ++q) w[q] = c4[q];
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float c = w[e >> 1][2 * (e & 1)], sn = w[e >> 1][2 * (e & 1) + 1];
+            const float x = to_f(ka[i][e]), y = to_f(kb[i][e]);
+            ka[i][e] = from_f<T>(x * c - y * sn);
+            kb[i][e] = from_f<T>(y * c + x * sn);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const int d = 16 * fp + 4 * e + g;
+            const float c = cs[2 * d], sn = cs[2 * d + 1];
+            const float x = to_f(ka[i][e]), y = to_f(kb[i][e]);
+            ka[i][e] = from_f<T>(x * c - y * sn);
+            kb[i][e] = from_f<T>(y * c + x * sn);
+          }
         }
       }
     }
@@ -226,7 +252,8 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
 
 template <typename T, int D, int UK, int UV>
 static hipError_t compact_t(const CompactParams& p, hipStream_t s) {
-  compact_kernel<T, D, UK, UV><<<p.n_pages, 256, 0, s>>>(p);
+  constexpr int per_round = kDies * kDieRun;  // grid rounded up; the surplus workgroups exit at once
+  compact_kernel<T, D, UK, UV><<<(p.n_pages + per_round - 1) / per_round * per_round, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // besides the vendor peaks -- a pure streaming read of HBM and a register-only
 // bf16 matrix-core loop (at whatever clock the chip holds under that load).
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <string>
 
 #include "../../include/forkattn.h"
@@ -14,21 +15,24 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 
-// Every 16-byte word of the buffer read once (non-temporal), grid-stride; the xor of
-// everything read goes to sink so no load can be dropped.
+// Every 16-byte word of the buffer read once (non-temporal): workgroup b reads the
+// contiguous chunk [b * chunk, (b + 1) * chunk) in 16 KiB steps, each lane keeping four
+// independent 16-byte loads in flight; the xor of everything read goes to sink so no load
+// can be dropped.
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf, size_t n16,
-                                                          unsigned* __restrict__ sink) {
+                                                          size_t chunk16, unsigned* __restrict__ sink) {
   u32x4 acc = {0u, 0u, 0u, 0u};
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {  // four independent loads in flight per lane
+  const size_t lo = (size_t)blockIdx.x * chunk16;
+  const size_t hi = lo + chunk16 < n16 ? lo + chunk16 : n16;
+  size_t i = lo + threadIdx.x;
+  for (; i + 768 < hi; i += 1024) {
     const u32x4 a = __builtin_nontemporal_load(buf + i);
-    const u32x4 b = __builtin_nontemporal_load(buf + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(buf + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(buf + i + 3 * stride);
+    const u32x4 b = __builtin_nontemporal_load(buf + i + 256);
+    const u32x4 c = __builtin_nontemporal_load(buf + i + 512);
+    const u32x4 d = __builtin_nontemporal_load(buf + i + 768);
     acc ^= a ^ b ^ c ^ d;
   }
-  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(buf + i);
+  for (; i < hi; i += 256) acc ^= __builtin_nontemporal_load(buf + i);
   const unsigned x = acc.x ^ acc.y ^ acc.z ^ acc.w;
   if (x == 0x9e3779b9u) sink[threadIdx.x] = x;  // practically never taken; keeps the loads live
 }
@@ -65,8 +69,12 @@ int kv_probe_stream_read(const void* buf, size_t bytes, void* sink, hipStream_t 
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) {
-    stream_read_kernel<<<8 * (ncu > 0 ? ncu : 256), 256, 0, stream>>>(static_cast<const u32x4*>(buf), bytes / 16,
-                                                                       static_cast<unsigned*>(sink));
+    // about eight workgroups per compute unit, each over a contiguous chunk of >= 16 KiB
+    const size_t n16 = bytes / 16;
+    const size_t want = 8 * (size_t)(ncu > 0 ? ncu : 256);
+    const size_t chunk16 = std::max<size_t>(1024, (n16 + want - 1) / want);
+    stream_read_kernel<<<(unsigned)((n16 + chunk16 - 1) / chunk16), 256, 0, stream>>>(
+        static_cast<const u32x4*>(buf), n16, chunk16, static_cast<unsigned*>(sink));
     e = hipGetLastError();
   }
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("stream probe: ") + hipGetErrorString(e));

@@ -95,7 +95,10 @@ int kv_pool_bytes(const kv_pool_config* cfg, size_t* bytes);
 /* Device workspace the pool needs for its own staging (append / write / drop plans). */
 int kv_pool_workspace_size(const kv_pool_config* cfg, size_t* bytes);
 
-/* Create a pool.  k_pages / v_pages: device buffers of kv_pool_bytes() each;
+/* Create a pool (Octopus, "Zero-Copy Radix Forking": every thread's KV lives in one pool
+ * of fixed-size pages that forks share by reference; Agentrix README, cache-lifecycle
+ * item: a page is reclaimed only when its reference count reaches zero).
+ * k_pages / v_pages: device buffers of kv_pool_bytes() each;
  * workspace: device buffer of kv_pool_workspace_size() bytes.
  * Passing k_pages = v_pages = workspace = NULL creates a METADATA-ONLY pool: every
  * page-table operation works and is bit-identical, no device work is issued and the
