@@ -490,14 +490,13 @@ def bench_restore(reps=20, n_seg=4, seg_len=128):
         "us_mean": float(np.mean(ms)) * 1e3, "us_p10": float(np.percentile(ms, 10)) * 1e3,
         "host_plan_ms": host_plan_ms,
         "context_kv_bytes": kv_bytes,
-        "streamed_kv_bytes": kv_bytes * (n // 16),
-        "streamed_GBps": kv_bytes * (n // 16) / (float(np.mean(ms)) * 1e-3) / 1e9,
         "rows": n * hq,
         "roofline": {"bound": "mfma", "unit": "TFLOP/s", "peak": 2500.0, "algorithmic_flops_per_call": flops,
                      "achieved": tflops, "frac": tflops / 2500.0},
-        "note": "the attention runs as one split-K decode of n x Hq rows: every context page is streamed once per "
-                "group of 64 / G = 16 restored tokens, so it reads the context n / 16 times; the plan (host) is "
-                "built once and cached, the events enclose the kernels",
+        "note": "the attention runs as a split-K tiled prefill: the context's pages are relaid once into "
+                "operand-order images, every workgroup takes 64 restored tokens x 4 query heads of one KV head over "
+                "one piece of the key range (32 x 32 x 16 matrix instructions), and the pieces' partials are merged "
+                "by log-sum-exp; the plan (host) is built once and cached, the events enclose the kernels",
     }
 
 

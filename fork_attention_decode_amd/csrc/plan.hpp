@@ -120,6 +120,30 @@ struct CompactParams {
   int32_t pool_pages;        // pool capacity: head h's blocks start at h * pool_pages
 };
 
+// Causal attention of a sequence's last nq tokens as a split-K tiled prefill over its
+// pages (bf16, d = 128): keys 0 .. T-1 are the visible tokens (own, then mounts) at
+// locs[t] = page * 16 + slot; query row r (q row r, key index q_off + r) sees key t
+// unless q_off + r < t < n_own.  CSR rows (row_ptr, ent = col | diag bit << 31, order
+// by descending length) are (query block r / n_split, key piece r % n_split); each
+// writes partials (lse2, normalised o) at slot (row * hq + head) * n_split + piece.
+struct RestoreLaunch {
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  int32_t pool_pages;
+  const int32_t* locs;
+  const int32_t* row_ptr;
+  const int32_t* ent;
+  const int32_t* order;
+  char* kimg;  // [hkv][ceil(T / 64)][16 KiB]
+  char* vimg;
+  float* part_lse2;
+  float* part_o;
+  int32_t T, n_own, q_off, nq, hq, hkv, n_rows, n_split;
+  float sm_scale;
+};
+constexpr int kRestoreImgBytes = 16384;  // one 64-key image block of one KV head (K or V)
+
 hipError_t launch_page_write(int dtype, int d, int hkv, int pool_pages, void* k_pages, void* v_pages,
                              const void* k_new, const void* v_new, const PageWrite* writes,
                              int n_writes, hipStream_t s);
@@ -130,5 +154,6 @@ hipError_t launch_merge(int dtype, int d, const MergeParams& p, hipStream_t s);
 hipError_t launch_plan_patch(void* ws, const int32_t* patches, int n, hipStream_t s);
 hipError_t launch_compact(int dtype, int d, const CompactParams& p, hipStream_t s);
 bool compact_supported(int dtype, int d, int hkv);  // the kernel's register budget
+hipError_t fa_launch_restore(const RestoreLaunch& r, hipStream_t s);
 
 }  // namespace fa

@@ -803,8 +803,116 @@ static int causal_plan(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t hq) {
   return st;
 }
 
+}  // extern "C"
+
+// bf16 pools with d = 128 restore through the tiled prefill; other pools through rows of
+// the split-K decode.
+static bool restore_by_prefill(const kv_pool* P) { return P->cfg.dtype == KV_BF16 && P->cfg.head_dim == 128; }
+
+// Plan of the tiled-prefill restore (cached per sequence state, n and head count).
+static int restore_plan(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t hq) {
+  const kv_pool_config& C = P->cfg;
+  Seq* S = fa_seq(P, seq);
+  if (!S) FAIL(P, KV_ERR_NOT_FOUND, "no live sequence");
+  if (n < 1 || n > S->n) FAIL(P, KV_ERR_INVALID, "the attended tokens must be the sequence's last n (n >= 1)");
+  if (hq < C.n_kv_heads || hq % C.n_kv_heads) FAIL(P, KV_ERR_INVALID, "n_q_heads must be a multiple of n_kv_heads");
+  RestorePlan& R = P->restore;
+  if (R.valid && R.version == P->version && R.seq == seq && R.n == n && R.hq == hq) return KV_OK;
+  const int32_t PS = C.page_size, H = C.n_kv_heads;
+  const int64_t N = S->n;
+  int64_t T = N;
+  for (const Mount& m : S->mounts) T += m.n;
+  if (T > INT32_MAX / 2 || n * hq > ((int64_t)1 << 30)) FAIL(P, KV_ERR_UNSUPPORTED, "context too long");
+  // visible keys: own tokens, then each mount's range
+  std::vector<int32_t> locs;
+  locs.reserve((size_t)T);
+  for (int64_t t = 0; t < N; ++t) locs.push_back(S->pages[(size_t)(t / PS)] * 16 + (int32_t)(t % PS));
+  for (const Mount& m : S->mounts)
+    for (int64_t j = 0; j < m.n; ++j) {
+      const int64_t tok = m.off + j;
+      locs.push_back(m.pages[(size_t)(tok / PS)] * 16 + (int32_t)(tok % PS));
+    }
+  // rows: query block qb (restored tokens 64 qb ..) x key piece; the visible key blocks of
+  // a query block are the own blocks through its last query's and every block from the
+  // first mounted key on; a block is masked inside when some own key in it can follow
+  // some query of the block
+  const int64_t q_off = N - n;
+  const int32_t nb = (int32_t)((T + 63) / 64), nqb = (int32_t)((n + 63) / 64);
+  const int32_t G = hq / H, n_hg = (G + 3) / 4;
+  std::vector<std::vector<int32_t>> cols((size_t)nqb);
+  size_t shortest = SIZE_MAX;
+  for (int32_t qb = 0; qb < nqb; ++qb) {
+    const int64_t i_min = q_off + 64 * qb, i_max = q_off + std::min<int64_t>(64 * qb + 63, n - 1);
+    for (int32_t kb = 0; kb < nb; ++kb) {
+      const int64_t k0 = 64 * (int64_t)kb;
+      if (k0 > i_max && k0 + 63 < N) continue;  // own keys after every query of the block
+      const bool diag = k0 + 63 > i_min && k0 < N;
+      cols[qb].push_back(kb | (diag ? (int32_t)0x80000000u : 0));
+    }
+    shortest = std::min(shortest, cols[qb].size());
+  }
+  // pieces: one workgroup per compute unit (the kernel's LDS ring holds one per unit),
+  // so the launch is one wave of workgroups of nearly equal length
+  const int64_t base_rows = (int64_t)nqb * H * n_hg;
+  int32_t n_split = (int32_t)std::min<int64_t>(32, std::max<int64_t>(1, (P->n_cu + base_rows - 1) / base_rows));
+  n_split = (int32_t)std::max<size_t>(1, std::min<size_t>((size_t)n_split, shortest));
+  const int32_t n_rows = nqb * n_split;
+  std::vector<int32_t> row_ptr((size_t)n_rows + 1, 0), ent;
+  for (int32_t qb = 0; qb < nqb; ++qb) {
+    const size_t L = cols[qb].size();
+    for (int32_t pc = 0; pc < n_split; ++pc) {
+      const size_t a = L * pc / n_split, b = L * (pc + 1) / n_split;
+      ent.insert(ent.end(), cols[qb].begin() + a, cols[qb].begin() + b);
+      row_ptr[(size_t)qb * n_split + pc + 1] = (int32_t)ent.size();
+    }
+  }
+  std::vector<int32_t> order((size_t)n_rows);
+  for (int32_t r = 0; r < n_rows; ++r) order[r] = r;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return row_ptr[a + 1] - row_ptr[a] > row_ptr[b + 1] - row_ptr[b];
+  });
+  std::vector<int32_t> count((size_t)(n * hq), n_split);
+  size_t off = 0;
+  R.off_locs = off; off = align256(off + locs.size() * 4);
+  R.off_rowptr = off; off = align256(off + row_ptr.size() * 4);
+  R.off_ent = off; off = align256(off + std::max<size_t>(1, ent.size()) * 4);
+  R.off_order = off; off = align256(off + order.size() * 4);
+  R.off_count = off; off = align256(off + count.size() * 4);
+  const size_t blob_bytes = off;
+  R.off_kimg = off; off += (size_t)H * nb * kRestoreImgBytes;
+  R.off_vimg = off; off += (size_t)H * nb * kRestoreImgBytes;
+  off = align256(off);
+  R.off_plse = off; off = align256(off + (size_t)n * hq * n_split * 4);
+  R.off_po = off; off = align256(off + (size_t)n * hq * n_split * C.head_dim * 4);
+  R.ws_need = off;
+  R.blob.assign(blob_bytes, 0);
+  std::memcpy(R.blob.data() + R.off_locs, locs.data(), locs.size() * 4);
+  std::memcpy(R.blob.data() + R.off_rowptr, row_ptr.data(), row_ptr.size() * 4);
+  if (!ent.empty()) std::memcpy(R.blob.data() + R.off_ent, ent.data(), ent.size() * 4);
+  std::memcpy(R.blob.data() + R.off_order, order.data(), order.size() * 4);
+  std::memcpy(R.blob.data() + R.off_count, count.data(), count.size() * 4);
+  R.T = (int32_t)T;
+  R.n_own = (int32_t)N;
+  R.n_rows = n_rows;
+  R.n_split = n_split;
+  R.valid = true;
+  R.version = P->version;
+  R.seq = seq;
+  R.n = n;
+  R.hq = hq;
+  R.ws = nullptr;
+  return KV_OK;
+}
+
+extern "C" {
+
 int kv_causal_attend_workspace_size(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t n_q_heads, size_t* bytes) {
   if (!P || !bytes) FAIL(P, KV_ERR_INVALID, "null argument");
+  if (restore_by_prefill(P)) {
+    if (int st = restore_plan(P, seq, n, n_q_heads)) return st;
+    *bytes = P->restore.ws_need;
+    return KV_OK;
+  }
   if (int st = causal_plan(P, seq, n, n_q_heads)) return st;
   *bytes = P->plan.ws_need;
   return KV_OK;
@@ -815,6 +923,56 @@ int kv_causal_attend(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t n_q_heads, c
   if (!P) FAIL(P, KV_ERR_INVALID, "null pool");
   if (!P->device) FAIL(P, KV_ERR_INVALID, "metadata-only pool has no KV data");
   if (!q || !out || !workspace) FAIL(P, KV_ERR_INVALID, "null device pointer");
+  if (restore_by_prefill(P)) {
+    if (!(sm_scale > 0.f)) FAIL(P, KV_ERR_INVALID, "softmax scale must be positive");
+    if (int st = restore_plan(P, seq, n, n_q_heads)) return st;
+    RestorePlan& R = P->restore;
+    if (ws_bytes < R.ws_need) FAIL(P, KV_ERR_WORKSPACE, "causal attention workspace too small");
+    char* w = static_cast<char*>(workspace);
+    hipError_t e = hipSuccess;
+    if (R.ws != workspace) {
+      e = fa_upload(P, w, R.blob.data(), R.blob.size(), s);
+      if (e == hipSuccess) R.ws = workspace;
+    }
+    if (e == hipSuccess) {
+      RestoreLaunch rl;
+      rl.q = q;
+      rl.k_pages = P->k;
+      rl.v_pages = P->v;
+      rl.pool_pages = P->cfg.n_pages;
+      rl.locs = reinterpret_cast<const int32_t*>(w + R.off_locs);
+      rl.row_ptr = reinterpret_cast<const int32_t*>(w + R.off_rowptr);
+      rl.ent = reinterpret_cast<const int32_t*>(w + R.off_ent);
+      rl.order = reinterpret_cast<const int32_t*>(w + R.off_order);
+      rl.kimg = w + R.off_kimg;
+      rl.vimg = w + R.off_vimg;
+      rl.part_lse2 = reinterpret_cast<float*>(w + R.off_plse);
+      rl.part_o = reinterpret_cast<float*>(w + R.off_po);
+      rl.T = R.T;
+      rl.n_own = R.n_own;
+      rl.q_off = (int32_t)(R.n_own - n);
+      rl.nq = (int32_t)n;
+      rl.hq = n_q_heads;
+      rl.hkv = P->cfg.n_kv_heads;
+      rl.n_rows = R.n_rows;
+      rl.n_split = R.n_split;
+      rl.sm_scale = sm_scale;
+      e = fa_launch_restore(rl, s);
+    }
+    if (e == hipSuccess) {
+      MergeParams mp;
+      mp.count = reinterpret_cast<const int32_t*>(w + R.off_count);
+      mp.max_parts = R.n_split;
+      mp.part_lse2 = reinterpret_cast<const float*>(w + R.off_plse);
+      mp.part_o = reinterpret_cast<const float*>(w + R.off_po);
+      mp.out = out;
+      mp.lse = lse;
+      mp.n_rows = (int32_t)(n * n_q_heads);
+      e = launch_merge(P->cfg.dtype, P->cfg.head_dim, mp, s);
+    }
+    if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("causal attention: ") + hipGetErrorString(e));
+    return KV_OK;
+  }
   if (int st = causal_plan(P, seq, n, n_q_heads)) return st;
   DecodePlanCache& pc = P->plan;  // cached for the same sequence state (never a decode plan)
   if (ws_bytes < pc.ws_need) FAIL(P, KV_ERR_WORKSPACE, "causal attention workspace too small");

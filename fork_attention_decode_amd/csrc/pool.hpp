@@ -117,6 +117,22 @@ struct DecodeWindow {
   void* ws = nullptr;
 };
 
+// Causal attention of a sequence's last n tokens as a split-K tiled prefill (bf16 pools,
+// d = 128): the visible keys' locations, the CSR of (query block, key piece) rows and the
+// merge counts, uploaded once per sequence state into the caller's workspace.
+struct RestorePlan {
+  bool valid = false;
+  uint64_t version = 0;
+  kv_seq_t seq = -1;
+  int64_t n = 0;
+  int32_t hq = 0;
+  std::vector<char> blob;  // [locs | row_ptr | ent | order | counts], uploaded
+  size_t off_locs = 0, off_rowptr = 0, off_ent = 0, off_order = 0, off_count = 0;
+  size_t off_kimg = 0, off_vimg = 0, off_plse = 0, off_po = 0, ws_need = 0;
+  int32_t T = 0, n_own = 0, n_rows = 0, n_split = 1;
+  void* ws = nullptr;  // workspace the blob was last uploaded to
+};
+
 }  // namespace fa
 
 struct kv_pool {
@@ -150,6 +166,7 @@ struct kv_pool {
   int32_t epoch = 0;
   fa::DecodePlanCache plan;
   fa::ChangeJournal journal;
+  fa::RestorePlan restore;
   fa::DecodeWindow window;
   // key scoring: the chunk list last uploaded (sequence, page-table version, workspace)
   struct ScoreChunks {

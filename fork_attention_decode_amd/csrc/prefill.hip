@@ -33,6 +33,7 @@
 #include <math.h>
 #include <string>
 #include "../../include/forkattn.h"
+#include "plan.hpp"
 
 int fa_set_err(struct kv_pool* P, int code, const std::string& m);
 
@@ -64,6 +65,16 @@ struct Params {
   float* lse;
   int32_t T, hq, hkv, G, n_hg, nb;
   float scale_log2, sm_scale;
+  // query rows: row r of q / out is the query at key index q_off + r, r < nq; a query
+  // at index i sees key t unless i < t < n_own (causal inside [0, n_own); keys from
+  // n_own on are visible to every query).  The packed prefill: q_off = 0, nq = n_own = T.
+  int32_t q_off, nq, n_own;
+  // split mode: CSR row r covers query block r / n_split, key range piece r % n_split;
+  // partial (lse2, normalised o) of (query row, head, piece) at slot
+  // (row * hq + head) * n_split + piece
+  int32_t n_split;
+  float* part_lse2;
+  float* part_o;
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -162,6 +173,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 //
 // 8 waves, two per SIMD (waves w and w + 4 share one): wave w takes query head slot
 // w / 2 and tokens [q0 + 32 (w % 2), +32) of the block.
+template <bool kSplit>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32_t* __restrict__ row_ptr,
                                                           const int32_t* __restrict__ ent,
                                                           const int32_t* __restrict__ order) {
@@ -173,10 +185,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
   const int rest = b / p.hkv;
   const int hg = rest % p.n_hg;
   const int row = order[rest / p.n_hg];
+  const int qblock = kSplit ? row / p.n_split : row;
   const int hslot = hg * 4 + (wave >> 1);
   const bool active = hslot < p.G;
   const int qhead = h * p.G + (active ? hslot : 0);  // an idle wave computes head 0 and stores nothing
-  const int q0 = row * kB + 32 * (wave & 1);         // this wave's 32 queries
+  const int r0 = qblock * kB + 32 * (wave & 1);      // this wave's 32 query rows
+  const int q0 = p.q_off + r0;                       // ... at key indices q0 ..
   const int j0 = row_ptr[row];
   const int n = row_ptr[row + 1] - j0;
   const int hi = lane >> 5, lo = lane & 31;
@@ -203,12 +217,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
   // queries: B operand of S^T = K Q^T, lane holds Q[q0 + lo][16 ks + 8 hi + 0..7]
   bf16x8 qf[8];
   {
-    const int tq = q0 + lo;
-    const bf16_t* src = p.q + ((size_t)(tq < p.T ? tq : 0) * p.hq + qhead) * kD + 8 * hi;
+    const int tr = r0 + lo;
+    const bf16_t* src = p.q + ((size_t)(tr < p.nq ? tr : 0) * p.hq + qhead) * kD + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       qf[ks] = *reinterpret_cast<const bf16x8*>(src + 16 * ks);
-      if (tq >= p.T) qf[ks] = bf16x8{};
+      if (tr >= p.nq) qf[ks] = bf16x8{};
     }
   }
   f32x16 o[4];
@@ -241,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32(kf[kt][ks], qf[ks], s[kt]);
   };
-  // diagonal block (key > query) and keys past T -> -inf; rare, so behind a branch
+  // diagonal block (query < key < n_own) and keys past T -> -inf; rare, so behind a branch
   auto mask = [&](int e, f32x16 (&s)[2]) {
     const int c = e & ~kDiagBit;
     if (e < 0 || (ragged && c == p.nb - 1)) {
@@ -252,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb + 32 * kt + 8 * (r >> 2) + (r & 3);
-          s[kt][r] = (key > lim || key >= p.T) ? -INFINITY : s[kt][r];
+          s[kt][r] = ((key > lim && key < p.n_own) || key >= p.T) ? -INFINITY : s[kt][r];
         }
     }
   };
@@ -385,21 +399,96 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
   if (!active) return;
 
   const float lt = xhalf_sum(l);
-  const int tq = q0 + lo;
-  if (tq >= p.T) return;
+  const int tr = r0 + lo;
+  if (tr >= p.nq) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a row with no visible key: zeros, lse -inf
-  bf16_t* dst = p.out + ((size_t)tq * p.hq + qhead) * kD + 4 * hi;
+  if constexpr (kSplit) {  // this piece's normalised partial, fp32
+    const size_t slot = ((size_t)tr * p.hq + qhead) * p.n_split + row % p.n_split;
+    float* dst = p.part_o + slot * kD + 4 * hi;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 w;
+      for (int g = 0; g < 4; ++g) {
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
+        f32x4v w;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) w[q] = (bf16_t)(o[dt][4 * g + q] * inv);
-      *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * g) = w;
+        for (int q = 0; q < 4; ++q) w[q] = o[dt][4 * g + q] * inv;
+        *reinterpret_cast<f32x4v*>(dst + 32 * dt + 8 * g) = w;
+      }
+    if (hi == 0) p.part_lse2[slot] = lt > 0.f ? m * c2 + __log2f(lt) : -INFINITY;
+  } else {
+    bf16_t* dst = p.out + ((size_t)tr * p.hq + qhead) * kD + 4 * hi;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = (bf16_t)(o[dt][4 * g + q] * inv);
+        *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * g) = w;
+      }
+    if (p.lse && hi == 0)
+      p.lse[(size_t)qhead * p.nq + tr] = lt > 0.f ? (m * c2 + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+// ---- relayout of a sequence's visible keys out of the page pool: image block c of KV
+// head h holds visible keys 64 c .. 64 c + 63, key t read from locs[t] = page * 16 + slot
+// (pool block (page, h) at (h * pool_pages + page) * 16 * 128: K slot (f, g, slot) =
+// K[slot][32 f + 8 g .. + 8], V^T element d * 16 + slot); keys >= T read as zero.
+__global__ __launch_bounds__(256) void page_relayout_kernel(const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
+                                                            const int32_t* __restrict__ locs, char* __restrict__ kimg,
+                                                            char* __restrict__ vimg, int T, int nb, int pool_pages) {
+  const int c = blockIdx.x, h = blockIdx.y;
+  const size_t img = ((size_t)h * nb + c) * kImg;
+  const size_t head = (size_t)h * pool_pages;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = i * 256 + threadIdx.x;
+    const int lane = s & 63;
+    {  // K slot (kt, ks, lane): K[32 kt + lane % 32][16 ks + 8 (lane / 32) + 0..7]
+      const int ks = (s >> 6) & 7, kt = s >> 9;
+      const int key = c * kB + 32 * kt + (lane & 31);
+      i32x4 val = {0, 0, 0, 0};
+      if (key < T) {
+        const int loc = locs[key];
+        const int d0 = 16 * ks + 8 * (lane >> 5);
+        const bf16_t* blk = kp + (head + (loc >> 4)) * 16 * kD;
+        val = *reinterpret_cast<const i32x4*>(blk + (((d0 >> 5) * 4 + ((d0 & 31) >> 3)) * 16 + (loc & 15)) * 8);
+      }
+      *reinterpret_cast<i32x4*>(kimg + img + (size_t)s * 16) = val;
     }
-  if (p.lse && hi == 0)
-    p.lse[(size_t)qhead * p.T + tq] = lt > 0.f ? (m * c2 + __log2f(lt)) * 0.69314718055994531f : -INFINITY;
+    {  // V slot (dt, kt, hf, lane): V[key(e)][32 dt + lane % 32], keys in two runs of four
+      const int hf = (s >> 6) & 1, kt = (s >> 7) & 1, dt = s >> 8;
+      const int d = 32 * dt + (lane & 31);
+      bf16x8 val;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int key0 = c * kB + 32 * kt + 16 * hf + 8 * half + 4 * (lane >> 5);
+        const int loc0 = key0 + 3 < T ? locs[key0] : -1;
+        const int loc3 = key0 + 3 < T ? locs[key0 + 3] : -1;
+        if (loc0 >= 0 && (loc0 & 3) == 0 && loc3 == loc0 + 3) {
+          // four consecutive slots of one page: 8 contiguous bytes of the V^T row
+          typedef bf16_t bf16x4v __attribute__((__vector_size__(4 * sizeof(bf16_t))));
+          const bf16x4v x = *reinterpret_cast<const bf16x4v*>(vp + (head + (loc0 >> 4)) * 16 * kD + d * 16 + (loc0 & 15));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[4 * half + e] = x[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = key0 + e;
+            bf16_t x = (bf16_t)0.f;
+            if (key < T) {
+              const int loc = locs[key];
+              x = vp[(head + (loc >> 4)) * 16 * kD + d * 16 + (loc & 15)];
+            }
+            val[4 * half + e] = x;
+          }
+        }
+      }
+      *reinterpret_cast<bf16x8*>(vimg + img + (size_t)s * 16) = val;
+    }
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -491,7 +580,12 @@ extern "C" int dag_attn_run(const void* q, void* out, float* lse, int32_t T, int
   p.nb = (T + kB - 1) / kB;
   p.sm_scale = sm_scale;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  prefill_kernel<<<(size_t)p.nb * n_kv_heads * p.n_hg, kThreads, 0, stream>>>(
+  p.q_off = 0;
+  p.nq = T;
+  p.n_own = T;
+  p.n_split = 1;
+  p.part_lse2 = p.part_o = nullptr;
+  prefill_kernel<false><<<(size_t)p.nb * n_kv_heads * p.n_hg, kThreads, 0, stream>>>(
       p, row_ptr, reinterpret_cast<const int32_t*>(ws + w.ent), reinterpret_cast<const int32_t*>(ws + w.order));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill: ") + hipGetErrorString(e));
@@ -511,4 +605,37 @@ extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, voi
     return st;
   return dag_attn_run(q, out, lse, T, n_q_heads, n_kv_heads, head_dim, row_ptr, nnz, block, sm_scale, workspace,
                       ws_bytes, stream);
+}
+
+// Restore of a sequence's last tokens as a split-K tiled prefill over its pages: the
+// visible keys are relaid into operand-order images, then the prefill kernel runs the
+// CSR rows (query block, key-range piece) and writes one partial per (query row, head,
+// piece), merged afterwards by the decode merge.
+hipError_t fa::fa_launch_restore(const RestoreLaunch& r, hipStream_t stream) {
+  const int nb = (r.T + kB - 1) / kB;
+  page_relayout_kernel<<<dim3(nb, r.hkv), 256, 0, stream>>>(static_cast<const bf16_t*>(r.k_pages),
+                                                            static_cast<const bf16_t*>(r.v_pages), r.locs, r.kimg,
+                                                            r.vimg, r.T, nb, r.pool_pages);
+  Params p;
+  p.q = static_cast<const bf16_t*>(r.q);
+  p.kimg = r.kimg;
+  p.vimg = r.vimg;
+  p.out = nullptr;
+  p.lse = nullptr;
+  p.T = r.T;
+  p.hq = r.hq;
+  p.hkv = r.hkv;
+  p.G = r.hq / r.hkv;
+  p.n_hg = (p.G + 3) / 4;
+  p.nb = nb;
+  p.sm_scale = r.sm_scale;
+  p.scale_log2 = r.sm_scale * 1.4426950408889634f;
+  p.q_off = r.q_off;
+  p.nq = r.nq;
+  p.n_own = r.n_own;
+  p.n_split = r.n_split;
+  p.part_lse2 = r.part_lse2;
+  p.part_o = r.part_o;
+  prefill_kernel<true><<<(size_t)r.n_rows * r.hkv * p.n_hg, kThreads, 0, stream>>>(p, r.row_ptr, r.ent, r.order);
+  return hipGetLastError();
 }

@@ -185,7 +185,8 @@ def check_close(got: np.ndarray, ref: np.ndarray, max_abs: float, mean_abs: floa
     return mx, mn
 
 
-def check_decode_both(o, lse, ref, head_dim: int, dtype: str, what: str, rerotated_keys: bool = False):
+def check_decode_both(o, lse, ref, head_dim: int, dtype: str, what: str, rerotated_keys: bool = False,
+                      gamma: float = None, rounded_p_sum: bool = False):
     """The coarse gate (bf16: max-abs 2e-2 / mean-abs 2e-3; fp32: 1e-4; LSE 2e-3) and the
     error-model bars, for outputs o [.., d] / lse against ref = (o, lse, a, s_abs) of the
     oracle with magnitudes.  Returns (max-abs, mean-abs, worst O / bar, worst LSE / bar)."""
@@ -193,5 +194,6 @@ def check_decode_both(o, lse, ref, head_dim: int, dtype: str, what: str, rerotat
     tol = (2e-2, 2e-3) if dtype == "bf16" else (1e-4, 1e-4)
     mx, mn = check_close(o, ro, *tol, what)
     check_close(lse, rl, 2e-3, 2e-3, what + " lse")
-    wo, wl = check_decode_model(o, lse, ro, rl, a, s_abs, head_dim, dtype, what, rerotated_keys)
+    wo, wl = check_decode_model(o, lse, ro, rl, a, s_abs, head_dim, dtype, what, rerotated_keys, gamma,
+                                rounded_p_sum)
     return mx, mn, wo, wl

@@ -4,8 +4,10 @@ kv_causal_attend over the appended tokens) against the fp64 oracle
 mounts.  Bars as for decode: bf16 outputs max-abs 2e-2 and mean-abs 2e-3, LSE max-abs
 2e-3.  Cases: two segments with positions far apart appended to a fork whose tail page
 is shared (copy-on-write), a thread with mounts, a single token, a whole fresh
-sequence (plain causal attention, several work-item groups), and the timed restore
-workload at full size (sampled tokens, every head).
+sequence (plain causal attention, several work-item groups), fp32 and d = 64 pools (the
+decode-row path), and the timed restore workload at full size (sampled tokens, every
+head).  Bars: also the error model's (tests/harness.py: decode_bars), with the tiled
+prefill's row sum over the rounded P for bf16 / d = 128 pools.
 """
 import numpy as np
 import pytest
@@ -25,21 +27,28 @@ def _restore(sc, seq, seg_lens, seg_pos, seed, label, rows=None):
     pool, _ = build_device_pool(sc)
     table, _ = pt.replay(sc, with_data=True, to_f64=lambda a: W.storage_to_f64(a, sc.dtype))
     f = W.bf16_bits_to_f64
+    dt = sc.dtype
+    store = (lambda x: W.to_bf16_bits(x)) if dt == "bf16" else (lambda x: x.astype(np.float32))
+    f = (lambda a: W.storage_to_f64(a, dt))
     for n, p0 in zip(seg_lens, seg_pos):
-        kb = W.to_bf16_bits(rng.standard_normal((n, hkv, d)) / np.sqrt(d))
-        vb = W.to_bf16_bits(rng.standard_normal((n, hkv, d)))
+        kb = store(rng.standard_normal((n, hkv, d)) / np.sqrt(d))
+        vb = store(rng.standard_normal((n, hkv, d)))
         pos = np.arange(p0, p0 + n, dtype=np.int64)
-        pool.append(seq, k=to_torch(kb, "bf16"), v=to_torch(vb, "bf16"), positions=pos)
+        pool.append(seq, k=to_torch(kb, dt), v=to_torch(vb, dt), positions=pos)
         table.append(seq, n, k=f(kb), v=f(vb), pos=pos)
     n_all = int(sum(seg_lens))
-    qb = W.to_bf16_bits(rng.standard_normal((n_all, hq, d)))
-    out, lse = pool.causal_attend(seq, to_torch(qb, "bf16"), sc.sm_scale)
+    qb = store(rng.standard_normal((n_all, hq, d)))
+    out, lse = pool.causal_attend(seq, to_torch(qb, dt), sc.sm_scale)
     torch.cuda.synchronize()
-    o, l = out_to_f64(out, "bf16"), lse.double().cpu().numpy()
+    o, l = out_to_f64(out, dt), lse.double().cpu().numpy()
     if rows is not None:
         o, l = o[rows], l[rows]
     ref = att.causal_last(table, seq, f(qb), sc.sm_scale, rows=rows, with_magnitudes=True)
-    mx, mn, wo, wl = check_decode_both(o, l, ref, d, "bf16", label)
+    # bf16 pools with d = 128 restore by the tiled prefill (row sums over the rounded P,
+    # accumulator chains of up to 4,096 steps); others by rows of the split-K decode
+    tiled = dt == "bf16" and d == 128
+    mx, mn, wo, wl = check_decode_both(o, l, ref, d, dt, label, gamma=2.0 ** -12 if tiled else None,
+                                       rounded_p_sum=tiled)
     assert np.array_equal(pool.positions(seq), table.positions(seq))
     print(f"[ok] {label}: {len(o)} of {n_all} tokens, max-abs {mx:.3g} mean-abs {mn:.3g}; error / model bar: "
           f"O {wo:.3f}, LSE {wl:.3f}", flush=True)
@@ -65,6 +74,16 @@ def test_single_token_and_fresh_sequence():
     # a new root (id 2) filled by one segment of 300 tokens: plain causal attention
     sc.ops.append(("create",))
     _restore(sc, 2, [300], [0], 98, "fresh sequence, 300 tokens")
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 64)])
+def test_restore_by_decode_rows(dtype, d):
+    # pools the tiled prefill does not take (fp32, d = 64) restore as rows of the split-K
+    # decode; a fork with mounts-free context, two segments
+    sc = W.fork_scenario(prefix=333, branches=2, private=[20, 50], hq=8, hkv=2, d=d, dtype=dtype, rope_theta=1e4,
+                         seed=91)
+    sc.n_pages += 16
+    _restore(sc, 2, [70, 9], [3000, 5000], 90, f"restore {dtype} d={d} by decode rows")
 
 
 def test_restore_full_size():
