@@ -36,12 +36,27 @@ METRIC = "fork-decode branch-tokens/s + achieved HBM GB/s (% of peak); DAG-prefi
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_traffic.json")
+PREFILL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_kernel_traffic.json")
 PREFILL_FLOPS = 27488461783040  # 4 * 128 * 1,677,762,560 visible pairs * 32 query heads
 PREFILL_BWD_FLOPS = 68721154457600  # 10 * 128 * pairs * heads: S again, dP, dV, dK, dQ (2.5 x the forward)
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_traffic():
+    """HBM bytes per prefill_kernel launch (FETCH + WRITE) from the committed rocprofv3
+    runs, or None once the kernel source differs from the profiled one."""
+    import hashlib
+    try:
+        rec = json.load(open(PREFILL_TRAFFIC_FILE))
+        h = hashlib.sha256()
+        for f in rec["source_files"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["source_sha256"] else None
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def measured_traffic():
@@ -281,7 +296,7 @@ def bench_prefill(reps, warmup, cpu_budget=0.0):
         "block_pairs": mask.nnz,
         "visible_token_pairs": 1677762560,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": tflops / BF16_PEAK_TFLOPS, "traffic": prefill_traffic(),
                      "kernel": "prefill_kernel (dag_attn_run)", "algorithmic_flops_per_launch": PREFILL_FLOPS,
                      "kernel_ms_mean": t * 1e3, "kernel_ms_p10": float(np.percentile(run_ms, 10)),
                      "kernel_ms_p90": float(np.percentile(run_ms, 90))},
@@ -637,6 +652,22 @@ def measure_ceilings():
             ms.append(a.elapsed_time(e))
         out[label] = {"GBps": nbytes / (float(np.median(ms)) * 1e-3) / 1e9, "us_median": float(np.median(ms)) * 1e3}
         del bufs
+    # device-to-device copy of 1 GiB (torch's copy kernel): read + write traffic ceiling
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(3)
+    dst.copy_(src)
+    ms = []
+    for _ in range(5):
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        e.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(e))
+    out["copy_1GiB"] = {"GBps_read_plus_write": 2 * (1 << 30) / (float(np.median(ms)) * 1e-3) / 1e9,
+                        "us_median": float(np.median(ms)) * 1e3}
+    del src, dst
     n_iter, n_wg = 2000, 2048
     flops = 4 * 8 * n_iter * 32768 * n_wg
     fa.kv_probe_mfma_loop(200, n_wg, sink.data_ptr(), st)
@@ -651,8 +682,8 @@ def measure_ceilings():
     tf = flops / (float(np.median(ms)) * 1e-3) / 1e12
     out["mfma_bf16"] = {"TFLOPs": tf, "implied_clock_GHz": tf * 1e12 / (256 * 4096) / 1e9,
                         "us_median": float(np.median(ms)) * 1e3}
-    out["note"] = ("probe kernels of the library (kv_probe_stream_read, kv_probe_mfma_loop), HIP events, median of "
-                   "10 / 5 launches; the vendor peaks are 8,000 GB/s and 2,500 TFLOP/s")
+    out["note"] = ("probe kernels of the library (kv_probe_stream_read, kv_probe_mfma_loop) and torch's device copy, "
+                   "HIP events, median of 10 / 5 launches; the vendor peaks are 8,000 GB/s and 2,500 TFLOP/s")
     return out
 
 
@@ -890,6 +921,9 @@ def main():
     if ceilings and "prefill" in result:
         r = result["prefill"]["roofline"]
         r["frac_of_measured_mfma_ceiling"] = r["achieved"] / ceilings["mfma_bf16"]["TFLOPs"]
+    if ceilings and "akv" in result:
+        c = result["akv"]["compaction"]
+        c["frac_of_measured_copy_ceiling"] = c["GBps"] / ceilings["copy_1GiB"]["GBps_read_plus_write"]
     print(json.dumps(result))
 
 
