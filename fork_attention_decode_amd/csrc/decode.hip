@@ -237,7 +237,17 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, const int32_t
   const bool active = wave * 16 < rec[2];
   const int2 c0 = reinterpret_cast<const int2*>(rec + kRecChunk)[lane];
   const int2 c1 = reinterpret_cast<const int2*>(rec + kRecChunk)[64 + lane];
-  const int mp0 = c0.x, ml0 = c0.y, mp1 = c1.x, ml1 = c1.y;
+  const int mp0 = c0.x, mp1 = c1.x;
+  int ml0 = c0.y, ml1 = c1.y;
+  // a decode window: a reserved page's range ends at this step's length.  The table loads
+  // are issued before the ring's and applied after them, so they land during its fill
+  // (entries past the count are stale and never read)
+  // Both paths issue the same two loads (outside a window, of the record's first int), so
+  // the ring's first loads never wait for them.
+  const bool cut0 = p.cut_hi && lane < n && (ml0 >> 16), cut1 = p.cut_hi && 64 + lane < n && (ml1 >> 16);
+  const int32_t* tab = p.cut_hi ? p.cut_hi : rec;  // a window's table holds at least one entry
+  const int cv0 = tab[cut0 ? (ml0 >> 16) - 1 : 0];
+  const int cv1 = tab[cut1 ? (ml1 >> 16) - 1 : 0];
   const int orow = rec[kRecRow + wave * 16 + c16];
   const int slot = rec[kRecSlot + wave * 16 + c16];
 
@@ -284,6 +294,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, const int32_t
   for (int j = 0; j < NB - 2; ++j) issue(j);
   typename TR::KF qf[NF];  // queries load while the ring fills
   load_q_row<T, D>(p, orow, lane, qf);
+  auto cut = [](int lh, int e) {
+    const int lo = lh & 0xff, hi = (lh >> 8) & 0xff;
+    e = min(hi, max(lo, e));
+    return e > lo ? (lo | e << 8) : 0;
+  };
+  if (cut0) ml0 = cut(ml0, cv0);
+  if (cut1) ml1 = cut(ml1, cv1);
 
   const int n_pairs = (n + 1) / 2;
   for (int i = 0; i < n_pairs; ++i) {
@@ -404,6 +421,37 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   if (p.lse && half == 0 && lane == 0) p.lse[row] = S > 0.f ? (M + __log2f(S)) * 0.69314718055994531f : -INFINITY;
 }
 
+// ---- merge of few partials per row (a split-K prefill's key pieces): one thread per
+// (row, 4 dims), so a launch over tens of thousands of rows issues a few instructions per
+// partial instead of a wave-wide reduction per row.  The row's lse values are read by each
+// of its threads (the same addresses, served once per wave).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_few_kernel(MergeParams p) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  constexpr int TPR = D / 4;  // threads per row
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int row = (int)(gid / TPR), c = (int)(gid % TPR);
+  if (row >= p.n_rows) return;
+  const int cnt = p.count[row];
+  const size_t base = (size_t)row * p.max_parts;
+  float M = -INFINITY;
+  for (int j = 0; j < cnt; ++j) M = fmaxf(M, p.part_lse2[base + j]);
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  float S = 0.f;
+  if (M > -INFINITY) {
+    for (int j = 0; j < cnt; ++j) {
+      const float w = fast_exp2(p.part_lse2[base + j] - M);
+      S += w;
+      acc += w * *reinterpret_cast<const f4*>(p.part_o + (base + j) * D + 4 * c);
+    }
+  }
+  const float inv = S > 0.f ? 1.f / S : 0.f;
+  T* out = reinterpret_cast<T*>(p.out) + (size_t)row * D + 4 * c;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = from_f32<T>(acc[k] * inv);
+  if (p.lse && c == 0) p.lse[row] = S > 0.f ? (M + __log2f(S)) * 0.69314718055994531f : -INFINITY;
+}
+
 // kPolicy: kCachePolicyNT for a single pass over the pages; 0 (cached) where the same
 // pages are streamed again by other items of the launch
 template <typename T, int D, int kPolicy>
@@ -412,8 +460,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int it = blockIdx.x;
-  decode_item<T, D, kPolicy>(p, it < p.n_head ? p.items + (size_t)it * kRecInts : p.tail + (size_t)(it - p.n_head) * kRecInts,
-                    wave, lane, lds);
+  decode_item<T, D, kPolicy>(p, p.items + (size_t)it * kRecInts, wave, lane, lds);
 }
 
 // ---------------------------------------------------------------- page writes (append)
@@ -498,6 +545,22 @@ static hipError_t merge_t(const MergeParams& p, hipStream_t s) {
   if (p.n_rows == 0) return hipSuccess;
   merge_kernel<T, D><<<(p.n_rows * kMergeSplit + kWaves - 1) / kWaves, 256, 0, s>>>(p);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t merge_few_t(const MergeParams& p, hipStream_t s) {
+  if (p.n_rows == 0) return hipSuccess;
+  const int64_t threads = (int64_t)p.n_rows * (D / 4);
+  merge_few_kernel<T, D><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_few(int dtype, int d, const MergeParams& p, hipStream_t s) {
+  if (dtype == 0 && d == 128) return merge_few_t<bf16_t, 128>(p, s);
+  if (dtype == 0 && d == 64) return merge_few_t<bf16_t, 64>(p, s);
+  if (dtype == 1 && d == 128) return merge_few_t<float, 128>(p, s);
+  if (dtype == 1 && d == 64) return merge_few_t<float, 64>(p, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_merge(int dtype, int d, const MergeParams& p, hipStream_t s) {

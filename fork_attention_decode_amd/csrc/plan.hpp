@@ -49,12 +49,12 @@ struct DecodeParams {
   const void* q;            // [n_seqs][Hq][d]
   const void* k_pages;
   const void* v_pages;
-  const int32_t* items;     // [n_head][kRecInts]: items 0 .. n_head - 1
-  const int32_t* tail;      // [n_items - n_head][kRecInts]: the rest (a decode window's per-step items)
+  const int32_t* items;     // [n_items][kRecInts]
+  const int32_t* cut_hi;    // decode windows: per cut id, the slot end of that reserved page after this
+                            // step (a chunk whose lohi carries id + 1 in bits 16..31); null otherwise
   float* part_lse2;         // [n_partials] log2-domain log-sum-exp of the partial
   float* part_o;            // [n_partials][d] normalised partial output
   int32_t n_items;
-  int32_t n_head;
   int32_t cached;           // 1: cached loads (the launch streams the same pages several times)
   int32_t n_pages;          // pool capacity: head h's blocks start at h * n_pages
   float scale_log2;         // sm_scale * log2(e)
@@ -149,6 +149,8 @@ hipError_t launch_page_write(int dtype, int d, int hkv, int pool_pages, void* k_
                              int n_writes, hipStream_t s);
 hipError_t launch_decode(int dtype, int d, const DecodeParams& p, hipStream_t s);
 hipError_t launch_merge(int dtype, int d, const MergeParams& p, hipStream_t s);
+// the same merge for rows with few partials each (one thread per row and 4 dims)
+hipError_t launch_merge_few(int dtype, int d, const MergeParams& p, hipStream_t s);
 // ws[patches[2 i]] = patches[2 i + 1] for i < n (int offsets into a decode workspace;
 // distinct offsets)
 hipError_t launch_plan_patch(void* ws, const int32_t* patches, int n, hipStream_t s);

@@ -41,10 +41,17 @@ size_t fa_pool_ws_need(const kv_pool_config* c);
 
 namespace {
 
+// one visible run: slots [lo, hi) of a page read by query `reader` (12 bytes: the sort
+// moves tens of thousands of these per plan)
 struct Entry {
   int32_t page;
-  int32_t lo, hi;
-  int32_t reader;
+  int32_t rd;
+  uint16_t l, h;
+  Entry() = default;
+  Entry(int32_t p, int32_t lo, int32_t hi, int32_t reader) : page(p), rd(reader), l((uint16_t)lo), h((uint16_t)hi) {}
+  int32_t lo() const { return l; }
+  int32_t hi() const { return h; }
+  int32_t reader() const { return rd; }
 };
 
 struct Segment {
@@ -150,31 +157,68 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
   pc.pending.clear();
 
   // 1. visible runs
-  std::vector<Entry> ent;
+  std::vector<Seq*> qs((size_t)n);
+  size_t n_ent = 0;
   for (int32_t i = 0; i < n; ++i) {
-    Seq* S = fa_seq(P, seqs[i]);
-    if (!S) FAIL(P, KV_ERR_NOT_FOUND, "no live sequence in the query list");
+    qs[i] = fa_seq(P, seqs[i]);
+    if (!qs[i]) FAIL(P, KV_ERR_NOT_FOUND, "no live sequence in the query list");
+    const int64_t n_own = len_cap ? std::min<int64_t>(len_cap[i], qs[i]->n) : qs[i]->n;
+    n_ent += (size_t)((n_own + PS - 1) / PS);
+    for (const Mount& m : qs[i]->mounts) n_ent += m.pages.size();
+  }
+  // the entry buffers persist per thread: fresh ones of this size cost page faults
+  static thread_local std::vector<Entry> ent, sorted;
+  ent.clear();
+  ent.reserve(n_ent);
+  int32_t max_page = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* S = qs[i];
     const int64_t n_own = len_cap ? std::min<int64_t>(len_cap[i], S->n) : S->n;
-    for (size_t L = 0; (int64_t)L * PS < n_own; ++L)
+    for (size_t L = 0; (int64_t)L * PS < n_own; ++L) {
       ent.push_back({S->pages[L], 0, (int32_t)std::min<int64_t>(PS, n_own - (int64_t)L * PS), i});
+      max_page = std::max(max_page, S->pages[L]);
+    }
     for (const Mount& m : S->mounts) {
       for (size_t j = 0; j < m.pages.size(); ++j) {
         const int64_t a = std::max<int64_t>(0, m.off - (int64_t)j * PS);
         const int64_t b = std::min<int64_t>(PS, m.off + m.n - (int64_t)j * PS);
-        if (a < b) ent.push_back({m.pages[j], (int32_t)a, (int32_t)b, i});
+        if (a < b) {
+          ent.push_back({m.pages[j], (int32_t)a, (int32_t)b, i});
+          max_page = std::max(max_page, m.pages[j]);
+        }
       }
     }
   }
-  {  // stable radix sort by page id, 16 bits a pass (readers of a page keep query order);
-     // the cost follows the entries, not the pool's page count
-    std::vector<Entry> sorted(ent.size());
-    std::vector<int32_t> at((size_t)1 << 16 | 1);
-    for (int shift = 0; shift < 32 && (shift == 0 || (C.n_pages - 1) >> shift); shift += 16) {
-      std::fill(at.begin(), at.end(), 0);
-      for (const Entry& e : ent) at[((uint32_t)e.page >> shift & 0xffffu) + 1]++;
-      for (size_t d = 1; d < at.size(); ++d) at[d] += at[d - 1];
-      for (const Entry& e : ent) sorted[(size_t)at[(uint32_t)e.page >> shift & 0xffffu]++] = e;
+  {  // stable counting sort by page id (readers of a page keep query order): one pass when
+     // the page ids are dense enough for a histogram over all of them, else LSD radix
+     // passes of at most 11 bits
+    sorted.resize(ent.size());
+    if ((size_t)max_page + 1 <= std::max<size_t>(4096, 2 * ent.size())) {
+      std::vector<int32_t> h((size_t)max_page + 2, 0);
+      for (const Entry& e : ent) h[(size_t)e.page + 1]++;
+      for (size_t d = 1; d < h.size(); ++d) h[d] += h[d - 1];
+      for (const Entry& e : ent) sorted[(size_t)h[(size_t)e.page]++] = e;
       ent.swap(sorted);
+    } else {
+      int bits = 0;
+      while (bits < 31 && ((int64_t)1 << bits) <= max_page) ++bits;
+      const int n_pass = (bits + 10) / 11;
+      const int db = (bits + n_pass - 1) / n_pass;
+      const uint32_t mask = (1u << db) - 1;
+      std::vector<int32_t> hist((size_t)n_pass << db, 0);
+      for (const Entry& e : ent)
+        for (int k = 0; k < n_pass; ++k) hist[((size_t)k << db) + ((uint32_t)e.page >> (k * db) & mask)]++;
+      for (int k = 0; k < n_pass; ++k) {
+        int32_t* h = hist.data() + ((size_t)k << db);
+        int32_t run = 0;
+        for (uint32_t d = 0; d <= mask; ++d) {
+          const int32_t c = h[d];
+          h[d] = run;
+          run += c;
+        }
+        for (const Entry& e : ent) sorted[(size_t)h[(uint32_t)e.page >> (k * db) & mask]++] = e;
+        ent.swap(sorted);
+      }
     }
   }
 
@@ -206,18 +250,18 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
     size_t b = a;
     bool uniform = true;
     while (b < ent.size() && ent[b].page == ent[a].page) {
-      uniform = uniform && ent[b].lo == ent[a].lo && ent[b].hi == ent[a].hi;
+      uniform = uniform && ent[b].lo() == ent[a].lo() && ent[b].hi() == ent[a].hi();
       ++b;
     }
     if (uniform) {
       key.clear();
-      for (size_t e = a; e < b; ++e) key.push_back(ent[e].reader);
-      emit(ent[a].page, ent[a].lo, ent[a].hi, key);
+      for (size_t e = a; e < b; ++e) key.push_back(ent[e].reader());
+      emit(ent[a].page, ent[a].lo(), ent[a].hi(), key);
     } else {
       std::vector<int32_t> cuts;
       for (size_t e = a; e < b; ++e) {
-        cuts.push_back(ent[e].lo);
-        cuts.push_back(ent[e].hi);
+        cuts.push_back(ent[e].lo());
+        cuts.push_back(ent[e].hi());
       }
       std::sort(cuts.begin(), cuts.end());
       cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
@@ -226,7 +270,7 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
         for (size_t c = 0; c + 1 < cuts.size(); ++c) {
           key.clear();
           for (size_t e = a; e < b; ++e)
-            if (ent[e].lo <= cuts[c] && ent[e].hi >= cuts[c + 1]) key.push_back(ent[e].reader);
+            if (ent[e].lo() <= cuts[c] && ent[e].hi() >= cuts[c + 1]) key.push_back(ent[e].reader());
           if (!key.empty()) emit(ent[a].page, cuts[c], cuts[c + 1], key);
         }
       } else {
@@ -234,18 +278,18 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
         // the readers of the most common range share one chunk, every other reader reads
         // its own range alone, instead of one reader set per distinct range
         std::map<std::pair<int32_t, int32_t>, int32_t> freq;
-        for (size_t e = a; e < b; ++e) ++freq[{ent[e].lo, ent[e].hi}];
+        for (size_t e = a; e < b; ++e) ++freq[{ent[e].lo(), ent[e].hi()}];
         std::pair<int32_t, int32_t> top = freq.begin()->first;
         for (const auto& f : freq)
           if (f.second > freq[top]) top = f.first;
         key.clear();
         for (size_t e = a; e < b; ++e)
-          if (ent[e].lo == top.first && ent[e].hi == top.second) key.push_back(ent[e].reader);
+          if (ent[e].lo() == top.first && ent[e].hi() == top.second) key.push_back(ent[e].reader());
         emit(ent[a].page, top.first, top.second, key);
         for (size_t e = a; e < b; ++e)
-          if (!(ent[e].lo == top.first && ent[e].hi == top.second)) {
-            key.assign(1, ent[e].reader);
-            emit(ent[a].page, ent[e].lo, ent[e].hi, key);
+          if (!(ent[e].lo() == top.first && ent[e].hi() == top.second)) {
+            key.assign(1, ent[e].reader());
+            emit(ent[a].page, ent[e].lo(), ent[e].hi(), key);
           }
       }
     }
@@ -267,9 +311,9 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
   struct Item {
     int32_t chunk_begin, n_chunks, kv_head, rows;
     const Segment* seg;
-    size_t g0;
-    std::vector<int32_t> orow;
+    int32_t g0;
   };
+  auto orow_of = [&](const Item& it, int32_t r) { return it.seg->readers[(size_t)it.g0 + r / G] * hq + it.kv_head * G + r % G; };
   std::vector<Item> items;
   int64_t unique_tokens = 0, n_chunks_total = 0;
   const int32_t n_out = n * hq;
@@ -285,13 +329,8 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
       for (int32_t h = 0; h < C.n_kv_heads; ++h) {
         for (int32_t t = 0; t < n_it; ++t) {
           const int32_t c0 = (int32_t)((int64_t)nc * t / n_it), c1 = (int32_t)((int64_t)nc * (t + 1) / n_it);
-          Item it{c0, c1 - c0, h, rows, &s, g0, {}};
-          for (int32_t r = 0; r < rows; ++r) {
-            const int32_t orow = s.readers[g0 + r / G] * hq + h * G + r % G;
-            it.orow.push_back(orow);
-            row_count[orow]++;
-          }
-          items.push_back(std::move(it));
+          items.push_back(Item{c0, c1 - c0, h, rows, &s, (int32_t)g0});
+          for (int32_t r = 0; r < rows; ++r) row_count[(size_t)orow_of(items.back(), r)]++;
         }
       }
     }
@@ -327,16 +366,18 @@ static int build_plan(kv_pool* P, const kv_seq_t* seqs, int32_t n, int32_t hq, c
     rec[1] = it.kv_head;
     rec[2] = it.rows;
     rec[3] = 0;
-    for (int32_t r = 0; r < kMaxRows; ++r) {
-      rec[kRecRow + r] = r < it.rows ? it.orow[r] : -1;
-      rec[kRecSlot + r] = r < it.rows ? it.orow[r] * max_parts + fill[it.orow[r]]++ : 0;
+    for (int32_t r = 0; r < it.rows; ++r) {
+      const int32_t o = orow_of(it, r);
+      rec[kRecRow + r] = o;
+      rec[kRecSlot + r] = o * max_parts + fill[(size_t)o]++;
+    }
+    for (int32_t r = it.rows; r < kMaxRows; ++r) {
+      rec[kRecRow + r] = -1;
+      rec[kRecSlot + r] = 0;
     }
     n_part += it.rows;
-    for (int32_t c = 0; c < it.n_chunks; ++c) {
-      const Chunk& ch = it.seg->chunks[it.chunk_begin + c];
-      rec[kRecChunk + 2 * c] = ch.page;
-      rec[kRecChunk + 2 * c + 1] = ch.lohi;
-    }
+    static_assert(sizeof(Chunk) == 2 * sizeof(int32_t), "chunk records are (page, lohi) int pairs");
+    std::memcpy(rec + kRecChunk, it.seg->chunks.data() + it.chunk_begin, (size_t)it.n_chunks * sizeof(Chunk));
   }
   put(pc.blob, pc.off_mptr, mptr);
   // what a later patch needs (decode plans): each query's tail page chunk and the last
@@ -470,8 +511,7 @@ static hipError_t launch_partials(kv_pool_t* P, const void* q, float sm_scale, c
   dp.k_pages = P->k;
   dp.v_pages = P->v;
   dp.items = reinterpret_cast<const int32_t*>(w + pc.off_items);
-  dp.tail = dp.items;
-  dp.n_head = pc.n_items;
+  dp.cut_hi = nullptr;
   dp.cached = 0;
   dp.part_lse2 = reinterpret_cast<float*>(w + pc.off_plse);
   dp.part_o = reinterpret_cast<float*>(w + pc.off_po);
@@ -561,9 +601,12 @@ int fork_attn_decode(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, 
 // Agentrix (the ForkAttention section) and AgentKV run fork attention inside a captured
 // decode loop; a window reserves the slots of the next n_steps tokens of every sequence
 // (tail copy-on-write and new pages, in exactly the order n_steps rounds of one append
-// per sequence would take them) and plans each step's decode once, so a step is three
+// per sequence would take them) and plans the decode once over the contexts through the
+// window's last token; a chunk of a reserved page carries a cut id, and each step has a
+// small table giving every id the page's slot end after that step.  A step is three
 // launches with fixed arguments: the new K / V into their reserved slots, the split-K
-// partials, the merge.
+// partials (every item shared by all steps, reserved chunks cut by the step's table),
+// the merge.
 
 int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, int32_t n_steps, size_t* ws_need) {
   if (!P || !ws_need) FAIL(P, KV_ERR_INVALID, "null argument");
@@ -630,58 +673,61 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
     return e;  // the page table keeps the reservation; the window is unusable
   }
   DecodePlanCache& pc = P->plan;
-  // the chunk records of reserved pages: (record int, query index, logical page)
-  std::unordered_map<int32_t, int64_t> owner;  // reserved page -> i * 2^32 + logical page
+  // chunks of reserved pages carry a cut id (bits 16..31 of their slot range, id + 1):
+  // one per (query, reserved logical page), shared by the KV heads; step st's table gives
+  // each id the slot end of its page after st + 1 window tokens
+  std::unordered_map<int32_t, int32_t> cut_of;  // reserved page -> cut id
+  std::vector<std::pair<int32_t, int64_t>> cuts;  // cut id -> (query, first token of the page)
   for (int32_t i = 0; i < n; ++i) {
     Seq* S = fa_seq(P, seqs[i]);
-    for (int64_t L = base[i] / PS; L < (int64_t)S->pages.size(); ++L)
-      owner[S->pages[(size_t)L]] = ((int64_t)i << 32) | L;
-  }
-  // items that read a reserved page form the per-step tail (their slot ranges change
-  // with the step); the rest, and the merge counts, are shared by every step
-  const int32_t* recs0 = reinterpret_cast<const int32_t*>(pc.blob.data() + pc.off_items);
-  std::vector<int32_t> head, tail;
-  for (int32_t it = 0; it < pc.n_items; ++it) {
-    const int32_t* rec = recs0 + (size_t)it * kRecInts;
-    bool mine = false;
-    for (int32_t c = 0; c < rec[0] && !mine; ++c) mine = owner.count(rec[kRecChunk + 2 * c]) != 0;
-    (mine ? tail : head).push_back(it);
-  }
-  struct Patch {
-    size_t at;  // int offset in the tail records
-    int32_t i;
-    int64_t L;
-  };
-  std::vector<Patch> patches;
-  for (size_t t = 0; t < tail.size(); ++t) {
-    const int32_t* rec = recs0 + (size_t)tail[t] * kRecInts;
-    for (int32_t c = 0; c < rec[0]; ++c) {
-      const auto f = owner.find(rec[kRecChunk + 2 * c]);
-      if (f == owner.end()) continue;
-      const int64_t o = f->second;
-      patches.push_back({t * kRecInts + kRecChunk + 2 * c + 1, (int32_t)(o >> 32), o & 0xffffffff});
+    for (int64_t L = base[i] / PS; L < (int64_t)S->pages.size(); ++L) {
+      cut_of[S->pages[(size_t)L]] = (int32_t)cuts.size();
+      cuts.push_back({i, L * PS});
     }
   }
-  const size_t rec_bytes = (size_t)kRecInts * sizeof(int32_t);
+  if (cuts.size() >= ((size_t)1 << 15) - 1) {
+    P->plan.valid = false;
+    W = DecodeWindow();
+    FAIL(P, KV_ERR_UNSUPPORTED, "too many reserved pages in one window");
+  }
+  // items that read a reserved page go last (measured: the window's steps are slower with
+  // them first, in plain heaviest-first order)
+  int32_t* recs0 = reinterpret_cast<int32_t*>(pc.blob.data() + pc.off_items);
+  std::vector<int32_t> plain, with_cut;
+  for (int32_t it = 0; it < pc.n_items; ++it) {
+    int32_t* rec = recs0 + (size_t)it * kRecInts;
+    bool any = false;
+    for (int32_t c = 0; c < rec[0]; ++c) {
+      const auto f = cut_of.find(rec[kRecChunk + 2 * c]);
+      if (f != cut_of.end()) {
+        rec[kRecChunk + 2 * c + 1] |= (f->second + 1) << 16;
+        any = true;
+      }
+    }
+    (any ? with_cut : plain).push_back(it);
+  }
+  if (!with_cut.empty()) {
+    std::vector<int32_t> moved((size_t)pc.n_items * kRecInts);
+    size_t at = 0;
+    for (const std::vector<int32_t>* list : {&plain, &with_cut})
+      for (int32_t it : *list) std::memcpy(moved.data() + kRecInts * at++, recs0 + (size_t)it * kRecInts, kRecInts * sizeof(int32_t));
+    std::memcpy(recs0, moved.data(), moved.size() * sizeof(int32_t));
+  }
   size_t off = 0;
   W.off_cow = off;
   off = align256(off + cow.size() * sizeof(PageWrite));
-  const size_t off_head = off;
-  off = align256(off + head.size() * rec_bytes);
-  const size_t off_mptr = off;
-  const size_t mptr_bytes = (size_t)pc.n_out_rows * sizeof(int32_t);
-  off = align256(off + mptr_bytes);
+  const size_t plan_at = off;  // the plan image (items, merge counts), shared by every step
+  off = align256(off + pc.blob.size());
   W.steps.resize((size_t)n_steps);
   for (int32_t st = 0; st < n_steps; ++st) {
     DecodeWindow::Step& ws = W.steps[st];
-    ws.off_items = off_head;
-    ws.off_mptr = off_mptr;
-    ws.n_head = (int32_t)head.size();
+    ws.off_items = plan_at + pc.off_items;
+    ws.off_mptr = plan_at + pc.off_mptr;
     ws.n_items = pc.n_items;
     ws.n_out_rows = pc.n_out_rows;
     ws.max_parts = pc.max_parts;
-    ws.off_plan = off;  // this step's tail records
-    off = align256(off + tail.size() * rec_bytes);
+    ws.off_cut = off;
+    off = align256(off + std::max<size_t>(1, cuts.size()) * sizeof(int32_t));
     ws.off_writes = off;
     off = align256(off + (size_t)n * sizeof(PageWrite));
   }
@@ -693,20 +739,13 @@ int kv_window_plan(kv_pool_t* P, const kv_seq_t* seqs, int32_t n, int32_t hq, in
   W.ws_need = std::max<size_t>(off, 256);
   W.blob.resize(W.off_plse);  // alignment gaps are never read
   if (!cow.empty()) std::memcpy(W.blob.data() + W.off_cow, cow.data(), cow.size() * sizeof(PageWrite));
-  for (size_t h = 0; h < head.size(); ++h)
-    std::memcpy(W.blob.data() + off_head + h * rec_bytes, recs0 + (size_t)head[h] * kRecInts, rec_bytes);
-  std::memcpy(W.blob.data() + off_mptr, pc.blob.data() + pc.off_mptr, mptr_bytes);
+  std::memcpy(W.blob.data() + plan_at, pc.blob.data(), pc.blob.size());
   for (int32_t st = 0; st < n_steps; ++st) {
     const DecodeWindow::Step& ws = W.steps[st];
-    int32_t* recs = reinterpret_cast<int32_t*>(W.blob.data() + ws.off_plan);
-    for (size_t t = 0; t < tail.size(); ++t)
-      std::memcpy(recs + t * kRecInts, recs0 + (size_t)tail[t] * kRecInts, rec_bytes);
-    for (const Patch& q : patches) {
-      const int64_t len = base[q.i] + st + 1 - q.L * PS;  // valid slots of the page after step st
-      const int32_t lohi = recs[q.at], lo = lohi & 0xff, hi = lohi >> 8;
-      const int32_t nh = (int32_t)std::min<int64_t>(hi, std::max<int64_t>(lo, len));
-      recs[q.at] = nh > lo ? (lo | nh << 8) : 0;
-    }
+    int32_t* cut = reinterpret_cast<int32_t*>(W.blob.data() + ws.off_cut);
+    cut[0] = 0;
+    for (size_t c = 0; c < cuts.size(); ++c)
+      cut[c] = (int32_t)std::max<int64_t>(0, std::min<int64_t>(PS, base[cuts[c].first] + st + 1 - cuts[c].second));
     std::memcpy(W.blob.data() + ws.off_writes, writes[st].data(), (size_t)n * sizeof(PageWrite));
   }
   P->plan.valid = false;  // the cached plan now describes the window's last step only
@@ -755,8 +794,7 @@ int kv_window_step(kv_pool_t* P, int32_t step, const void* k, const void* v, con
     dp.k_pages = P->k;
     dp.v_pages = P->v;
     dp.items = reinterpret_cast<const int32_t*>(w + ws.off_items);
-    dp.tail = reinterpret_cast<const int32_t*>(w + ws.off_plan);
-    dp.n_head = ws.n_head;
+    dp.cut_hi = reinterpret_cast<const int32_t*>(w + ws.off_cut);
     dp.cached = 0;
     dp.part_lse2 = reinterpret_cast<float*>(w + W.off_plse);
     dp.part_o = reinterpret_cast<float*>(w + W.off_po);
@@ -968,7 +1006,7 @@ int kv_causal_attend(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t n_q_heads, c
       mp.out = out;
       mp.lse = lse;
       mp.n_rows = (int32_t)(n * n_q_heads);
-      e = launch_merge(P->cfg.dtype, P->cfg.head_dim, mp, s);
+      e = launch_merge_few(P->cfg.dtype, P->cfg.head_dim, mp, s);
     }
     if (e != hipSuccess) FAIL(P, KV_ERR_HIP, std::string("causal attention: ") + hipGetErrorString(e));
     return KV_OK;
@@ -988,8 +1026,7 @@ int kv_causal_attend(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t n_q_heads, c
     dp.k_pages = P->k;
     dp.v_pages = P->v;
     dp.items = reinterpret_cast<const int32_t*>(w + pc.off_items);
-    dp.tail = dp.items;
-    dp.n_head = pc.n_items;
+    dp.cut_hi = nullptr;
     dp.cached = 1;  // every context page is streamed once per group of 64 / G restored tokens
     dp.part_lse2 = reinterpret_cast<float*>(w + pc.off_plse);
     dp.part_o = reinterpret_cast<float*>(w + pc.off_po);

@@ -102,10 +102,10 @@ struct DecodePlanCache {
 // one decode plan per step, so each step is a fixed set of kernel launches.
 struct DecodeWindow {
   struct Step {
-    size_t off_plan = 0;   // this step's tail item records
-    size_t off_items = 0;  // the head item records (shared by every step)
+    size_t off_cut = 0;    // this step's slot end per cut id (reserved pages)
+    size_t off_items = 0;  // the item records (shared by every step)
     size_t off_mptr = 0, off_writes = 0;
-    int32_t n_head = 0, n_items = 0, n_out_rows = 0, max_parts = 1;
+    int32_t n_items = 0, n_out_rows = 0, max_parts = 1;
   };
   bool valid = false;
   uint64_t version = 0;
@@ -113,7 +113,7 @@ struct DecodeWindow {
   int32_t n_q_heads = 0, n_steps = 0, n_cow = 0;
   size_t off_cow = 0, off_plse = 0, off_po = 0, ws_need = 0;
   std::vector<Step> steps;
-  std::vector<char> blob;  // plans, step writes and tail copies, at their workspace offsets
+  std::vector<char> blob;  // plan, per-step cut tables and writes, at their workspace offsets
   void* ws = nullptr;
 };
 

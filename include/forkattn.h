@@ -338,8 +338,9 @@ int dag_attn_run(const void* q, void* out, float* lse, int32_t T, int32_t n_q_he
  *     that step's token) on the host; *ws_need = workspace bytes.  Works on
  *     metadata-only pools too (page table only).  Sequences must be distinct; n_q_heads
  *     as for fork_attn_decode.  KV_ERR_OOM leaves everything unchanged.
- *   kv_window_upload: uploads the plans into `workspace` (DEVICE, >= ws_need bytes,
- *     caller-owned, used by every step) and enqueues the tail copies.
+ *   kv_window_upload: uploads the plan (one image shared by every step, plus each
+ *     step's slot ends of the reserved pages) into `workspace` (DEVICE, >= ws_need
+ *     bytes, caller-owned, used by every step) and enqueues the tail copies.
  *   kv_window_step(step): writes k, v (DEVICE [n][Hkv][d], pool dtype, keys rotated for
  *     their reserved positions) into the step's slots and decodes q (DEVICE
  *     [n][Hq][d]) into out / lse as fork_attn_decode would over the contexts through
@@ -362,8 +363,10 @@ int kv_window_step(kv_pool_t* pool, int32_t step, const void* k, const void* v, 
  * ended at that token.  q: DEVICE [n][Hq][d] (pool dtype, rotated by the caller); out:
  * DEVICE [n][Hq][d]; lse: DEVICE fp32 [n][Hq] or NULL.  workspace: DEVICE, at least
  * kv_causal_attend_workspace_size bytes for the same sequence state, n and n_q_heads.
- * The attention runs as n rows of one split-K decode (every context page is read once
- * per group of 64 / G rows).  1 <= n <= the sequence's length.  Stream-ordered. */
+ * bf16 pools with d = 128 run it as one tiled prefill: the visible keys are relaid once
+ * into matrix-core operand images, 64 of the n tokens and one piece of the key range per
+ * workgroup, then the pieces are merged by log-sum-exp; other pools run n rows of one
+ * split-K decode.  1 <= n <= the sequence's length.  Stream-ordered. */
 int kv_causal_attend_workspace_size(kv_pool_t* pool, kv_seq_t seq, int64_t n, int32_t n_q_heads,
                                     size_t* bytes);
 int kv_causal_attend(kv_pool_t* pool, kv_seq_t seq, int64_t n, int32_t n_q_heads, const void* q,
