@@ -69,6 +69,27 @@ def test_ragged_fork_bf16(private):
     _check(sc, o, lse, f"ragged fork {private}")
 
 
+def test_edge_shapes_bf16():
+    """Degenerate and maximal shapes: 64 query heads on one KV head (a work item's full 64
+    rows from one reader), a branch with no private token, the root decoding beside its
+    forks, one sequence listed twice, and an empty query list."""
+    import dataclasses
+    import torch
+    sc = W.fork_scenario(prefix=100, branches=3, private=[0, 5, 40], hq=64, hkv=1, d=128, seed=11)
+    pool, o, lse = _run(sc, "64 query heads on one KV head")
+    _check(sc, o, lse, "64 query heads on one KV head")
+    # root (0), branch 2 twice, branch 1: rows 1 and 2 read the same context with different queries
+    sc2 = dataclasses.replace(sc, queries=[0, 2, 2, 1], q=sc.q[[0, 1, 2, 0]])
+    out, lse2 = pool.decode(sc2.queries, to_torch(sc2.q, sc2.dtype), sc2.sm_scale)
+    torch.cuda.synchronize()
+    _check(sc2, out_to_f64(out, sc2.dtype), lse2.double().cpu().numpy(), "root + repeated sequence")
+    # an empty query list: no launch, nothing written
+    q0 = torch.empty((0, sc.n_q_heads, sc.head_dim), dtype=torch.bfloat16, device="cuda")
+    out0, lse0 = pool.decode([], q0, sc.sm_scale)
+    torch.cuda.synchronize()
+    assert out0.shape == (0, sc.n_q_heads, sc.head_dim) and lse0.shape == (0, sc.n_q_heads)
+
+
 def test_many_rows_split_groups_bf16():
     # 20 branches x G=8 rows -> 160 rows on the shared prefix: three reader groups
     sc = W.fork_scenario(prefix=300, branches=20, private=5, hq=16, hkv=2, d=128, seed=9)
