@@ -141,6 +141,8 @@ struct RestoreLaunch {
   float* part_o;
   int32_t T, n_own, q_off, nq, hq, hkv, n_rows, n_split;
   float sm_scale;
+  bool kgather;  // K read straight from the pool (kimg unused): the visible keys in whole pages,
+  const int32_t* gpages;  // gpages[g] = the page of keys 16 g .. 16 g + 15 (padded to 4 per 64-key block)
 };
 constexpr int kRestoreImgBytes = 16384;  // one 64-key image block of one KV head (K or V)
 

@@ -23,6 +23,7 @@
 #include <atomic>
 #include <cstring>
 #include <map>
+#include <climits>
 #include <unordered_map>
 
 using namespace fa;
@@ -910,14 +911,29 @@ static int restore_plan(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t hq) {
     return row_ptr[a + 1] - row_ptr[a] > row_ptr[b + 1] - row_ptr[b];
   });
   std::vector<int32_t> count((size_t)(n * hq), n_split);
+  // K is read straight from the pool when the visible keys fill whole pages in order (own
+  // tokens always do; mounts when they start on a page boundary) and one KV head's blocks
+  // fit a 2 GiB buffer range; else it is relaid into images like V.  gpages[g] = the page
+  // of keys 16 g .. 16 g + 15 (4 per 64-key block; padding and a partial last page point
+  // at valid pages, their keys are masked)
+  std::vector<int32_t> gpages((size_t)nb * 4, 0);
+  bool aligned = PS == 16;
+  for (int64_t t = 0; t < T && aligned; ++t) {
+    const int32_t loc = locs[(size_t)t];
+    if (t % 16 == 0) gpages[(size_t)(t / 16)] = loc >> 4;
+    aligned = loc == gpages[(size_t)(t / 16)] * 16 + (int32_t)(t % 16);
+  }
+  for (size_t g = (size_t)((T + 15) / 16); g < gpages.size() && g > 0; ++g) gpages[g] = gpages[g - 1];
+  R.kgather = aligned && (int64_t)C.n_pages * 16 * C.head_dim * 2 <= INT32_MAX;
   size_t off = 0;
   R.off_locs = off; off = align256(off + locs.size() * 4);
   R.off_rowptr = off; off = align256(off + row_ptr.size() * 4);
   R.off_ent = off; off = align256(off + std::max<size_t>(1, ent.size()) * 4);
   R.off_order = off; off = align256(off + order.size() * 4);
   R.off_count = off; off = align256(off + count.size() * 4);
+  R.off_gpages = off; off = align256(off + gpages.size() * 4);
   const size_t blob_bytes = off;
-  R.off_kimg = off; off += (size_t)H * nb * kRestoreImgBytes;
+  R.off_kimg = off; off += R.kgather ? 0 : (size_t)H * nb * kRestoreImgBytes;
   R.off_vimg = off; off += (size_t)H * nb * kRestoreImgBytes;
   off = align256(off);
   R.off_plse = off; off = align256(off + (size_t)n * hq * n_split * 4);
@@ -929,6 +945,7 @@ static int restore_plan(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t hq) {
   if (!ent.empty()) std::memcpy(R.blob.data() + R.off_ent, ent.data(), ent.size() * 4);
   std::memcpy(R.blob.data() + R.off_order, order.data(), order.size() * 4);
   std::memcpy(R.blob.data() + R.off_count, count.data(), count.size() * 4);
+  std::memcpy(R.blob.data() + R.off_gpages, gpages.data(), gpages.size() * 4);
   R.T = (int32_t)T;
   R.n_own = (int32_t)N;
   R.n_rows = n_rows;
@@ -995,6 +1012,8 @@ int kv_causal_attend(kv_pool_t* P, kv_seq_t seq, int64_t n, int32_t n_q_heads, c
       rl.n_rows = R.n_rows;
       rl.n_split = R.n_split;
       rl.sm_scale = sm_scale;
+      rl.kgather = R.kgather;
+      rl.gpages = reinterpret_cast<const int32_t*>(w + R.off_gpages);
       e = fa_launch_restore(rl, s);
     }
     if (e == hipSuccess) {

@@ -126,10 +126,11 @@ struct RestorePlan {
   kv_seq_t seq = -1;
   int64_t n = 0;
   int32_t hq = 0;
-  std::vector<char> blob;  // [locs | row_ptr | ent | order | counts], uploaded
-  size_t off_locs = 0, off_rowptr = 0, off_ent = 0, off_order = 0, off_count = 0;
+  std::vector<char> blob;  // [locs | row_ptr | ent | order | counts | page per 16 keys], uploaded
+  size_t off_locs = 0, off_rowptr = 0, off_ent = 0, off_order = 0, off_count = 0, off_gpages = 0;
   size_t off_kimg = 0, off_vimg = 0, off_plse = 0, off_po = 0, ws_need = 0;
   int32_t T = 0, n_own = 0, n_rows = 0, n_split = 1;
+  bool kgather = false;  // K read straight from the pool by the prefill kernel (no K images)
   void* ws = nullptr;  // workspace the blob was last uploaded to
 };
 

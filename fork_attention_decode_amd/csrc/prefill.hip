@@ -75,6 +75,11 @@ struct Params {
   int32_t n_split;
   float* part_lse2;
   float* part_o;
+  // K gathered from the pool (restore of a pool sequence): head h's K blocks at
+  // kpool + (h * pool_pages + page) * 4 KiB; keys 16 g .. 16 g + 15 of the context are
+  // slots 0..15 of page gpages[g] (the kernel's gpages argument)
+  const char* kpool;
+  int32_t pool_pages;
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -173,10 +178,15 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 //
 // 8 waves, two per SIMD (waves w and w + 4 share one): wave w takes query head slot
 // w / 2 and tokens [q0 + 32 (w % 2), +32) of the block.
-template <bool kSplit>
+// kMode 0: the packed prefill; 1: split-K pieces over K / V images; 2: split-K pieces with
+// K gathered straight from the page pool (V from its image).
+template <int kMode>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32_t* __restrict__ row_ptr,
                                                           const int32_t* __restrict__ ent,
-                                                          const int32_t* __restrict__ order) {
+                                                          const int32_t* __restrict__ order,
+                                                          const int32_t* __restrict__ gpages) {
+  constexpr bool kSplit = kMode != 0, kGather = kMode == 2;
+  constexpr int kLPW = kLoadsPerWave;  // vector-memory operations per stage per wave
   __shared__ __attribute__((aligned(1024))) char ring[kStages * kStage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in a scalar register
@@ -205,9 +215,29 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
   auto ent_of = [&](int j) { return ent[j0 + (j < n ? j : n - 1)]; };
   auto col_of = [&](int j) { return ent_of(j) & ~kDiagBit; };
   auto issue = [&](int j) {  // past the end: reload the last block into a slot nobody reads
+    char* dst = ring + (j % kStages) * kStage + my_off;
+    if constexpr (kGather) {
+      if (wave < 4) {
+        // K unit (kt, ks, lane) = K[32 kt + lane % 32][16 ks + 8 (lane / 32) ..], kt = wave / 2:
+        // slot (f, g, t) of its page block, f = ks / 2, g = 2 (ks % 2) + lane / 32, t = lane % 16
+        // (the block's page ids are scalar loads)
+        const int kt = wave >> 1;
+        const int g0 = 4 * col_of(j) + 2 * kt;
+        const int pg0 = gpages[g0], pg1 = gpages[g0 + 1];  // wave-uniform: scalar loads
+        const int pg = lo < 16 ? pg0 : pg1, slot = lo & 15;
+        const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.kpool + (size_t)h * p.pool_pages * 4096), 0, p.pool_pages * 4096, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < kLoadsPerWave; ++i) {
+          const int ks = 4 * (wave & 1) + i, f = ks >> 1, g = 2 * (ks & 1) + hi;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                                                   16, pg * 4096 + ((f * 4 + g) * 16 + slot) * 16, 0, 0, 0);
+        }
+        return;
+      }
+    }
     const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(my_img + (size_t)col_of(j) * kImg), 0, kLoadsPerWave * 1024, 0x00020000);
-    char* dst = ring + (j % kStages) * kStage + my_off;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
@@ -296,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
   bool resc = false;
   auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     const int e1 = ent_of(j + 1);
-    wait_vmcnt<kLoadsPerWave>();             // this wave's part of block j + 1 landed (j + 2 in flight)
+    wait_vmcnt<kLPW>();                      // this wave's part of block j + 1 landed (j + 2 in flight)
     asm volatile("s_barrier" ::: "memory");  // ... every wave's; slot j - 1 is consumed by all
     issue(j + 3);
     if (resc) {  // wave-uniform, rare: the new maximum outgrew the stale one by more than tau
@@ -382,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
     issue(0);
     issue(1);
     issue(2);
-    wait_vmcnt<2 * kLoadsPerWave>();         // block 0 landed for this wave ...
+    wait_vmcnt<2 * kLPW>();                  // block 0 landed for this wave ...
     asm volatile("s_barrier" ::: "memory");  // ... and for every wave
     scores(0, sa);
     mask(ent_of(0), sa);
@@ -438,7 +468,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
 // K[slot][32 f + 8 g .. + 8], V^T element d * 16 + slot); keys >= T read as zero.
 __global__ __launch_bounds__(256) void page_relayout_kernel(const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
                                                             const int32_t* __restrict__ locs, char* __restrict__ kimg,
-                                                            char* __restrict__ vimg, int T, int nb, int pool_pages) {
+                                                            char* __restrict__ vimg, int T, int nb, int pool_pages,
+                                                            bool with_k) {
   const int c = blockIdx.x, h = blockIdx.y;
   const size_t img = ((size_t)h * nb + c) * kImg;
   const size_t head = (size_t)h * pool_pages;
@@ -446,7 +477,7 @@ __global__ __launch_bounds__(256) void page_relayout_kernel(const bf16_t* __rest
   for (int i = 0; i < 4; ++i) {
     const int s = i * 256 + threadIdx.x;
     const int lane = s & 63;
-    {  // K slot (kt, ks, lane): K[32 kt + lane % 32][16 ks + 8 (lane / 32) + 0..7]
+    if (with_k) {  // K slot (kt, ks, lane): K[32 kt + lane % 32][16 ks + 8 (lane / 32) + 0..7]
       const int ks = (s >> 6) & 7, kt = s >> 9;
       const int key = c * kB + 32 * kt + (lane & 31);
       i32x4 val = {0, 0, 0, 0};
@@ -585,8 +616,11 @@ extern "C" int dag_attn_run(const void* q, void* out, float* lse, int32_t T, int
   p.n_own = T;
   p.n_split = 1;
   p.part_lse2 = p.part_o = nullptr;
-  prefill_kernel<false><<<(size_t)p.nb * n_kv_heads * p.n_hg, kThreads, 0, stream>>>(
-      p, row_ptr, reinterpret_cast<const int32_t*>(ws + w.ent), reinterpret_cast<const int32_t*>(ws + w.order));
+  p.kpool = nullptr;
+  p.pool_pages = 0;
+  prefill_kernel<0><<<(size_t)p.nb * n_kv_heads * p.n_hg, kThreads, 0, stream>>>(
+      p, row_ptr, reinterpret_cast<const int32_t*>(ws + w.ent), reinterpret_cast<const int32_t*>(ws + w.order),
+      nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill: ") + hipGetErrorString(e));
   return KV_OK;
@@ -608,14 +642,16 @@ extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, voi
 }
 
 // Restore of a sequence's last tokens as a split-K tiled prefill over its pages: the
-// visible keys are relaid into operand-order images, then the prefill kernel runs the
-// CSR rows (query block, key-range piece) and writes one partial per (query row, head,
-// piece), merged afterwards by the decode merge.
+// visible keys' V (and K, unless the keys fill whole pages in order) are relaid into
+// operand-order images, then the prefill kernel runs the CSR rows (query block, key-range
+// piece), gathering K straight from the page blocks where it can (a page block's 16-byte
+// K slots are the image's units, so the copy into LDS only needs per-lane offsets), and
+// writes one partial per (query row, head, piece), merged afterwards.
 hipError_t fa::fa_launch_restore(const RestoreLaunch& r, hipStream_t stream) {
   const int nb = (r.T + kB - 1) / kB;
   page_relayout_kernel<<<dim3(nb, r.hkv), 256, 0, stream>>>(static_cast<const bf16_t*>(r.k_pages),
                                                             static_cast<const bf16_t*>(r.v_pages), r.locs, r.kimg,
-                                                            r.vimg, r.T, nb, r.pool_pages);
+                                                            r.vimg, r.T, nb, r.pool_pages, !r.kgather);
   Params p;
   p.q = static_cast<const bf16_t*>(r.q);
   p.kimg = r.kimg;
@@ -636,6 +672,12 @@ hipError_t fa::fa_launch_restore(const RestoreLaunch& r, hipStream_t stream) {
   p.n_split = r.n_split;
   p.part_lse2 = r.part_lse2;
   p.part_o = r.part_o;
-  prefill_kernel<true><<<(size_t)r.n_rows * r.hkv * p.n_hg, kThreads, 0, stream>>>(p, r.row_ptr, r.ent, r.order);
+  p.kpool = static_cast<const char*>(r.k_pages);
+  p.pool_pages = r.pool_pages;
+  const size_t grid = (size_t)r.n_rows * r.hkv * p.n_hg;
+  if (r.kgather)
+    prefill_kernel<2><<<grid, kThreads, 0, stream>>>(p, r.row_ptr, r.ent, r.order, r.gpages);
+  else
+    prefill_kernel<1><<<grid, kThreads, 0, stream>>>(p, r.row_ptr, r.ent, r.order, nullptr);
   return hipGetLastError();
 }
