@@ -3,7 +3,8 @@ kv_causal_attend over the appended tokens) against the fp64 oracle
 (oracle/attention.causal_last): token j sees the own tokens through itself, then the
 mounts.  Bars as for decode: bf16 outputs max-abs 2e-2 and mean-abs 2e-3, LSE max-abs
 2e-3.  Cases: two segments with positions far apart appended to a fork whose tail page
-is shared (copy-on-write), a thread with mounts, a single token, a whole fresh
+is shared (copy-on-write), a thread with mounts (misaligned: K relaid; page-aligned: K
+gathered from the pool), a single token, a whole fresh
 sequence (plain causal attention, several work-item groups), fp32 and d = 64 pools (the
 decode-row path), and the timed restore workload at full size (sampled tokens, every
 head).  Bars: also the error model's (tests/harness.py: decode_bars), with the tiled
@@ -65,6 +66,16 @@ def test_restore_into_a_thread_with_mounts():
                         seed=94)
     sc.n_pages += 16
     _restore(sc, 2, [17, 1, 40], [700, 900, 1200], 95, "segments into a thread with mounts")
+
+
+def test_restore_into_a_thread_with_page_aligned_mounts():
+    # mounts that start on page boundaries and span whole pages, own context a multiple of
+    # 16 after the restore: every visible 16-key group is one page, so K is gathered
+    # straight from the pool (the misaligned mounts above take the relayout)
+    sc = W.dag_scenario(root=304, threads=3, private=96, mounts_per_thread=2, mount_len=32, hq=8, hkv=2, d=128,
+                        seed=88)
+    sc.n_pages += 16
+    _restore(sc, 2, [17, 1, 46], [700, 900, 1200], 89, "segments into a thread with page-aligned mounts")
 
 
 def test_single_token_and_fresh_sequence():
