@@ -32,6 +32,13 @@
 #include "plan.hpp"
 
 namespace fa {
+// 32-bit word q of a stored V^T row holds the slots of word v_word(q) of the row in slot
+// order (SPW slots per word; the slot permutation moves whole 4-slot runs)
+template <int SPW>
+__device__ constexpr int v_word(int q) { return v_pos(SPW * q) / SPW; }
+}  // namespace fa
+
+namespace fa {
 
 typedef __bf16 bf16_t;
 
@@ -166,11 +173,12 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
     if (r < n_vr) {
       const int h = r / D, d = r % D;
       const u32x4* old = reinterpret_cast<const u32x4*>(vp + dst + (size_t)h * np * BLK + d * 16);
+      // rows are held in slot order: stored word q holds the slots of word v_word(q)
 #pragma unroll
       for (int w4 = 0; w4 < WPR / 4; ++w4) {
         const u32x4 x = keep_rest ? old[w4] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[i][4 * w4 + e] = x[e];
+        for (int e = 0; e < 4; ++e) vr[i][v_word<SPW>(4 * w4 + e)] = x[e];
       }
       for (int k = 0; k < nrun; ++k) {  // wave-uniform
         const int t0 = s_run[k][0], len = s_run[k][1], loc = s_run[k][2];
@@ -183,7 +191,7 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
         for (int w4 = 0; w4 < WPR / 4; ++w4) {
           const u32x4 x = srow[w4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) src[1 + 4 * w4 + e] = x[e];
+          for (int e = 0; e < 4; ++e) src[1 + v_word<SPW>(4 * w4 + e)] = x[e];
         }
 #pragma unroll
         for (int w = 0; w < WPR; ++w) {
@@ -245,7 +253,8 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactParams p) {
       u32x4* row = reinterpret_cast<u32x4*>(vp + dst + (size_t)h * np * BLK + d * 16);
 #pragma unroll
       for (int w4 = 0; w4 < WPR / 4; ++w4)
-        row[w4] = u32x4{vr[i][4 * w4], vr[i][4 * w4 + 1], vr[i][4 * w4 + 2], vr[i][4 * w4 + 3]};
+        row[w4] = u32x4{vr[i][v_word<SPW>(4 * w4)], vr[i][v_word<SPW>(4 * w4 + 1)], vr[i][v_word<SPW>(4 * w4 + 2)],
+                        vr[i][v_word<SPW>(4 * w4 + 3)]};
     }
   }
 }

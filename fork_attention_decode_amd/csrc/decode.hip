@@ -282,7 +282,7 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, const int32_t
     for (int f = 0; f < NF; ++f) kf[f] = *reinterpret_cast<const typename TR::KF*>(slot + f * 1024 + lane * 16);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      vf[db] = *reinterpret_cast<const typename TR::VF*>(slot + HALF + ((db * 16 + c16) * 16 + 4 * g) * (int)sizeof(T));
+      vf[db] = *reinterpret_cast<const typename TR::VF*>(slot + HALF + ((db * 16 + c16) * 16 + v_pos(4 * g)) * (int)sizeof(T));
   };
 
   f32x4 o[NDB];
@@ -494,17 +494,20 @@ __global__ __launch_bounds__(256) void page_write_kernel(T* __restrict__ kp, T* 
     }
     *reinterpret_cast<vec_t*>(kp + blk + (size_t)sn * E) = val;
   }
-  // V^T: row d holds 16 tokens = 16 * sizeof(T) bytes = sizeof(T) slots of E tokens
+  // V^T: row d holds 16 tokens = 16 * sizeof(T) bytes = sizeof(T) pieces of E positions;
+  // position q holds slot v_pos(q)
   constexpr int PPR = sizeof(T);
   for (int pc = threadIdx.x; pc < D * PPR; pc += blockDim.x) {
-    const int d = pc / PPR, t0 = (pc % PPR) * E;
-    if (w.src_page < 0 && (t0 + E <= w.lo || t0 >= w.hi)) continue;
-    vec_t val = *reinterpret_cast<const vec_t*>((w.src_page >= 0 ? vp + sblk : vp + blk) + (size_t)d * 16 + t0);
+    const int d = pc / PPR, q0 = (pc % PPR) * E;
+    bool any = w.src_page >= 0;
+    for (int e = 0; e < E; ++e) any = any || (v_pos(q0 + e) >= w.lo && v_pos(q0 + e) < w.hi);
+    if (!any) continue;
+    vec_t val = *reinterpret_cast<const vec_t*>((w.src_page >= 0 ? vp + sblk : vp + blk) + (size_t)d * 16 + q0);
     for (int e = 0; e < E; ++e) {
-      const int t = t0 + e;
+      const int t = v_pos(q0 + e);
       if (t >= w.lo && t < w.hi) val[e] = vn[((size_t)(w.tok_base + (t - w.lo)) * hkv + h) * D + d];
     }
-    *reinterpret_cast<vec_t*>(vp + blk + (size_t)d * 16 + t0) = val;
+    *reinterpret_cast<vec_t*>(vp + blk + (size_t)d * 16 + q0) = val;
   }
 }
 

@@ -24,6 +24,13 @@ struct PageWrite {
 };
 
 // A run of token slots inside one physical page, read by one segment's rows.
+// V^T rows of a page block keep the page's 16 slots in the order 0-3, 8-11, 4-7, 12-15
+// (bits 2 and 3 of the slot swapped): slot t of row d is element d * 16 + v_pos(t).  The
+// decode reads 4-slot runs (contiguous either way); the tiled prefill's V operand unit, the
+// slots {0-3, 8-11} or {4-7, 12-15} of a row, is then 16 contiguous bytes it can copy
+// straight from the page.  v_pos is its own inverse.
+__host__ __device__ constexpr int v_pos(int t) { return ((t & 4) << 1) | ((t & 8) >> 1) | (t & 3); }
+
 struct Chunk {
   int32_t page;
   int32_t lohi;  // lo | hi << 8, 0 <= lo < hi <= 16

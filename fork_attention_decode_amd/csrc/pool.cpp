@@ -613,7 +613,7 @@ int kv_pool_read_page(kv_pool_t* P, int32_t page, int32_t head, void* k_out, voi
         }
   for (int d = 0; d < D; ++d)
     for (int t = 0; t < kPage; ++t)
-      std::memcpy(vo + ((size_t)t * D + d) * es, vr.data() + ((size_t)d * kPage + t) * es, es);
+      std::memcpy(vo + ((size_t)t * D + d) * es, vr.data() + ((size_t)d * kPage + v_pos(t)) * es, es);
   return KV_OK;
 }
 

@@ -79,6 +79,7 @@ struct Params {
   // kpool + (h * pool_pages + page) * 4 KiB; keys 16 g .. 16 g + 15 of the context are
   // slots 0..15 of page gpages[g] (the kernel's gpages argument)
   const char* kpool;
+  const char* vpool;
   int32_t pool_pages;
 };
 
@@ -232,6 +233,25 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
           const int ks = 4 * (wave & 1) + i, f = ks >> 1, g = 2 * (ks & 1) + hi;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024),
                                                    16, pg * 4096 + ((f * 4 + g) * 16 + slot) * 16, 0, 0, 0);
+        }
+        return;
+      }
+      const int c = col_of(j);
+      if (c != p.nb - 1 || !(p.T & (kB - 1))) {
+        // V unit (dt, kt, hf, lane) = V[t][32 dt + lane % 32] for slots t0 .. t0 + 3 and
+        // t0 + 8 .. t0 + 11 of page 2 kt + hf, t0 = 4 (lane / 32): in the pool's V^T slot
+        // order these are the 16 bytes at row d, byte 16 (lane / 32).  Waves 4-7: dt =
+        // wave - 4, copy i = (kt, hf).  (A last block that the context ends inside takes V
+        // from its image: the page's slots past the context hold no data of it.)
+        const int dt = wave - 4, d = 32 * dt + lo;
+        const int pg_0 = gpages[4 * c], pg_1 = gpages[4 * c + 1], pg_2 = gpages[4 * c + 2], pg_3 = gpages[4 * c + 3];
+        const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.vpool + (size_t)h * p.pool_pages * 4096), 0, p.pool_pages * 4096, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < kLoadsPerWave; ++i) {
+          const int pg = i == 0 ? pg_0 : (i == 1 ? pg_1 : (i == 2 ? pg_2 : pg_3));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                                                   16, pg * 4096 + d * 32 + 16 * hi, 0, 0, 0);
         }
         return;
       }
@@ -469,8 +489,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(Params p, const int32
 __global__ __launch_bounds__(256) void page_relayout_kernel(const bf16_t* __restrict__ kp, const bf16_t* __restrict__ vp,
                                                             const int32_t* __restrict__ locs, char* __restrict__ kimg,
                                                             char* __restrict__ vimg, int T, int nb, int pool_pages,
-                                                            bool with_k) {
-  const int c = blockIdx.x, h = blockIdx.y;
+                                                            bool with_k, int c_first) {
+  const int c = c_first + blockIdx.x, h = blockIdx.y;
   const size_t img = ((size_t)h * nb + c) * kImg;
   const size_t head = (size_t)h * pool_pages;
 #pragma unroll
@@ -501,7 +521,7 @@ __global__ __launch_bounds__(256) void page_relayout_kernel(const bf16_t* __rest
         if (loc0 >= 0 && (loc0 & 3) == 0 && loc3 == loc0 + 3) {
           // four consecutive slots of one page: 8 contiguous bytes of the V^T row
           typedef bf16_t bf16x4v __attribute__((__vector_size__(4 * sizeof(bf16_t))));
-          const bf16x4v x = *reinterpret_cast<const bf16x4v*>(vp + (head + (loc0 >> 4)) * 16 * kD + d * 16 + (loc0 & 15));
+          const bf16x4v x = *reinterpret_cast<const bf16x4v*>(vp + (head + (loc0 >> 4)) * 16 * kD + d * 16 + v_pos(loc0 & 15));
 #pragma unroll
           for (int e = 0; e < 4; ++e) val[4 * half + e] = x[e];
         } else {
@@ -511,7 +531,7 @@ __global__ __launch_bounds__(256) void page_relayout_kernel(const bf16_t* __rest
             bf16_t x = (bf16_t)0.f;
             if (key < T) {
               const int loc = locs[key];
-              x = vp[(head + (loc >> 4)) * 16 * kD + d * 16 + (loc & 15)];
+              x = vp[(head + (loc >> 4)) * 16 * kD + d * 16 + v_pos(loc & 15)];
             }
             val[4 * half + e] = x;
           }
@@ -617,6 +637,7 @@ extern "C" int dag_attn_run(const void* q, void* out, float* lse, int32_t T, int
   p.n_split = 1;
   p.part_lse2 = p.part_o = nullptr;
   p.kpool = nullptr;
+  p.vpool = nullptr;
   p.pool_pages = 0;
   prefill_kernel<0><<<(size_t)p.nb * n_kv_heads * p.n_hg, kThreads, 0, stream>>>(
       p, row_ptr, reinterpret_cast<const int32_t*>(ws + w.ent), reinterpret_cast<const int32_t*>(ws + w.order),
@@ -641,17 +662,22 @@ extern "C" int dag_attn_prefill(const void* q, const void* k, const void* v, voi
                       ws_bytes, stream);
 }
 
-// Restore of a sequence's last tokens as a split-K tiled prefill over its pages: the
-// visible keys' V (and K, unless the keys fill whole pages in order) are relaid into
-// operand-order images, then the prefill kernel runs the CSR rows (query block, key-range
-// piece), gathering K straight from the page blocks where it can (a page block's 16-byte
-// K slots are the image's units, so the copy into LDS only needs per-lane offsets), and
-// writes one partial per (query row, head, piece), merged afterwards.
+// Restore of a sequence's last tokens as a split-K tiled prefill over its pages.  When the
+// visible keys fill whole pages in order, the prefill kernel copies K and V straight from
+// the page blocks into its LDS ring (a page block's 16-byte K slots and 16-byte runs of
+// its V^T rows are the operand images' units, so the copies only need per-lane offsets);
+// only the V of a last block that the context ends inside is relaid into an image.  Else
+// K and V are relaid into operand-order images first.  The kernel runs the CSR rows
+// (query block, key-range piece) and writes one partial per (query row, head, piece),
+// merged afterwards.
 hipError_t fa::fa_launch_restore(const RestoreLaunch& r, hipStream_t stream) {
   const int nb = (r.T + kB - 1) / kB;
-  page_relayout_kernel<<<dim3(nb, r.hkv), 256, 0, stream>>>(static_cast<const bf16_t*>(r.k_pages),
-                                                            static_cast<const bf16_t*>(r.v_pages), r.locs, r.kimg,
-                                                            r.vimg, r.T, nb, r.pool_pages, !r.kgather);
+  // gather mode: only the V image of a last block that the context ends inside
+  const int c_first = r.kgather ? nb - 1 : 0;
+  if (!r.kgather || (r.T & (kB - 1)))
+    page_relayout_kernel<<<dim3(nb - c_first, r.hkv), 256, 0, stream>>>(
+        static_cast<const bf16_t*>(r.k_pages), static_cast<const bf16_t*>(r.v_pages), r.locs, r.kimg, r.vimg, r.T, nb,
+        r.pool_pages, !r.kgather, c_first);
   Params p;
   p.q = static_cast<const bf16_t*>(r.q);
   p.kimg = r.kimg;
@@ -673,6 +699,7 @@ hipError_t fa::fa_launch_restore(const RestoreLaunch& r, hipStream_t stream) {
   p.part_lse2 = r.part_lse2;
   p.part_o = r.part_o;
   p.kpool = static_cast<const char*>(r.k_pages);
+  p.vpool = static_cast<const char*>(r.v_pages);
   p.pool_pages = r.pool_pages;
   const size_t grid = (size_t)r.n_rows * r.hkv * p.n_hg;
   if (r.kgather)

@@ -85,7 +85,9 @@ typedef struct {
  *       fp32: K[t][16 f + 4 e + g],      e = 0..3   (f < d/16)
  *     so that lane (t + 16 g) of a wave loads, with one contiguous 1 KiB access per f,
  *     exactly the operand fragment it feeds to the matrix instruction.
- *   V is stored transposed: element d * 16 + t holds V[t][d].
+ *   V is stored transposed, with the 16 slots of a row in the order 0-3, 8-11, 4-7,
+ *     12-15: element d * 16 + v(t) holds V[t][d], v(t) = t with bits 2 and 3 swapped, so
+ *     the slot pairs of 4-runs {0-3, 8-11} and {4-7, 12-15} are 16 contiguous bytes each.
  * Use kv_pool_read_page() to read a page back in plain [t][d] order.
  * ------------------------------------------------------------------------------- */
 
