@@ -508,10 +508,11 @@ def bench_restore(reps=20, n_seg=4, seg_len=128):
         "rows": n * hq,
         "roofline": {"bound": "mfma", "unit": "TFLOP/s", "peak": 2500.0, "algorithmic_flops_per_call": flops,
                      "achieved": tflops, "frac": tflops / 2500.0},
-        "note": "the attention runs as a split-K tiled prefill: the context's pages are relaid once into "
-                "operand-order images, every workgroup takes 64 restored tokens x 4 query heads of one KV head over "
-                "one piece of the key range (32 x 32 x 16 matrix instructions), and the pieces' partials are merged "
-                "by log-sum-exp; the plan (host) is built once and cached, the events enclose the kernels",
+        "note": "the attention runs as a split-K tiled prefill: every workgroup takes 64 restored tokens x 4 query "
+                "heads of one KV head over one piece of the key range (32 x 32 x 16 matrix instructions), copying the "
+                "context's K and V straight from the pool's pages into its LDS ring (the visible keys fill whole "
+                "pages), and the pieces' partials are merged by log-sum-exp; the plan (host) is built once and "
+                "cached, the events enclose the kernels",
     }
 
 
