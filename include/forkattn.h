@@ -365,10 +365,12 @@ int kv_window_step(kv_pool_t* pool, int32_t step, const void* k, const void* v, 
  * ended at that token.  q: DEVICE [n][Hq][d] (pool dtype, rotated by the caller); out:
  * DEVICE [n][Hq][d]; lse: DEVICE fp32 [n][Hq] or NULL.  workspace: DEVICE, at least
  * kv_causal_attend_workspace_size bytes for the same sequence state, n and n_q_heads.
- * bf16 pools with d = 128 run it as one tiled prefill: the visible keys are relaid once
- * into matrix-core operand images, 64 of the n tokens and one piece of the key range per
- * workgroup, then the pieces are merged by log-sum-exp; other pools run n rows of one
- * split-K decode.  1 <= n <= the sequence's length.  Stream-ordered. */
+ * bf16 pools with d = 128 run it as one tiled prefill, 64 of the n tokens and one piece of
+ * the key range per workgroup, then the pieces are merged by log-sum-exp: when the visible
+ * keys fill whole pages in order (own tokens always; mounts when page-aligned) K and V are
+ * copied straight from the pages, else they are first relaid into matrix-core operand
+ * images in the workspace.  Other pools run n rows of one split-K decode.
+ * 1 <= n <= the sequence's length.  Stream-ordered. */
 int kv_causal_attend_workspace_size(kv_pool_t* pool, kv_seq_t seq, int64_t n, int32_t n_q_heads,
                                     size_t* bytes);
 int kv_causal_attend(kv_pool_t* pool, kv_seq_t seq, int64_t n, int32_t n_q_heads, const void* q,
