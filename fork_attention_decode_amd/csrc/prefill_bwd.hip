@@ -16,18 +16,22 @@
 //     and K transposed.  The TP order pairs query (or key) 4 k + r of two 16-row tiles
 //     with the lanes and registers where an accumulator tile holds them, so P and dS
 //     feed the next products straight from the accumulators, with no shuffles;
-//   * dkdv_kernel: one workgroup per (two 64-key blocks, KV head), 8 waves of 16 keys, K
-//     and V fragments held in registers; it walks the union of the two blocks' columns
-//     of the mask (a CSC over column pairs built on the device, rows ascending) and, for
-//     each listed query block and each of the G query heads, stages that block's record
-//     in LDS (double-buffered: the next record's loads are in flight while the current
-//     one computes) and computes S = Q K^T, P, dP = dO V^T, dS, then dV += P^T dO and
-//     dK += dS^T Q: dK and dV of the G heads accumulate in registers, with no atomics;
+//   * dkdv_kernel: one workgroup per (two 64-key blocks, KV head), 8 waves, wave = 32 keys
+//     (K and V fragments held in registers) x one 32-row half of every query block; it
+//     walks the union of the two blocks' columns of the mask (a CSC over column pairs
+//     built on the device, highest query block first) and, for each listed query block and each of
+//     the G query heads, brings that block's record into LDS with buffer loads that write
+//     LDS directly (double-buffered: the next record's loads are in flight while the
+//     current one computes) and computes S = Q K^T, P, dP = dO V^T, dS, then dV += P^T dO
+//     and dK += dS^T Q: each Q / dO fragment read from LDS feeds two MFMAs; dK and dV of
+//     the G heads accumulate in registers, with no atomics, and the two query halves
+//     meet in LDS at the end;
 //   * dq_kernel: one workgroup per (64-query block, 4 query heads of a KV head), 8 waves
 //     of 32 queries (two 16-query tiles, so each K / V fragment read from LDS feeds two
-//     MFMAs), Q and dO fragments in registers; it walks the block's CSR row, stages each
-//     key block's K / V / K^T (double-buffered) once for the 4 heads and computes
-//     S^T = K Q^T, P^T, dP^T = V dO^T, dS^T and dQ += dS K;
+//     MFMAs), Q and dO fragments in registers; it walks the block's CSR row (its entries
+//     with an in-range column packed on the device, read as scalar loads), brings each
+//     key block's K / V / K^T into LDS the same way (double-buffered) once for the 4
+//     heads and computes S^T = K Q^T, P^T, dP^T = V dO^T, dS^T and dQ += dS K;
 //   * the mask kinds are those of the forward: kind 1 (the diagonal block) hides key >
 //     query, keys >= T are hidden, a row with lse = -inf contributes nothing.
 #include <hip/hip_runtime.h>
@@ -51,6 +55,7 @@ constexpr int kImg = kB * kD * 2;          // bytes of one 64 x 128 bf16 image (
 constexpr int kQRec = 4 * kImg + 2 * kB * 4;  // Q OPO, dO OPO, Q TP, dO TP, lse2[64], D[64]
 constexpr int kKRec = 3 * kImg;            // K OPO, V OPO, K TP
 constexpr int kThreads = 256;
+constexpr int kQRecL = (kQRec + 1023) / 1024 * 1024;  // an LDS record buffer: whole 1 KiB units
 constexpr unsigned kRowMask = 0xffffffu;   // CSC entry: query block | listed bits << 24 | diagonal bits << 26
 
 // OPO unit of element (r, 8 c8 .. 8 c8 + 7) of a 64 x 128 block: fragment (r / 16, c8 / 4),
@@ -247,29 +252,29 @@ __global__ __launch_bounds__(kThreads) void csc_fill_kernel(const int32_t* __res
   }
 }
 
-// a record staged through registers: the loads of the next stage are issued before the
-// current stage computes and written to the other LDS buffer after it
-template <int kUnits, int kThr>
-struct Stager {
-  static constexpr int kPer = (kUnits + kThr - 1) / kThr;
-  i32x4 r[kPer];
-  __device__ __forceinline__ void load(const char* __restrict__ src) {
-    const i32x4* s = reinterpret_cast<const i32x4*>(src);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int u = threadIdx.x + i * kThr;
-      if (kUnits % kThr == 0 || u < kUnits) r[i] = s[u];
-    }
+// the CSR rows without their skipped entries, for the dQ pass: rent[row_ptr[r] + i] =
+// column | diagonal << 31 of the row's i-th entry whose column is in [0, nb), rcnt[r] = how
+// many; one wave per row
+__global__ __launch_bounds__(64) void row_pack_kernel(const int32_t* __restrict__ row_ptr,
+                                                      const int32_t* __restrict__ col,
+                                                      const uint8_t* __restrict__ kind, int32_t nb,
+                                                      int32_t* __restrict__ rent, int32_t* __restrict__ rcnt) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const int a = row_ptr[r], b = row_ptr[r + 1];
+  int n = 0;
+  for (int base = a; base < b; base += 64) {
+    const int e = base + lane;
+    const int c = e < b ? col[e] : -1;
+    const bool ok = c >= 0 && c < nb;
+    const uint64_t bal = __ballot(ok);
+    if (ok) rent[a + n + __popcll(bal & ((1ull << lane) - 1ull))] = c | (kind[e] ? (int32_t)0x80000000u : 0);
+    n += __popcll(bal);
   }
-  __device__ __forceinline__ void store(char* dst) const {
-    i32x4* d = reinterpret_cast<i32x4*>(dst);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int u = threadIdx.x + i * kThr;
-      if (kUnits % kThr == 0 || u < kUnits) d[u] = r[i];
-    }
-  }
-};
+  if (lane == 0) rcnt[r] = n;
+}
+
+// s_waitcnt vmcnt(0), the other counters left free (gfx9 encoding)
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -303,48 +308,67 @@ constexpr int kDkdvThreads = 256 * kKeyBlocksPerWg;
 constexpr int kHeadsPerWg = 4;                     // dQ workgroup: up to 4 query heads, 8 waves of 32 queries
 constexpr int kDqThreads = 512;
 
-// grid (Hkv, ceil(n_blocks / 2)): dK, dV of two 64-key blocks for one KV head; wave w takes
-// keys 16 (w % 4) .. + 15 of block 2 blockIdx.y + w / 4.  The workgroup walks the union
-// of the two columns; a wave whose column lacks the query block skips it.
-__global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) char rec[2][kQRec];
+// grid (Hkv, ceil(n_blocks / 2)): dK, dV of two 64-key blocks for one KV head.  Wave w takes
+// keys 32 (w % 4) .. + 31 of the two blocks (two 16-key tiles, K and V fragments held in
+// registers) over query rows 32 (w / 4) .. + 31 of every staged record, so each Q / dO
+// fragment read from LDS feeds both key tiles; waves w and w + 4 add their dK, dV at the
+// end through LDS.  The workgroup walks the union of the two columns; a wave whose column
+// lacks the query block skips it.
+__global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p, const uint32_t* __restrict__ crow) {
+  __shared__ __attribute__((aligned(16))) char rec[2][kQRecL];
   const int g = blockIdx.x, lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kbi = w >> 2, kt = w & 3;
+  const int kq = w & 3, qh = w >> 2;              // 32-key group of the 128, query half
+  const int kbi = kq >> 1;                        // key block within the workgroup
   const int kb = kKeyBlocksPerWg * blockIdx.y + kbi;
   const bool live = kb < p.nb;
-  bf16x8 kf[4], vf[4];  // the wave's 16 keys as the B operand (key = lane % 16)
+  bf16x8 kf[2][4], vf[2][4];  // key tiles kt = 0, 1 (16 keys each) as the B operand
   if (live) {
     const char* krec = p.krec + ((size_t)kb * p.hkv + g) * kKRec;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      kf[f] = *reinterpret_cast<const bf16x8*>(krec + ((kt * 4 + f) * 64 + lane) * 16);
-      vf[f] = *reinterpret_cast<const bf16x8*>(krec + kImg + ((kt * 4 + f) * 64 + lane) * 16);
-    }
-  }
-  f32x4 dk[8], dv[8];
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-  for (int n = 0; n < 8; ++n) dk[n] = dv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int key_tok = kb * kB + kt * 16 + (lane & 15);
+      for (int f = 0; f < 4; ++f) {
+        const int t16 = 2 * (kq & 1) + kt;  // 16-key tile of the block
+        kf[kt][f] = *reinterpret_cast<const bf16x8*>(krec + ((t16 * 4 + f) * 64 + lane) * 16);
+        vf[kt][f] = *reinterpret_cast<const bf16x8*>(krec + kImg + ((t16 * 4 + f) * 64 + lane) * 16);
+      }
+  }
+  f32x4 dk[2][8], dv[2][8];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) dk[kt][n] = dv[kt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int key0 = kb * kB + 32 * (kq & 1) + (lane & 15);  // + 16 kt
   const int e0 = p.col_ptr[blockIdx.y], e1 = p.col_ptr[blockIdx.y + 1];
   // stages: (entry, head of the group), entries from the highest query block down, so
   // workgroups whose lists share a tail (every prefix column reaches the last branch
   // blocks) start on the same records and read them while they sit in the die's L2
   const int n_st = (e1 - e0) * p.G;
-  auto ent_of = [&](int st) { return p.crow[e1 - 1 - st / p.G]; };
-  Stager<kQRec / 16, kDkdvThreads> stg;
-  auto src = [&](int st) {
+  // (crow is a separate restrict argument so that its reads are scalar loads, which
+  // leave the vector-memory count of the records in flight alone)
+  auto ent_of = [&](int st) { return crow[e1 - 1 - st / p.G]; };
+  // a record goes from memory straight into LDS (no registers): 1 KiB per wave
+  // instruction, wave w issuing units w, w + 8, ...; the descriptor ends at the record,
+  // so the last unit's second half reads as zero
+  auto issue = [&](int st, char* dst) {
     const int qb = (int)(ent_of(st) & kRowMask);
-    return p.qrec + ((size_t)qb * p.hq + g * p.G + st % p.G) * kQRec;
+    const char* src = p.qrec + ((size_t)qb * p.hq + g * p.G + st % p.G) * kQRec;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, kQRec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < (kQRecL / 1024 + 7) / 8; ++i) {
+      const int j = w + 8 * i;
+      if (j < kQRecL / 1024)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
+                                                 lane * 16, j * 1024, 0, 0);
+    }
   };
-  if (n_st > 0) {
-    stg.load(src(0));
-    stg.store(rec[0]);
-  }
+  if (n_st > 0) issue(0, rec[0]);
+  wait_vmcnt0();
   __syncthreads();
   for (int st = 0; st < n_st; ++st) {
     const int cur = st & 1;
-    if (st + 1 < n_st) stg.load(src(st + 1));
+    if (st + 1 < n_st) issue(st + 1, rec[cur ^ 1]);
     const uint32_t ent = ent_of(st);
     const int qb = (int)(ent & kRowMask);
     if (live && ((ent >> (24 + kbi)) & 1u)) {
@@ -352,61 +376,93 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p) {
       const char* r = rec[cur];
       const float* lse2 = reinterpret_cast<const float*>(r + 4 * kImg);
       const float* dd = lse2 + kB;
-      f32x4 s[4], dp[4];
+      f32x4 s[2][2], dp[2][2];  // [kt][query tile of this half]
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        s[t] = dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) s[kt][tt] = dp[kt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
-          const int u = ((t * 4 + f) * 64 + lane) * 16;
-          s[t] = mfma(*reinterpret_cast<const bf16x8*>(r + u), kf[f], s[t]);
-          dp[t] = mfma(*reinterpret_cast<const bf16x8*>(r + kImg + u), vf[f], dp[t]);
-        }
-      }
-      // s[t][i]: query 16 t + 4 (lane / 16) + i, key lane % 16 of the wave
+          const int u = (((2 * qh + tt) * 4 + f) * 64 + lane) * 16;
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(r + u);
+          const bf16x8 da = *reinterpret_cast<const bf16x8*>(r + kImg + u);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int q0 = 16 * t + 4 * (lane >> 4);
+          for (int kt = 0; kt < 2; ++kt) {
+            s[kt][tt] = mfma(qa, kf[kt][f], s[kt][tt]);
+            dp[kt][tt] = mfma(da, vf[kt][f], dp[kt][tt]);
+          }
+        }
+      // s[kt][tt][i]: query 16 (2 qh + tt) + 4 (lane / 16) + i, key key0 + 16 kt
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int q0 = 16 * (2 * qh + tt) + 4 * (lane >> 4);
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + q0);
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + q0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool vis = key_tok < p.T && (!diag || key_tok <= qb * kB + q0 + i);
-          const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], p.c2, -l4[i])) : 0.f;
-          s[t][i] = pr;
-          dp[t][i] = pr * (dp[t][i] - d4[i]);
-        }
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key_tok = key0 + 16 * kt;
+            const bool vis = key_tok < p.T && (!diag || key_tok <= qb * kB + q0 + i);
+            const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][tt][i], p.c2, -l4[i])) : 0.f;
+            s[kt][tt][i] = pr;
+            dp[kt][tt][i] = pr * (dp[kt][tt][i] - d4[i]);
+          }
       }
+      bf16x8 ap[2], ads[2];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const bf16x8 ap = pack_pair(s[2 * h2], s[2 * h2 + 1]);
-        const bf16x8 ads = pack_pair(dp[2 * h2], dp[2 * h2 + 1]);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const int u = ((n * 2 + h2) * 64 + lane) * 16;
-          dv[n] = mfma(ap, *reinterpret_cast<const bf16x8*>(r + 3 * kImg + u), dv[n]);
-          dk[n] = mfma(ads, *reinterpret_cast<const bf16x8*>(r + 2 * kImg + u), dk[n]);
-        }
+      for (int kt = 0; kt < 2; ++kt) {
+        ap[kt] = pack_pair(s[kt][0], s[kt][1]);
+        ads[kt] = pack_pair(dp[kt][0], dp[kt][1]);
       }
-    }
-    if (st + 1 < n_st) stg.store(rec[cur ^ 1]);
-    __syncthreads();  // stage st + 1 is in place; every wave is done with stage st
-  }
-  // dk[n][i]: key 4 (lane / 16) + i of the wave, dim 16 n + lane % 16
-  if (!live) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = kb * kB + kt * 16 + 4 * (lane >> 4) + i;
-    if (j < p.T) {
-      float* dkr = p.dk + ((size_t)j * p.hkv + g) * kD + (lane & 15);
-      float* dvr = p.dv + ((size_t)j * p.hkv + g) * kD + (lane & 15);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        dkr[16 * n] = dk[n][i] * p.scale;
-        dvr[16 * n] = dv[n][i];
+        const int u = ((n * 2 + qh) * 64 + lane) * 16;
+        const bf16x8 dot = *reinterpret_cast<const bf16x8*>(r + 3 * kImg + u);
+        const bf16x8 qt = *reinterpret_cast<const bf16x8*>(r + 2 * kImg + u);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          dv[kt][n] = mfma(ap[kt], dot, dv[kt][n]);
+          dk[kt][n] = mfma(ads[kt], qt, dk[kt][n]);
+        }
       }
     }
+    wait_vmcnt0();
+    __syncthreads();  // stage st + 1 is in place; every wave is done with stage st
   }
+  // waves 4-7 hand their query half's sums to waves 0-3 through the (now free) records
+  float* xr = reinterpret_cast<float*>(&rec[0][0]) + (size_t)kq * (2 * 2 * 8 * 4 * 64);
+  if (qh == 1) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xr[(((0 * 2 + kt) * 8 + n) * 4 + i) * 64 + lane] = dk[kt][n][i];
+          xr[(((1 * 2 + kt) * 8 + n) * 4 + i) * 64 + lane] = dv[kt][n][i];
+        }
+  }
+  __syncthreads();
+  if (qh == 1 || !live) return;
+  // dk[kt][n][i]: key key0 - lane % 16 + 16 kt + 4 (lane / 16) + i, dim 16 n + lane % 16
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = kb * kB + 32 * (kq & 1) + 16 * kt + 4 * (lane >> 4) + i;
+      if (j < p.T) {
+        float* dkr = p.dk + ((size_t)j * p.hkv + g) * kD + (lane & 15);
+        float* dvr = p.dv + ((size_t)j * p.hkv + g) * kD + (lane & 15);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          dkr[16 * n] = (dk[kt][n][i] + xr[(((0 * 2 + kt) * 8 + n) * 4 + i) * 64 + lane]) * p.scale;
+          dvr[16 * n] = dv[kt][n][i] + xr[(((1 * 2 + kt) * 8 + n) * 4 + i) * 64 + lane];
+        }
+      }
+    }
 }
 
 // grid (Hq / hw, n_blocks), hw = 4, 2 or 1 query heads of one KV head per workgroup (the
@@ -414,7 +470,8 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p) {
 // (two 16-query tiles) of head blockIdx.x hw + w / 2 (waves past the hw heads only help
 // stage).  Each key block's record staged in LDS serves the workgroup's heads, and each
 // K / V fragment read from LDS feeds the products of both tiles.
-__global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw) {
+__global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw, const int32_t* __restrict__ rent,
+                                                        const int32_t* __restrict__ rcnt) {
   __shared__ __attribute__((aligned(16))) char rec[2][kKRec];
   const int qb = blockIdx.y, lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -442,25 +499,34 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw) {
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int n = 0; n < 8; ++n) dq[u][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int e0 = p.row_ptr[qb], e1 = p.row_ptr[qb + 1];
-  Stager<kKRec / 16, kDqThreads> stg;
-  // stages: the row's entries whose column is inside [0, nb) (others are never followed)
-  auto col_ok = [&](int e) { return p.col[e] >= 0 && p.col[e] < p.nb; };
-  auto next_ok = [&](int e) {
-    while (e < e1 && !col_ok(e)) ++e;
-    return e;
+  // stages: the row's entries with a column in [0, nb), as packed by row_pack_kernel
+  // (rent and rcnt are separate restrict arguments, so their reads are scalar loads,
+  // which leave the vector-memory count of the records in flight alone; the entry after
+  // next is read while the current one computes)
+  const int e0 = p.row_ptr[qb], n_e = rcnt[qb];
+  // a key block's record goes from memory straight into LDS: 48 units of 1 KiB, wave w
+  // issuing units w, w + 8, ...
+  auto issue = [&](int ent, char* dst) {
+    const char* src = p.krec + ((size_t)(ent & 0x7fffffff) * p.hkv + g) * kKRec;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, kKRec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kKRec / 1024 / 8; ++i) {
+      const int j = w + 8 * i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
+                                               lane * 16, j * 1024, 0, 0);
+    }
   };
-  int e = next_ok(e0);
-  if (e < e1) {
-    stg.load(p.krec + ((size_t)p.col[e] * p.hkv + g) * kKRec);
-    stg.store(rec[0]);
-  }
+  static_assert(kKRec % (8 * 1024) == 0 && kDqThreads == 512, "record units per wave");
+  int ent = n_e > 0 ? rent[e0] : 0;
+  if (n_e > 0) issue(ent, rec[0]);
+  int ent_n = n_e > 1 ? rent[e0 + 1] : 0;
+  wait_vmcnt0();
   __syncthreads();
-  for (int cur = 0; e < e1; cur ^= 1) {
-    const int en = next_ok(e + 1);
-    if (en < e1) stg.load(p.krec + ((size_t)p.col[en] * p.hkv + g) * kKRec);
-    const int kb = p.col[e];
-    const bool diag = p.kind[e] != 0;
+  for (int i = 0, cur = 0; i < n_e; ++i, cur ^= 1) {
+    if (i + 1 < n_e) issue(ent_n, rec[cur ^ 1]);
+    const int ent_nn = i + 2 < n_e ? rent[e0 + i + 2] : 0;
+    const int kb = ent & 0x7fffffff;
+    const bool diag = ent < 0;
     const char* r = rec[cur];
     if (active) {
     f32x4 s[2][4], dp[2][4];
@@ -505,9 +571,10 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw) {
       }
     }
     }
-    if (en < e1) stg.store(rec[cur ^ 1]);
+    wait_vmcnt0();
     __syncthreads();  // the next key block is in place; every wave is done with this one
-    e = en;
+    ent = ent_n;
+    ent_n = ent_nn;
   }
   // dq[u][n][i]: query 4 (lane / 16) + i of tile u, dim 16 n + lane % 16
   if (!active) return;
@@ -527,7 +594,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t qrec, krec, count, col_ptr, crow, total;
+  size_t qrec, krec, count, col_ptr, crow, rcnt, rent, total;
 };
 BwdLayout bwd_layout(int32_t T, int32_t hq, int32_t hkv, int64_t nnz) {
   const size_t nb = (size_t)(T + kB - 1) / kB;
@@ -537,7 +604,9 @@ BwdLayout bwd_layout(int32_t T, int32_t hq, int32_t hkv, int64_t nnz) {
   w.count = align256(w.krec + nb * hkv * kKRec);
   w.col_ptr = align256(w.count + nb * 4);
   w.crow = align256(w.col_ptr + (nb + 1) * 4);
-  w.total = w.crow + (size_t)nnz * 4;
+  w.rcnt = align256(w.crow + (size_t)nnz * 4);
+  w.rent = align256(w.rcnt + nb * 4);
+  w.total = w.rent + (size_t)nnz * 4;
   return w;
 }
 
@@ -592,6 +661,9 @@ extern "C" int dag_attn_backward(const void* q, const void* k, const void* v, co
   csc_count_kernel<<<(unsigned)n_pair, kThreads, 0, stream>>>(row_ptr, col, (int32_t)nb, count);
   csc_scan_kernel<<<1, 1024, 0, stream>>>(count, n_pair, col_ptr);
   csc_fill_kernel<<<(unsigned)n_pair, kThreads, 0, stream>>>(row_ptr, col, kind, (int32_t)nb, col_ptr, crow);
+  int32_t* rcnt = reinterpret_cast<int32_t*>(ws + w.rcnt);
+  int32_t* rent = reinterpret_cast<int32_t*>(ws + w.rent);
+  row_pack_kernel<<<(unsigned)nb, 64, 0, stream>>>(row_ptr, col, kind, (int32_t)nb, rent, rcnt);
   BwdParams p;
   p.qrec = ws + w.qrec;
   p.krec = ws + w.krec;
@@ -610,9 +682,9 @@ extern "C" int dag_attn_backward(const void* q, const void* k, const void* v, co
   p.nb = (int32_t)nb;
   p.scale = sm_scale;
   p.c2 = sm_scale * 1.4426950408889634f;
-  dkdv_kernel<<<dim3(n_kv_heads, (unsigned)n_pair), kDkdvThreads, 0, stream>>>(p);
+  dkdv_kernel<<<dim3(n_kv_heads, (unsigned)n_pair), kDkdvThreads, 0, stream>>>(p, p.crow);
   const int hw = p.G % kHeadsPerWg == 0 ? kHeadsPerWg : (p.G % 2 == 0 ? 2 : 1);
-  dq_kernel<<<dim3(n_q_heads / hw, (unsigned)nb), kDqThreads, 0, stream>>>(p, hw);
+  dq_kernel<<<dim3(n_q_heads / hw, (unsigned)nb), kDqThreads, 0, stream>>>(p, hw, rent, rcnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill backward: ") + hipGetErrorString(e));
   return KV_OK;

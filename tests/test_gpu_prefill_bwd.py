@@ -93,6 +93,43 @@ def test_dag_many_edges():
     _full_check(pi, 66, "backward DAG with 10 edges")
 
 
+def test_skipped_columns_change_nothing():
+    # entries whose column is outside [0, nb) are skipped: the same mask with such entries
+    # added at the ends of some rows (kept ascending, some marked diagonal) gives the same
+    # gradients, bit for bit
+    import torch
+    import fork_attention_decode_amd as fa
+    from types import SimpleNamespace
+    pi = W.prefill_inputs(prefix=192, branches=3, branch_len=[128, 256, 100], n_edges=3, edge_len=64, hq=8,
+                          hkv=2, seed=68)
+    dob = _dout(pi, 69)
+    mask = fa.DagMask(pi.segments, pi.edges, pi.T, pi.block)
+    q, k, v, do = (to_torch(x, "bf16") for x in (pi.q, pi.k, pi.v, dob))
+    out, lse = fa.prefill(q, k, v, mask, pi.sm_scale)
+    ref = fa.prefill_backward(q, k, v, out, do, lse, mask, pi.sm_scale)
+    row_ptr, col, kind = mask.host
+    nb = len(row_ptr) - 1
+    rp, cols, kinds = [0], [], []
+    for r in range(nb):
+        c, kd = list(col[row_ptr[r]:row_ptr[r + 1]]), list(kind[row_ptr[r]:row_ptr[r + 1]])
+        if r % 2 == 0:
+            c, kd = [-1 - r] + c, [1] + kd
+        if r % 3 == 0:
+            c, kd = c + [nb, nb + 7], kd + [0, 1]
+        cols += c
+        kinds += kd
+        rp.append(len(cols))
+    print(f"[case] skipped columns: nb={nb}, nnz {mask.nnz} -> {len(cols)}", flush=True)
+    padded = SimpleNamespace(T=mask.T, block=mask.block, nnz=len(cols),
+                             row_ptr=torch.tensor(rp, dtype=torch.int32, device="cuda"),
+                             col=torch.tensor(cols, dtype=torch.int32, device="cuda"),
+                             kind=torch.tensor(kinds, dtype=torch.uint8, device="cuda"))
+    got = fa.prefill_backward(q, k, v, out, do, lse, padded, pi.sm_scale)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(a, b), f"{name} differs with skipped entries"
+
+
 def test_packed_dag_full_size():
     """81,920 tokens, 32 / 8 heads: sampled dq rows and last-branch keys against the
     oracle, and the two sums over all keys."""
