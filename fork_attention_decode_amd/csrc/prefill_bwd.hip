@@ -394,7 +394,21 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p, const u
             dp[kt][tt] = mfma(da, vf[kt][f], dp[kt][tt]);
           }
         }
-      // s[kt][tt][i]: query 16 (2 qh + tt) + 4 (lane / 16) + i, key key0 + 16 kt
+      // s[kt][tt][i]: query 16 (2 qh + tt) + 4 (lane / 16) + i, key key0 + 16 kt.  Hidden
+      // scores become -inf (P = 0) behind a wave-uniform branch: only a diagonal block and
+      // the last block (keys >= T) hide any.  A row that takes no part has lse2 = +inf, so
+      // its P is 0 as well.
+      if (diag || kb == p.nb - 1) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key_tok = key0 + 16 * kt, q_tok = qb * kB + 16 * (2 * qh + tt) + 4 * (lane >> 4) + i;
+              if (key_tok >= p.T || (diag && key_tok > q_tok)) s[kt][tt][i] = -INFINITY;
+            }
+      }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int q0 = 16 * (2 * qh + tt) + 4 * (lane >> 4);
@@ -404,9 +418,7 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p, const u
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key_tok = key0 + 16 * kt;
-            const bool vis = key_tok < p.T && (!diag || key_tok <= qb * kB + q0 + i);
-            const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][tt][i], p.c2, -l4[i])) : 0.f;
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][tt][i], p.c2, -l4[i]));
             s[kt][tt][i] = pr;
             dp[kt][tt][i] = pr * (dp[kt][tt][i] - d4[i]);
           }
@@ -546,16 +558,26 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw, con
         }
       }
     }
-    // s[u][t][i]: key 16 t + 4 (lane / 16) + i, query lane % 16 of tile u
+    // s[u][t][i]: key 16 t + 4 (lane / 16) + i, query lane % 16 of tile u.  Hidden scores
+    // become -inf (P = 0) behind a wave-uniform branch, as in dkdv_kernel.
+    if (diag || kb == p.nb - 1) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb * kB + 16 * t + 4 * (lane >> 4) + i;
+            if (key >= p.T || (diag && key > q_tok[u])) s[u][t][i] = -INFINITY;
+          }
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = kb * kB + 16 * t + 4 * (lane >> 4) + i;
-          const bool vis = key < p.T && (!diag || key <= q_tok[u]);
-          const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][i], p.c2, -lq[u])) : 0.f;
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][t][i], p.c2, -lq[u]));
           dp[u][t][i] = pr * (dp[u][t][i] - dq_d[u]);
         }
 #pragma unroll
