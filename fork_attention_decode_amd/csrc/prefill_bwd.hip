@@ -10,12 +10,13 @@
 //
 // Mapping onto CDNA4 (v_mfma_f32_16x16x32_bf16 throughout):
 //   * prep passes write, per (64-query block, query head), the Q and dO blocks in operand
-//     order (OPO: 16 rows x 8 dims per lane, one 1 KiB wave read per fragment), the same
-//     blocks transposed for use as the B operand of a product that sums over queries
-//     (TP), the log2 normalisers and D; and per (64-key block, KV head) K and V in OPO
-//     and K transposed.  The TP order pairs query (or key) 4 k + r of two 16-row tiles
-//     with the lanes and registers where an accumulator tile holds them, so P and dS
-//     feed the next products straight from the accumulators, with no shuffles;
+//     order (OPO: 16 rows x 8 dims per lane, one 1 KiB wave read per fragment), the log2
+//     normalisers and D; and per (64-key block, KV head) K and V in OPO.  Where a block is
+//     the B operand of a product that sums over its rows (Q, dO for dK, dV; K for dQ) the
+//     kernels read it from the same image with the LDS transpose load, in an order (TP)
+//     that pairs row 4 k + r of two 16-row tiles with the lanes and registers where an
+//     accumulator tile holds them, so P and dS feed the next products straight from the
+//     accumulators, with no shuffles;
 //   * dkdv_kernel: one workgroup per (two 64-key blocks, KV head), 8 waves, wave = 32 keys
 //     (K and V fragments held in registers) x one 32-row half of every query block; it
 //     walks the union of the two blocks' columns of the mask (a CSC over column pairs
@@ -52,8 +53,8 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kB = 64;                     // block edge (tokens)
 constexpr int kD = 128;                    // head dim
 constexpr int kImg = kB * kD * 2;          // bytes of one 64 x 128 bf16 image (1024 units of 16 B)
-constexpr int kQRec = 4 * kImg + 2 * kB * 4;  // Q OPO, dO OPO, Q TP, dO TP, lse2[64], D[64]
-constexpr int kKRec = 3 * kImg;            // K OPO, V OPO, K TP
+constexpr int kQRec = 2 * kImg + 2 * kB * 4;  // Q OPO, dO OPO, lse2[64], D[64]
+constexpr int kKRec = 2 * kImg;            // K OPO, V OPO
 constexpr int kThreads = 256;
 constexpr int kQRecL = (kQRec + 1023) / 1024 * 1024;  // an LDS record buffer: whole 1 KiB units
 constexpr unsigned kRowMask = 0xffffffu;   // CSC entry: query block | listed bits << 24 | diagonal bits << 26
@@ -62,12 +63,27 @@ constexpr unsigned kRowMask = 0xffffffu;   // CSC entry: query block | listed bi
 // lane r % 16 + 16 (c8 % 4)
 __device__ __forceinline__ int opo_unit(int r, int c8) { return ((r >> 4) * 4 + (c8 >> 2)) * 64 + (r & 15) + 16 * (c8 & 3); }
 
-// TP position (in elements) of element (r, c): B operand of a product over r (two
-// 32-row steps s) and c (8 tiles n of 16 columns); lane c % 16 + 16 k holds, in order, rows
-// 32 s + 4 k + (0..3) and 32 s + 16 + 4 k + (0..3)
-__device__ __forceinline__ int tp_pos(int r, int c) {
-  const int s = r >> 5, rr = r & 31, k = (rr & 15) >> 2, j = (rr & 3) + 4 * (rr >> 4);
-  return (((c >> 4) * 2 + s) * 64 + (c & 15) + 16 * k) * 8 + j;
+// The B operand of a product over the rows r of a 64 x 128 OPO image (two 32-row steps s,
+// eight 16-column tiles n), in TP order: lane c % 16 + 16 k holds, in order, rows
+// 32 s + 4 k + (0..3) and 32 s + 16 + 4 k + (0..3) of column 16 n + c % 16 -- the rows where
+// two 16-row accumulator tiles hold the other operand, so P and dS feed the product
+// straight from the accumulators.  Read with the LDS transpose load (ds_read_b64_tr_b16):
+// within each 16-lane group, lane j receives element j % 4 of what lanes 4 e + j / 4 of the
+// group loaded (e = 0..3), so lane 4 e + c of group k loads 8 bytes of row 32 s + 4 k + e,
+// columns 16 n + 4 c .. + 3; every instruction reads 512 contiguous bytes of the image.
+__device__ __forceinline__ int tp_lane_off(int lane) {
+  const int k = lane >> 4, e = (lane & 15) >> 2, c = lane & 3;
+  return ((4 * k + e) + 16 * (c >> 1)) * 16 + 8 * (c & 1);
+}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 tp_frag(const char* img, int s, int n, int lane_off) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const char* a = img + (8 * s + (n >> 1)) * 1024 + 512 * (n & 1) + lane_off;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + 4 * 1024));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 struct QPrep {
@@ -81,12 +97,11 @@ struct QPrep {
 
 // grid (Hq, n_blocks): the record of (query block, head)
 __global__ __launch_bounds__(kThreads) void q_prep_kernel(QPrep p) {
-  __shared__ __attribute__((aligned(16))) bf16_t tp[2][kB * kD];
   const int h = blockIdx.x, qb = blockIdx.y, tid = threadIdx.x;
   char* rec = p.qrec + ((size_t)qb * p.hq + h) * kQRec;
   i32x4* q_opo = reinterpret_cast<i32x4*>(rec);
   i32x4* do_opo = reinterpret_cast<i32x4*>(rec + kImg);
-  float* lse2 = reinterpret_cast<float*>(rec + 4 * kImg);
+  float* lse2 = reinterpret_cast<float*>(rec + 2 * kImg);
   float* dd = lse2 + kB;
   for (int u = tid; u < kB * 16; u += kThreads) {  // 16 units per row; 16 consecutive threads share a row
     const int r = u >> 4, c8 = u & 15;
@@ -104,11 +119,7 @@ __global__ __launch_bounds__(kThreads) void q_prep_kernel(QPrep p) {
                  oe = __builtin_bit_cast(bf16x8, ov);
     float dot = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      tp[0][tp_pos(r, 8 * c8 + e)] = qe[e];
-      tp[1][tp_pos(r, 8 * c8 + e)] = de[e];
-      dot = __builtin_fmaf((float)de[e], (float)oe[e], dot);
-    }
+    for (int e = 0; e < 8; ++e) dot = __builtin_fmaf((float)de[e], (float)oe[e], dot);
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) dot += __shfl_xor(dot, off);
     if (c8 == 0) {
@@ -121,19 +132,11 @@ __global__ __launch_bounds__(kThreads) void q_prep_kernel(QPrep p) {
       lse2[r] = l2;
     }
   }
-  __syncthreads();
-  i32x4* q_tp = reinterpret_cast<i32x4*>(rec + 2 * kImg);
-  i32x4* do_tp = reinterpret_cast<i32x4*>(rec + 3 * kImg);
-  for (int u = tid; u < kB * 16; u += kThreads) {
-    q_tp[u] = reinterpret_cast<const i32x4*>(tp[0])[u];
-    do_tp[u] = reinterpret_cast<const i32x4*>(tp[1])[u];
-  }
 }
 
-// grid (Hkv, n_blocks): K OPO, V OPO, K TP of (key block, KV head)
+// grid (Hkv, n_blocks): K OPO, V OPO of (key block, KV head)
 __global__ __launch_bounds__(kThreads) void k_prep_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                           char* __restrict__ krec, int32_t T, int32_t hkv) {
-  __shared__ __attribute__((aligned(16))) bf16_t tp[kB * kD];
   const int g = blockIdx.x, kb = blockIdx.y, tid = threadIdx.x;
   char* rec = krec + ((size_t)kb * hkv + g) * kKRec;
   i32x4* k_opo = reinterpret_cast<i32x4*>(rec);
@@ -149,13 +152,7 @@ __global__ __launch_bounds__(kThreads) void k_prep_kernel(const bf16_t* __restri
     }
     k_opo[opo_unit(r, c8)] = kv;
     v_opo[opo_unit(r, c8)] = vv;
-    const bf16x8 ke = __builtin_bit_cast(bf16x8, kv);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tp[tp_pos(r, 8 * c8 + e)] = ke[e];
   }
-  __syncthreads();
-  i32x4* k_tp = reinterpret_cast<i32x4*>(rec + 2 * kImg);
-  for (int u = tid; u < kB * 16; u += kThreads) k_tp[u] = reinterpret_cast<const i32x4*>(tp)[u];
 }
 
 // The mask's transpose over pairs of key-block columns, query blocks ascending within a
@@ -315,8 +312,12 @@ constexpr int kDqThreads = 512;
 // end through LDS.  The workgroup walks the union of the two columns; a wave whose column
 // lacks the query block skips it.
 __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p, const uint32_t* __restrict__ crow) {
-  __shared__ __attribute__((aligned(16))) char rec[2][kQRecL];
+  // two record buffers; at the end the same LDS holds the dK, dV halves being added
+  constexpr int kLds = 2 * kQRecL > 4 * 2 * 2 * 8 * 4 * 64 * 4 ? 2 * kQRecL : 4 * 2 * 2 * 8 * 4 * 64 * 4;
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
+  auto rec = [&](int i) { return lds + i * kQRecL; };
   const int g = blockIdx.x, lane = threadIdx.x & 63;
+  const int tpo = tp_lane_off(lane);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kq = w & 3, qh = w >> 2;              // 32-key group of the 128, query half
   const int kbi = kq >> 1;                        // key block within the workgroup
@@ -363,18 +364,18 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p, const u
                                                  lane * 16, j * 1024, 0, 0);
     }
   };
-  if (n_st > 0) issue(0, rec[0]);
+  if (n_st > 0) issue(0, rec(0));
   wait_vmcnt0();
   __syncthreads();
   for (int st = 0; st < n_st; ++st) {
     const int cur = st & 1;
-    if (st + 1 < n_st) issue(st + 1, rec[cur ^ 1]);
+    if (st + 1 < n_st) issue(st + 1, rec(cur ^ 1));
     const uint32_t ent = ent_of(st);
     const int qb = (int)(ent & kRowMask);
     if (live && ((ent >> (24 + kbi)) & 1u)) {
       const bool diag = (ent >> (26 + kbi)) & 1u;
-      const char* r = rec[cur];
-      const float* lse2 = reinterpret_cast<const float*>(r + 4 * kImg);
+      const char* r = rec(cur);
+      const float* lse2 = reinterpret_cast<const float*>(r + 2 * kImg);
       const float* dd = lse2 + kB;
       f32x4 s[2][2], dp[2][2];  // [kt][query tile of this half]
 #pragma unroll
@@ -431,9 +432,8 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p, const u
       }
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const int u = ((n * 2 + qh) * 64 + lane) * 16;
-        const bf16x8 dot = *reinterpret_cast<const bf16x8*>(r + 3 * kImg + u);
-        const bf16x8 qt = *reinterpret_cast<const bf16x8*>(r + 2 * kImg + u);
+        const bf16x8 dot = tp_frag(r + kImg, qh, n, tpo);
+        const bf16x8 qt = tp_frag(r, qh, n, tpo);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           dv[kt][n] = mfma(ap[kt], dot, dv[kt][n]);
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p, const u
     __syncthreads();  // stage st + 1 is in place; every wave is done with stage st
   }
   // waves 4-7 hand their query half's sums to waves 0-3 through the (now free) records
-  float* xr = reinterpret_cast<float*>(&rec[0][0]) + (size_t)kq * (2 * 2 * 8 * 4 * 64);
+  float* xr = reinterpret_cast<float*>(lds) + (size_t)kq * (2 * 2 * 8 * 4 * 64);
   if (qh == 1) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -486,6 +486,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw, con
                                                         const int32_t* __restrict__ rcnt) {
   __shared__ __attribute__((aligned(16))) char rec[2][kKRec];
   const int qb = blockIdx.y, lane = threadIdx.x & 63;
+  const int tpo = tp_lane_off(lane);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool active = (w >> 1) < hw;
   const int h = blockIdx.x * hw + (active ? w >> 1 : 0), qt0 = 2 * (w & 1);
@@ -502,8 +503,8 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw, con
       qf[u][f] = *reinterpret_cast<const bf16x8*>(qrec + ((qt * 4 + f) * 64 + lane) * 16);
       df[u][f] = *reinterpret_cast<const bf16x8*>(qrec + kImg + ((qt * 4 + f) * 64 + lane) * 16);
     }
-    lq[u] = reinterpret_cast<const float*>(qrec + 4 * kImg)[qt * 16 + (lane & 15)];
-    dq_d[u] = reinterpret_cast<const float*>(qrec + 4 * kImg)[kB + qt * 16 + (lane & 15)];
+    lq[u] = reinterpret_cast<const float*>(qrec + 2 * kImg)[qt * 16 + (lane & 15)];
+    dq_d[u] = reinterpret_cast<const float*>(qrec + 2 * kImg)[kB + qt * 16 + (lane & 15)];
     q_tok[u] = qb * kB + qt * 16 + (lane & 15);
   }
   f32x4 dq[2][8];
@@ -587,7 +588,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw, con
       for (int u = 0; u < 2; ++u) ads[u] = pack_pair(dp[u][2 * h2], dp[u][2 * h2 + 1]);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const bf16x8 kt = *reinterpret_cast<const bf16x8*>(r + 2 * kImg + ((n * 2 + h2) * 64 + lane) * 16);
+        const bf16x8 kt = tp_frag(r, h2, n, tpo);
 #pragma unroll
         for (int u = 0; u < 2; ++u) dq[u][n] = mfma(ads[u], kt, dq[u][n]);
       }

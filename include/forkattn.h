@@ -390,8 +390,8 @@ int kv_causal_attend(kv_pool_t* pool, kv_seq_t seq, int64_t n, int32_t n_q_heads
  *   fp32 [T][Hkv][d]; every element is written (keys no query sees get 0).
  *   row_ptr / col / kind: DEVICE CSR as for the forward (entries whose column is
  *   outside [0, nb) are skipped).  workspace: DEVICE, at least
- *   dag_attn_backward_workspace_size() bytes (per 64-token block and query head a 66,048 B
- *   record of Q / dout images, per block and KV head a 49,152 B record of K / V images,
+ *   dag_attn_backward_workspace_size() bytes (per 64-token block and query head a 33,280 B
+ *   record of Q / dout images, per block and KV head a 32,768 B record of K / V images,
  *   the mask's transpose and its rows' in-range entries).
  * Errors as for dag_attn_prefill (d = 128, block = 64).  Stream-ordered. */
 int dag_attn_backward_workspace_size(int32_t T, int32_t n_q_heads, int32_t n_kv_heads,
