@@ -48,7 +48,8 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxScoreRows = 256;  // representative queries x query heads per KV head
-constexpr int kGroup = 4;           // chunks a wave takes at once
+constexpr int kWaves = 4;           // waves per scoring workgroup = pages per ring slot
+constexpr int kSlots = 4;           // ring slots (3 in flight while one computes)
 constexpr int kChunksPerWg = 128;
 constexpr float kEmpty = -1e30f;    // running max of an empty (max, sum) state
 
@@ -64,23 +65,6 @@ struct ScoreParams {
   float c2;  // sm_scale * log2(e)
 };
 
-// stage the representative queries of KV head h in A-operand order: unit (row r, f, g)
-// = Q[r][32 f + 8 g .. + 8] at lane r % 16 + 16 g of tile r / 16; rows past R are zero
-template <int D>
-__device__ __forceinline__ void stage_q(const ScoreParams& p, int h, int n_tiles, int row0, char* qa) {
-  constexpr int NF = D / 32;
-  const int R = p.n_rep * p.G;
-  for (int u = threadIdx.x; u < n_tiles * 16 * NF * 4; u += blockDim.x) {
-    const int g = u & 3, f = (u >> 2) % NF, r = (u >> 2) / NF;
-    i32x4 val = {0, 0, 0, 0};
-    if (row0 + r < R) {
-      const int rep = (row0 + r) / p.G, qh = h * p.G + (row0 + r) % p.G;
-      val = *reinterpret_cast<const i32x4*>(p.q + ((size_t)rep * p.hq + qh) * D + 32 * f + 8 * g);
-    }
-    *reinterpret_cast<i32x4*>(qa + (((r >> 4) * NF + f) * 64 + (r & 15) + 16 * g) * 16) = val;
-  }
-}
-
 // (m, l) <- the log-sum-exp union of (m, l) and (mo, lo); empty states are (kEmpty, 0)
 __device__ __forceinline__ void lse_combine(float& m, float& l, float mo, float lo) {
   const float mn = fmaxf(m, mo);
@@ -88,110 +72,134 @@ __device__ __forceinline__ void lse_combine(float& m, float& l, float mo, float 
   m = mn;
 }
 
-// K fragments of the P chunks c .. c + P - 1 of KV head h (lane t + 16 g holds
-// K[t][32 f + 8 g .. + 8]); ch is the workgroup's chunk list in LDS, indexed from its
-// first chunk.  Chunks at or past n report an empty slot range and load chunk n - 1
-// again (an L2 hit), so the loads stay unconditional.
-template <int D, int P, bool NT>
-__device__ __forceinline__ void load_group(const ScoreParams& p, const int* ch, int h, int c, int n, int lane,
-                                           bf16x8 (&kf)[P][D / 32], int (&lohi)[P]) {
-#pragma unroll
-  for (int pp = 0; pp < P; ++pp) {
-    const int cc = min(c + pp, n - 1);
-    lohi[pp] = c + pp < n ? ch[2 * cc + 1] : 0;
-    const bf16_t* blk = p.k_pages + ((size_t)h * p.pool_pages + ch[2 * cc]) * 16 * D;
-#pragma unroll
-    for (int f = 0; f < D / 32; ++f)
-      kf[pp][f] = __builtin_bit_cast(bf16x8, NT ? __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(blk + (f * 64 + lane) * 8))
-                                                : *reinterpret_cast<const i32x4*>(blk + (f * 64 + lane) * 8));
-  }
+// s_waitcnt vmcnt(N), the other counters left free (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// S tiles of row tile T against the P chunks: keys as A (acc[pp][i] = key 4 (lane / 16) + i,
-// row 16 T + lane % 16) or keys as B (acc[pp][i] = row 16 T + 4 (lane / 16) + i, key
-// lane % 16)
-template <int D, int P, bool KeysA>
-__device__ __forceinline__ void s_tile(const char* qa, int T, int lane, const bf16x8 (&kf)[P][D / 32],
-                                       f32x4 (&acc)[P]) {
-  constexpr int NF = D / 32;
-#pragma unroll
-  for (int pp = 0; pp < P; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const bf16x8 q = *reinterpret_cast<const bf16x8*>(qa + ((T * NF + f) * 64 + lane) * 16);
-#pragma unroll
-    for (int pp = 0; pp < P; ++pp)
-      acc[pp] = KeysA ? __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[pp][f], q, acc[pp], 0, 0, 0)
-                      : __builtin_amdgcn_mfma_f32_16x16x32_bf16(q, kf[pp][f], acc[pp], 0, 0, 0);
-  }
-}
+template <int D>
+constexpr int kPageBytes = 16 * D * 2;  // one page's K block
 
-// all RT row tiles of one group: the MFMAs of tile T + 1 are issued beside the vector
-// work of tile T (one wave keeps both units busy), one tile step per scheduling region
-template <int D, int RT, int P, bool KeysA, class F>
-__device__ __forceinline__ void group_tiles(const char* qa, int lane, const bf16x8 (&kf)[P][D / 32], F&& valu) {
-  f32x4 acc[2][P];
-  s_tile<D, P, KeysA>(qa, 0, lane, kf, acc[0]);
-#pragma unroll
-  for (int T = 0; T < RT; ++T) {
-    if (T + 1 < RT) s_tile<D, P, KeysA>(qa, T + 1, lane, kf, acc[(T + 1) & 1]);
-    valu(T, acc[T & 1]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// a wave's groups c0, c0 + 4 P, ... below n (indices into the LDS chunk list)
-template <int D, int P, bool NT, class F>
-__device__ __forceinline__ void for_groups(const ScoreParams& p, const int* ch, int h, int c0, int n, int lane,
-                                           F&& body) {
-  for (int c = c0; c < n; c += 4 * P) {
-    bf16x8 kf[P][D / 32];
-    int lohi[P];
-    load_group<D, P, NT>(p, ch, h, c, n, lane, kf, lohi);
-    body(c, kf, lohi);
-  }
-}
+// A workgroup barrier without the fence of __syncthreads (which would also wait for the
+// ring copies in flight); the LDS writes before it (the key sums) are waited for here.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // the workgroup's chunks C0 .. C1 - 1 into LDS
 __device__ __forceinline__ void stage_chunks(const ScoreParams& p, int C0, int C1, int* ch) {
   for (int i = threadIdx.x; i < 2 * (C1 - C0); i += blockDim.x) ch[i] = p.chunks[2 * C0 + i];
 }
 
-// pass 1: grid (nx, hkv); RT 16-row tiles cover the head's rows row0 .. row0 + 16 RT.
-// The keys are the MFMA's A operand here (the pool's K block is laid out for either
-// side), so each lane holds 4 keys of one row per tile and keeps one (max, sum) per
-// tile.  Each wave takes groups of kGroup consecutive chunks: every Q fragment read
-// from LDS feeds kGroup MFMAs.
+// The K blocks stream through a ring of kSlots slots in LDS, kWaves pages per slot (wave w
+// copies page w of each slot with buffer loads that write LDS, issued kSlots - 1 slots
+// ahead; a slot past the end reloads the last chunk into a slot nobody reads, so every
+// wave always has the same number of loads in flight).  Every wave then computes on all
+// the slot's pages for its own row tiles: each K fragment read from LDS feeds TW MFMAs.
+template <int D>
+__device__ __forceinline__ void ring_issue(const ScoreParams& p, const int* ch, int h, int j, int n, int wave,
+                                           int lane, char* ring) {
+  constexpr int LPW = kPageBytes<D> / 1024;
+  const int c = min(kWaves * j + wave, n - 1);
+  const int page = __builtin_amdgcn_readfirstlane(ch[2 * c]);
+  const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.k_pages + ((size_t)h * p.pool_pages + page) * 16 * D), 0, kPageBytes<D>, 0x00020000);
+  char* dst = ring + ((j % kSlots) * kWaves + wave) * kPageBytes<D>;
+#pragma unroll
+  for (int i = 0; i < LPW; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(dst + i * 1024), 16,
+                                             lane * 16, i * 1024, 0, 0);
+}
+
+// K fragments of the kWaves pages of ring slot j (lane t + 16 g holds K[t][32 f + 8 g .. + 8])
+template <int D>
+__device__ __forceinline__ void ring_frags(const char* ring, int j, int lane, bf16x8 (&kf)[kWaves][D / 32]) {
+#pragma unroll
+  for (int pp = 0; pp < kWaves; ++pp)
+#pragma unroll
+    for (int f = 0; f < D / 32; ++f)
+      kf[pp][f] = *reinterpret_cast<const bf16x8*>(ring + ((j % kSlots) * kWaves + pp) * kPageBytes<D> +
+                                                   (f * 64 + lane) * 16);
+}
+
+// this wave's query fragments: row tile T, lane r % 16 + 16 g holds Q[row 16 T + r][32 f +
+// 8 g .. + 8] (the A and B operand orders agree); rows past R are zero
+template <int D, int TW>
+__device__ __forceinline__ void load_q(const ScoreParams& p, int h, int row0, int T0, int lane,
+                                       bf16x8 (&qf)[TW][D / 32]) {
+  const int R = p.n_rep * p.G;
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    const int row = row0 + 16 * (T0 + t) + (lane & 15);
+    const int rep = row / p.G, qh = h * p.G + row % p.G;
+#pragma unroll
+    for (int f = 0; f < D / 32; ++f) {
+      i32x4 v = {0, 0, 0, 0};
+      if (row < R) v = *reinterpret_cast<const i32x4*>(p.q + ((size_t)rep * p.hq + qh) * D + 32 * f + 8 * (lane >> 4));
+      qf[t][f] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+}
+
+// pass 1: grid (nx, hkv), kWaves waves; RT 16-row tiles cover the head's rows row0 ..
+// row0 + 16 RT, TW per wave (waves past RT / TW only copy).  The keys are the MFMA's A
+// operand here (the pool's K block is laid out for either side), so each lane holds 4 keys
+// of one row per tile and keeps one (max, sum) per tile, rescaled lazily.
 template <int D, int RT>
-__global__ __launch_bounds__(256) void norm_kernel(ScoreParams p, int row0) {
-  constexpr int NF = D / 32, P = kGroup;
+__global__ __launch_bounds__(kWaves * 64) void norm_kernel(ScoreParams p, int row0) {
+  constexpr int NF = D / 32, TW = RT >= kWaves ? RT / kWaves : 1, LPW = kPageBytes<D> / 1024;
   static_assert(RT <= 8, "row tiles per launch");
-  __shared__ __attribute__((aligned(16))) char qa[RT * 16 * D * 2];
-  __shared__ float red[4][2][RT * 16];
-  __shared__ int ch[2 * kChunksPerWg];
+  // one LDS array: with several, the compiler tells their accesses apart and then waits
+  // for every copy in flight before each read of the ring
+  __shared__ __attribute__((aligned(1024))) char lds[kSlots * kWaves * kPageBytes<D> + 8 * kChunksPerWg];
+  char* const ring = lds;
+  int* const ch = reinterpret_cast<int*>(lds + kSlots * kWaves * kPageBytes<D>);
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int C0 = blockIdx.x * kChunksPerWg;
-  const int C1 = min(C0 + kChunksPerWg, p.n_ch);
-  stage_q<D>(p, h, RT, row0, qa);
-  stage_chunks(p, C0, C1, ch);
-  __syncthreads();
-  float m[RT], l[RT];
+  const int n = min(C0 + kChunksPerWg, p.n_ch) - C0;
+  const int n_slots = (n + kWaves - 1) / kWaves;
+  const bool act = wave * TW < RT;
+  stage_chunks(p, C0, C0 + n, ch);
+  bf16x8 qf[TW][NF];
+  load_q<D, TW>(p, h, row0, act ? wave * TW : 0, lane, qf);
+  float m[TW], l[TW];
 #pragma unroll
-  for (int T = 0; T < RT; ++T) m[T] = kEmpty, l[T] = 0.f;
+  for (int t = 0; t < TW; ++t) m[t] = kEmpty, l[t] = 0.f;
   const int key0 = 4 * (lane >> 4);
   const float c2 = p.c2;
-  // cached loads (measured a little faster than non-temporal ones here)
-  for_groups<D, P, false>(p, ch, h, wave * P, C1 - C0, lane, [&](int c, const bf16x8(&kf)[P][NF], const int(&lohi)[P]) {
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSlots - 1; ++j) ring_issue<D>(p, ch, h, j, n, wave, lane, ring);
+  for (int j = 0; j < n_slots; ++j) {
+    wait_vmcnt<(kSlots - 2) * LPW>();  // this wave's page of slot j landed ...
+    ring_barrier();                    // ... and every wave's; slot j - 1 is consumed
+    ring_issue<D>(p, ch, h, j + kSlots - 1, n, wave, lane, ring);
+    if (!act) continue;
+    bf16x8 kf[kWaves][NF];
+    ring_frags<D>(ring, j, lane, kf);
+    int lohi[kWaves];
     bool full = true;
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp) full = full && lohi[pp] == (16 << 8);
-    group_tiles<D, RT, P, true>(qa, lane, kf, [&](int T, f32x4(&acc)[P]) {
-      // acc[pp][i]: key 4 (lane / 16) + i of chunk C0 + c + pp, row 16 T + lane % 16
+    for (int pp = 0; pp < kWaves; ++pp) {
+      const int c = kWaves * j + pp;
+      lohi[pp] = c < n ? ch[2 * c + 1] : 0;  // past the end: an empty slot range
+      full = full && lohi[pp] == (16 << 8);
+    }
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      f32x4 acc[kWaves];
+#pragma unroll
+      for (int pp = 0; pp < kWaves; ++pp) {
+        acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc[pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[pp][f], qf[t][f], acc[pp], 0, 0, 0);
+      }
+      // acc[pp][i]: key 4 (lane / 16) + i of page pp of the slot, row 16 T + lane % 16
       if (!full) {
 #pragma unroll
-        for (int pp = 0; pp < P; ++pp)
+        for (int pp = 0; pp < kWaves; ++pp)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const bool valid = key0 + i >= (lohi[pp] & 0xff) && key0 + i < (lohi[pp] >> 8);
@@ -200,51 +208,44 @@ __global__ __launch_bounds__(256) void norm_kernel(ScoreParams p, int row0) {
       }
       // lazy rescale: the sum is taken against the running max as it stands, and only a
       // lane whose keys reach 2^64 times that (the first keys, against an empty state)
-      // takes the max of the group and rescales
+      // takes the max of the slot and rescales
       float sum = 0.f;
 #pragma unroll
-      for (int pp = 0; pp < P; ++pp)
+      for (int pp = 0; pp < kWaves; ++pp)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[pp][i], c2, -m[T]));
+        for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[pp][i], c2, -m[t]));
       if (sum <= 0x1p64f) {
-        l[T] += sum;
+        l[t] += sum;
       } else {
         float mx = acc[0][0];
 #pragma unroll
-        for (int pp = 0; pp < P; ++pp)
+        for (int pp = 0; pp < kWaves; ++pp)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[pp][i]);
-        const float mn = fmaxf(m[T], mx * c2);
+        const float mn = fmaxf(m[t], mx * c2);
         sum = 0.f;
 #pragma unroll
-        for (int pp = 0; pp < P; ++pp)
+        for (int pp = 0; pp < kWaves; ++pp)
 #pragma unroll
           for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[pp][i], c2, -mn));
-        l[T] = __builtin_fmaf(l[T], __builtin_amdgcn_exp2f(m[T] - mn), sum);
-        m[T] = mn;
+        l[t] = __builtin_fmaf(l[t], __builtin_amdgcn_exp2f(m[t] - mn), sum);
+        m[t] = mn;
       }
-    });
-  });
-  // row 16 T + lane % 16 is held by the 4 lanes lane % 16 + 16 k
-#pragma unroll
-  for (int T = 0; T < RT; ++T) {
-    lse_combine(m[T], l[T], __shfl_xor(m[T], 16), __shfl_xor(l[T], 16));
-    lse_combine(m[T], l[T], __shfl_xor(m[T], 32), __shfl_xor(l[T], 32));
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int T = 0; T < RT; ++T) {
-      red[wave][0][16 * T + lane] = m[T];
-      red[wave][1][16 * T + lane] = l[T];
     }
   }
-  __syncthreads();
-  for (int r = threadIdx.x; r < RT * 16; r += 256) {
-    float M = red[0][0][r], L = red[0][1][r];
-    for (int w = 1; w < 4; ++w) lse_combine(M, L, red[w][0][r], red[w][1][r]);
-    float* dst = p.part + ((size_t)(h * p.RP + row0 + r) * 2) * p.nx + blockIdx.x;
-    dst[0] = M;
-    dst[p.nx] = L;
+  wait_vmcnt<0>();  // no load may land in LDS after the workgroup ends
+  if (!act) return;
+  // row 16 T + lane % 16 is held by the 4 lanes lane % 16 + 16 k, and by no other wave
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    lse_combine(m[t], l[t], __shfl_xor(m[t], 16), __shfl_xor(l[t], 16));
+    lse_combine(m[t], l[t], __shfl_xor(m[t], 32), __shfl_xor(l[t], 32));
+    if (lane < 16) {
+      const int r = 16 * (wave * TW + t) + lane;
+      float* dst = p.part + ((size_t)(h * p.RP + row0 + r) * 2) * p.nx + blockIdx.x;
+      dst[0] = m[t];
+      dst[p.nx] = l[t];
+    }
   }
 }
 
@@ -264,46 +265,81 @@ __global__ __launch_bounds__(256) void norm_merge_kernel(ScoreParams p) {
   }
 }
 
-// pass 2: grid (ceil(n_lp / kChunksPerWg), hkv) over the own pages (the first n_lp
-// chunks); rows of KV head h: r = rep * G + g (query head h * G + g), padded with zero
-// queries and +inf normalisers to RT whole 16-row tiles
+// pass 2: grid (ceil(n_lp / kChunksPerWg), hkv), kWaves waves, over the own pages (the
+// first n_lp chunks); rows of KV head h: r = rep * G + g (query head h * G + g), padded
+// with zero queries and +inf normalisers to RT whole 16-row tiles, TW per wave.  Keys are
+// the B operand (a lane holds one key of 4 rows): the sum over a wave's rows stays in the
+// lane plus two shuffles, and the waves' sums meet in LDS, added one slot later.
 template <int D, int RT>
-__global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
-  constexpr int NF = D / 32, P = kGroup;
-  __shared__ __attribute__((aligned(16))) char qa[RT * 16 * D * 2];  // A fragments [tile][f][lane]
-  __shared__ __attribute__((aligned(16))) float lse2[RT * 16];
-  __shared__ int ch[2 * kChunksPerWg];
+__global__ __launch_bounds__(kWaves * 64) void score_kernel(ScoreParams p) {
+  constexpr int NF = D / 32, TW = RT >= kWaves ? RT / kWaves : 1, LPW = kPageBytes<D> / 1024;
+  constexpr int NA = RT >= kWaves ? kWaves : RT;  // waves with row tiles
+  // one LDS array (as in norm_kernel): ring, chunk list, the waves' key sums [2][kWaves][64]
+  __shared__ __attribute__((aligned(1024))) char lds[kSlots * kWaves * kPageBytes<D> + 8 * kChunksPerWg +
+                                                     2 * kWaves * kWaves * 16 * 4];
+  char* const ring = lds;
+  int* const ch = reinterpret_cast<int*>(lds + kSlots * kWaves * kPageBytes<D>);
+  float* const red = reinterpret_cast<float*>(lds + kSlots * kWaves * kPageBytes<D> + 8 * kChunksPerWg);
   const int h = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int C0 = blockIdx.x * kChunksPerWg;
-  const int C1 = min(C0 + kChunksPerWg, p.n_lp);
-  stage_q<D>(p, h, RT, 0, qa);
-  stage_chunks(p, C0, C1, ch);
-  for (int r = threadIdx.x; r < RT * 16; r += 256) lse2[r] = p.lse2[h * p.RP + r];
-  __syncthreads();
-
+  const int n = min(C0 + kChunksPerWg, p.n_lp) - C0;
+  const int n_slots = (n + kWaves - 1) / kWaves;
+  const bool act = wave < NA;
+  stage_chunks(p, C0, C0 + n, ch);
+  bf16x8 qf[TW][NF];
+  load_q<D, TW>(p, h, 0, act ? wave * TW : 0, lane, qf);
+  f32x4 l4[TW];  // log2 normalisers of rows 16 T + 4 (lane / 16) + i
+#pragma unroll
+  for (int t = 0; t < TW; ++t)
+    l4[t] = *reinterpret_cast<const f32x4*>(p.lse2 + h * p.RP + 16 * ((act ? wave * TW : 0) + t) + 4 * (lane >> 4));
   const float c2 = p.c2;
-  for_groups<D, P, true>(p, ch, h, wave * P, C1 - C0, lane, [&](int c, const bf16x8(&kf)[P][NF], const int(&)[P]) {
-    float s[P];
+  // slot j's key sums (one lane per key of the slot's pages) to the partials
+  auto flush = [&](int j) {
+    float v = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp) s[pp] = 0.f;
-    group_tiles<D, RT, P, false>(qa, lane, kf, [&](int T, f32x4(&acc)[P]) {
-      // acc[pp][i]: row 16 T + 4 (lane / 16) + i, key lane % 16 of own page C0 + c + pp
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + 16 * T + 4 * (lane >> 4));
+    for (int w = 0; w < NA; ++w) v += red[((j & 1) * kWaves + w) * 64 + lane];
+    const int c = kWaves * j + (lane >> 4);
+    const int64_t t = (int64_t)(C0 + c) * 16 + (lane & 15);
+    if (c < n && t < p.n_tok) p.partial[(size_t)h * p.n_tok + t] = v;
+  };
+  __syncthreads();
 #pragma unroll
-      for (int pp = 0; pp < P; ++pp)
+  for (int j = 0; j < kSlots - 1; ++j) ring_issue<D>(p, ch, h, j, n, wave, lane, ring);
+  for (int j = 0; j < n_slots; ++j) {
+    wait_vmcnt<(kSlots - 2) * LPW>();  // this wave's page of slot j landed ...
+    ring_barrier();                    // ... and every wave's; slot j - 1 is consumed
+    ring_issue<D>(p, ch, h, j + kSlots - 1, n, wave, lane, ring);
+    if (wave == 0 && j > 0) flush(j - 1);
+    if (!act) continue;
+    bf16x8 kf[kWaves][NF];
+    ring_frags<D>(ring, j, lane, kf);
+    float s[kWaves];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[pp] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[pp][i], c2, -l4[i]));
-    });
+    for (int pp = 0; pp < kWaves; ++pp) s[pp] = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp) {
+    for (int t = 0; t < TW; ++t) {
+#pragma unroll
+      for (int pp = 0; pp < kWaves; ++pp) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int f = 0; f < NF; ++f) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[t][f], kf[pp][f], acc, 0, 0, 0);
+        // acc[i]: row 16 T + 4 (lane / 16) + i, key lane % 16 of page pp
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[pp] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], c2, -l4[t][i]));
+      }
+    }
+#pragma unroll
+    for (int pp = 0; pp < kWaves; ++pp) {
       float v = s[pp] + __shfl_xor(s[pp], 16);
       v += __shfl_xor(v, 32);
-      const int64_t t = (int64_t)(C0 + c + pp) * 16 + lane;
-      if (lane < 16 && C0 + c + pp < C1 && t < p.n_tok) p.partial[(size_t)h * p.n_tok + t] = v;
+      if (lane < 16) red[((j & 1) * kWaves + wave) * 64 + pp * 16 + lane] = v;
     }
-  });
+  }
+  wait_vmcnt<0>();  // no load may land in LDS after the workgroup ends
+  __syncthreads();
+  if (wave == 0 && n_slots > 0) flush(n_slots - 1);
 }
 
 __global__ __launch_bounds__(256) void score_sum_kernel(const float* __restrict__ partial, float* __restrict__ scores,

@@ -52,9 +52,10 @@ def _scores(sc, seq, n_rep, seed, label):
     return pool, got, ref
 
 
-@pytest.mark.parametrize("n_rep,private", [(1, 37), (8, 300), (32, 1000)])
+@pytest.mark.parametrize("n_rep,private", [(1, 37), (8, 300), (16, 130), (32, 1000)])
 def test_scores_fork(n_rep, private):
-    # a fork over a shared prefix: the fork's own context is prefix + private tokens
+    # a fork over a shared prefix: the fork's own context is prefix + private tokens; 4, 32, 64
+    # and 128 rows per KV head (1, 2, 4 and 8 row tiles)
     sc = W.fork_scenario(prefix=517, branches=2, private=[private, 5], hq=8, hkv=2, d=128, seed=41)
     _, got, ref = _scores(sc, 1, n_rep, 42, f"scores n_rep={n_rep} private={private}")
     assert abs(got.sum() - 1.0) < 1e-2  # no mounts: every softmax sums to 1
