@@ -93,6 +93,23 @@ def test_dag_many_edges():
     _full_check(pi, 66, "backward DAG with 10 edges")
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_random_dag_shapes(seed):
+    # seeded random shapes: prefix, ragged last branch, edges, head counts (G = 1 .. 8); the
+    # key-block pairs, the head pairs of the dK/dV stages and the packed rows of the dQ pass
+    # all see uneven counts
+    rng = np.random.default_rng(1000 + seed)
+    hq, hkv = [(4, 1), (8, 2), (6, 2), (2, 2), (8, 1)][seed]
+    branches = int(rng.integers(1, 5))
+    blen = [64 * int(rng.integers(1, 4)) for _ in range(branches - 1)] + [int(rng.integers(1, 200))]
+    prefix = 64 * int(rng.integers(1, 4))
+    n_edges = int(rng.integers(0, branches * (branches - 1) // 2 + 1))
+    pi = W.prefill_inputs(prefix=prefix, branches=branches, branch_len=blen, n_edges=n_edges, edge_len=64, hq=hq,
+                          hkv=hkv, seed=70 + seed)
+    _full_check(pi, 80 + seed, f"backward random DAG seed={seed} prefix={prefix} branches={blen} "
+                               f"edges={n_edges} Hq={hq} Hkv={hkv}")
+
+
 def test_skipped_columns_change_nothing():
     # entries whose column is outside [0, nb) are skipped: the same mask with such entries
     # added at the ends of some rows (kept ascending, some marked diagonal) gives the same
