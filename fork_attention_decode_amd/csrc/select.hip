@@ -9,16 +9,18 @@
 // score(t) = mean over the n_rep x Hq (representative query, head) pairs of the softmax
 // probability of own token t in that query's attention over the sequence's visible
 // context.  Two passes over the keys, each streaming a page's K block once per KV head
-// and computing S = Q K^T for all of the head's rows (query x head-of-group) on
-// v_mfma_f32_16x16x32_bf16, a wave taking 4 pages at a time and issuing the MFMAs of one
-// 16-row tile beside the exponentials of the tile before:
+// through a ring in LDS (buffer loads that write LDS, several slots ahead) and computing
+// S = Q K^T for all of the head's rows (query x head-of-group) on
+// v_mfma_f32_16x16x32_bf16, each wave taking a share of the row tiles over every page of
+// a slot (its query fragments in registers):
 //   1. norm_kernel (keys as the A operand, so a lane holds 4 keys of one row): every lane
 //      keeps an online (max, sum) per row tile over the visible chunks (own pages, then
-//      mounts), rescaled lazily, reduced over the lanes and waves of the workgroup into
-//      one partial per row; norm_merge_kernel folds the workgroups' partials into each
-//      row's log2 normaliser;
+//      mounts), rescaled lazily, reduced over the lanes into one partial per row and
+//      workgroup; norm_merge_kernel folds the workgroups' partials into each row's log2
+//      normaliser;
 //   2. score_kernel (keys as B, so a lane holds one key of 4 rows): over the own pages,
-//      the sum over rows of exp2(S c2 - lse2) stays in the lane plus two shuffles.
+//      the sum over a wave's rows of exp2(S c2 - lse2) stays in the lane plus two
+//      shuffles, and the waves' sums meet in LDS.
 // Keep selection: radix select of the budget-th largest score on an order-preserving
 // integer image of the floats (4 passes of 8 bits over many workgroups), then ties kept
 // in index order (a slice's ties start after the earlier slices' count of the last
