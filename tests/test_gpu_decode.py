@@ -69,6 +69,30 @@ def test_ragged_fork_bf16(private):
     _check(sc, o, lse, f"ragged fork {private}")
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4, 5])
+def test_random_trees_bf16(seed):
+    # seeded random shapes: forks over a shared prefix (odd seeds: a DAG of threads with
+    # mounts), head counts, and for some seeds a plan for 1 or 3 compute units (long work
+    # items, so chunk slots past 64 are used)
+    rng = np.random.default_rng(2000 + seed)
+    hq, hkv = [(8, 2), (4, 1), (16, 4), (8, 8), (12, 2), (32, 8)][seed]
+    if seed % 2 == 0:
+        branches = int(rng.integers(1, 7))
+        private = [int(x) for x in rng.integers(0, 400, size=branches)]
+        sc = W.fork_scenario(prefix=int(rng.integers(1, 3000)), branches=branches, private=private, hq=hq, hkv=hkv,
+                             d=128, seed=20 + seed)
+    else:
+        threads = int(rng.integers(2, 6))
+        mpt = int(rng.integers(1, threads))
+        private = int(rng.integers(40, 400))
+        sc = W.dag_scenario(root=int(rng.integers(1, 2000)), threads=threads, private=private, mounts_per_thread=mpt,
+                            mount_len=int(rng.integers(1, private + 1)), hq=hq, hkv=hkv, d=128, seed=20 + seed)
+    n_cu = [None, 3, None, 1, None, None][seed]
+    label = f"random tree seed={seed} Hq={hq} Hkv={hkv} n_cu={n_cu}"
+    pool, o, lse = _run(sc, label, n_cu=n_cu)
+    _check(sc, o, lse, label)
+
+
 def test_edge_shapes_bf16():
     """Degenerate and maximal shapes: 64 query heads on one KV head (a work item's full 64
     rows from one reader), a branch with no private token, the root decoding beside its
