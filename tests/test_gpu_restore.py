@@ -87,6 +87,33 @@ def test_single_token_and_fresh_sequence():
     _restore(sc, 2, [300], [0], 98, "fresh sequence, 300 tokens")
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_restore_random_shapes(seed):
+    # seeded random shapes: forks (even seeds) or threads with mounts (odd seeds, page-aligned
+    # or not), head counts, and 1 .. 4 segments of random lengths (restored spans from one
+    # token to several 64-token row groups, own contexts ending anywhere in a page)
+    rng = np.random.default_rng(3000 + seed)
+    hq, hkv = [(8, 2), (4, 1), (16, 4), (8, 8)][seed]
+    if seed % 2 == 0:
+        sc = W.fork_scenario(prefix=int(rng.integers(1, 1500)), branches=2,
+                             private=[int(x) for x in rng.integers(0, 200, size=2)], hq=hq, hkv=hkv, d=128,
+                             seed=60 + seed)
+        seq = 1
+    else:
+        aligned = seed == 3
+        private = 16 * int(rng.integers(3, 12)) if aligned else int(rng.integers(40, 200))
+        sc = W.dag_scenario(root=16 * int(rng.integers(1, 60)) if aligned else int(rng.integers(1, 900)), threads=3,
+                            private=private, mounts_per_thread=2,
+                            mount_len=16 * int(rng.integers(1, private // 16 + 1)) if aligned
+                            else int(rng.integers(1, private + 1)), hq=hq, hkv=hkv, d=128, seed=60 + seed)
+        seq = 2
+    n_seg = int(rng.integers(1, 5))
+    lens = [int(x) for x in rng.integers(1, 120, size=n_seg)]
+    pos = [5000 * (i + 1) + int(rng.integers(0, 1000)) for i in range(n_seg)]
+    sc.n_pages += 64
+    _restore(sc, seq, lens, pos, 70 + seed, f"random restore seed={seed} Hq={hq} Hkv={hkv}")
+
+
 @pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 64)])
 def test_restore_by_decode_rows(dtype, d):
     # pools the tiled prefill does not take (fp32, d = 64) restore as rows of the split-K
