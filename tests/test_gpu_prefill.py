@@ -68,6 +68,23 @@ def test_plain_causal(T):
     _check(pi, o, lse, list(range(T)), f"causal T={T}")
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+def test_random_dag_shapes(seed):
+    # seeded random shapes: prefix, ragged last branch, edges of random length, head
+    # counts (G = 1 .. 8); every row is compared
+    rng = np.random.default_rng(4000 + seed)
+    hq, hkv = [(8, 2), (4, 1), (12, 2), (2, 2), (16, 2)][seed]
+    branches = int(rng.integers(1, 6))
+    blen = [64 * int(rng.integers(1, 5)) for _ in range(branches - 1)] + [int(rng.integers(1, 300))]
+    prefix = 64 * int(rng.integers(1, 5))
+    n_edges = int(rng.integers(0, branches * (branches - 1) // 2 + 1))
+    pi = W.prefill_inputs(prefix=prefix, branches=branches, branch_len=blen, n_edges=n_edges,
+                          edge_len=64 * int(rng.integers(1, 3)), hq=hq, hkv=hkv, seed=40 + seed)
+    label = f"random DAG seed={seed} prefix={prefix} branches={blen} edges={n_edges}"
+    _, o, lse = _run(pi, label)
+    _check(pi, o, lse, list(range(pi.T)), label)
+
+
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (16, 2), (4, 2), (2, 2), (6, 2), (8, 1)])
 def test_small_dag_heads(hq, hkv):
     # G = 4, 8 (two head groups per workgroup set), 2, 1 and 3 (idle waves)
