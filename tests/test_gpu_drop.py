@@ -166,6 +166,32 @@ def test_decode_after_drop(repos):
     print(f"[ok] max-abs {mx:.3g} mean-abs {mn:.3g}; error / model bar: O {wo:.3f}, LSE {wl:.3f}", flush=True)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_random_drops(seed):
+    # seeded random shapes: request count, context length, dropped fraction and span
+    # lengths, repos or not; page contents, tables and counts exact, then a decode
+    import torch
+    rng = np.random.default_rng(5000 + seed)
+    repos = bool(seed % 2)
+    ctx = int(rng.integers(20, 2500))
+    sc = W.drop_scenario(requests=int(rng.integers(1, 4)), ctx=ctx, frac=float(rng.uniform(0.05, 0.9)),
+                         span_min=int(rng.integers(1, 20)), span_max=int(rng.integers(20, 300)), hq=8, hkv=2, d=128,
+                         seed=50 + seed, repos=repos)
+    print(f"[case] random drops seed={seed} ctx={ctx} repos={repos}: "
+          f"{[op[2] for op in sc.ops if op[0] == 'drop']}", flush=True)
+    pool, kept = build_device_pool(sc)
+    ora, okept = _oracle(sc)
+    for a, b in zip(kept, okept):
+        assert np.array_equal(a, b)
+    _check_state(sc, pool, ora, sorted(set(sc.queries)), exact_k=lambda s: not repos)
+    out, lse = pool.decode(sc.queries, to_torch(sc.q, sc.dtype), sc.sm_scale)
+    torch.cuda.synchronize()
+    mx, mn, wo, wl = check_decode_both(out_to_f64(out, "bf16"), lse.double().cpu().numpy(),
+                                       oracle_decode(sc, with_magnitudes=True), 128, "bf16",
+                                       f"decode after random drops seed={seed}", rerotated_keys=repos)
+    print(f"[ok] max-abs {mx:.3g} mean-abs {mn:.3g}; error / model bar: O {wo:.3f}, LSE {wl:.3f}", flush=True)
+
+
 def test_akv_drop_repos_full_size():
     """16 requests x 131,072 tokens, 40 % dropped, repos, decode; the oracle checks two
     sampled requests end to end (page table, sampled pages, decode output)."""
