@@ -18,9 +18,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU forms (v_pk_*_f32) are disabled for every device pass: the kernels
 # use plain fp32 VALU arithmetic only.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-source device flags.  The prefill kernel keeps its matrix-core results in
-# architectural VGPRs (the softmax reads them with VALU instructions); without this the
-# allocator parks them in AGPRs and copies them back every block.
+# Per-source device flags.  The prefill and the key-scoring kernels keep their
+# matrix-core results in architectural VGPRs (the softmax and the exponential sums read
+# them with VALU instructions); without this the allocator parks them in AGPRs and copies
+# them back every block.
 EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "select.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 
