@@ -273,6 +273,29 @@ __global__ __launch_bounds__(64) void row_pack_kernel(const int32_t* __restrict_
 // s_waitcnt vmcnt(0), the other counters left free (gfx9 encoding)
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
 
+// query blocks by descending count of packed entries (ties by index): order[rank] = block,
+// so the dQ pass starts its longest rows first and ends on short ones (the dK/dV pass
+// keeps the natural column order: its first columns, the prefix's, are its longest)
+__global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ cost, int32_t* __restrict__ order,
+                                                   int nb) {
+  __shared__ int tile[256];
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  const int cr = r < nb ? cost[r] : 0;
+  int rank = 0;
+  for (int base = 0; base < nb; base += 256) {
+    const int t = base + threadIdx.x;
+    __syncthreads();
+    tile[threadIdx.x] = t < nb ? cost[t] : -1;
+    __syncthreads();
+    const int m = nb - base < 256 ? nb - base : 256;
+    for (int i = 0; i < m; ++i) {
+      const int ci = tile[i];
+      rank += (ci > cr) || (ci == cr && base + i < r);
+    }
+  }
+  if (r < nb) order[rank] = r;
+}
+
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -478,14 +501,15 @@ __global__ __launch_bounds__(kDkdvThreads) void dkdv_kernel(BwdParams p, const u
 }
 
 // grid (Hq / hw, n_blocks), hw = 4, 2 or 1 query heads of one KV head per workgroup (the
-// largest that divides G): dQ of a 64-query block; wave w takes queries 32 (w % 2) .. + 31
+// largest that divides G): dQ of query block order[blockIdx.y] (longest rows first); wave w takes queries 32 (w % 2) .. + 31
 // (two 16-query tiles) of head blockIdx.x hw + w / 2 (waves past the hw heads only help
 // stage).  Each key block's record staged in LDS serves the workgroup's heads, and each
 // K / V fragment read from LDS feeds the products of both tiles.
 __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw, const int32_t* __restrict__ rent,
-                                                        const int32_t* __restrict__ rcnt) {
+                                                        const int32_t* __restrict__ rcnt,
+                                                        const int32_t* __restrict__ order) {
   __shared__ __attribute__((aligned(16))) char rec[2][kKRec];
-  const int qb = blockIdx.y, lane = threadIdx.x & 63;
+  const int qb = order[blockIdx.y], lane = threadIdx.x & 63;
   const int tpo = tp_lane_off(lane);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool active = (w >> 1) < hw;
@@ -617,7 +641,7 @@ __global__ __launch_bounds__(kDqThreads) void dq_kernel(BwdParams p, int hw, con
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-  size_t qrec, krec, count, col_ptr, crow, rcnt, rent, total;
+  size_t qrec, krec, count, col_ptr, crow, rcnt, rent, order, total;
 };
 BwdLayout bwd_layout(int32_t T, int32_t hq, int32_t hkv, int64_t nnz) {
   const size_t nb = (size_t)(T + kB - 1) / kB;
@@ -629,7 +653,8 @@ BwdLayout bwd_layout(int32_t T, int32_t hq, int32_t hkv, int64_t nnz) {
   w.crow = align256(w.col_ptr + (nb + 1) * 4);
   w.rcnt = align256(w.crow + (size_t)nnz * 4);
   w.rent = align256(w.rcnt + nb * 4);
-  w.total = w.rent + (size_t)nnz * 4;
+  w.order = align256(w.rent + (size_t)nnz * 4);
+  w.total = w.order + nb * 4;
   return w;
 }
 
@@ -687,6 +712,8 @@ extern "C" int dag_attn_backward(const void* q, const void* k, const void* v, co
   int32_t* rcnt = reinterpret_cast<int32_t*>(ws + w.rcnt);
   int32_t* rent = reinterpret_cast<int32_t*>(ws + w.rent);
   row_pack_kernel<<<(unsigned)nb, 64, 0, stream>>>(row_ptr, col, kind, (int32_t)nb, rent, rcnt);
+  int32_t* order = reinterpret_cast<int32_t*>(ws + w.order);
+  rank_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, stream>>>(rcnt, order, (int32_t)nb);
   BwdParams p;
   p.qrec = ws + w.qrec;
   p.krec = ws + w.krec;
@@ -707,7 +734,7 @@ extern "C" int dag_attn_backward(const void* q, const void* k, const void* v, co
   p.c2 = sm_scale * 1.4426950408889634f;
   dkdv_kernel<<<dim3(n_kv_heads, (unsigned)n_pair), kDkdvThreads, 0, stream>>>(p, p.crow);
   const int hw = p.G % kHeadsPerWg == 0 ? kHeadsPerWg : (p.G % 2 == 0 ? 2 : 1);
-  dq_kernel<<<dim3(n_q_heads / hw, (unsigned)nb), kDqThreads, 0, stream>>>(p, hw, rent, rcnt);
+  dq_kernel<<<dim3(n_q_heads / hw, (unsigned)nb), kDqThreads, 0, stream>>>(p, hw, rent, rcnt, order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fa_set_err(nullptr, KV_ERR_HIP, std::string("prefill backward: ") + hipGetErrorString(e));
   return KV_OK;

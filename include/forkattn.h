@@ -392,7 +392,7 @@ int kv_causal_attend(kv_pool_t* pool, kv_seq_t seq, int64_t n, int32_t n_q_heads
  *   outside [0, nb) are skipped).  workspace: DEVICE, at least
  *   dag_attn_backward_workspace_size() bytes (per 64-token block and query head a 33,280 B
  *   record of Q / dout images, per block and KV head a 32,768 B record of K / V images,
- *   the mask's transpose and its rows' in-range entries).
+ *   the mask's transpose, its rows' in-range entries and their order).
  * Errors as for dag_attn_prefill (d = 128, block = 64).  Stream-ordered. */
 int dag_attn_backward_workspace_size(int32_t T, int32_t n_q_heads, int32_t n_kv_heads,
                                      int32_t block, int64_t nnz, size_t* bytes);
